@@ -1,0 +1,159 @@
+"""Test-case construction shared by the oracle pins and the GPU parity tests.
+
+Nothing here computes an expected value: these helpers only assemble inputs
+(seeded draws from ``sub_bit_vq_amd.synth`` plus plain indexing), and the
+dense fp64 attention that pins the oracle comes from torch's own
+``scaled_dot_product_attention``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from sub_bit_vq_amd import synth
+
+N_SINK, N_RECENT = 64, 256
+
+
+def natural_codebook(cb: torch.Tensor) -> torch.Tensor:
+    """[Tc][H][S][256][cg] storage -> [H][S][256][G] with entry i = t*cg + c."""
+    Tc, H, S, K, cg = cb.shape
+    return cb.permute(1, 2, 3, 0, 4).reshape(H, S, K, Tc * cg)
+
+
+def natural_subvectors(x: torch.Tensor, group: int) -> torch.Tensor:
+    """x [n][H][Tc][d] -> [n][H][S][G] with entry i = t*cg + c of sub-vector j
+    taken from channel j*cg + c of loop step t."""
+    n, H, Tc, d = x.shape
+    cg = group // Tc
+    S = d // cg
+    return x.reshape(n, H, Tc, S, cg).permute(0, 1, 3, 2, 4).reshape(n, H, S, Tc * cg)
+
+
+def kv_from_codewords(idx: torch.Tensor, cb: torch.Tensor) -> torch.Tensor:
+    """Tokens whose every sub-vector is exactly a codeword.
+
+    idx uint8 [n][H][S]; cb [Tc][H][S][256][cg] -> x [n][H][Tc][d] (cb dtype)."""
+    Tc, H, S, K, cg = cb.shape
+    n = idx.shape[0]
+    hh = torch.arange(H).view(1, H, 1)
+    jj = torch.arange(S).view(1, 1, S)
+    rows = [cb[t][hh, jj, idx.long()] for t in range(Tc)]      # each [n][H][S][cg]
+    return torch.stack(rows, dim=2).reshape(n, H, Tc, S * cg)
+
+
+def bf16_representable_fp32(cb: torch.Tensor) -> torch.Tensor:
+    """fp32 codebook whose entries are exactly bf16 values (so bf16 tokens can
+    equal codewords)."""
+    return cb.to(torch.bfloat16).to(torch.float32)
+
+
+def sdpa_fp64(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: float) -> torch.Tensor:
+    """Dense attention from torch (CPU, fp64): q [d], K/V [L][d] -> [d]."""
+    q64 = q.to(torch.float64).view(1, 1, 1, -1)
+    K64 = K.to(torch.float64).view(1, 1, K.shape[0], -1)
+    V64 = V.to(torch.float64).view(1, 1, V.shape[0], -1)
+    return F.scaled_dot_product_attention(q64, K64, V64, scale=scale).view(-1)
+
+
+@dataclass
+class Cache:
+    """A complete decode-attention test case (host tensors)."""
+    batch: int
+    n_heads: int
+    head_dim: int
+    loop_steps: int
+    group: int
+    t_max: int
+    lengths: list
+    vq_len: list | None
+    q: torch.Tensor            # bf16 [Tc][B][H][d]
+    k_tokens: list             # per sequence bf16 [L][H][Tc][d] (original tokens)
+    v_tokens: list
+    k_index: torch.Tensor      # uint8 [B][H][t_max][S]
+    v_index: torch.Tensor
+    k_codebook: torch.Tensor   # [Tc][H][S][256][cg]
+    v_codebook: torch.Tensor
+    k_window: torch.Tensor     # bf16 [B][Tc][H][n_sink+n_recent][d]
+    v_window: torch.Tensor
+    n_sink: int = N_SINK
+    n_recent: int = N_RECENT
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def n_sub(self):
+        return self.head_dim // (self.group // self.loop_steps)
+
+    def vq_range(self, b):
+        return synth.window_positions(self.lengths[b], self.n_sink, self.n_recent,
+                                      None if self.vq_len is None else self.vq_len[b])[1]
+
+
+def make_cache(*, batch=1, n_heads=1, head_dim=64, loop_steps=4, group=16, lengths=(512,),
+               cb_dtype=torch.bfloat16, seed=0, codeword_tokens=False, vq_len=None,
+               encode=None, t_max=None, n_sink=N_SINK, n_recent=N_RECENT) -> Cache:
+    """Seeded cache.  VQ tokens either come from the loop-correlated generator
+    and are encoded with ``encode(x, codebook, index, seq, first_token)``, or
+    (``codeword_tokens=True``) are drawn as exact codewords of random indices,
+    in which case the index cache holds those indices directly."""
+    lengths = list(lengths)
+    assert len(lengths) == batch
+    cg = group // loop_steps
+    S = head_dim // cg
+    t_max = t_max or max(max(lengths), 1)
+    kcb = synth.codebooks(n_heads, head_dim, loop_steps, group, seed * 7919 + 1, dtype=cb_dtype)
+    vcb = synth.codebooks(n_heads, head_dim, loop_steps, group, seed * 7919 + 2, dtype=cb_dtype)
+    if cb_dtype == torch.float32 and codeword_tokens:
+        kcb, vcb = bf16_representable_fp32(kcb), bf16_representable_fp32(vcb)
+    q = synth.queries(batch, n_heads, head_dim, loop_steps, seed * 7919 + 3)
+    k_index = torch.zeros((batch, n_heads, t_max, S), dtype=torch.uint8)
+    v_index = torch.zeros_like(k_index)
+    W = n_sink + n_recent
+    k_window = torch.zeros((batch, loop_steps, n_heads, W, head_dim), dtype=torch.bfloat16)
+    v_window = torch.zeros_like(k_window)
+    k_tokens, v_tokens = [], []
+    for b, L in enumerate(lengths):
+        kt = synth.loop_correlated_kv(L, n_heads, loop_steps, head_dim, seed * 7919 + 100 + 2 * b)
+        vt = synth.loop_correlated_kv(L, n_heads, loop_steps, head_dim, seed * 7919 + 101 + 2 * b)
+        vql = None if vq_len is None else vq_len[b]
+        vq = synth.window_positions(L, n_sink, n_recent, vql)[1]
+        if len(vq):
+            lo, hi = vq.start, vq.stop
+            if codeword_tokens:
+                ik = synth.random_indices((hi - lo, n_heads, S), seed * 7919 + 500 + 2 * b)
+                iv = synth.random_indices((hi - lo, n_heads, S), seed * 7919 + 501 + 2 * b)
+                kt[lo:hi] = kv_from_codewords(ik, kcb).to(torch.bfloat16)
+                vt[lo:hi] = kv_from_codewords(iv, vcb).to(torch.bfloat16)
+                k_index[b, :, lo:hi] = ik.permute(1, 0, 2)
+                v_index[b, :, lo:hi] = iv.permute(1, 0, 2)
+            elif encode is not None:
+                encode(kt[lo:hi], kcb, k_index, b, lo)
+                encode(vt[lo:hi], vcb, v_index, b, lo)
+        synth.fill_window(k_window, b, kt, L, n_sink, n_recent, vql)
+        synth.fill_window(v_window, b, vt, L, n_sink, n_recent, vql)
+        k_tokens.append(kt)
+        v_tokens.append(vt)
+    return Cache(batch, n_heads, head_dim, loop_steps, group, t_max, lengths, vq_len, q,
+                 k_tokens, v_tokens, k_index, v_index, kcb, vcb, k_window, v_window,
+                 n_sink, n_recent)
+
+
+def oracle_encoder(oracle_mod, n_heads, head_dim, loop_steps, group):
+    """encode(x, cb, index, seq, first) callback running the CPU oracle in place."""
+    def enc(x, cb, index, seq, first):
+        arr = index.numpy()
+        oracle_mod.encode(x, cb, n_heads=n_heads, head_dim=head_dim, loop_steps=loop_steps,
+                          group=group, index=arr, seq=seq, first_token=first)
+    return enc
+
+
+def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of max_ch |got - ref| / max_ch |ref| (rows = leading dims)."""
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    num = np.abs(got - ref).max(axis=1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((num / den).max()) if num.size else 0.0
