@@ -1,0 +1,322 @@
+"""LoopVQ decode-attention throughput on one MI355X.
+
+One step = one eviction period of the pages' serving loop (LoopVQ project
+page, "Serving in SGLang"): 8 generated tokens, each decoded at the Tc = 4
+loop steps of one Ouro-1.4B-like layer (16 heads, head_dim 128, 0.5 bit,
+G = 16) over a 32768-token context, then the encoding of the oldest 8-token
+recent page (its K and V) into the index cache.  The context is held at 32768
+tokens for the 8 decodes.
+
+Metric: context-token x loop-steps per second (sum over decode calls of the
+context length).  Inputs are resident in HBM before the timed region; the
+index caches and windows are rotated over distinct copies so that the working
+set exceeds the 256 MB last-level cache twice.  The step is captured once in a
+HIP graph and replayed.
+
+Extra fields: ``roofline`` for the decode-attention kernel (algorithmic cache
+bytes per launch / its mean duration from HIP events) and ``cpu_baseline`` (the
+C oracle on a bounded sample of the same workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import pathlib
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+LLC_BYTES = 256 << 20
+WORKLOADS = {
+    # name: (B, H, d, Tc, G, context)
+    "ouro1p4b_layer_32k_0p5bit": (1, 16, 128, 4, 16, 32768),
+    "ouro1p4b_layer_32k_0p25bit": (1, 16, 128, 4, 32, 32768),
+}
+PAGE = 8          # tokens per eviction page
+N_SINK, N_RECENT = 64, 256
+METRIC = "VQ-KV decode attn: context-token·loop-steps/s at 32K; % HBM roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cache_bytes(H, d, Tc, G, L):
+    """Algorithmic bytes of one decode call: K and V index rows of every VQ
+    token plus the bf16 K and V of the sink and recent tokens of the step."""
+    S = d // (G // Tc)
+    n_vq = max(0, L - N_SINK - N_RECENT)
+    n_win = min(L, N_SINK) + min(max(L - N_SINK, 0), N_RECENT)
+    return n_vq * H * 2 * S + n_win * H * 2 * d * 2
+
+
+def kernel_source_hash(name):
+    return hashlib.sha256((ROOT / "sub_bit_vq_amd" / "csrc" / name).read_bytes()).hexdigest()[:16]
+
+
+def counters_traffic(workload, bytes_per_launch):
+    """HBM traffic per decode launch from the committed rocprofv3 counter
+    summary, or None when missing or taken on a different kernel source."""
+    p = ROOT / "profiles" / f"decode_attn_{workload}_counters.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text())
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash("decode_attn.hip"):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Setup:
+    def __init__(self, lv, synth, torch, workload, rotate, seed=1001):
+        B, H, d, Tc, G, L = WORKLOADS[workload]
+        self.B, self.H, self.d, self.Tc, self.G, self.L = B, H, d, Tc, G, L
+        dev = torch.device("cuda")
+        T = L + PAGE
+        self.cfg = lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                             max_tokens=T)
+        self.kcb = synth.codebooks(H, d, Tc, G, seed * 10 + 1, device=dev)
+        self.vcb = synth.codebooks(H, d, Tc, G, seed * 10 + 2, device=dev)
+        # one query per (token of the page, loop step)
+        self.q = torch.stack([synth.queries(B, H, d, Tc, seed * 10 + 3 + i, device=dev)
+                              for i in range(PAGE)])                 # [PAGE][Tc][B][H][d]
+        base = lv.allocate(self.cfg, dev)
+        k = synth.loop_correlated_kv(L + PAGE, H, Tc, d, seed * 10 + 5, device=dev)
+        v = synth.loop_correlated_kv(L + PAGE, H, Tc, d, seed * 10 + 6, device=dev)
+        lo, hi = N_SINK, L - N_RECENT
+        lv.lvq_encode(self.cfg, k[lo:hi], self.kcb, base["k_index"], 0, lo)
+        lv.lvq_encode(self.cfg, v[lo:hi], self.vcb, base["v_index"], 0, lo)
+        slots = [p if p < N_SINK else N_SINK + (p - N_SINK) % N_RECENT
+                 for p in list(range(N_SINK)) + list(range(L - N_RECENT, L))]
+        pos = torch.tensor(list(range(N_SINK)) + list(range(L - N_RECENT, L)), device=dev)
+        sl = torch.tensor(slots, device=dev)
+        base["k_window"][0][:, :, sl, :] = k[pos].permute(2, 1, 0, 3)
+        base["v_window"][0][:, :, sl, :] = v[pos].permute(2, 1, 0, 3)
+        # the page to encode: the next 8 tokens (written to rows L .. L+7)
+        self.page_k, self.page_v = k[L:L + PAGE].contiguous(), v[L:L + PAGE].contiguous()
+        torch.cuda.synchronize()
+        self.ctx = torch.tensor([L] * B, dtype=torch.int32, device=dev)
+        self.out = base["out"]
+        self.ws = base["workspace"]
+        copy_bytes = (base["k_index"].numel() * 2 + base["k_window"].numel() * 4)
+        self.rotate = rotate or max(2, math.ceil(2 * LLC_BYTES / copy_bytes))
+        self.copies = []
+        for r in range(self.rotate):
+            c = {key: base[key].clone() for key in ("k_index", "v_index", "k_window", "v_window")}
+            self.copies.append(c)
+        del base, k, v
+        torch.cuda.synchronize()
+        self.calls = [lv.PreparedDecode(self.cfg, self.ctx, L, c["k_index"], c["v_index"],
+                                        self.kcb, self.vcb, c["k_window"], c["v_window"],
+                                        self.ws, self.out) for c in self.copies]
+        self.lv = lv
+        self.n_call = 0
+
+    def decode(self, tok, t):
+        call = self.calls[self.n_call % self.rotate]
+        self.n_call += 1
+        call(t, self.q[tok, t])
+
+    def step(self):
+        for tok in range(PAGE):
+            for t in range(self.Tc):
+                self.decode(tok, t)
+        c = self.copies[self.n_call % self.rotate]
+        self.lv.lvq_encode(self.cfg, self.page_k, self.kcb, c["k_index"], 0, self.L)
+        self.lv.lvq_encode(self.cfg, self.page_v, self.vcb, c["v_index"], 0, self.L)
+
+    @property
+    def tokens_steps_per_step(self):
+        return PAGE * self.Tc * self.B * self.L
+
+
+def spin_cycles_for(torch, ms):
+    """Cycles of torch's spin kernel that last about ``ms`` milliseconds."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(1_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    return int(per_ms * ms)
+
+
+def decode_kernel_time_ms(setup, torch, n=256):
+    """Mean duration of one decode launch from HIP events on the launch stream.
+    A spin kernel first lets the host enqueue every launch ahead of the GPU."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    cycles = spin_cycles_for(torch, 50.0)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+    for i in range(n):
+        evs[i][0].record()
+        setup.decode(i % PAGE, i % setup.Tc)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ts) / n, ts[n // 2]
+
+
+def cpu_baseline(setup, torch, budget_s=15.0):
+    """The C oracle on a bounded sample of the same workload: whole decode
+    calls (all heads, loop step 0) repeated for about ``budget_s`` seconds, and
+    one page encode, combined into the time of one step."""
+    import oracle
+    c = setup.copies[0]
+    kidx, vidx = c["k_index"].cpu(), c["v_index"].cpu()
+    kw, vw = c["k_window"].cpu(), c["v_window"].cpu()
+    kcb, vcb = setup.kcb.cpu(), setup.vcb.cpu()
+    q = setup.q[0, 0].cpu()
+    threads = oracle.max_threads()
+    calls = 0
+    t0 = time.perf_counter()
+    while calls < 1 or time.perf_counter() - t0 < budget_s:
+        oracle.decode_attn(loop_step=0, q=q, ctx_len=[setup.L] * setup.B, k_index=kidx,
+                           v_index=vidx, k_codebook=kcb, v_codebook=vcb, k_window=kw,
+                           v_window=vw, n_sink=N_SINK, n_recent=N_RECENT, group=setup.G,
+                           threads=threads)
+        calls += 1
+    t_dec = (time.perf_counter() - t0) / calls
+    t1 = time.perf_counter()
+    oracle.encode(setup.page_k.cpu(), kcb, n_heads=setup.H, head_dim=setup.d,
+                  loop_steps=setup.Tc, group=setup.G, threads=threads)
+    t_enc = time.perf_counter() - t1
+    t_step = PAGE * setup.Tc * t_dec + 2 * t_enc
+    return {
+        "value": setup.tokens_steps_per_step / t_step,
+        "unit": "ctx-token*loop-steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{calls} whole decode calls (16 heads, 32768-token context, loop step 0, "
+                   f"{t_dec * 1e3:.1f} ms each) and one 8-token page encode ({t_enc * 1e3:.1f} ms, "
+                   f"counted for K and V), combined as one step of 32 decodes + 2 encodes; "
+                   f"OpenMP threads {threads} of {os.cpu_count()} logical CPUs"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ouro1p4b_layer_32k_0p5bit", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = auto, >= 2x LLC)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
+    ap.add_argument("--profile-decode", type=int, default=0,
+                    help="only run N decode launches (for rocprofv3 runs) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the LoopVQ path shards by heads or sequences with no exchange).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sub_bit_vq_amd import loopvq as lv
+    from sub_bit_vq_amd import synth
+
+    lv.library()
+    log(f"workload {args.workload}: setup")
+    setup = Setup(lv, synth, torch, args.workload, args.rotate)
+    log(f"rotation over {setup.rotate} cache copies, "
+        f"{lv.lvq_decode_splits(setup.cfg, setup.L)} VQ splits per head")
+
+    if args.profile_decode:
+        for i in range(args.profile_decode):
+            setup.decode(i % PAGE, i % setup.Tc)
+        torch.cuda.synchronize()
+        log(f"ran {args.profile_decode} decode launches")
+        return
+
+    # warmup (eager), then capture one step in a graph
+    for _ in range(max(1, args.warmup)):
+        setup.step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        # capture a whole rotation cycle so every graph replay touches each copy
+        n_steps_graph = max(1, setup.rotate // math.gcd(setup.rotate, PAGE * setup.Tc))
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(n_steps_graph):
+                setup.step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"graph: {n_steps_graph} steps per replay")
+    else:
+        n_steps_graph = 1
+
+    reps = max(1, math.ceil(args.steps / n_steps_graph))
+    steps = reps * n_steps_graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        if graph is not None:
+            graph.replay()
+        else:
+            setup.step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / steps
+    value = setup.tokens_steps_per_step / (ms_per_step / 1e3)
+    log(f"{steps} steps in {ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step)")
+
+    mean_ms, med_ms = decode_kernel_time_ms(setup, torch)
+    bpl = cache_bytes(setup.H, setup.d, setup.Tc, setup.G, setup.L)
+    achieved = bpl / (mean_ms / 1e3) / 1e9
+    log(f"decode launch: mean {mean_ms * 1e3:.2f} us, median {med_ms * 1e3:.2f} us, "
+        f"{achieved:.0f} GB/s on {bpl} cache bytes")
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch)
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "ctx-token*loop-steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded loop-correlated K/V, N(0,1) codebooks)",
+        "config": {
+            "workload": args.workload,
+            "batch": setup.B, "heads": setup.H, "head_dim": setup.d, "loop_steps": setup.Tc,
+            "group": setup.G, "context": setup.L, "n_sink": N_SINK, "n_recent": N_RECENT,
+            "step": "8 tokens x 4 loop-step decodes + 8-token page encode (K, V)",
+            "cache_copies": setup.rotate, "graph": graph is not None,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_kernel<32,4,bf16>" if setup.G == 16 else "decode_kernel<16,8,bf16>",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": counters_traffic(args.workload, bpl),
+            "bytes_per_launch": bpl,
+            "mean_launch_us": mean_ms * 1e3,
+            "median_launch_us": med_ms * 1e3,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * libloopvq -- LoopVQ sub-bit KV-cache decode attention and encoder for
+ * AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes.
+ *
+ * What it computes (the LoopVQ pages):
+ *  - LoopVQ project page (mscheong01.github.io/loopvq), "Method" and the
+ *    "Overview of LoopVQ" figure: the keys and values of a looped model are
+ *    vector-quantised with sub-vectors that span G/Tc channels at each of Tc
+ *    consecutive loop steps, so a single 8-bit index serves all Tc steps;
+ *    at loop step t the index is read through slice t of the codeword.
+ *  - same page, "Serving in SGLang": new keys/values are written in bf16
+ *    ("Write in bf16"); the first n_sink and the most recent n_recent tokens
+ *    stay bf16 at every loop step; older tokens are encoded into shared
+ *    indices ("Encode in pages"); at step t attention reads the keys and
+ *    values from the indices through codebook slice t and merges with the
+ *    bf16 attention over the sink and recent tokens ("Attend from indices").
+ *  - same page, "Results -- Long-context retrieval": n_sink = 64 and
+ *    n_recent = 256.
+ *
+ * Notation: B sequences, H heads (query heads = KV heads), d = head_dim,
+ * Tc = loop_steps, G = group (elements per sub-vector), cg = G / Tc channels
+ * per loop step, S = d / cg sub-vectors per token per head, 256 codes.
+ * bits per cached element = 8 / G.
+ *
+ * Storage layouts (all row-major, innermost last):
+ *   x (encoder input) bf16  [n_tokens][H][Tc][d]  (or strided, see lvq_encode)
+ *   codebook          f32 or bf16 [Tc][H][S][256][cg]: entry i = t*cg + c of
+ *                     codeword k of (head h, sub-vector j) at [t][h][j][k][c],
+ *                     so slice t of every codebook is contiguous
+ *   index cache       uint8 [B][H][max_tokens][S]; row p holds token p
+ *                     (absolute position); rows of bf16 tokens are unused
+ *   window buffers    bf16 [B][Tc][H][n_sink + n_recent][d]: sink token p
+ *                     (p < n_sink) in slot p; recent token p (p >= n_sink) in
+ *                     slot n_sink + ((p - n_sink) mod n_recent)  (a ring)
+ *   query             bf16 [B][H][d] (the query of the loop step decoded)
+ *   output            fp32 [B][H][d]
+ *
+ * Windows of a context of L tokens (L counts the current token):
+ *   sink   = [0, n_s),        n_s = min(L, n_sink)
+ *   VQ     = [n_s, n_s + n_v), n_v = vq_len[b] if given, else
+ *                              max(0, L - n_sink - n_recent)
+ *   recent = [n_s + n_v, L)
+ *
+ * Ownership and threading: the caller allocates and owns every buffer (device
+ * memory unless stated).  The library never allocates, never synchronises the
+ * host, keeps no global state and never prints.  Calls are asynchronous on the
+ * given HIP stream (NULL = the default stream).  Concurrent calls must use
+ * distinct workspaces.
+ */
+#ifndef LOOPVQ_H
+#define LOOPVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LVQ_OK = 0,
+    LVQ_ERR_INVALID_ARG = 1,  /* null pointer, inconsistent shape, bad index */
+    LVQ_ERR_UNSUPPORTED = 2,  /* valid shape the kernels are not built for    */
+    LVQ_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required   */
+    LVQ_ERR_HIP = 4           /* a HIP launch reported an error               */
+} lvq_status;
+
+typedef enum { LVQ_F32 = 0, LVQ_BF16 = 1 } lvq_dtype;
+
+typedef struct {
+    int32_t batch;          /* B, >= 1                                        */
+    int32_t n_heads;        /* H, >= 1                                        */
+    int32_t head_dim;       /* d                                              */
+    int32_t loop_steps;     /* Tc, divides group                              */
+    int32_t group;          /* G; cg = G/Tc must divide d                     */
+    int32_t n_sink;         /* bf16 sink tokens, >= 0 (64 on the pages)       */
+    int32_t n_recent;       /* bf16 recent tokens, >= 1 (256 on the pages)    */
+    int32_t max_tokens;     /* rows of the index cache per (b, h)             */
+    int32_t codebook_dtype; /* lvq_dtype                                      */
+    int32_t decode_splits;  /* VQ splits per (b, h) for lvq_decode_attn;
+                               0 = chosen by the library; 1..LVQ_MAX_SPLITS.
+                               Changes only the rounding of the result.        */
+} lvq_config;
+
+#define LVQ_MAX_SPLITS 64
+#define LVQ_CODES 256
+
+typedef struct {
+    int32_t ndim;
+    int64_t shape[6];
+    int64_t stride[6];      /* in elements                                    */
+    uint64_t bytes;
+} lvq_tensor;
+
+typedef struct {
+    int32_t n_sub;                     /* S                                   */
+    int32_t sub_channels;              /* cg                                  */
+    int32_t n_codes;                   /* 256                                 */
+    int32_t window_slots;              /* n_sink + n_recent                   */
+    double bits_per_element;           /* 8 / G                               */
+    double compression_vs_bf16;        /* 16 / bits_per_element               */
+    double read_reduction_per_step;    /* bf16 K+V bytes per token and loop
+                                          step / index bytes read per token and
+                                          loop step = 2G/Tc                    */
+    lvq_tensor k_index, v_index;       /* uint8                               */
+    lvq_tensor k_codebook, v_codebook; /* codebook_dtype                      */
+    lvq_tensor k_window, v_window;     /* bf16                                */
+    lvq_tensor query;                  /* bf16                                */
+    lvq_tensor output;                 /* fp32                                */
+    uint64_t workspace_bytes;          /* for lvq_decode_attn                 */
+} lvq_layout;
+
+/*
+ * Sizes and strides of every buffer for a configuration (pure host
+ * arithmetic; no device is touched).  The bits-per-element and read-reduction
+ * figures are the quantities the project page reports ("Highlights";
+ * "Efficiency -- Latency").
+ * Errors: LVQ_ERR_INVALID_ARG for a null pointer or an inconsistent config.
+ */
+lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
+
+/*
+ * Encoder: nearest codeword of every loop-stacked sub-vector (LoopVQ project
+ * page, "Component 1 -- Loop-axis vector quantization" and "Serving in SGLang
+ * -- Encode in pages"; the news article "How LoopVQ works").
+ *
+ * Sub-vector j of (token n, head h) has entries x_i = x[n][h][t][j*cg + c],
+ * i = t*cg + c.  Its code is the k minimising the squared distance
+ * D_k = sum_i (x_i - c_{k,i})^2 evaluated in IEEE fp32 (separate subtract,
+ * square and add, ascending i); the lowest k wins ties.  The result is
+ * bit-identical to that definition: the kernel screens all 256 codes with a
+ * bf16 MFMA contraction and re-scores exactly every sub-vector whose two best
+ * screen values lie within the screen's error bound.
+ *
+ * x          device bf16; element (n, h, t, ch) at
+ *            x[n*x_strides[0] + h*x_strides[1] + t*x_strides[2] + ch];
+ *            x_strides == NULL means the dense [n_tokens][H][Tc][d] layout.
+ *            Strides are in elements; channels must be contiguous and every
+ *            stride a multiple of cg.
+ * codebook   device, cfg->codebook_dtype, layout above (one call encodes one
+ *            tensor: call once with the K codebook and once with the V one)
+ * index_cache device uint8 [B][H][max_tokens][S]; rows
+ *            [first_token, first_token + n_tokens) of sequence seq are written
+ * n_tokens   may be 0 (nothing launched)
+ * Errors: LVQ_ERR_INVALID_ARG (null pointers, seq or rows out of range,
+ * bad strides), LVQ_ERR_UNSUPPORTED (G not in {8, 16, 32}, cg not in
+ * {2, 4, 8}, or fp32 codebooks with G = 32), LVQ_ERR_HIP.
+ */
+lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_strides,
+                      int64_t n_tokens, const void *codebook, uint8_t *index_cache,
+                      int32_t seq, int64_t first_token, void *stream);
+
+/*
+ * Decode attention of loop step t (LoopVQ project page, "Serving in SGLang --
+ * Attend from indices"): for every (b, h),
+ *   out = sum_n softmax_n(sm_scale * q . K_n) V_n
+ * over all L_b tokens, where VQ tokens use K_n[j*cg + c] =
+ * k_codebook[t][h][j][k_index[b][h][n][j]][c] (likewise V) and sink/recent
+ * tokens use the bf16 window buffers of step t.  fp32 accumulation.
+ *
+ * q          device bf16 [B][H][d]
+ * ctx_len    device int32 [B]: L_b, precondition 0 <= L_b <= max_tokens
+ *            (clamped on the device; L_b = 0 writes zeros)
+ * vq_len     device int32 [B] or NULL (exact windows).  Precondition
+ *            L_b - n_s - n_recent <= vq_len[b] <= L_b - n_s (clamped on the
+ *            device; a recent window longer than n_recent keeps only the
+ *            newest n_recent tokens).
+ * max_ctx_len host int32: an upper bound of every L_b; sizes the launch.
+ * workspace  device, >= layout.workspace_bytes; zero-filled once after
+ *            allocation; every completed call leaves it zero-filled again.
+ * out        device fp32 [B][H][d]
+ * Errors: LVQ_ERR_INVALID_ARG (null pointers, loop_step outside [0, Tc),
+ * max_ctx_len outside [0, max_tokens], sm_scale not finite),
+ * LVQ_ERR_UNSUPPORTED (d > 256 or d % 8 != 0, S not in {8, 16, 32, 64},
+ * cg not in {2, 4, 8}), LVQ_ERR_WORKSPACE, LVQ_ERR_HIP.
+ */
+lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void *q,
+                           const int32_t *ctx_len, const int32_t *vq_len,
+                           int32_t max_ctx_len, const uint8_t *k_index,
+                           const uint8_t *v_index, const void *k_codebook,
+                           const void *v_codebook, const void *k_window,
+                           const void *v_window, float sm_scale, void *workspace,
+                           uint64_t workspace_bytes, float *out, void *stream);
+
+/* Number of VQ splits per (b, h) lvq_decode_attn launches for max_ctx_len
+ * (host arithmetic only); 0 on an invalid config. */
+int32_t lvq_decode_splits(const lvq_config *cfg, int32_t max_ctx_len);
+
+/* Static, NUL-terminated description of a status code. */
+const char *lvq_status_string(lvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOPVQ_H */

@@ -1,0 +1,66 @@
+// Internal interface between the C ABI (loopvq_host.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lvq {
+
+// Workspace of lvq_decode_attn: per (b, h), LVQ_MAX_SPLITS + 1 partial slots of
+// (m, l, o[d]) floats (slot 0 = bf16 windows, slots 1.. = VQ splits), then one
+// uint32 arrival ticket per (b, h).
+constexpr int kMaxSplits = 64;
+constexpr int kSlots = kMaxSplits + 1;
+
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+inline uint64_t partial_bytes(int64_t B, int64_t H, int64_t d) {
+    return align_up((uint64_t)B * H * kSlots * (d + 2) * sizeof(float), 256);
+}
+inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
+    return partial_bytes(B, H, d) + align_up((uint64_t)B * H * sizeof(uint32_t), 256);
+}
+
+struct DecodeArgs {
+    int B, H, d, Tc, cg, S, n_sink, n_recent;
+    int64_t t_max;
+    int loop_step;
+    int n_split;      // VQ splits per (b, h)
+    int chunk;        // VQ tokens per split (multiple of 64)
+    int cb_bf16;
+    const uint16_t *q;          // [B][H][d]
+    const int32_t *ctx_len;     // [B]
+    const int32_t *vq_len;      // [B] or null
+    const uint8_t *k_index;     // [B][H][t_max][S]
+    const uint8_t *v_index;
+    const void *k_cb;           // [Tc][H][S][256][cg]
+    const void *v_cb;
+    const uint16_t *k_win;      // [B][Tc][H][W][d]
+    const uint16_t *v_win;
+    float sm_scale;
+    float *partials;            // [B][H][kSlots][d + 2]
+    uint32_t *tickets;          // [B][H]
+    float *out;                 // [B][H][d]
+};
+
+struct EncodeArgs {
+    int H, d, Tc, G, cg, S;
+    int cb_bf16;
+    const uint16_t *x;
+    int64_t sx_tok, sx_head, sx_step;   // element strides of x
+    int64_t n_tokens;
+    const void *cb;             // [Tc][H][S][256][cg]
+    uint8_t *index;             // [B][H][t_max][S]
+    int64_t t_max;
+    int64_t seq;
+    int64_t first_token;
+};
+
+// Kernel-support predicates (host) and launchers (return the HIP error of the
+// launch).
+bool decode_supported(int d, int S, int cg);
+bool encode_supported(int G, int cg, int cb_bf16);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
+
+}  // namespace lvq

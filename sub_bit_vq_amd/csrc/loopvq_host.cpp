@@ -1,0 +1,225 @@
+// C ABI of libloopvq: argument validation, buffer layout and launch
+// configuration.  Everything before the kernel launch is plain host
+// arithmetic, so every error path returns before any HIP call.
+#include "../../include/loopvq.h"
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+bool config_ok(const lvq_config *c) {
+    if (!c) return false;
+    if (c->batch < 1 || c->n_heads < 1 || c->head_dim < 1) return false;
+    if (c->loop_steps < 1 || c->group < 1) return false;
+    if (c->group % c->loop_steps != 0) return false;
+    const int cg = c->group / c->loop_steps;
+    if (c->head_dim % cg != 0) return false;
+    if (c->n_sink < 0 || c->n_recent < 1 || c->max_tokens < 0) return false;
+    if (c->codebook_dtype != LVQ_F32 && c->codebook_dtype != LVQ_BF16) return false;
+    if (c->decode_splits < 0 || c->decode_splits > LVQ_MAX_SPLITS) return false;
+    if (c->batch > 65535 || c->n_heads > 65535) return false;
+    return true;
+}
+
+void set_tensor(lvq_tensor *t, int ndim, const int64_t *shape, uint64_t elem_bytes) {
+    t->ndim = ndim;
+    for (int i = 0; i < 6; ++i) t->shape[i] = t->stride[i] = 0;
+    int64_t s = 1;
+    for (int i = ndim - 1; i >= 0; --i) {
+        t->shape[i] = shape[i];
+        t->stride[i] = s;
+        s *= shape[i];
+    }
+    t->bytes = (uint64_t)s * elem_bytes;
+}
+
+int64_t max_vq_tokens(const lvq_config *c, int32_t max_ctx_len, bool exact_windows) {
+    const int64_t L = max_ctx_len;
+    const int64_t n_s = L < c->n_sink ? L : c->n_sink;
+    const int64_t v = exact_windows ? L - c->n_sink - c->n_recent : L - n_s;
+    return v > 0 ? v : 0;
+}
+
+// Splits per (b, h): enough workgroups to occupy the chip (about two per
+// compute unit across 256 CUs), each split at least 256 tokens.
+int32_t choose_splits(const lvq_config *c, int64_t max_vq) {
+    if (max_vq <= 0) return 1;
+    int64_t want = c->decode_splits;
+    if (want == 0) {
+        const int64_t target_groups = 512;
+        const int64_t bh = (int64_t)c->batch * c->n_heads;
+        want = (target_groups + bh - 1) / bh;
+        const int64_t by_len = (max_vq + 255) / 256;
+        if (want > by_len) want = by_len;
+    }
+    if (want < 1) want = 1;
+    if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
+    return (int32_t)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *lvq_status_string(lvq_status s) {
+    switch (s) {
+        case LVQ_OK: return "ok";
+        case LVQ_ERR_INVALID_ARG: return "invalid argument";
+        case LVQ_ERR_UNSUPPORTED: return "unsupported shape";
+        case LVQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case LVQ_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
+    if (!o || !config_ok(c)) return LVQ_ERR_INVALID_ARG;
+    std::memset(o, 0, sizeof *o);
+    const int64_t B = c->batch, H = c->n_heads, d = c->head_dim, Tc = c->loop_steps;
+    const int64_t cg = c->group / c->loop_steps, S = d / cg, W = (int64_t)c->n_sink + c->n_recent;
+    const uint64_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
+    o->n_sub = (int32_t)S;
+    o->sub_channels = (int32_t)cg;
+    o->n_codes = LVQ_CODES;
+    o->window_slots = (int32_t)W;
+    o->bits_per_element = 8.0 / (double)c->group;
+    o->compression_vs_bf16 = 16.0 / o->bits_per_element;
+    // per token and loop step: bf16 K and V read 2 * d * 2 bytes; the index
+    // rows (K and V, shared by all loop steps) are re-read whole: 2 * S bytes
+    o->read_reduction_per_step = (4.0 * (double)d) / (2.0 * (double)S);
+    const int64_t idx_shape[4] = {B, H, c->max_tokens, S};
+    set_tensor(&o->k_index, 4, idx_shape, 1);
+    set_tensor(&o->v_index, 4, idx_shape, 1);
+    const int64_t cb_shape[5] = {Tc, H, S, LVQ_CODES, cg};
+    set_tensor(&o->k_codebook, 5, cb_shape, cbe);
+    set_tensor(&o->v_codebook, 5, cb_shape, cbe);
+    const int64_t win_shape[5] = {B, Tc, H, W, d};
+    set_tensor(&o->k_window, 5, win_shape, 2);
+    set_tensor(&o->v_window, 5, win_shape, 2);
+    const int64_t q_shape[3] = {B, H, d};
+    set_tensor(&o->query, 3, q_shape, 2);
+    set_tensor(&o->output, 3, q_shape, 4);
+    o->workspace_bytes = lvq::workspace_bytes(B, H, d);
+    return LVQ_OK;
+}
+
+int32_t lvq_decode_splits(const lvq_config *c, int32_t max_ctx_len) {
+    if (!config_ok(c) || max_ctx_len < 0 || max_ctx_len > c->max_tokens) return 0;
+    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true));
+}
+
+lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strides,
+                      int64_t n_tokens, const void *codebook, uint8_t *index_cache,
+                      int32_t seq, int64_t first_token, void *stream) {
+    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
+    if (!x || !codebook || !index_cache) return LVQ_ERR_INVALID_ARG;
+    if (n_tokens < 0 || seq < 0 || seq >= c->batch) return LVQ_ERR_INVALID_ARG;
+    if (first_token < 0 || first_token + n_tokens > c->max_tokens) return LVQ_ERR_INVALID_ARG;
+    const int cg = c->group / c->loop_steps;
+    const int64_t H = c->n_heads, d = c->head_dim, Tc = c->loop_steps;
+    int64_t st[3] = {H * Tc * d, Tc * d, d};
+    if (x_strides) {
+        for (int i = 0; i < 3; ++i) {
+            st[i] = x_strides[i];
+            if (st[i] < 0 || st[i] % cg != 0) return LVQ_ERR_INVALID_ARG;
+        }
+    }
+    // sub-vector runs of cg bf16 are read as one vector
+    if (reinterpret_cast<uintptr_t>(x) % (2 * (uintptr_t)cg) != 0) return LVQ_ERR_INVALID_ARG;
+    if (!lvq::encode_supported(c->group, cg, c->codebook_dtype == LVQ_BF16))
+        return LVQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return LVQ_OK;
+    lvq::EncodeArgs a{};
+    a.H = c->n_heads;
+    a.d = c->head_dim;
+    a.Tc = c->loop_steps;
+    a.G = c->group;
+    a.cg = cg;
+    a.S = c->head_dim / cg;
+    a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
+    a.x = static_cast<const uint16_t *>(x);
+    a.sx_tok = st[0];
+    a.sx_head = st[1];
+    a.sx_step = st[2];
+    a.n_tokens = n_tokens;
+    a.cb = codebook;
+    a.index = index_cache;
+    a.t_max = c->max_tokens;
+    a.seq = seq;
+    a.first_token = first_token;
+    hipError_t e = lvq::launch_encode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;
+}
+
+lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q,
+                           const int32_t *ctx_len, const int32_t *vq_len,
+                           int32_t max_ctx_len, const uint8_t *k_index,
+                           const uint8_t *v_index, const void *k_codebook,
+                           const void *v_codebook, const void *k_window,
+                           const void *v_window, float sm_scale, void *workspace,
+                           uint64_t workspace_bytes, float *out, void *stream) {
+    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
+    if (!q || !ctx_len || !k_index || !v_index || !k_codebook || !v_codebook || !k_window ||
+        !v_window || !out)
+        return LVQ_ERR_INVALID_ARG;
+    if (loop_step < 0 || loop_step >= c->loop_steps) return LVQ_ERR_INVALID_ARG;
+    if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return LVQ_ERR_INVALID_ARG;
+    if (!std::isfinite(sm_scale)) return LVQ_ERR_INVALID_ARG;
+    // index rows and window rows are read with 8- or 16-byte vector loads
+    {
+        const int cg0 = c->group / c->loop_steps, S0 = c->head_dim / cg0;
+        const uintptr_t ia = S0 >= 16 ? 16 : 8;
+        if (reinterpret_cast<uintptr_t>(k_index) % ia || reinterpret_cast<uintptr_t>(v_index) % ia)
+            return LVQ_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(k_window) % 16 || reinterpret_cast<uintptr_t>(v_window) % 16)
+            return LVQ_ERR_INVALID_ARG;
+    }
+    const int cg = c->group / c->loop_steps;
+    const int S = c->head_dim / cg;
+    if (!lvq::decode_supported(c->head_dim, S, cg)) return LVQ_ERR_UNSUPPORTED;
+    const uint64_t need = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
+    if (!workspace || workspace_bytes < need) return LVQ_ERR_WORKSPACE;
+
+    const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
+    const int32_t n_split = choose_splits(c, max_vq);
+    int64_t chunk = (max_vq + n_split - 1) / n_split;
+    chunk = (chunk + 63) / 64 * 64;
+    if (chunk < 64) chunk = 64;
+
+    lvq::DecodeArgs a{};
+    a.B = c->batch;
+    a.H = c->n_heads;
+    a.d = c->head_dim;
+    a.Tc = c->loop_steps;
+    a.cg = cg;
+    a.S = S;
+    a.n_sink = c->n_sink;
+    a.n_recent = c->n_recent;
+    a.t_max = c->max_tokens;
+    a.loop_step = loop_step;
+    a.n_split = n_split;
+    a.chunk = (int)chunk;
+    a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
+    a.q = static_cast<const uint16_t *>(q);
+    a.ctx_len = ctx_len;
+    a.vq_len = vq_len;
+    a.k_index = k_index;
+    a.v_index = v_index;
+    a.k_cb = k_codebook;
+    a.v_cb = v_codebook;
+    a.k_win = static_cast<const uint16_t *>(k_window);
+    a.v_win = static_cast<const uint16_t *>(v_window);
+    a.sm_scale = sm_scale;
+    a.partials = static_cast<float *>(workspace);
+    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                             lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
+    a.out = out;
+    hipError_t e = lvq::launch_decode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;
+}
+
+}  // extern "C"

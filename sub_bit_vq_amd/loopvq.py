@@ -1,0 +1,251 @@
+"""Thin Python binding of libloopvq (``include/loopvq.h``).
+
+Argument marshalling only: torch tensors are checked against the layout the
+library documents and passed as raw device pointers on torch's current HIP
+stream.  Every step of the computation runs in the library's kernels; there is
+no fallback, and a missing ``libloopvq.so`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import pathlib
+
+import torch
+
+_HERE = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libloopvq.so"
+
+LVQ_OK, LVQ_ERR_INVALID_ARG, LVQ_ERR_UNSUPPORTED, LVQ_ERR_WORKSPACE, LVQ_ERR_HIP = range(5)
+LVQ_F32, LVQ_BF16 = 0, 1
+LVQ_MAX_SPLITS = 64
+N_CODES = 256
+
+EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_decode_attn", "lvq_decode_splits",
+           "lvq_status_string")
+
+
+class LoopVQError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {lvq_status_string(status)} (status {status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
+        "max_tokens", "codebook_dtype", "decode_splits")]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("shape", ctypes.c_int64 * 6),
+                ("stride", ctypes.c_int64 * 6), ("bytes", ctypes.c_uint64)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("n_sub", ctypes.c_int32), ("sub_channels", ctypes.c_int32),
+                ("n_codes", ctypes.c_int32), ("window_slots", ctypes.c_int32),
+                ("bits_per_element", ctypes.c_double), ("compression_vs_bf16", ctypes.c_double),
+                ("read_reduction_per_step", ctypes.c_double),
+                ("k_index", _Tensor), ("v_index", _Tensor), ("k_codebook", _Tensor),
+                ("v_codebook", _Tensor), ("k_window", _Tensor), ("v_window", _Tensor),
+                ("query", _Tensor), ("output", _Tensor), ("workspace_bytes", ctypes.c_uint64)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Mirror of ``lvq_config``."""
+    batch: int
+    n_heads: int
+    head_dim: int
+    loop_steps: int = 4
+    group: int = 16
+    n_sink: int = 64
+    n_recent: int = 256
+    max_tokens: int = 0
+    codebook_dtype: int = LVQ_BF16
+    decode_splits: int = 0
+
+    def c(self) -> _Config:
+        return _Config(*(int(getattr(self, f.name)) for f in dataclasses.fields(self)))
+
+    @property
+    def torch_codebook_dtype(self):
+        return torch.bfloat16 if self.codebook_dtype == LVQ_BF16 else torch.float32
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libloopvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m sub_bit_vq_amd.build`")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        cfgp = ctypes.POINTER(_Config)
+        lib.lvq_cache_layout.restype = i32
+        lib.lvq_cache_layout.argtypes = [cfgp, ctypes.POINTER(_Layout)]
+        lib.lvq_encode.restype = i32
+        lib.lvq_encode.argtypes = [cfgp, vp, ctypes.POINTER(i64), i64, vp, vp, i32, i64, vp]
+        lib.lvq_decode_attn.restype = i32
+        lib.lvq_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                        ctypes.c_float, vp, u64, vp, vp]
+        lib.lvq_decode_splits.restype = i32
+        lib.lvq_decode_splits.argtypes = [cfgp, i32]
+        lib.lvq_status_string.restype = ctypes.c_char_p
+        lib.lvq_status_string.argtypes = [i32]
+        _lib = lib
+    return _lib
+
+
+def lvq_status_string(status: int) -> str:
+    return library().lvq_status_string(int(status)).decode()
+
+
+def _tensor_dict(t: _Tensor) -> dict:
+    return {"shape": tuple(t.shape[: t.ndim]), "stride": tuple(t.stride[: t.ndim]),
+            "bytes": int(t.bytes)}
+
+
+def lvq_cache_layout(cfg: Config) -> dict:
+    """Sizes and shapes of every buffer (host arithmetic only)."""
+    lay = _Layout()
+    st = library().lvq_cache_layout(ctypes.byref(cfg.c()), ctypes.byref(lay))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_cache_layout", st)
+    out = {f: getattr(lay, f) for f in ("n_sub", "sub_channels", "n_codes", "window_slots",
+                                         "bits_per_element", "compression_vs_bf16",
+                                         "read_reduction_per_step", "workspace_bytes")}
+    for f in ("k_index", "v_index", "k_codebook", "v_codebook", "k_window", "v_window", "query",
+              "output"):
+        out[f] = _tensor_dict(getattr(lay, f))
+    return out
+
+
+def lvq_decode_splits(cfg: Config, max_ctx_len: int) -> int:
+    return int(library().lvq_decode_splits(ctypes.byref(cfg.c()), int(max_ctx_len)))
+
+
+def _dev_ptr(t, name, dtype=None, shape=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def lvq_encode(cfg: Config, x: torch.Tensor, codebook: torch.Tensor, index_cache: torch.Tensor,
+               seq: int = 0, first_token: int = 0, stream=None) -> None:
+    """Encode bf16 ``x`` ``[n][H][Tc][d]`` (any element strides with contiguous
+    channels) into rows ``[first_token, first_token + n)`` of sequence ``seq``."""
+    lay = lvq_cache_layout(cfg)
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a bf16 device tensor")
+    if x.dim() != 4 or tuple(x.shape[1:]) != (cfg.n_heads, cfg.loop_steps, cfg.head_dim):
+        raise ValueError(f"x: expected [n][{cfg.n_heads}][{cfg.loop_steps}][{cfg.head_dim}]")
+    if x.stride(3) != 1:
+        raise ValueError("x: channels must be contiguous")
+    strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    cbp = _dev_ptr(codebook, "codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"])
+    ip = _dev_ptr(index_cache, "index_cache", torch.uint8, lay["k_index"]["shape"])
+    st = library().lvq_encode(ctypes.byref(cfg.c()), ctypes.c_void_p(x.data_ptr()), strides,
+                              int(x.shape[0]), cbp, ip, int(seq), int(first_token),
+                              _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_encode", st)
+
+
+def lvq_decode_attn(cfg: Config, loop_step: int, q: torch.Tensor, ctx_len: torch.Tensor,
+                    max_ctx_len: int, k_index, v_index, k_codebook, v_codebook, k_window,
+                    v_window, workspace: torch.Tensor, out: torch.Tensor, sm_scale: float = 1.0,
+                    vq_len: torch.Tensor | None = None, stream=None) -> None:
+    """Decode attention of ``loop_step``; writes fp32 ``out`` ``[B][H][d]``."""
+    lay = lvq_cache_layout(cfg)
+    B = cfg.batch
+    args = [
+        _dev_ptr(q, "q", torch.bfloat16, lay["query"]["shape"]),
+        _dev_ptr(ctx_len, "ctx_len", torch.int32, (B,)),
+        _dev_ptr(vq_len, "vq_len", torch.int32, (B,), allow_none=True),
+        int(max_ctx_len),
+        _dev_ptr(k_index, "k_index", torch.uint8, lay["k_index"]["shape"]),
+        _dev_ptr(v_index, "v_index", torch.uint8, lay["v_index"]["shape"]),
+        _dev_ptr(k_codebook, "k_codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"]),
+        _dev_ptr(v_codebook, "v_codebook", cfg.torch_codebook_dtype, lay["v_codebook"]["shape"]),
+        _dev_ptr(k_window, "k_window", torch.bfloat16, lay["k_window"]["shape"]),
+        _dev_ptr(v_window, "v_window", torch.bfloat16, lay["v_window"]["shape"]),
+        ctypes.c_float(sm_scale),
+        _dev_ptr(workspace, "workspace"),
+        ctypes.c_uint64(workspace.numel() * workspace.element_size()),
+        _dev_ptr(out, "out", torch.float32, lay["output"]["shape"]),
+    ]
+    st = library().lvq_decode_attn(ctypes.byref(cfg.c()), int(loop_step), *args, _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_decode_attn", st)
+
+
+def allocate(cfg: Config, device="cuda") -> dict:
+    """Zero-filled device buffers for a configuration (index caches, windows,
+    workspace and output); codebooks, queries and lengths are the caller's."""
+    lay = lvq_cache_layout(cfg)
+    z = lambda key, dt: torch.zeros(lay[key]["shape"], dtype=dt, device=device)  # noqa: E731
+    return {
+        "k_index": z("k_index", torch.uint8), "v_index": z("v_index", torch.uint8),
+        "k_window": z("k_window", torch.bfloat16), "v_window": z("v_window", torch.bfloat16),
+        "out": z("output", torch.float32),
+        "workspace": torch.zeros(int(lay["workspace_bytes"]), dtype=torch.uint8, device=device),
+    }
+
+
+class PreparedDecode:
+    """``lvq_decode_attn`` with every buffer marshalled once, for tight serving
+    or benchmark loops: a call costs one ctypes transition.  Buffers are
+    validated here exactly as :func:`lvq_decode_attn` validates them."""
+
+    def __init__(self, cfg: Config, ctx_len, max_ctx_len, k_index, v_index, k_codebook,
+                 v_codebook, k_window, v_window, workspace, out, sm_scale=1.0, vq_len=None):
+        lay = lvq_cache_layout(cfg)
+        B = cfg.batch
+        self._cfg = cfg.c()
+        self._qshape = lay["query"]["shape"]
+        self._lib = library()
+        self._args = (
+            _dev_ptr(ctx_len, "ctx_len", torch.int32, (B,)),
+            _dev_ptr(vq_len, "vq_len", torch.int32, (B,), allow_none=True),
+            int(max_ctx_len),
+            _dev_ptr(k_index, "k_index", torch.uint8, lay["k_index"]["shape"]),
+            _dev_ptr(v_index, "v_index", torch.uint8, lay["v_index"]["shape"]),
+            _dev_ptr(k_codebook, "k_codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"]),
+            _dev_ptr(v_codebook, "v_codebook", cfg.torch_codebook_dtype, lay["v_codebook"]["shape"]),
+            _dev_ptr(k_window, "k_window", torch.bfloat16, lay["k_window"]["shape"]),
+            _dev_ptr(v_window, "v_window", torch.bfloat16, lay["v_window"]["shape"]),
+            ctypes.c_float(sm_scale),
+            _dev_ptr(workspace, "workspace"),
+            ctypes.c_uint64(workspace.numel() * workspace.element_size()),
+            _dev_ptr(out, "out", torch.float32, lay["output"]["shape"]),
+        )
+        self._keep = (ctx_len, vq_len, k_index, v_index, k_codebook, v_codebook, k_window,
+                      v_window, workspace, out)
+
+    def __call__(self, loop_step: int, q: torch.Tensor, stream=None) -> None:
+        qp = _dev_ptr(q, "q", torch.bfloat16, self._qshape)
+        st = self._lib.lvq_decode_attn(ctypes.byref(self._cfg), int(loop_step), qp, *self._args,
+                                       _stream(stream))
+        if st != LVQ_OK:
+            raise LoopVQError("lvq_decode_attn", st)

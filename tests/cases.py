@@ -157,3 +157,51 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
     num = np.abs(got - ref).max(axis=1)
     den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
     return float((num / den).max()) if num.size else 0.0
+
+
+# ---------------------------------------------------------------------------
+# Device-side helpers for the GPU parity tests (HIP library through the
+# binding; expected values always come from the oracle on host copies).
+# ---------------------------------------------------------------------------
+
+def lvq_config(lv, c: Cache, **kw):
+    return lv.Config(batch=c.batch, n_heads=c.n_heads, head_dim=c.head_dim,
+                     loop_steps=c.loop_steps, group=c.group, n_sink=c.n_sink,
+                     n_recent=c.n_recent, max_tokens=c.t_max,
+                     codebook_dtype=lv.LVQ_BF16 if c.k_codebook.dtype == torch.bfloat16
+                     else lv.LVQ_F32, **kw)
+
+
+class DeviceCache:
+    """Device copies of a :class:`Cache` plus output and workspace."""
+
+    def __init__(self, lv, c: Cache, device="cuda", **cfg_kw):
+        self.lv = lv
+        self.c = c
+        self.cfg = lvq_config(lv, c, **cfg_kw)
+        d = device
+        self.q = c.q.to(d)
+        self.ctx = torch.tensor(c.lengths, dtype=torch.int32, device=d)
+        self.vq = None if c.vq_len is None else torch.tensor(c.vq_len, dtype=torch.int32, device=d)
+        self.k_index, self.v_index = c.k_index.to(d), c.v_index.to(d)
+        self.k_cb, self.v_cb = c.k_codebook.to(d), c.v_codebook.to(d)
+        self.k_win, self.v_win = c.k_window.to(d), c.v_window.to(d)
+        bufs = lv.allocate(self.cfg, d)
+        self.out, self.ws = bufs["out"], bufs["workspace"]
+
+    def decode(self, t, sm_scale=1.0, cfg=None, max_ctx=None):
+        cfg = cfg or self.cfg
+        self.lv.lvq_decode_attn(cfg, t, self.q[t].contiguous(), self.ctx,
+                                max(self.c.lengths) if max_ctx is None else max_ctx,
+                                self.k_index, self.v_index, self.k_cb, self.v_cb, self.k_win,
+                                self.v_win, self.ws, self.out, sm_scale=sm_scale, vq_len=self.vq)
+        torch.cuda.synchronize()
+        return self.out.double().cpu().numpy()
+
+
+def oracle_decode(oracle_mod, c: Cache, t, sm_scale=1.0, heads=None):
+    return oracle_mod.decode_attn(loop_step=t, q=c.q[t], ctx_len=c.lengths, k_index=c.k_index,
+                                  v_index=c.v_index, k_codebook=c.k_codebook,
+                                  v_codebook=c.v_codebook, k_window=c.k_window,
+                                  v_window=c.v_window, n_sink=c.n_sink, n_recent=c.n_recent,
+                                  group=c.group, sm_scale=sm_scale, vq_len=c.vq_len, heads=heads)

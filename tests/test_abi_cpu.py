@@ -1,0 +1,167 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+``include/loopvq.h`` declares, computes layouts that reproduce the pages'
+bit budgets, and rejects bad arguments before anything is launched."""
+import ctypes
+import json
+import pathlib
+import re
+
+import numpy as np
+import pytest
+
+from sub_bit_vq_amd import loopvq as lv
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+GOLDEN = json.loads((ROOT / "tests" / "golden" / "page_constants.json").read_text())
+
+WORKLOADS = {  # (B, H, d, Tc, G, max_tokens, cb dtype)
+    "tiny_0p5bit_fp32cb": (1, 1, 64, 4, 16, 512, lv.LVQ_F32),
+    "ouro1p4b_layer_32k_0p5bit": (1, 16, 128, 4, 16, 32768, lv.LVQ_BF16),
+    "ouro1p4b_layer_32k_0p25bit": (1, 16, 128, 4, 32, 32768, lv.LVQ_BF16),
+    "batch64_ragged_0p5bit": (64, 16, 128, 4, 16, 18432, lv.LVQ_BF16),
+}
+
+
+def _cfg(B, H, d, Tc, G, T, dt, **kw):
+    return lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G, max_tokens=T,
+                     codebook_dtype=dt, **kw)
+
+
+def test_library_exports_header_symbols():
+    header = (ROOT / "include" / "loopvq.h").read_text()
+    declared = set(re.findall(r"^\s*(?:const\s+char\s*\*|lvq_status|int32_t)\s*(lvq_\w+)\s*\(",
+                              header, flags=re.M))
+    assert declared == set(lv.EXPORTS)
+    lib = lv.library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for s in range(5):
+        assert lv.lvq_status_string(s)
+    assert "unknown" in lv.lvq_status_string(99)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_layout_shapes(name):
+    B, H, d, Tc, G, T, dt = WORKLOADS[name]
+    lay = lv.lvq_cache_layout(_cfg(B, H, d, Tc, G, T, dt))
+    cg = G // Tc
+    S = d // cg
+    assert lay["n_sub"] == S and lay["sub_channels"] == cg and lay["n_codes"] == 256
+    assert lay["k_index"]["shape"] == (B, H, T, S) and lay["k_index"]["bytes"] == B * H * T * S
+    assert lay["k_codebook"]["shape"] == (Tc, H, S, 256, cg)
+    assert lay["k_codebook"]["bytes"] == Tc * H * S * 256 * cg * (2 if dt == lv.LVQ_BF16 else 4)
+    assert lay["k_window"]["shape"] == (B, Tc, H, 64 + 256, d)
+    assert lay["query"]["shape"] == (B, H, d) and lay["output"]["bytes"] == B * H * d * 4
+    assert lay["workspace_bytes"] >= B * H * (lv.LVQ_MAX_SPLITS + 1) * (d + 2) * 4 + B * H * 4
+
+
+def test_layout_reproduces_page_bit_budgets():
+    """bits/element, compression and bytes read per token and loop step, as
+    the project page prints them (Highlights; Efficiency -- Latency), for the
+    loop-step count of its redundancy figure."""
+    Tc = GOLDEN["loop_steps_per_code"]["value"]
+    for row in GOLDEN["bit_budgets"]:
+        G = int(round(8 / row["bits_per_element"]))
+        lay = lv.lvq_cache_layout(_cfg(1, 16, 128, Tc, G, 1024, lv.LVQ_BF16))
+        assert lay["bits_per_element"] == row["bits_per_element"]
+        assert lay["compression_vs_bf16"] == row["compression_vs_bf16"]
+        assert lay["read_reduction_per_step"] == row["bytes_read_reduction_per_token_per_loop_step"]
+
+
+def test_default_windows_match_pages():
+    w = {e["name"]: e["value"] for e in GOLDEN["window"]}
+    cfg = lv.Config(batch=1, n_heads=1, head_dim=64)
+    assert (cfg.n_sink, cfg.n_recent) == (w["n_sink"], w["n_recent"])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(batch=0), dict(n_heads=0), dict(head_dim=0), dict(loop_steps=0), dict(group=18),
+    dict(group=16, head_dim=66), dict(n_sink=-1), dict(n_recent=0), dict(max_tokens=-1),
+    dict(codebook_dtype=7), dict(decode_splits=65), dict(decode_splits=-1),
+])
+def test_layout_rejects_bad_config(bad):
+    base = dict(batch=1, n_heads=2, head_dim=64, loop_steps=4, group=16, max_tokens=100)
+    base.update(bad)
+    with pytest.raises(lv.LoopVQError) as e:
+        lv.lvq_cache_layout(lv.Config(**base))
+    assert e.value.status == lv.LVQ_ERR_INVALID_ARG
+
+
+def test_decode_splits():
+    cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
+    assert lv.lvq_decode_splits(cfg, 32768) == 32        # 512 groups over 16 heads
+    assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded
+    assert lv.lvq_decode_splits(cfg, 320 + 300) == 2     # >= 256 tokens per split
+    assert lv.lvq_decode_splits(cfg, 40000) == 0         # beyond max_tokens
+    cfg3 = _cfg(*WORKLOADS["batch64_ragged_0p5bit"])
+    assert lv.lvq_decode_splits(cfg3, 18432) == 1
+    assert lv.lvq_decode_splits(_cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, decode_splits=7),
+                                32768) == 7
+
+
+# --- argument validation: every case fails before any HIP call ---------------
+
+_HOST = np.zeros(1 << 16, np.uint8)            # an aligned host address; never dereferenced
+P = ctypes.c_void_p((_HOST.ctypes.data + 255) // 256 * 256)
+
+
+def _decode(cfg, **over):
+    lay = lv.lvq_cache_layout(cfg)
+    a = dict(loop_step=0, q=P, ctx_len=P, vq_len=None, max_ctx_len=cfg.max_tokens, k_index=P,
+             v_index=P, k_cb=P, v_cb=P, k_win=P, v_win=P, sm_scale=1.0, ws=P,
+             ws_bytes=lay["workspace_bytes"], out=P)
+    a.update(over)
+    return lv.library().lvq_decode_attn(
+        ctypes.byref(cfg.c()), a["loop_step"], a["q"], a["ctx_len"], a["vq_len"],
+        a["max_ctx_len"], a["k_index"], a["v_index"], a["k_cb"], a["v_cb"], a["k_win"],
+        a["v_win"], ctypes.c_float(a["sm_scale"]), a["ws"], ctypes.c_uint64(a["ws_bytes"]),
+        a["out"], None)
+
+
+def test_decode_validation():
+    cfg = _cfg(1, 2, 64, 4, 16, 1024, lv.LVQ_BF16)
+    INV, UNS, WS = lv.LVQ_ERR_INVALID_ARG, lv.LVQ_ERR_UNSUPPORTED, lv.LVQ_ERR_WORKSPACE
+    assert _decode(cfg, q=None) == INV
+    assert _decode(cfg, k_index=None) == INV
+    assert _decode(cfg, out=None) == INV
+    assert _decode(cfg, loop_step=4) == INV
+    assert _decode(cfg, loop_step=-1) == INV
+    assert _decode(cfg, max_ctx_len=1025) == INV
+    assert _decode(cfg, sm_scale=float("nan")) == INV
+    assert _decode(cfg, k_win=ctypes.c_void_p(P.value + 8)) == INV      # misaligned
+    assert _decode(cfg, ws=None) == WS
+    assert _decode(cfg, ws_bytes=lv.lvq_cache_layout(cfg)["workspace_bytes"] - 1) == WS
+    assert _decode(_cfg(1, 2, 384, 4, 16, 1024, lv.LVQ_BF16)) == UNS     # d > 256
+    assert _decode(_cfg(1, 2, 64, 1, 1, 1024, lv.LVQ_BF16)) == UNS       # cg = 1
+    bad = lv.Config(batch=1, n_heads=1, head_dim=64, group=18)
+    assert lv.library().lvq_decode_attn(ctypes.byref(bad.c()), 0, *([P] * 2), None, 0,
+                                        *([P] * 6), ctypes.c_float(1.0), P,
+                                        ctypes.c_uint64(1 << 30), P, None) == INV
+
+
+def _encode(cfg, **over):
+    a = dict(x=P, strides=None, n=16, cb=P, index=P, seq=0, first=0)
+    a.update(over)
+    st = None if a["strides"] is None else (ctypes.c_int64 * 3)(*a["strides"])
+    return lv.library().lvq_encode(ctypes.byref(cfg.c()), a["x"], st, a["n"], a["cb"], a["index"],
+                                   a["seq"], a["first"], None)
+
+
+def test_encode_validation():
+    cfg = _cfg(2, 2, 64, 4, 16, 100, lv.LVQ_BF16)
+    INV, UNS = lv.LVQ_ERR_INVALID_ARG, lv.LVQ_ERR_UNSUPPORTED
+    assert _encode(cfg, x=None) == INV
+    assert _encode(cfg, cb=None) == INV
+    assert _encode(cfg, index=None) == INV
+    assert _encode(cfg, seq=2) == INV
+    assert _encode(cfg, seq=-1) == INV
+    assert _encode(cfg, first=90, n=11) == INV
+    assert _encode(cfg, n=-1) == INV
+    assert _encode(cfg, strides=(512, 256, 63)) == INV                  # not a multiple of cg
+    assert _encode(cfg, x=ctypes.c_void_p(P.value + 2)) == INV         # misaligned
+    assert _encode(_cfg(1, 1, 64, 4, 64, 100, lv.LVQ_BF16)) == UNS      # G = 64
+    assert _encode(_cfg(1, 1, 128, 4, 32, 100, lv.LVQ_F32)) == UNS      # fp32, G = 32
+    assert _encode(cfg, n=0) == lv.LVQ_OK                              # nothing to launch

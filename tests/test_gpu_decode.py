@@ -1,0 +1,284 @@
+"""GPU parity of lvq_decode_attn against the CPU oracle (MI355X).
+
+Bar: per (b, h) row, max_ch |gpu - oracle| / max_ch |oracle| <= 2e-3 (fp32
+accumulation on the GPU, fp64 in the oracle).  Inputs are seeded; index
+caches are drawn, or encoded by the oracle -- never by the HIP encoder.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cases import (DeviceCache, make_cache, oracle_decode, oracle_encoder, rel_err_rows)
+from sub_bit_vq_amd import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def lv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_bit_vq_amd import loopvq
+    loopvq.library()
+    return loopvq
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _check(dc, t, sm_scale=1.0, heads=None, tol=TOL):
+    got = dc.decode(t, sm_scale)
+    ref = oracle_decode(oracle, dc.c, t, sm_scale, heads=heads)
+    if heads is not None:
+        got, ref = got[:, heads[0]:heads[1]], ref[:, heads[0]:heads[1]]
+    err = rel_err_rows(got, ref)
+    assert np.isfinite(got).all()
+    assert err <= tol, f"loop step {t}: rel err {err:.3e}"
+    return got, err
+
+
+def test_tiny_workload_every_loop_step(lv):
+    """B1 H1 d64 Tc4 G16, fp32 codebooks, 512-token context (middle 192 tokens
+    VQ-coded), indices from the oracle encoder, all four loop steps."""
+    _note("tiny workload")
+    c = make_cache(batch=1, n_heads=1, head_dim=64, group=16, lengths=(512,),
+                   cb_dtype=torch.float32, seed=1000,
+                   encode=oracle_encoder(oracle, 1, 64, 4, 16))
+    dc = DeviceCache(lv, c)
+    for t in range(4):
+        _check(dc, t)
+
+
+SHAPES = [  # (head_dim, group, cb dtype)
+    (64, 16, torch.bfloat16),
+    (128, 16, torch.bfloat16),
+    (128, 32, torch.bfloat16),
+    (64, 32, torch.bfloat16),
+    (64, 16, torch.float32),
+    (128, 8, torch.bfloat16),
+    (256, 16, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("head_dim,group,cb_dtype", SHAPES)
+def test_ragged_shapes(lv, head_dim, group, cb_dtype):
+    """Ragged batch covering L <= 64, <= 320 and > 320, several splits and a
+    ragged tail; VQ tokens are exact codewords of drawn indices."""
+    _note(f"ragged d={head_dim} G={group} {cb_dtype}")
+    lengths = (1, 40, 64, 200, 320, 321, 700, 2500, 5000)
+    c = make_cache(batch=len(lengths), n_heads=2, head_dim=head_dim, group=group,
+                   lengths=lengths, cb_dtype=cb_dtype, seed=head_dim + group,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    for t in (0, 3):
+        _check(dc, t)
+
+
+def test_loop_correlated_encoded_cache(lv):
+    """Realistic (skewed) code histogram: loop-correlated K/V encoded by the
+    oracle, 0.5-bit, 4 heads, 3000-token context."""
+    _note("oracle-encoded cache")
+    c = make_cache(batch=2, n_heads=4, head_dim=128, group=16, lengths=(3000, 1500), seed=7,
+                   encode=oracle_encoder(oracle, 4, 128, 4, 16))
+    dc = DeviceCache(lv, c)
+    for t in range(4):
+        _check(dc, t)
+
+
+def test_split_count_invariance(lv):
+    _note("split invariance")
+    c = make_cache(batch=2, n_heads=2, head_dim=128, group=16, lengths=(9000, 4000), seed=11,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    ref = oracle_decode(oracle, c, 1)
+    outs = []
+    for splits in (1, 2, 5, 17, 64):
+        cfg = dataclasses.replace(dc.cfg, decode_splits=splits)
+        got = dc.decode(1, cfg=cfg)
+        assert rel_err_rows(got, ref) <= TOL, splits
+        outs.append(got)
+    for o in outs[1:]:
+        assert rel_err_rows(o, outs[0]) <= 2e-5
+
+
+def test_token_permutation_invariance(lv):
+    """Permuting the VQ tokens (their K and V index rows together) changes
+    only the rounding."""
+    _note("token permutation")
+    c = make_cache(batch=1, n_heads=2, head_dim=64, group=16, lengths=(4000,), seed=12,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    base = dc.decode(2)
+    lo, hi = c.vq_range(0).start, c.vq_range(0).stop
+    perm = torch.randperm(hi - lo, generator=torch.Generator().manual_seed(3)) + lo
+    dc.k_index[0, :, lo:hi] = dc.k_index[0, :, perm.cuda()]
+    dc.v_index[0, :, lo:hi] = dc.v_index[0, :, perm.cuda()]
+    assert rel_err_rows(dc.decode(2), base) <= 2e-5
+
+
+def test_slice_isolation_nan(lv):
+    """NaN in codebook slices t' != t must not reach the step-t output."""
+    _note("slice isolation")
+    c = make_cache(batch=1, n_heads=2, head_dim=128, group=16, lengths=(2000,), seed=13,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    for t in range(4):
+        clean = oracle_decode(oracle, c, t)
+        kcb, vcb = dc.k_cb.clone(), dc.v_cb.clone()
+        for tp in range(4):
+            if tp != t:
+                dc.k_cb[tp] = float("nan")
+                dc.v_cb[tp] = float("nan")
+        got = dc.decode(t)
+        dc.k_cb.copy_(kcb)
+        dc.v_cb.copy_(vcb)
+        assert np.isfinite(got).all()
+        assert rel_err_rows(got, clean) <= TOL
+
+
+def test_page_lag_vq_len(lv):
+    """vq_len above the exact-window count: the recent ring holds fewer than
+    256 tokens and some of its slots are stale."""
+    _note("page lag")
+    lengths = (700, 1000, 3333)
+    vq = [L - 320 + e for L, e in zip(lengths, (8, 5, 255))]
+    c = make_cache(batch=3, n_heads=2, head_dim=64, group=16, lengths=lengths, seed=14,
+                   codeword_tokens=True, vq_len=vq)
+    dc = DeviceCache(lv, c)
+    for t in (0, 2):
+        _check(dc, t)
+
+
+def test_sm_scale(lv):
+    _note("sm_scale")
+    c = make_cache(batch=1, n_heads=2, head_dim=128, group=16, lengths=(1500,), seed=15,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    _check(dc, 1, sm_scale=0.3)
+    _check(dc, 1, sm_scale=1.0 / np.sqrt(128))   # 1/sqrt(d) applied a second time
+
+
+def test_empty_context_and_repeat(lv):
+    """L = 0 gives zeros; repeated calls on one workspace give identical
+    results (the merge tickets reset themselves)."""
+    _note("empty + repeat")
+    c = make_cache(batch=3, n_heads=2, head_dim=64, group=16, lengths=(1, 900, 1), seed=16,
+                   codeword_tokens=True)
+    c.lengths[0] = 0
+    dc = DeviceCache(lv, c)
+    a = dc.decode(0)
+    assert np.all(a[0] == 0.0)
+    ref = oracle_decode(oracle, c, 0)
+    assert rel_err_rows(a, ref) <= TOL
+    for _ in range(3):
+        assert np.array_equal(dc.decode(0), a)
+    b = dc.decode(3)
+    assert rel_err_rows(b, oracle_decode(oracle, c, 3)) <= TOL
+
+
+def test_max_ctx_len_bound(lv):
+    """max_ctx_len larger than every L (it only sizes the launch)."""
+    _note("max_ctx bound")
+    c = make_cache(batch=2, n_heads=1, head_dim=64, group=16, lengths=(1000, 400), seed=17,
+                   codeword_tokens=True, t_max=6000)
+    dc = DeviceCache(lv, c)
+    lv.lvq_decode_attn(dc.cfg, 1, dc.q[1].contiguous(), dc.ctx, 6000, dc.k_index, dc.v_index,
+                       dc.k_cb, dc.v_cb, dc.k_win, dc.v_win, dc.ws, dc.out)
+    torch.cuda.synchronize()
+    got = dc.out.double().cpu().numpy()
+    assert rel_err_rows(got, oracle_decode(oracle, c, 1)) <= TOL
+
+
+# --- full-size workloads: sampled against the oracle ---------------------------
+
+def _full_size_cache(lv, H, d, G, lengths, seed, device="cuda"):
+    """Device-resident cache at full size: windows from the loop-correlated
+    generator, VQ indices drawn uniformly (drawn, so the oracle can take
+    them as input)."""
+    B = len(lengths)
+    Tc = 4
+    cg = G // Tc
+    S = d // cg
+    T = max(lengths)
+    cfg = lv.Config(batch=B, n_heads=H, head_dim=d, group=G, max_tokens=T)
+    bufs = lv.allocate(cfg, device)
+    kcb = synth.codebooks(H, d, Tc, G, seed + 1, device=device)
+    vcb = synth.codebooks(H, d, Tc, G, seed + 2, device=device)
+    q = synth.queries(B, H, d, Tc, seed + 3, device=device)
+    for b, L in enumerate(lengths):
+        ki = synth.random_indices((H, L, S), seed + 10 + 2 * b, device=device)
+        vi = synth.random_indices((H, L, S), seed + 11 + 2 * b, device=device)
+        bufs["k_index"][b, :, :L] = ki
+        bufs["v_index"][b, :, :L] = vi
+        # only the window tokens are needed in bf16
+        sink, _, recent = synth.window_positions(L, 64, 256)
+        win = list(sink) + list(recent)
+        kt = synth.loop_correlated_kv(len(win), H, Tc, d, seed + 20 + 2 * b, device=device)
+        vt = synth.loop_correlated_kv(len(win), H, Tc, d, seed + 21 + 2 * b, device=device)
+        slots = torch.tensor([synth.window_slot(p, 64, 256) for p in win], device=device)
+        bufs["k_window"][b][:, :, slots, :] = kt.permute(2, 1, 0, 3)
+        bufs["v_window"][b][:, :, slots, :] = vt.permute(2, 1, 0, 3)
+    ctx = torch.tensor(lengths, dtype=torch.int32, device=device)
+    return cfg, bufs, kcb, vcb, q, ctx
+
+
+def _host_slice(t, b):
+    return t[b:b + 1].cpu()
+
+
+@pytest.mark.parametrize("G", [16, 32])
+def test_full_32k_context(lv, G):
+    """One 32768-token sequence, 16 heads, d = 128, 0.5 bit (G = 16) and
+    0.25 bit (G = 32): every head at loop steps 0 and 3 against the oracle,
+    in the launch configuration the benchmark times."""
+    _note(f"32K G={G}")
+    cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 16, 128, G, [32768], seed=100 + G)
+    for t in (0, 3):
+        lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, 32768, bufs["k_index"],
+                           bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
+                           bufs["workspace"], bufs["out"])
+        torch.cuda.synchronize()
+        got = bufs["out"].double().cpu().numpy()
+        ref = oracle.decode_attn(loop_step=t, q=q[t].cpu(), ctx_len=[32768],
+                                 k_index=bufs["k_index"].cpu(), v_index=bufs["v_index"].cpu(),
+                                 k_codebook=kcb.cpu(), v_codebook=vcb.cpu(),
+                                 k_window=bufs["k_window"].cpu(), v_window=bufs["v_window"].cpu(),
+                                 n_sink=64, n_recent=256, group=G)
+        err = rel_err_rows(got, ref)
+        _note(f"  t={t} rel err {err:.2e}")
+        assert err <= TOL
+
+
+def test_batched_ragged_64(lv):
+    """Batch 64, L_b = 2048 + U{4096, 8192, 16384}, 16 heads: sampled (b, h)
+    rows of one sequence per length class against the oracle."""
+    _note("batch 64 ragged")
+    lengths = synth.ragged_lengths(64, seed=1003)
+    cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 16, 128, 16, lengths, seed=300)
+    t = 2
+    lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, max(lengths), bufs["k_index"],
+                       bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
+                       bufs["workspace"], bufs["out"])
+    torch.cuda.synchronize()
+    out = bufs["out"].double().cpu().numpy()
+    picked = {}
+    for b, L in enumerate(lengths):
+        picked.setdefault(L, b)
+    kcb_h, vcb_h = kcb.cpu(), vcb.cpu()
+    for L, b in sorted(picked.items()):
+        ref = oracle.decode_attn(loop_step=t, q=_host_slice(q[t], b), ctx_len=[L],
+                                 k_index=_host_slice(bufs["k_index"], b),
+                                 v_index=_host_slice(bufs["v_index"], b),
+                                 k_codebook=kcb_h, v_codebook=vcb_h,
+                                 k_window=_host_slice(bufs["k_window"], b),
+                                 v_window=_host_slice(bufs["v_window"], b),
+                                 n_sink=64, n_recent=256, group=16, heads=(0, 16))
+        err = rel_err_rows(out[b:b + 1], ref)
+        _note(f"  b={b} L={L} rel err {err:.2e}")
+        assert err <= TOL

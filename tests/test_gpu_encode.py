@@ -1,0 +1,190 @@
+"""GPU parity of lvq_encode against the CPU oracle (MI355X): bit-exact
+indices, including constructed exact ties and near-ties that the MFMA screen
+cannot separate, strided inputs, placement and a sampled full-size run."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from cases import kv_from_codewords
+from sub_bit_vq_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sub_bit_vq_amd import loopvq
+    loopvq.library()
+    return loopvq
+
+
+def _note(msg):
+    print(f"[gpu] {msg}", file=sys.stderr, flush=True)
+
+
+def _gpu_encode(lv, x, cb, H, d, Tc, G, T=None, B=1, seq=0, first=0, fill=0):
+    n = x.shape[0]
+    T = T or first + n
+    dt = lv.LVQ_BF16 if cb.dtype == torch.bfloat16 else lv.LVQ_F32
+    cfg = lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G, max_tokens=T,
+                    codebook_dtype=dt)
+    idx = torch.full((B, H, T, d // (G // Tc)), fill, dtype=torch.uint8, device="cuda")
+    lv.lvq_encode(cfg, x.cuda() if x.device.type != "cuda" else x, cb.cuda(), idx, seq, first)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+def _oracle_encode(x, cb, H, d, Tc, G, T=None, B=1, seq=0, first=0, fill=0):
+    n = x.shape[0]
+    T = T or first + n
+    idx = np.full((B, H, T, d // (G // Tc)), fill, np.uint8)
+    oracle.encode(x, cb, n_heads=H, head_dim=d, loop_steps=Tc, group=G, index=idx, seq=seq,
+                  first_token=first)
+    return idx
+
+
+def _assert_same(got, ref, what):
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}"
+
+
+def test_tiny_workload_fp32_codebooks(lv):
+    """B1 H1 d64 Tc4 G16, fp32 N(0,1) codebooks, 512 loop-correlated tokens."""
+    _note("tiny fp32")
+    x = synth.loop_correlated_kv(512, 1, 4, 64, seed=2000)
+    cb = synth.codebooks(1, 64, 4, 16, seed=2001, dtype=torch.float32)
+    _assert_same(_gpu_encode(lv, x, cb, 1, 64, 4, 16), _oracle_encode(x, cb, 1, 64, 4, 16),
+                 "tiny")
+
+
+SHAPES = [  # (H, d, Tc, G, cb dtype)
+    (2, 128, 4, 16, torch.bfloat16),
+    (2, 128, 4, 32, torch.bfloat16),
+    (3, 64, 4, 16, torch.bfloat16),
+    (2, 64, 4, 8, torch.bfloat16),
+    (2, 64, 2, 16, torch.bfloat16),
+    (1, 64, 8, 16, torch.bfloat16),
+    (1, 64, 4, 32, torch.bfloat16),
+    (2, 64, 4, 16, torch.float32),
+    (1, 64, 4, 8, torch.float32),
+    (1, 64, 8, 16, torch.float32),
+]
+
+
+@pytest.mark.parametrize("H,d,Tc,G,cb_dtype", SHAPES)
+def test_shapes_multi_chunk_ragged_tail(lv, H, d, Tc, G, cb_dtype):
+    """2500 tokens: three 1024-token workgroups, the last one ragged."""
+    _note(f"shape H={H} d={d} Tc={Tc} G={G} {cb_dtype}")
+    seed = H * 1000 + d + Tc * 10 + G
+    x = synth.loop_correlated_kv(2500, H, Tc, d, seed)
+    cb = synth.codebooks(H, d, Tc, G, seed + 1, dtype=cb_dtype)
+    _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
+                 "shape")
+
+
+def test_codeword_inputs(lv):
+    _note("codeword inputs")
+    H, d, Tc, G = 2, 128, 4, 16
+    S = d // (G // Tc)
+    cb = synth.codebooks(H, d, Tc, G, seed=31)
+    idx = synth.random_indices((300, H, S), seed=32)
+    x = kv_from_codewords(idx, cb).to(torch.bfloat16)
+    got = _gpu_encode(lv, x, cb, H, d, Tc, G)
+    assert np.array_equal(got[0].transpose(1, 0, 2), idx.numpy())
+
+
+def _tie_codebook(H, d, Tc, G, seed):
+    """Integer-valued codebooks (small range) so that many codes sit at
+    exactly equal or nearly equal distances from integer-valued inputs."""
+    g = torch.Generator().manual_seed(seed)
+    cg = G // Tc
+    S = d // cg
+    nat = torch.randint(-2, 3, (H, S, 256, Tc, cg), generator=g).float()
+    return nat.permute(3, 0, 1, 2, 4).contiguous()
+
+
+@pytest.mark.parametrize("cb_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("G", [16, 32])
+def test_exact_ties(lv, cb_dtype, G):
+    """Integer codebooks and integer inputs: exact fp32 ties everywhere; the
+    lowest index must win on every sub-vector."""
+    if cb_dtype == torch.float32 and G == 32:
+        pytest.skip("fp32 codebooks are supported for G <= 16")
+    _note(f"exact ties G={G} {cb_dtype}")
+    H, d, Tc = 2, 64, 4
+    cb = _tie_codebook(H, d, Tc, G, seed=40 + G).to(cb_dtype)
+    g = torch.Generator().manual_seed(41)
+    x = torch.randint(-2, 3, (700, H, Tc, d), generator=g).to(torch.bfloat16)
+    _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
+                 "ties")
+
+
+def test_near_ties(lv):
+    """Inputs at (or a few ulps from) the midpoint of two codewords: the two
+    screen values are closer than the screen's error bound, so the exact
+    re-score decides; it must reproduce the oracle bit for bit."""
+    _note("near ties")
+    H, d, Tc, G = 2, 128, 4, 16
+    cg = G // Tc
+    S = d // cg
+    cb = synth.codebooks(H, d, Tc, G, seed=50)
+    g = torch.Generator().manual_seed(51)
+    n = 1200
+    a = torch.randint(0, 256, (n, H, S), generator=g, dtype=torch.uint8)
+    b = torch.randint(0, 256, (n, H, S), generator=g, dtype=torch.uint8)
+    xa = kv_from_codewords(a, cb).float()
+    xb = kv_from_codewords(b, cb).float()
+    mid = 0.5 * (xa + xb)
+    jitter = torch.randint(-2, 3, mid.shape, generator=g).float() * 2.0 ** -8 * mid.abs()
+    x = (mid + jitter).to(torch.bfloat16)
+    _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
+                 "near ties")
+
+
+def test_strided_input_from_window_buffer(lv):
+    """Encode a page of 8 recent tokens straight from the bf16 window buffer
+    ([b][t][h][slot][d]) into rows of sequence 1 (the eviction-page case)."""
+    _note("strided window page")
+    H, d, Tc, G, B = 2, 128, 4, 16, 2
+    W = 320
+    win = synth.loop_correlated_kv(B * W, H, Tc, d, seed=60).view(B, W, H, Tc, d)
+    win = win.permute(0, 3, 2, 1, 4).contiguous()                 # [B][Tc][H][W][d]
+    cb = synth.codebooks(H, d, Tc, G, seed=61)
+    slots = slice(64 + 16, 64 + 24)
+    dwin = win.cuda()
+    x_dev = dwin[1][:, :, slots, :].permute(2, 1, 0, 3)           # [8][H][Tc][d] view
+    assert not x_dev.is_contiguous()
+    got = _gpu_encode(lv, x_dev, cb, H, d, Tc, G, T=500, B=B, seq=1, first=400, fill=0xAB)
+    x_host = win[1][:, :, slots, :].permute(2, 1, 0, 3).contiguous()
+    ref = _oracle_encode(x_host, cb, H, d, Tc, G, T=500, B=B, seq=1, first=400, fill=0xAB)
+    _assert_same(got, ref, "strided")
+
+
+def test_placement_and_untouched_rows(lv):
+    _note("placement")
+    H, d, Tc, G = 2, 64, 4, 16
+    x = synth.loop_correlated_kv(77, H, Tc, d, seed=70)
+    cb = synth.codebooks(H, d, Tc, G, seed=71)
+    got = _gpu_encode(lv, x, cb, H, d, Tc, G, T=300, B=3, seq=2, first=123, fill=0xCD)
+    ref = _oracle_encode(x, cb, H, d, Tc, G, T=300, B=3, seq=2, first=123, fill=0xCD)
+    _assert_same(got, ref, "placement")
+
+
+def test_full_prefill_sampled(lv):
+    """32768 tokens x 16 heads x 4 loop steps x 128 channels, G = 16 (the
+    prefill-encoder workload): the GPU encodes everything, the oracle a seeded
+    sample of 256 tokens (all heads and sub-vectors)."""
+    _note("full prefill sampled")
+    N, H, Tc, d, G = 32768, 16, 4, 128, 16
+    x = synth.loop_correlated_kv(N, H, Tc, d, seed=1004, device="cuda")
+    cb = synth.codebooks(H, d, Tc, G, seed=1005, device="cuda")
+    got = _gpu_encode(lv, x, cb, H, d, Tc, G)[0]                 # [H][N][S]
+    pick = torch.randperm(N, generator=torch.Generator().manual_seed(9))[:256].sort().values
+    xs = x[pick.cuda()].cpu()
+    ref = _oracle_encode(xs, cb.cpu(), H, d, Tc, G)[0]            # [H][256][S]
+    _assert_same(got[:, pick.numpy()], ref, "prefill sample")
