@@ -135,6 +135,25 @@ class Setup:
         return PAGE * self.Tc * self.B * self.L
 
 
+class PrefillEncode:
+    """Prefill encoder workload: 32768 tokens x 16 heads x 4 loop steps x 128
+    channels of bf16 K (and V), G = 16, into a 32768-row index cache."""
+
+    N = 32768
+
+    def __init__(self, lv, synth, torch, setup, seed=1004):
+        dev = torch.device("cuda")
+        self.lv = lv
+        self.cfg = lv.Config(batch=1, n_heads=setup.H, head_dim=setup.d, loop_steps=setup.Tc,
+                             group=setup.G, max_tokens=self.N)
+        self.x = synth.loop_correlated_kv(self.N, setup.H, setup.Tc, setup.d, seed, device=dev)
+        self.cb = setup.kcb
+        self.idx = lv.allocate(self.cfg, dev)["k_index"]
+
+    def run(self):
+        self.lv.lvq_encode(self.cfg, self.x, self.cb, self.idx, 0, 0)
+
+
 def spin_cycles_for(torch, ms):
     """Cycles of torch's spin kernel that last about ``ms`` milliseconds."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -212,6 +231,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run N decode launches (for rocprofv3 runs) and exit")
+    ap.add_argument("--profile-encode", type=int, default=0,
+                    help="only run N prefill encodes of 32768 tokens (for rocprofv3 runs) and exit")
+    ap.add_argument("--copy-calibrate", action="store_true",
+                    help="with --profile-*: also run plain 512 MiB device copies, whose HBM "
+                         "counters give the scale of FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -229,11 +253,23 @@ def main():
     log(f"rotation over {setup.rotate} cache copies, "
         f"{lv.lvq_decode_splits(setup.cfg, setup.L)} VQ splits per head")
 
-    if args.profile_decode:
+    if args.profile_decode or args.profile_encode:
+        if args.copy_calibrate:
+            src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log("ran 3 copies of 536870912 bytes")
+            del src, dst
         for i in range(args.profile_decode):
             setup.decode(i % PAGE, i % setup.Tc)
+        if args.profile_encode:
+            enc = PrefillEncode(lv, synth, torch, setup)
+            for _ in range(args.profile_encode):
+                enc.run()
         torch.cuda.synchronize()
-        log(f"ran {args.profile_decode} decode launches")
+        log(f"ran {args.profile_decode} decode launches, {args.profile_encode} prefill encodes")
         return
 
     # warmup (eager), then capture one step in a graph
@@ -303,7 +339,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<32,4,bf16>" if setup.G == 16 else "decode_kernel<16,8,bf16>",
+            "kernel": ("lvq_decode_attn = decode_main<%d,%d,bf16> + decode_merge<%d>"
+                       % (setup.d // (setup.G // setup.Tc), setup.G // setup.Tc, setup.d)),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

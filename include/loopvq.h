@@ -156,7 +156,12 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  *   out = sum_n softmax_n(sm_scale * q . K_n) V_n
  * over all L_b tokens, where VQ tokens use K_n[j*cg + c] =
  * k_codebook[t][h][j][k_index[b][h][n][j]][c] (likewise V) and sink/recent
- * tokens use the bf16 window buffers of step t.  fp32 accumulation.
+ * tokens use the bf16 window buffers of step t.  fp32 accumulation; VQ value
+ * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
+ * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).
+ * Two kernel launches on `stream`: the split workgroups, then the merge.
+ * Results agree across runs to rounding only (partial sums are combined in
+ * an order that depends on the split count, not on scheduling).
  *
  * q          device bf16 [B][H][d]
  * ctx_len    device int32 [B]: L_b, precondition 0 <= L_b <= max_tokens
@@ -166,13 +171,17 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  *            device; a recent window longer than n_recent keeps only the
  *            newest n_recent tokens).
  * max_ctx_len host int32: an upper bound of every L_b; sizes the launch.
- * workspace  device, >= layout.workspace_bytes; zero-filled once after
- *            allocation; every completed call leaves it zero-filled again.
+ * k_codebook, v_codebook  16-byte aligned.
+ * workspace  device, >= layout.workspace_bytes, 256-byte aligned; needs no
+ *            initialisation (each call writes every slot it reads).
  * out        device fp32 [B][H][d]
- * Errors: LVQ_ERR_INVALID_ARG (null pointers, loop_step outside [0, Tc),
- * max_ctx_len outside [0, max_tokens], sm_scale not finite),
- * LVQ_ERR_UNSUPPORTED (d > 256 or d % 8 != 0, S not in {8, 16, 32, 64},
- * cg not in {2, 4, 8}), LVQ_ERR_WORKSPACE, LVQ_ERR_HIP.
+ * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
+ * outside [0, Tc), max_ctx_len outside [0, max_tokens], sm_scale not
+ * finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64}, cg not in
+ * {2, 4, 8}, or the score table (4*S*256 bytes) plus the value table
+ * (S*256*cg entries of 2 bytes for bf16, 4 for fp32 codebooks) of one
+ * (head, loop step) above ~150 KiB of LDS: e.g. d = 256 at G = 16),
+ * LVQ_ERR_WORKSPACE, LVQ_ERR_HIP.
  */
 lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void *q,
                            const int32_t *ctx_len, const int32_t *vq_len,
@@ -182,8 +191,9 @@ lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void 
                            const void *v_window, float sm_scale, void *workspace,
                            uint64_t workspace_bytes, float *out, void *stream);
 
-/* Number of VQ splits per (b, h) lvq_decode_attn launches for max_ctx_len
- * (host arithmetic only); 0 on an invalid config. */
+/* Number of workgroups per (b, h) that lvq_decode_attn launches for
+ * max_ctx_len with exact windows (vq_len == NULL); host arithmetic only; 0 on
+ * an invalid config. */
 int32_t lvq_decode_splits(const lvq_config *cfg, int32_t max_ctx_len);
 
 /* Static, NUL-terminated description of a status code. */

@@ -6,11 +6,11 @@
 
 namespace lvq {
 
-// Workspace of lvq_decode_attn: per (b, h), LVQ_MAX_SPLITS + 1 partial slots of
-// (m, l, o[d]) floats (slot 0 = bf16 windows, slots 1.. = VQ splits), then one
-// uint32 arrival ticket per (b, h).
+// Workspace of lvq_decode_attn: per (b, h), kSlots partial slots of
+// (m, l, o[d]) floats, one per split (every call writes all of its splits
+// before the merge kernel reads them).
 constexpr int kMaxSplits = 64;
-constexpr int kSlots = kMaxSplits + 1;
+constexpr int kSlots = kMaxSplits;
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
@@ -18,14 +18,14 @@ inline uint64_t partial_bytes(int64_t B, int64_t H, int64_t d) {
     return align_up((uint64_t)B * H * kSlots * (d + 2) * sizeof(float), 256);
 }
 inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
-    return partial_bytes(B, H, d) + align_up((uint64_t)B * H * sizeof(uint32_t), 256);
+    return partial_bytes(B, H, d);
 }
 
 struct DecodeArgs {
     int B, H, d, Tc, cg, S, n_sink, n_recent;
     int64_t t_max;
     int loop_step;
-    int n_split;      // VQ splits per (b, h)
+    int n_split;      // workgroups per (b, h): VQ chunks and window-slot ranges
     int chunk;        // VQ tokens per split (multiple of 64)
     int cb_bf16;
     const uint16_t *q;          // [B][H][d]
@@ -39,7 +39,6 @@ struct DecodeArgs {
     const uint16_t *v_win;
     float sm_scale;
     float *partials;            // [B][H][kSlots][d + 2]
-    uint32_t *tickets;          // [B][H]
     float *out;                 // [B][H][d]
 };
 
@@ -58,7 +57,7 @@ struct EncodeArgs {
 
 // Kernel-support predicates (host) and launchers (return the HIP error of the
 // launch).
-bool decode_supported(int d, int S, int cg);
+bool decode_supported(int d, int S, int cg, int cb_bf16);
 bool encode_supported(int G, int cg, int cb_bf16);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);

@@ -44,17 +44,21 @@ int64_t max_vq_tokens(const lvq_config *c, int32_t max_ctx_len, bool exact_windo
     return v > 0 ? v : 0;
 }
 
-// Splits per (b, h): enough workgroups to occupy the chip (about two per
-// compute unit across 256 CUs), each split at least 256 tokens.
+// Splits per (b, h).  One decode workgroup fills a compute unit's LDS, so
+// aim for one workgroup per CU (256 on MI355X), keep splits at least 512
+// tokens long, and cut long ragged contexts into chunks of at most ~8K tokens
+// so that the longest sequences do not leave a tail.
 int32_t choose_splits(const lvq_config *c, int64_t max_vq) {
     if (max_vq <= 0) return 1;
     int64_t want = c->decode_splits;
     if (want == 0) {
-        const int64_t target_groups = 512;
+        const int64_t target_groups = 256;
         const int64_t bh = (int64_t)c->batch * c->n_heads;
         want = (target_groups + bh - 1) / bh;
-        const int64_t by_len = (max_vq + 255) / 256;
+        const int64_t by_len = (max_vq + 511) / 512;
         if (want > by_len) want = by_len;
+        const int64_t by_chunk = (max_vq + 8191) / 8192;
+        if (want < by_chunk) want = by_chunk;
     }
     if (want < 1) want = 1;
     if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
@@ -177,12 +181,17 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
             return LVQ_ERR_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(k_window) % 16 || reinterpret_cast<uintptr_t>(v_window) % 16)
             return LVQ_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(k_codebook) % 16 ||
+            reinterpret_cast<uintptr_t>(v_codebook) % 16)
+            return LVQ_ERR_INVALID_ARG;
     }
     const int cg = c->group / c->loop_steps;
     const int S = c->head_dim / cg;
-    if (!lvq::decode_supported(c->head_dim, S, cg)) return LVQ_ERR_UNSUPPORTED;
+    if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16))
+        return LVQ_ERR_UNSUPPORTED;
     const uint64_t need = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
     if (!workspace || workspace_bytes < need) return LVQ_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
 
     const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
     const int32_t n_split = choose_splits(c, max_vq);
@@ -215,8 +224,6 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.v_win = static_cast<const uint16_t *>(v_window);
     a.sm_scale = sm_scale;
     a.partials = static_cast<float *>(workspace);
-    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
-                                             lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
     a.out = out;
     hipError_t e = lvq::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;

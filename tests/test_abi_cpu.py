@@ -55,7 +55,7 @@ def test_layout_shapes(name):
     assert lay["k_codebook"]["bytes"] == Tc * H * S * 256 * cg * (2 if dt == lv.LVQ_BF16 else 4)
     assert lay["k_window"]["shape"] == (B, Tc, H, 64 + 256, d)
     assert lay["query"]["shape"] == (B, H, d) and lay["output"]["bytes"] == B * H * d * 4
-    assert lay["workspace_bytes"] >= B * H * (lv.LVQ_MAX_SPLITS + 1) * (d + 2) * 4 + B * H * 4
+    assert lay["workspace_bytes"] >= B * H * lv.LVQ_MAX_SPLITS * (d + 2) * 4
 
 
 def test_layout_reproduces_page_bit_budgets():
@@ -92,12 +92,12 @@ def test_layout_rejects_bad_config(bad):
 
 def test_decode_splits():
     cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
-    assert lv.lvq_decode_splits(cfg, 32768) == 32        # 512 groups over 16 heads
+    assert lv.lvq_decode_splits(cfg, 32768) == 16        # 256 workgroups over 16 heads
     assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded
-    assert lv.lvq_decode_splits(cfg, 320 + 300) == 2     # >= 256 tokens per split
+    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 3    # >= 512 tokens per split
     assert lv.lvq_decode_splits(cfg, 40000) == 0         # beyond max_tokens
     cfg3 = _cfg(*WORKLOADS["batch64_ragged_0p5bit"])
-    assert lv.lvq_decode_splits(cfg3, 18432) == 1
+    assert lv.lvq_decode_splits(cfg3, 18432) == 3        # chunks of at most ~8K tokens
     assert lv.lvq_decode_splits(_cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, decode_splits=7),
                                 32768) == 7
 
@@ -134,7 +134,10 @@ def test_decode_validation():
     assert _decode(cfg, k_win=ctypes.c_void_p(P.value + 8)) == INV      # misaligned
     assert _decode(cfg, ws=None) == WS
     assert _decode(cfg, ws_bytes=lv.lvq_cache_layout(cfg)["workspace_bytes"] - 1) == WS
-    assert _decode(_cfg(1, 2, 384, 4, 16, 1024, lv.LVQ_BF16)) == UNS     # d > 256
+    assert _decode(_cfg(1, 2, 384, 4, 16, 1024, lv.LVQ_BF16)) == UNS     # S = 96
+    assert _decode(_cfg(1, 2, 256, 4, 16, 1024, lv.LVQ_BF16)) == UNS     # tables exceed LDS
+    assert _decode(_cfg(1, 2, 128, 4, 16, 1024, lv.LVQ_F32)) == UNS      # fp32 tables too big
+    assert _decode(_cfg(1, 2, 64, 4, 16, 1024, lv.LVQ_BF16), k_cb=ctypes.c_void_p(P.value + 8)) == INV
     assert _decode(_cfg(1, 2, 64, 1, 1, 1024, lv.LVQ_BF16)) == UNS       # cg = 1
     bad = lv.Config(batch=1, n_heads=1, head_dim=64, group=18)
     assert lv.library().lvq_decode_attn(ctypes.byref(bad.c()), 0, *([P] * 2), None, 0,
