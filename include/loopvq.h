@@ -159,9 +159,9 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  * tokens use the bf16 window buffers of step t.  fp32 accumulation; VQ value
  * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
  * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).
- * Two kernel launches on `stream`: the split workgroups, then the merge.
- * Results agree across runs to rounding only (partial sums are combined in
- * an order that depends on the split count, not on scheduling).
+ * One kernel launch on `stream`; the last workgroup of every (b, h) merges
+ * the split partials.  Results depend on the split count only through
+ * rounding.
  *
  * q          device bf16 [B][H][d]
  * ctx_len    device int32 [B]: L_b, precondition 0 <= L_b <= max_tokens
@@ -172,8 +172,9 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  *            newest n_recent tokens).
  * max_ctx_len host int32: an upper bound of every L_b; sizes the launch.
  * k_codebook, v_codebook  16-byte aligned.
- * workspace  device, >= layout.workspace_bytes, 256-byte aligned; needs no
- *            initialisation (each call writes every slot it reads).
+ * workspace  device, >= layout.workspace_bytes, 256-byte aligned; zero-filled
+ *            once after allocation; every completed call leaves it valid for
+ *            the next (its arrival counters return to zero).
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
  * outside [0, Tc), max_ctx_len outside [0, max_tokens], sm_scale not

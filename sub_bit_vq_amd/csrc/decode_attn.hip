@@ -5,24 +5,26 @@
 // are read from shared 8-bit indices through codebook slice t, and the result
 // is merged with bf16 attention over the sink and recent tokens.
 //
-// Two launches per call:
-//  decode_main, grid (n_split, H, B), 512 threads.  Workgroup s of (b, h)
-//    takes VQ tokens [n_s + s*chunk, ...) and window slots
-//    [s*W/n_split, (s+1)*W/n_split).  It stages two tables in LDS:
-//      T[j][k]  = log2(e) * sm_scale * sum_c q[j*cg + c] * Bk_t[j][k][c]  (fp32)
-//      V[j][k]  = Bv_t[j][k][0..cg)  (fp16 for bf16 codebooks, else fp32)
-//    A token's score is sum_j T[j][idxK[n][j]] (S gathers) and its value
-//    row is gathered as V[j][idxV[n][j]] (S gathers of cg entries).
-//    R = S/8 lanes share a token, each owning 8 sub-vectors (8*cg output
-//    channels); every wave keeps its own running max, weight sum and
-//    accumulators (online softmax, base 2), so tiles need no barrier.
-//    Token weights p = 2^(s - m) enter the value sum as fp16 p * 2^14 through
-//    v_dot2_f32_f16, and the weight sum adds the same rounded values, so the
-//    result is an exact weighted average with weights perturbed by at most
-//    2^-11 relative.  Waves combine in LDS; the workgroup stores (m, l, o).
-//  decode_merge, grid (H, B): log-sum-exp merge of the n_split partials.
-// The kernel boundary orders the partial stores before the merge's loads;
-// no device-scope fence is needed.
+// One launch, n_split * H * B workgroups of 512 threads.  Workgroup s of (b, h) takes
+// VQ tokens [n_s + s*chunk, ...) and window slots [s*W/n_split, ...).  It
+// stages two tables of (h, t) in LDS:
+//     T[j][k] = log2(e) * sm_scale * sum_c q[j*cg + c] * Bk_t[j][k][c]  (fp32)
+//     V[j][k] = Bv_t[j][k][0..cg)  (fp16 for bf16 codebooks, else fp32)
+// A token's score is sum_j T[j][idxK[n][j]] (S gathers) and its value row is
+// gathered as V[j][idxV[n][j]] (S gathers of cg entries).  R = S/8 lanes
+// share a token, each owning 8 sub-vectors (8*cg output channels).  Every
+// wave keeps its own running max, weight sum and accumulators (online
+// softmax, base 2), so the token loop has no barrier; cross-lane reductions
+// use DPP, never the LDS crossbar, which the gathers saturate.  Token weights
+// p = 2^(s - m) enter the value sum as fp16 p * 2^14 through v_dot2_f32_f16,
+// and the weight sum adds the same rounded values, so the result is an exact
+// weighted average with weights perturbed by at most 2^-11 relative.
+// Index rows stream from HBM through a three-deep register ring; the first
+// two batches are issued before the tables are staged.
+// Each workgroup stores (m, l, o[d]) and takes a ticket; the last arrival of
+// (b, h) merges the partials (log-sum-exp) into out and resets the ticket.
+// Partials and tickets travel through agent-scope atomics only (no L2
+// writeback or invalidation).
 #include "kernels.h"
 
 #include <math.h>
@@ -34,7 +36,8 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;                     // token passes in flight per wave
+constexpr int kUnroll = 4;                     // token passes per batch
+constexpr int kRing = 3;                       // batches in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPScale = 16384.f;             // p' = p * 2^14 (normal in fp16 down to p ~ 4e-9)
 constexpr int kLdsLimit = 160 * 1024;
@@ -62,8 +65,9 @@ struct Shape {
     static constexpr int VB = kF16V ? 2 : 4;   // bytes per value-table entry
     static constexpr int kLut = S * 256;       // floats
     static constexpr int kVtabWords = S * 256 * CG * VB / 4;
-    static constexpr int kScratch = kWaves * (D + 2);
+    static constexpr int kScratch = kWaves * (2 + 4 * D);
     static constexpr int kLds = 4 * (kLut + kVtabWords + kScratch + D) + 64;
+    static_assert(S >= 8 && S % 8 == 0, "8 sub-vectors per lane");
 };
 
 struct Windows {
@@ -96,15 +100,51 @@ __device__ __forceinline__ bool slot_valid(int slot, const Windows &w, int n_sin
     return pos >= w.n_s + w.n_v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+// DPP lane permutations (VALU only): quad_perm xor 1, xor 2, row_ror 4, 8,
+// row_half_mirror
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kXor1 = 0xB1, kXor2 = 0x4E, kRor4 = 0x124, kRor8 = 0x128, kHalfMirror = 0x141;
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// sum over the R consecutive lanes of a token
+template <int R>
+__device__ __forceinline__ float token_sum(float v) {
+    if constexpr (R >= 2) v += dppf<kXor1>(v);
+    if constexpr (R >= 4) v += dppf<kXor2>(v);
+    if constexpr (R >= 8) v += dppf<kHalfMirror>(v);
     return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+
+// sum over the lanes of a 16-lane row that share lane % R
+template <int R>
+__device__ __forceinline__ float row_sum_same_r(float v) {
+    if constexpr (R <= 1) v += dppf<kXor1>(v);
+    if constexpr (R <= 2) v += dppf<kXor2>(v);
+    if constexpr (R <= 4) v += dppf<kRor4>(v);
+    v += dppf<kRor8>(v);
     return v;
+}
+
+// wave-uniform maximum / sum
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dppf<kXor1>(v));
+    v = fmaxf(v, dppf<kXor2>(v));
+    v = fmaxf(v, dppf<kRor4>(v));
+    v = fmaxf(v, dppf<kRor8>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dppf<kXor1>(v);
+    v += dppf<kXor2>(v);
+    v += dppf<kRor4>(v);
+    v += dppf<kRor8>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
 // Per-wave online-softmax state: running max m (base 2), weight sum l (scaled
@@ -134,113 +174,145 @@ struct Online {
 // ---------------------------------------------------------------------------
 // Table staging: score table and value table of (h, loop step t) into LDS.
 // ---------------------------------------------------------------------------
+// Table staging for (h, loop step t), in two phases so that the loads can be
+// issued before q is known: load() reads the K and V slices into registers,
+// finish() writes the score table and the value table into LDS.
 template <int S, int CG, typename CB>
-__device__ __forceinline__ void stage_tables(const DecodeArgs &a, int h, const float *qs,
-                                             float *lut, uint32_t *vtab) {
+struct Stage {
     using Sh = Shape<S, CG, CB>;
-    const size_t slice = ((size_t)a.loop_step * a.H + h) * (size_t)Sh::kLut * CG;
-    const CB *kcb = static_cast<const CB *>(a.k_cb) + slice;
-    const CB *vcb = static_cast<const CB *>(a.v_cb) + slice;
-    const int tid = threadIdx.x;
-    // T[e], e = j*256 + k: dot of q[j*cg ..] with codeword entries (contiguous)
-    constexpr int PER = Sh::kLut / kThreads;
-    static_assert(Sh::kLut % kThreads == 0, "score table must tile the workgroup");
-    float cw[PER][CG];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = tid + u * kThreads;
-#pragma unroll
-        for (int c = 0; c < CG; ++c) cw[u][c] = cb_at(kcb + (size_t)e * CG, c);
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = tid + u * kThreads;
-        const int j = e >> 8;
-        float acc = 0.f;
-#pragma unroll
-        for (int c = 0; c < CG; ++c) acc += qs[j * CG + c] * cw[u][c];
-        lut[e] = acc;
-    }
-    // value table: same entry order, converted to fp16 (bf16 codebooks) or
-    // copied (fp32 codebooks); 16 bytes of source per step
-    if constexpr (Sh::kF16V) {
-        constexpr int N8 = Sh::kLut * CG / 8;          // groups of 8 bf16
-        const uint4 *src = reinterpret_cast<const uint4 *>(vcb);
-        uint4 *dst = reinterpret_cast<uint4 *>(vtab);
-        for (int g = tid; g < N8; g += kThreads) {
-            const uint4 v = src[g];
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const half2_t hp = {(_Float16)bf16lo(w[i]), (_Float16)bf16hi(w[i])};
-                o[i] = __builtin_bit_cast(uint32_t, hp);
-            }
-            dst[g] = make_uint4(o[0], o[1], o[2], o[3]);
-        }
-    } else {
-        constexpr int N4 = Sh::kLut * CG / 4;          // groups of 4 fp32
-        const uint4 *src = reinterpret_cast<const uint4 *>(vcb);
-        uint4 *dst = reinterpret_cast<uint4 *>(vtab);
-        for (int g = tid; g < N4; g += kThreads) dst[g] = src[g];
-    }
-}
+    static constexpr int PER = Sh::kLut / kThreads;               // score entries per thread
+    static constexpr int KW = CG * (int)sizeof(CB) / 4;           // 32-bit words per entry
+    static constexpr int VGROUPS = Sh::kLut * CG * (int)sizeof(CB) / 16;
+    static constexpr int VPER = VGROUPS / kThreads;               // 16-byte V groups per thread
+    static_assert(Sh::kLut % kThreads == 0 && VGROUPS % kThreads == 0, "tables must tile");
+    uint32_t kw[PER][KW];
+    uint4 vv[VPER];
 
-// ---------------------------------------------------------------------------
-// Dense bf16 window slots [s0, s1): R lanes per slot, each owning CL channels.
-// ---------------------------------------------------------------------------
-template <int S, int CG, typename CB, typename OnlineT>
-__device__ __forceinline__ void window_slots(const DecodeArgs &a, int b, int h, const Windows &w,
-                                             int s0, int s1, const float *qs, OnlineT &st) {
-    using Sh = Shape<S, CG, CB>;
-    constexpr int D = Sh::D, R = Sh::R, TPW = Sh::TPW, CL = Sh::CL;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane % R, tg = lane / R;
-    const int W = a.n_sink + a.n_recent;
-    const size_t base = (((size_t)b * a.Tc + a.loop_step) * a.H + h) * (size_t)W * D + r * CL;
-    const uint16_t *kw = a.k_win + base;
-    const uint16_t *vw = a.v_win + base;
-    for (int sb = s0 + wave * TPW; sb < s1; sb += kWaves * TPW) {   // wave-uniform loop
-        const int slot = sb + tg;
-        const bool ok = slot < s1 && slot_valid(slot, w, a.n_sink, a.n_recent);
-        float dot = 0.f;
-        uint32_t vv[CL / 2];
-        if (ok) {
-            const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)slot * D);
-            const uint4 *vp = reinterpret_cast<const uint4 *>(vw + (size_t)slot * D);
+    __device__ __forceinline__ void load(const DecodeArgs &a, int h) {
+        const size_t slice = ((size_t)a.loop_step * a.H + h) * (size_t)Sh::kLut * CG;
+        const CB *kcb = static_cast<const CB *>(a.k_cb) + slice;
+        const uint4 *vcb = reinterpret_cast<const uint4 *>(static_cast<const CB *>(a.v_cb) + slice);
+        const int tid = threadIdx.x;
 #pragma unroll
-            for (int i = 0; i < CL / 8; ++i) {
-                const uint4 kk = kp[i];
-                const uint4 v4 = vp[i];
-                const uint32_t kwd[4] = {kk.x, kk.y, kk.z, kk.w};
-                vv[4 * i + 0] = v4.x;
-                vv[4 * i + 1] = v4.y;
-                vv[4 * i + 2] = v4.z;
-                vv[4 * i + 3] = v4.w;
+        for (int u = 0; u < PER; ++u) {
+            const uint32_t *src =
+                reinterpret_cast<const uint32_t *>(kcb + (size_t)(tid + u * kThreads) * CG);
+            if constexpr (KW == 1) {
+                kw[u][0] = src[0];
+            } else if constexpr (KW == 2) {
+                const uint2 t = *reinterpret_cast<const uint2 *>(src);
+                kw[u][0] = t.x;
+                kw[u][1] = t.y;
+            } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    dot += qs[r * CL + 8 * i + 2 * e] * bf16lo(kwd[e]);
-                    dot += qs[r * CL + 8 * i + 2 * e + 1] * bf16hi(kwd[e]);
+                for (int i = 0; i < KW; i += 4) {
+                    const uint4 t = *reinterpret_cast<const uint4 *>(src + i);
+                    kw[u][i] = t.x;
+                    kw[u][i + 1] = t.y;
+                    kw[u][i + 2] = t.z;
+                    kw[u][i + 3] = t.w;
                 }
             }
         }
 #pragma unroll
-        for (int off = 1; off < R; off <<= 1) dot += __shfl_xor(dot, off);
+        for (int u = 0; u < VPER; ++u) vv[u] = vcb[tid + u * kThreads];
+    }
+
+    __device__ __forceinline__ void finish(const float *qs, float *lut, uint32_t *vtab) const {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + u * kThreads;
+            const int j = e >> 8;
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                float v;
+                if constexpr (Sh::kF16V)
+                    v = (c & 1) ? bf16hi(kw[u][c >> 1]) : bf16lo(kw[u][c >> 1]);
+                else
+                    v = __uint_as_float(kw[u][c]);
+                acc += qs[j * CG + c] * v;
+            }
+            lut[e] = acc;
+        }
+#pragma unroll
+        for (int u = 0; u < VPER; ++u) {
+            if constexpr (Sh::kF16V) {
+                // 8 bf16 -> 8 fp16 at the same element offset
+                const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const half2_t hp = {(_Float16)bf16lo(w[i]), (_Float16)bf16hi(w[i])};
+                    o[i] = __builtin_bit_cast(uint32_t, hp);
+                }
+                reinterpret_cast<uint4 *>(vtab)[tid + u * kThreads] = make_uint4(o[0], o[1], o[2], o[3]);
+            } else {
+                reinterpret_cast<uint4 *>(vtab)[tid + u * kThreads] = vv[u];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Dense bf16 window slots [s0, s1): R lanes per slot, each owning CL channels.
+// Rows of one pass are loaded by `load`, then folded in by `fold`.
+// ---------------------------------------------------------------------------
+template <int S, int CG, typename CB>
+struct WindowPass {
+    using Sh = Shape<S, CG, CB>;
+    static constexpr int CL = Sh::CL;
+    uint32_t k[CL / 2], v[CL / 2];
+    bool ok;
+
+    __device__ __forceinline__ void load(const DecodeArgs &a, int b, int h, const Windows &w,
+                                         int slot, int s1) {
+        constexpr int D = Sh::D, R = Sh::R;
+        const int r = (threadIdx.x & 63) % R;
+        ok = slot < s1 && slot_valid(slot, w, a.n_sink, a.n_recent);
+        if (!ok) return;
+        const int W = a.n_sink + a.n_recent;
+        const size_t off = ((((size_t)b * a.Tc + a.loop_step) * a.H + h) * (size_t)W + slot) * D +
+                           r * CL;
+        const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_win + off);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_win + off);
+#pragma unroll
+        for (int i = 0; i < CL / 8; ++i) {
+            const uint4 kk = kp[i], vv = vp[i];
+            k[4 * i] = kk.x; k[4 * i + 1] = kk.y; k[4 * i + 2] = kk.z; k[4 * i + 3] = kk.w;
+            v[4 * i] = vv.x; v[4 * i + 1] = vv.y; v[4 * i + 2] = vv.z; v[4 * i + 3] = vv.w;
+        }
+    }
+
+    template <typename OnlineT>
+    __device__ __forceinline__ void fold(const float *qs, OnlineT &st) {
+        constexpr int R = Sh::R;
+        const int r = (threadIdx.x & 63) % R;
+        float dot = 0.f;
+        if (ok) {
+#pragma unroll
+            for (int i = 0; i < CL / 2; ++i) {
+                dot += qs[r * CL + 2 * i] * bf16lo(k[i]);
+                dot += qs[r * CL + 2 * i + 1] * bf16hi(k[i]);
+            }
+        }
+        dot = token_sum<R>(dot);
         const float s = ok ? dot : -INFINITY;
         const float mx = wave_max(s);
-        if (mx == -INFINITY) continue;
+        if (mx == -INFINITY) return;              // wave-uniform
         st.raise(mx);
         if (ok) {
             const float p = exp2f(s - st.m) * kPScale;
             if (r == 0) st.l += p;
 #pragma unroll
             for (int i = 0; i < CL / 2; ++i) {
-                st.acc[2 * i] += p * bf16lo(vv[i]);
-                st.acc[2 * i + 1] += p * bf16hi(vv[i]);
+                st.acc[2 * i] += p * bf16lo(v[i]);
+                st.acc[2 * i + 1] += p * bf16hi(v[i]);
             }
         }
     }
-}
+};
 
 template <int S>
 __device__ __forceinline__ int byte_of(const uint2 &w, int jj) {
@@ -248,91 +320,94 @@ __device__ __forceinline__ int byte_of(const uint2 &w, int jj) {
 }
 
 // ---------------------------------------------------------------------------
-// VQ tokens [t0, t1).
+// VQ tokens: a batch is kUnroll wave passes of index rows (8 bytes of the K
+// row and 8 of the V row per lane); batches are double-buffered.
 // ---------------------------------------------------------------------------
-template <int S, int CG, typename CB, typename OnlineT>
-__device__ __forceinline__ void vq_tokens(const DecodeArgs &a, int b, int h, int t0, int t1,
-                                          const float *lut, const uint32_t *vtab, OnlineT &st) {
-    using Sh = Shape<S, CG, CB>;
-    constexpr int R = Sh::R, TPW = Sh::TPW;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane % R, tg = lane / R;
-    const size_t rows = ((size_t)b * a.H + h) * (size_t)a.t_max;
-    const uint8_t *kidx = a.k_index + rows * S + 8 * r;
-    const uint8_t *vidx = a.v_index + rows * S + 8 * r;
-    const float *lut_r = lut + r * 8 * 256;
-    constexpr int VW = CG * Sh::VB / 4;                 // 32-bit words per value entry
-    const uint32_t *vt_r = vtab + (size_t)r * 8 * 256 * VW;
-    constexpr int STEP = kWaves * TPW;                   // tokens per pass of the workgroup
+struct Batch {
+    uint2 k[kUnroll], v[kUnroll];
+};
 
-    for (int base = t0 + wave * TPW; base < t1; base += STEP * kUnroll) {   // wave-uniform
-        uint2 kr[kUnroll], vr[kUnroll];
-        bool ok[kUnroll];
+template <int S, int CG, typename CB>
+__device__ __forceinline__ void load_batch(const uint8_t *kidx, const uint8_t *vidx, int base,
+                                           int t1, Batch &bt) {
+    using Sh = Shape<S, CG, CB>;
+    constexpr int STEP = kWaves * Sh::TPW;
+    const int tg = (threadIdx.x & 63) / Sh::R;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int n = base + u * STEP + tg;
-            ok[u] = n < t1;
-            if (ok[u]) {
-                kr[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
-                vr[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
-            } else {
-                kr[u] = make_uint2(0, 0);
-                vr[u] = make_uint2(0, 0);
+    for (int u = 0; u < kUnroll; ++u) {
+        const int n = base + u * STEP + tg;
+        if (n < t1) {
+            bt.k[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
+            bt.v[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
+        } else {
+            bt.k[u] = make_uint2(0, 0);
+            bt.v[u] = make_uint2(0, 0);
+        }
+    }
+}
+
+template <int S, int CG, typename CB, typename OnlineT>
+__device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1, const float *lut_r,
+                                           const uint32_t *vt_r, OnlineT &st) {
+    using Sh = Shape<S, CG, CB>;
+    constexpr int R = Sh::R, STEP = kWaves * Sh::TPW;
+    constexpr int VW = CG * Sh::VB / 4;                 // 32-bit words per value entry
+    const int lane = threadIdx.x & 63;
+    const int r = lane % R, tg = lane / R;
+    float s[kUnroll];
+    bool ok[kUnroll];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        ok[u] = base + u * STEP + tg < t1;
+        float acc = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc += lut_r[jj * 256 + byte_of<S>(bt.k[u], jj)];
+        acc = token_sum<R>(acc);
+        s[u] = ok[u] ? acc : -INFINITY;
+        mx = fmaxf(mx, s[u]);
+    }
+    st.raise(wave_max(mx));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (!ok[u]) continue;
+        if constexpr (Sh::kF16V) {
+            const _Float16 ph = (_Float16)(exp2f(s[u] - st.m) * kPScale);
+            if (r == 0) st.l += (float)ph;
+            const half2_t plo = {ph, (_Float16)0.f};
+            const half2_t phi = {(_Float16)0.f, ph};
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                const uint32_t *e = vt_r + (jj * 256 + byte_of<S>(bt.v[u], jj)) * VW;
+                uint32_t wv[VW];
+                if constexpr (VW == 1) {
+                    wv[0] = e[0];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VW; i += 2) {
+                        const uint2 t = *reinterpret_cast<const uint2 *>(e + i);
+                        wv[i] = t.x;
+                        wv[i + 1] = t.y;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < VW; ++i) {
+                    const half2_t hv = __builtin_bit_cast(half2_t, wv[i]);
+                    st.acc[jj * CG + 2 * i] =
+                        __builtin_amdgcn_fdot2(hv, plo, st.acc[jj * CG + 2 * i], false);
+                    st.acc[jj * CG + 2 * i + 1] =
+                        __builtin_amdgcn_fdot2(hv, phi, st.acc[jj * CG + 2 * i + 1], false);
+                }
             }
-        }
-        float s[kUnroll];
-        float mx = -INFINITY;
+        } else {
+            const float p = exp2f(s[u] - st.m) * kPScale;
+            if (r == 0) st.l += p;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float acc = 0.f;
+            for (int jj = 0; jj < 8; ++jj) {
+                const float *e = reinterpret_cast<const float *>(vt_r) +
+                                 (jj * 256 + byte_of<S>(bt.v[u], jj)) * CG;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) acc += lut_r[jj * 256 + byte_of<S>(kr[u], jj)];
-#pragma unroll
-            for (int off = 1; off < R; off <<= 1) acc += __shfl_xor(acc, off);
-            s[u] = ok[u] ? acc : -INFINITY;
-            mx = fmaxf(mx, s[u]);
-        }
-        st.raise(wave_max(mx));
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (!ok[u]) continue;
-            if constexpr (Sh::kF16V) {
-                const _Float16 ph = (_Float16)(exp2f(s[u] - st.m) * kPScale);
-                if (r == 0) st.l += (float)ph;
-                const half2_t plo = {ph, (_Float16)0.f};
-                const half2_t phi = {(_Float16)0.f, ph};
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const uint32_t *e = vt_r + (jj * 256 + byte_of<S>(vr[u], jj)) * VW;
-                    uint32_t wv[VW];
-                    if constexpr (VW == 1) {
-                        wv[0] = e[0];
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < VW; i += 2) {
-                            const uint2 t = *reinterpret_cast<const uint2 *>(e + i);
-                            wv[i] = t.x;
-                            wv[i + 1] = t.y;
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < VW; ++i) {
-                        const half2_t hv = __builtin_bit_cast(half2_t, wv[i]);
-                        st.acc[jj * CG + 2 * i] = __builtin_amdgcn_fdot2(hv, plo, st.acc[jj * CG + 2 * i], false);
-                        st.acc[jj * CG + 2 * i + 1] =
-                            __builtin_amdgcn_fdot2(hv, phi, st.acc[jj * CG + 2 * i + 1], false);
-                    }
-                }
-            } else {
-                const float p = exp2f(s[u] - st.m) * kPScale;
-                if (r == 0) st.l += p;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const float *e = reinterpret_cast<const float *>(vt_r) +
-                                     (jj * 256 + byte_of<S>(vr[u], jj)) * CG;
-#pragma unroll
-                    for (int c = 0; c < CG; ++c) st.acc[jj * CG + c] += p * e[c];
-                }
+                for (int c = 0; c < CG; ++c) st.acc[jj * CG + c] += p * e[c];
             }
         }
     }
@@ -341,100 +416,165 @@ __device__ __forceinline__ void vq_tokens(const DecodeArgs &a, int b, int h, int
 template <int S, int CG, typename CB>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     using Sh = Shape<S, CG, CB>;
-    constexpr int D = Sh::D, R = Sh::R, CL = Sh::CL;
+    constexpr int D = Sh::D, R = Sh::R, CL = Sh::CL, TPW = Sh::TPW;
+    constexpr int BSTEP = kWaves * TPW * kUnroll;   // tokens per batch of the workgroup
     static_assert(Sh::kLds <= kLdsLimit, "LDS budget");
+    static_assert(D <= kThreads, "one thread per output channel");
+    static_assert(kMaxSplits * (D + 2) <= Sh::kVtabWords, "merge reuses the value table");
     __shared__ float lut[Sh::kLut];
     __shared__ __align__(16) uint32_t vtab[Sh::kVtabWords];
     __shared__ float scratch[Sh::kScratch];
     __shared__ float qs[D];
+    __shared__ int is_last;
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+    // that consecutive logical workgroups (the splits of one head) share an
+    // XCD and its L2, which then serves their table slices once.
+    const unsigned total = gridDim.x, p = blockIdx.x;
+    const unsigned L = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
+    const int split = (int)(L % a.n_split);
+    const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tg = lane / R, r = lane % R;
     const Windows w = seq_windows(a, b);
     const int t0 = w.n_s + split * a.chunk;
     const int t1 = min(t0 + a.chunk, w.n_s + w.n_v);
     const int W = a.n_sink + a.n_recent;
     const int s0 = (int)((int64_t)W * split / a.n_split);
     const int s1 = (int)((int64_t)W * (split + 1) / a.n_split);
+    const size_t rows = ((size_t)b * a.H + h) * (size_t)a.t_max;
+    const uint8_t *kidx = a.k_index + rows * S + 8 * r;
+    const uint8_t *vidx = a.v_index + rows * S + 8 * r;
 
-    for (int i = tid; i < D; i += kThreads)
-        qs[i] = bf16f(a.q[((size_t)b * a.H + h) * D + i]) * (a.sm_scale * kLog2e);
+    // loads in the order they are needed: q, the two table slices, the first
+    // two index batches and the first window pass
+    const float qv = tid < D ? bf16f(a.q[((size_t)b * a.H + h) * D + tid]) : 0.f;
+    Stage<S, CG, CB> stg;
+    if (t0 < t1) stg.load(a, h);
+    int base = t0 + wave * TPW;
+    Batch r0, r1, r2;
+    load_batch<S, CG, CB>(kidx, vidx, base, t1, r0);
+    load_batch<S, CG, CB>(kidx, vidx, base + BSTEP, t1, r1);
+    // window slots: wave w takes s0 + w + kWaves * (tg + pass * TPW)
+    using Win = WindowPass<S, CG, CB>;
+    int wslot = s0 + wave;
+    Win win;
+    win.load(a, b, h, w, wslot + kWaves * tg, s1);
+
+    if (tid < D) qs[tid] = qv * (a.sm_scale * kLog2e);
     __syncthreads();
-    if (t0 < t1) stage_tables<S, CG, CB>(a, h, qs, lut, vtab);
+    if (t0 < t1) stg.finish(qs, lut, vtab);
     __syncthreads();
 
     Online<CL> st;
     st.init();
-    window_slots<S, CG, CB>(a, b, h, w, s0, s1, qs, st);
-    if (t0 < t1) vq_tokens<S, CG, CB>(a, b, h, t0, t1, lut, vtab, st);
+    while (wslot < s1) {                         // wave-uniform
+        win.fold(qs, st);
+        wslot += kWaves * TPW;
+        if (wslot < s1) win.load(a, b, h, w, wslot + kWaves * tg, s1);
+    }
+    const float *lut_r = lut + r * 8 * 256;
+    const uint32_t *vt_r = vtab + (size_t)r * 8 * 256 * (CG * Sh::VB / 4);
+    // three-deep ring, unrolled so that every batch lives in named registers
+    while (true) {                               // wave-uniform
+        if (base >= t1) break;
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r2);
+        fold_batch<S, CG, CB>(r0, base, t1, lut_r, vt_r, st);
+        base += BSTEP;
+        if (base >= t1) break;
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r0);
+        fold_batch<S, CG, CB>(r1, base, t1, lut_r, vt_r, st);
+        base += BSTEP;
+        if (base >= t1) break;
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r1);
+        fold_batch<S, CG, CB>(r2, base, t1, lut_r, vt_r, st);
+        base += BSTEP;
+    }
 
-    // combine the lanes of the wave that own the same channels, then the waves
+    // wave partial: per 16-lane row, sum the lanes that own the same channels
 #pragma unroll
-    for (int off = R; off < 64; off <<= 1)
-#pragma unroll
-        for (int i = 0; i < CL; ++i) st.acc[i] += __shfl_xor(st.acc[i], off);
+    for (int i = 0; i < CL; ++i) st.acc[i] = row_sum_same_r<R>(st.acc[i]);
     const float lw = wave_sum(st.l);
-    float *mine = scratch + wave * (D + 2);
-    if (lane < R) {
+    float *mine = scratch + wave * (2 + 4 * D);
+    const int row = lane >> 4, lr = lane & 15;
+    if (lr < R) {
 #pragma unroll
-        for (int i = 0; i < CL; ++i) mine[2 + lane * CL + i] = st.acc[i];
+        for (int i = 0; i < CL; ++i) mine[2 + row * D + lr * CL + i] = st.acc[i];
     }
     if (lane == 0) {
         mine[0] = st.m;
         mine[1] = lw;
     }
     __syncthreads();
+
+    // Workgroup partial (m, l, o) to the workspace, then the arrival ticket.
+    // The partial is written with agent-scope atomic stores, which are
+    // coherent across the XCDs' L2 caches, and every thread waits for its
+    // stores to complete before the ticket is taken; the merging workgroup
+    // reads them back with agent-scope atomic loads.  This publishes the
+    // partials without an L2 writeback (a device-scope release fence costs
+    // ~15 us when every workgroup issues one).
     float *part = a.partials + (((size_t)b * a.H + h) * kSlots + split) * (D + 2);
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v)
-        if (scratch[v * (D + 2) + 1] > 0.f) M = fmaxf(M, scratch[v * (D + 2)]);
-    for (int ch = tid; ch < D; ch += kThreads) {
+        if (scratch[v * (2 + 4 * D) + 1] > 0.f) M = fmaxf(M, scratch[v * (2 + 4 * D)]);
+    if (tid < D) {
         float o = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *pv = scratch + v * (D + 2);
-            if (pv[1] > 0.f) o += pv[2 + ch] * exp2f(pv[0] - M);
+            const float *pv = scratch + v * (2 + 4 * D);
+            if (pv[1] > 0.f)
+                o += ((pv[2 + tid] + pv[2 + D + tid]) + (pv[2 + 2 * D + tid] + pv[2 + 3 * D + tid])) *
+                     exp2f(pv[0] - M);
         }
-        part[2 + ch] = o;
+        __hip_atomic_store(&part[2 + tid], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) {
         float lt = 0.f;
 #pragma unroll
         for (int v = 0; v < kWaves; ++v) {
-            const float *pv = scratch + v * (D + 2);
+            const float *pv = scratch + v * (2 + 4 * D);
             if (pv[1] > 0.f) lt += pv[1] * exp2f(pv[0] - M);
         }
-        part[0] = M;
-        part[1] = lt;
+        __hip_atomic_store(&part[0], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&part[1], lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-}
-
-// Log-sum-exp merge of the n_split partials of (b, h) into out.
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge(DecodeArgs a) {
-    __shared__ float ml[2 * kMaxSplits];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const float *pb = a.partials + ((size_t)b * a.H + h) * kSlots * (D + 2);
-    const int n = a.n_split;
-    for (int i = tid; i < n; i += blockDim.x) {
-        ml[2 * i] = pb[i * (D + 2)];
-        ml[2 * i + 1] = pb[i * (D + 2) + 1];
+    __builtin_amdgcn_s_waitcnt(0);               // this thread's stores have completed
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&a.tickets[(size_t)b * a.H + h], 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == (unsigned)(a.n_split - 1);
     }
     __syncthreads();
-    float M = -INFINITY;
+    if (!is_last) return;
+
+    // merge all partials of (b, h), loaded in parallel into the value-table LDS
+    const int n = a.n_split;
+    const float *pb = a.partials + ((size_t)b * a.H + h) * kSlots * (D + 2);
+    float *pv = reinterpret_cast<float *>(vtab);
+    for (int i = tid; i < n * (D + 2); i += kThreads)
+        pv[i] = __hip_atomic_load(&pb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    float Mg = -INFINITY;
     for (int i = 0; i < n; ++i)
-        if (ml[2 * i + 1] > 0.f) M = fmaxf(M, ml[2 * i]);
-    float den = 0.f;
-    for (int i = 0; i < n; ++i)
-        if (ml[2 * i + 1] > 0.f) den += ml[2 * i + 1] * exp2f(ml[2 * i] - M);
-    for (int ch = tid; ch < D; ch += blockDim.x) {
-        float num = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < n; ++i)
-            if (ml[2 * i + 1] > 0.f) num += pb[i * (D + 2) + 2 + ch] * exp2f(ml[2 * i] - M);
-        a.out[((size_t)b * a.H + h) * D + ch] = den > 0.f ? num / den : 0.f;
+        if (pv[i * (D + 2) + 1] > 0.f) Mg = fmaxf(Mg, pv[i * (D + 2)]);
+    if (tid < D) {
+        float num = 0.f, den = 0.f;
+        for (int i = 0; i < n; ++i) {
+            const float *pi = pv + i * (D + 2);
+            if (pi[1] > 0.f) {
+                const float e = exp2f(pi[0] - Mg);
+                num += pi[2 + tid] * e;
+                den += pi[1] * e;
+            }
+        }
+        a.out[((size_t)b * a.H + h) * D + tid] = den > 0.f ? num / den : 0.f;
     }
+    if (tid == 0)
+        __hip_atomic_store(&a.tickets[(size_t)b * a.H + h], 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int S, int CG, typename CB>
@@ -444,7 +584,7 @@ constexpr bool fits() {
 
 template <int S, int CG>
 hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
-    const dim3 grid(a.n_split, a.H, a.B);
+    const dim3 grid((unsigned)a.n_split * a.H * a.B);
     if (a.cb_bf16) {
         if constexpr (fits<S, CG, uint16_t>())
             hipLaunchKernelGGL((decode_main<S, CG, uint16_t>), grid, dim3(kThreads), 0, st, a);
@@ -456,10 +596,6 @@ hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
         else
             return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge<S * CG>), dim3(a.H, a.B), dim3(S * CG < 256 ? S * CG : 256), 0,
-                       st, a);
     return hipGetLastError();
 }
 

@@ -7,8 +7,8 @@
 namespace lvq {
 
 // Workspace of lvq_decode_attn: per (b, h), kSlots partial slots of
-// (m, l, o[d]) floats, one per split (every call writes all of its splits
-// before the merge kernel reads them).
+// (m, l, o[d]) floats, one per split, then one uint32 arrival ticket per
+// (b, h) (zero between calls: the merging workgroup resets it).
 constexpr int kMaxSplits = 64;
 constexpr int kSlots = kMaxSplits;
 
@@ -18,7 +18,7 @@ inline uint64_t partial_bytes(int64_t B, int64_t H, int64_t d) {
     return align_up((uint64_t)B * H * kSlots * (d + 2) * sizeof(float), 256);
 }
 inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
-    return partial_bytes(B, H, d);
+    return partial_bytes(B, H, d) + align_up((uint64_t)B * H * sizeof(uint32_t), 256);
 }
 
 struct DecodeArgs {
@@ -39,6 +39,7 @@ struct DecodeArgs {
     const uint16_t *v_win;
     float sm_scale;
     float *partials;            // [B][H][kSlots][d + 2]
+    uint32_t *tickets;          // [B][H]
     float *out;                 // [B][H][d]
 };
 

@@ -195,6 +195,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
 
     const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
     const int32_t n_split = choose_splits(c, max_vq);
+    if ((int64_t)n_split * c->batch * c->n_heads > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
     int64_t chunk = (max_vq + n_split - 1) / n_split;
     chunk = (chunk + 63) / 64 * 64;
     if (chunk < 64) chunk = 64;
@@ -224,6 +225,8 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.v_win = static_cast<const uint16_t *>(v_window);
     a.sm_scale = sm_scale;
     a.partials = static_cast<float *>(workspace);
+    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
+                                             lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
     a.out = out;
     hipError_t e = lvq::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;
