@@ -177,8 +177,8 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  *            the next (its arrival counters return to zero).
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
- * outside [0, Tc), max_ctx_len outside [0, max_tokens], sm_scale not
- * finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64}, cg not in
+ * outside [0, Tc), max_tokens < 1, max_ctx_len outside [0, max_tokens],
+ * sm_scale not finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64}, cg not in
  * {2, 4, 8}, or the score table (4*S*256 bytes) plus the value table
  * (S*256*cg entries of 2 bytes for bf16, 4 for fp32 codebooks) of one
  * (head, loop step) above ~150 KiB of LDS: e.g. d = 256 at G = 16),

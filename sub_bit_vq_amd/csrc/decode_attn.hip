@@ -74,16 +74,13 @@ struct Windows {
     int L, n_s, n_v;
 };
 
-__device__ __forceinline__ Windows seq_windows(const DecodeArgs &a, int b) {
-    int L = a.ctx_len[b];
-    L = max(0, (int)min((int64_t)L, a.t_max));
-    const int n_s = min(L, a.n_sink);
-    int n_v;
-    if (a.vq_len) {
-        n_v = max(0, min(a.vq_len[b], L - n_s));
-    } else {
-        n_v = max(0, L - a.n_sink - a.n_recent);
-    }
+// Windows of a sequence from its raw length and VQ count (vq < 0: exact
+// windows), clamped to the documented preconditions.
+__device__ __forceinline__ Windows seq_windows(int Lraw, int vqraw, int64_t t_max, int n_sink,
+                                               int n_recent) {
+    const int L = max(0, (int)min((int64_t)Lraw, t_max));
+    const int n_s = min(L, n_sink);
+    const int n_v = vqraw >= 0 ? max(0, min(vqraw, L - n_s)) : max(0, L - n_sink - n_recent);
     return {L, n_s, n_v};
 }
 
@@ -188,10 +185,9 @@ struct Stage {
     uint32_t kw[PER][KW];
     uint4 vv[VPER];
 
-    __device__ __forceinline__ void load(const DecodeArgs &a, int h) {
-        const size_t slice = ((size_t)a.loop_step * a.H + h) * (size_t)Sh::kLut * CG;
-        const CB *kcb = static_cast<const CB *>(a.k_cb) + slice;
-        const uint4 *vcb = reinterpret_cast<const uint4 *>(static_cast<const CB *>(a.v_cb) + slice);
+    // kcb, vcb: the (h, t) slices, [S][256][cg]
+    __device__ __forceinline__ void load(const CB *kcb, const CB *vcb_) {
+        const uint4 *vcb = reinterpret_cast<const uint4 *>(vcb_);
         const int tid = threadIdx.x;
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -266,17 +262,14 @@ struct WindowPass {
     uint32_t k[CL / 2], v[CL / 2];
     bool ok;
 
-    __device__ __forceinline__ void load(const DecodeArgs &a, int b, int h, const Windows &w,
-                                         int slot, int s1) {
-        constexpr int D = Sh::D, R = Sh::R;
-        const int r = (threadIdx.x & 63) % R;
-        ok = slot < s1 && slot_valid(slot, w, a.n_sink, a.n_recent);
-        if (!ok) return;
-        const int W = a.n_sink + a.n_recent;
-        const size_t off = ((((size_t)b * a.Tc + a.loop_step) * a.H + h) * (size_t)W + slot) * D +
-                           r * CL;
-        const uint4 *kp = reinterpret_cast<const uint4 *>(a.k_win + off);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(a.v_win + off);
+    // kw, vw: the [W][d] window rows of (b, t, h), offset to this lane's channels
+    __device__ __forceinline__ void load(const uint16_t *kw, const uint16_t *vw, const Windows &w,
+                                         int slot, int s1, int n_sink, int n_recent) {
+        constexpr int D = Sh::D;
+        ok = slot < s1 && slot_valid(slot, w, n_sink, n_recent);
+        const int sl = min(slot, n_sink + n_recent - 1);   // unconditional, in-bounds load
+        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)sl * D);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(vw + (size_t)sl * D);
 #pragma unroll
         for (int i = 0; i < CL / 8; ++i) {
             const uint4 kk = kp[i], vv = vp[i];
@@ -327,22 +320,20 @@ struct Batch {
     uint2 k[kUnroll], v[kUnroll];
 };
 
+// Loads are unconditional: rows past t1 are clamped to the last row of the
+// cache (never used), which keeps the number of loads in flight a compile-time
+// constant, so waits on earlier loads never degrade to a full drain.
 template <int S, int CG, typename CB>
 __device__ __forceinline__ void load_batch(const uint8_t *kidx, const uint8_t *vidx, int base,
-                                           int t1, Batch &bt) {
+                                           int last_row, Batch &bt) {
     using Sh = Shape<S, CG, CB>;
     constexpr int STEP = kWaves * Sh::TPW;
     const int tg = (threadIdx.x & 63) / Sh::R;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int n = base + u * STEP + tg;
-        if (n < t1) {
-            bt.k[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
-            bt.v[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
-        } else {
-            bt.k[u] = make_uint2(0, 0);
-            bt.v[u] = make_uint2(0, 0);
-        }
+        const int n = min(base + u * STEP + tg, last_row);
+        bt.k[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
+        bt.v[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
     }
 }
 
@@ -436,34 +427,61 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tg = lane / R, r = lane % R;
-    const Windows w = seq_windows(a, b);
-    const int t0 = w.n_s + split * a.chunk;
-    const int t1 = min(t0 + a.chunk, w.n_s + w.n_v);
-    const int W = a.n_sink + a.n_recent;
-    const int s0 = (int)((int64_t)W * split / a.n_split);
-    const int s1 = (int)((int64_t)W * (split + 1) / a.n_split);
-    const size_t rows = ((size_t)b * a.H + h) * (size_t)a.t_max;
-    const uint8_t *kidx = a.k_index + rows * S + 8 * r;
-    const uint8_t *vidx = a.v_index + rows * S + 8 * r;
 
-    // loads in the order they are needed: q, the two table slices, the first
-    // two index batches and the first window pass
-    const float qv = tid < D ? bf16f(a.q[((size_t)b * a.H + h) * D + tid]) : 0.f;
+    // Everything derived from the arguments, computed once up front so that
+    // the argument and length loads form a single round trip.
+    const int n_sink = a.n_sink, n_recent = a.n_recent, W = n_sink + n_recent;
+    const int64_t t_max = a.t_max;
+    const int Lraw = a.ctx_len[b];
+    const int vqraw = a.vq_len ? a.vq_len[b] : -1;
+    const size_t bh = (size_t)b * a.H + h;
+    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)h * Sh::kLut * CG;
+    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)h * Sh::kLut * CG;
+    const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D + r * CL;
+    const uint16_t *kw = a.kwin_t + wbase;
+    const uint16_t *vw = a.vwin_t + wbase;
+    const uint8_t *kidx = a.k_index + bh * (size_t)t_max * S + 8 * r;
+    const uint8_t *vidx = a.v_index + bh * (size_t)t_max * S + 8 * r;
+    float *part = a.partials + (bh * kSlots + split) * (D + 2);
+    const float *parts = a.partials + bh * kSlots * (D + 2);
+    uint32_t *ticket = a.tickets + bh;
+    float *outp = a.out + bh * D;
+    const float scale = a.scale_log2;
+    const int n_split = a.n_split;
+
+    // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
+    // converted later so that no wait is placed here) and the table slices.
+    const uint32_t qraw = a.q[bh * D + min(tid, D - 1)];
     Stage<S, CG, CB> stg;
-    if (t0 < t1) stg.load(a, h);
-    int base = t0 + wave * TPW;
+    stg.load(kcb, vcb);
+
+    // The first two index batches are addressed from host-known values: a
+    // sequence with any VQ token has L > n_sink + ..., so its VQ range starts
+    // at n_sink.  Rows are clamped in-bounds and masked later by the true
+    // range, so these loads need not wait for the context length.
+    const int vq0 = n_sink + split * a.chunk;
+    const int last_row = (int)t_max - 1;       // the host guarantees t_max >= 1
     Batch r0, r1, r2;
-    load_batch<S, CG, CB>(kidx, vidx, base, t1, r0);
-    load_batch<S, CG, CB>(kidx, vidx, base + BSTEP, t1, r1);
+    load_batch<S, CG, CB>(kidx, vidx, vq0 + wave * TPW, last_row, r0);
+    load_batch<S, CG, CB>(kidx, vidx, vq0 + wave * TPW + BSTEP, last_row, r1);
+
+    const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
+    const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
+    const int t1 = min(t0 + a.chunk, w.n_s + w.n_v);
+    int base = t0 + wave * TPW;
+    const int s0 = (int)((int64_t)W * split / n_split);
+    const int s1 = (int)((int64_t)W * (split + 1) / n_split);
+
     // window slots: wave w takes s0 + w + kWaves * (tg + pass * TPW)
     using Win = WindowPass<S, CG, CB>;
     int wslot = s0 + wave;
     Win win;
-    win.load(a, b, h, w, wslot + kWaves * tg, s1);
+    win.load(kw, vw, w, wslot + kWaves * tg, s1, n_sink, n_recent);
 
-    if (tid < D) qs[tid] = qv * (a.sm_scale * kLog2e);
+    const float qv = bf16f((uint16_t)qraw);
+    if (tid < D) qs[tid] = qv * scale;
     __syncthreads();
-    if (t0 < t1) stg.finish(qs, lut, vtab);
+    stg.finish(qs, lut, vtab);
     __syncthreads();
 
     Online<CL> st;
@@ -471,22 +489,22 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     while (wslot < s1) {                         // wave-uniform
         win.fold(qs, st);
         wslot += kWaves * TPW;
-        if (wslot < s1) win.load(a, b, h, w, wslot + kWaves * tg, s1);
+        if (wslot < s1) win.load(kw, vw, w, wslot + kWaves * tg, s1, n_sink, n_recent);
     }
     const float *lut_r = lut + r * 8 * 256;
     const uint32_t *vt_r = vtab + (size_t)r * 8 * 256 * (CG * Sh::VB / 4);
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r2);
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r2);
         fold_batch<S, CG, CB>(r0, base, t1, lut_r, vt_r, st);
         base += BSTEP;
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r0);
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r0);
         fold_batch<S, CG, CB>(r1, base, t1, lut_r, vt_r, st);
         base += BSTEP;
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, t1, r1);
+        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r1);
         fold_batch<S, CG, CB>(r2, base, t1, lut_r, vt_r, st);
         base += BSTEP;
     }
@@ -514,7 +532,6 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // reads them back with agent-scope atomic loads.  This publishes the
     // partials without an L2 writeback (a device-scope release fence costs
     // ~15 us when every workgroup issues one).
-    float *part = a.partials + (((size_t)b * a.H + h) * kSlots + split) * (D + 2);
     float M = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v)
@@ -543,19 +560,18 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     __builtin_amdgcn_s_waitcnt(0);               // this thread's stores have completed
     __syncthreads();
     if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&a.tickets[(size_t)b * a.H + h], 1u,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = prev == (unsigned)(a.n_split - 1);
+        const unsigned prev =
+            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        is_last = prev == (unsigned)(n_split - 1);
     }
     __syncthreads();
     if (!is_last) return;
 
     // merge all partials of (b, h), loaded in parallel into the value-table LDS
-    const int n = a.n_split;
-    const float *pb = a.partials + ((size_t)b * a.H + h) * kSlots * (D + 2);
+    const int n = n_split;
     float *pv = reinterpret_cast<float *>(vtab);
     for (int i = tid; i < n * (D + 2); i += kThreads)
-        pv[i] = __hip_atomic_load(&pb[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pv[i] = __hip_atomic_load(&parts[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     float Mg = -INFINITY;
     for (int i = 0; i < n; ++i)
@@ -570,11 +586,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                 den += pi[1] * e;
             }
         }
-        a.out[((size_t)b * a.H + h) * D + tid] = den > 0.f ? num / den : 0.f;
+        outp[tid] = den > 0.f ? num / den : 0.f;
     }
     if (tid == 0)
-        __hip_atomic_store(&a.tickets[(size_t)b * a.H + h], 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int S, int CG, typename CB>

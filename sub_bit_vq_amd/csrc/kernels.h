@@ -38,6 +38,13 @@ struct DecodeArgs {
     const uint16_t *k_win;      // [B][Tc][H][W][d]
     const uint16_t *v_win;
     float sm_scale;
+    // derived by the host for the loop step of the call
+    const void *kcb_t;          // codebook slices of step t: [H][S][256][cg]
+    const void *vcb_t;
+    const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [H][W][d]
+    const uint16_t *vwin_t;
+    int64_t win_bstride;        // elements between sequences of a window buffer
+    float scale_log2;           // sm_scale * log2(e)
     float *partials;            // [B][H][kSlots][d + 2]
     uint32_t *tickets;          // [B][H]
     float *out;                 // [B][H][d]

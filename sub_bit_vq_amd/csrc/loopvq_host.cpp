@@ -172,6 +172,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
         return LVQ_ERR_INVALID_ARG;
     if (loop_step < 0 || loop_step >= c->loop_steps) return LVQ_ERR_INVALID_ARG;
     if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return LVQ_ERR_INVALID_ARG;
+    if (c->max_tokens < 1) return LVQ_ERR_INVALID_ARG;     // the index cache has rows
     if (!std::isfinite(sm_scale)) return LVQ_ERR_INVALID_ARG;
     // index rows and window rows are read with 8- or 16-byte vector loads
     {
@@ -224,6 +225,18 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.k_win = static_cast<const uint16_t *>(k_window);
     a.v_win = static_cast<const uint16_t *>(v_window);
     a.sm_scale = sm_scale;
+    {
+        const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
+        const size_t slice = (size_t)loop_step * c->n_heads * S * LVQ_CODES * cg * cbe;
+        a.kcb_t = static_cast<const char *>(k_codebook) + slice;
+        a.vcb_t = static_cast<const char *>(v_codebook) + slice;
+        const size_t W = (size_t)c->n_sink + c->n_recent;
+        const size_t step = (size_t)loop_step * c->n_heads * W * c->head_dim;
+        a.kwin_t = static_cast<const uint16_t *>(k_window) + step;
+        a.vwin_t = static_cast<const uint16_t *>(v_window) + step;
+        a.win_bstride = (int64_t)c->loop_steps * c->n_heads * W * c->head_dim;
+        a.scale_log2 = sm_scale * 1.4426950408889634f;
+    }
     a.partials = static_cast<float *>(workspace);
     a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
                                              lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
