@@ -34,9 +34,10 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 WORKLOADS = {
-    # name: (B, H, d, Tc, G, context)
+    # name: (B, H, d, Tc, G, context; "ragged" = 2048 + U{4096, 8192, 16384})
     "ouro1p4b_layer_32k_0p5bit": (1, 16, 128, 4, 16, 32768),
     "ouro1p4b_layer_32k_0p25bit": (1, 16, 128, 4, 32, 32768),
+    "batch64_ragged_0p5bit": (64, 16, 128, 4, 16, "ragged"),
 }
 PAGE = 8          # tokens per eviction page
 N_SINK, N_RECENT = 64, 256
@@ -47,13 +48,17 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def cache_bytes(H, d, Tc, G, L):
+def cache_bytes(H, d, Tc, G, lengths):
     """Algorithmic bytes of one decode call: K and V index rows of every VQ
-    token plus the bf16 K and V of the sink and recent tokens of the step."""
+    token plus the bf16 K and V of the sink and recent tokens of the step,
+    summed over the sequences of the batch."""
     S = d // (G // Tc)
-    n_vq = max(0, L - N_SINK - N_RECENT)
-    n_win = min(L, N_SINK) + min(max(L - N_SINK, 0), N_RECENT)
-    return n_vq * H * 2 * S + n_win * H * 2 * d * 2
+    total = 0
+    for L in lengths:
+        n_vq = max(0, L - N_SINK - N_RECENT)
+        n_win = min(L, N_SINK) + min(max(L - N_SINK, 0), N_RECENT)
+        total += n_vq * H * 2 * S + n_win * H * 2 * d * 2
+    return total
 
 
 def kernel_source_hash(name):
@@ -73,11 +78,18 @@ def counters_traffic(workload, bytes_per_launch):
 
 
 class Setup:
+    """Device-resident caches of one workload: index caches produced by the
+    HIP encoder from loop-correlated K/V, bf16 windows, codebooks, queries,
+    rotated over enough distinct copies to defeat the last-level cache."""
+
     def __init__(self, lv, synth, torch, workload, rotate, seed=1001):
         B, H, d, Tc, G, L = WORKLOADS[workload]
-        self.B, self.H, self.d, self.Tc, self.G, self.L = B, H, d, Tc, G, L
+        lengths = synth.ragged_lengths(B, seed=1003) if L == "ragged" else [L] * B
+        self.B, self.H, self.d, self.Tc, self.G = B, H, d, Tc, G
+        self.lengths = lengths
+        self.L = max(lengths)
         dev = torch.device("cuda")
-        T = L + PAGE
+        T = self.L + PAGE
         self.cfg = lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
                              max_tokens=T)
         self.kcb = synth.codebooks(H, d, Tc, G, seed * 10 + 1, device=dev)
@@ -86,21 +98,26 @@ class Setup:
         self.q = torch.stack([synth.queries(B, H, d, Tc, seed * 10 + 3 + i, device=dev)
                               for i in range(PAGE)])                 # [PAGE][Tc][B][H][d]
         base = lv.allocate(self.cfg, dev)
-        k = synth.loop_correlated_kv(L + PAGE, H, Tc, d, seed * 10 + 5, device=dev)
-        v = synth.loop_correlated_kv(L + PAGE, H, Tc, d, seed * 10 + 6, device=dev)
-        lo, hi = N_SINK, L - N_RECENT
-        lv.lvq_encode(self.cfg, k[lo:hi], self.kcb, base["k_index"], 0, lo)
-        lv.lvq_encode(self.cfg, v[lo:hi], self.vcb, base["v_index"], 0, lo)
-        slots = [p if p < N_SINK else N_SINK + (p - N_SINK) % N_RECENT
-                 for p in list(range(N_SINK)) + list(range(L - N_RECENT, L))]
-        pos = torch.tensor(list(range(N_SINK)) + list(range(L - N_RECENT, L)), device=dev)
-        sl = torch.tensor(slots, device=dev)
-        base["k_window"][0][:, :, sl, :] = k[pos].permute(2, 1, 0, 3)
-        base["v_window"][0][:, :, sl, :] = v[pos].permute(2, 1, 0, 3)
-        # the page to encode: the next 8 tokens (written to rows L .. L+7)
-        self.page_k, self.page_v = k[L:L + PAGE].contiguous(), v[L:L + PAGE].contiguous()
+        for b, Lb in enumerate(lengths):
+            k = synth.loop_correlated_kv(Lb + PAGE, H, Tc, d, seed * 10 + 5 + 2 * b, device=dev)
+            v = synth.loop_correlated_kv(Lb + PAGE, H, Tc, d, seed * 10 + 6 + 2 * b, device=dev)
+            lo, hi = N_SINK, Lb - N_RECENT
+            if hi > lo:
+                lv.lvq_encode(self.cfg, k[lo:hi], self.kcb, base["k_index"], b, lo)
+                lv.lvq_encode(self.cfg, v[lo:hi], self.vcb, base["v_index"], b, lo)
+            win = list(range(min(Lb, N_SINK))) + list(range(max(N_SINK, Lb - N_RECENT), Lb))
+            slots = [p if p < N_SINK else N_SINK + (p - N_SINK) % N_RECENT for p in win]
+            pos = torch.tensor(win, device=dev)
+            sl = torch.tensor(slots, device=dev)
+            base["k_window"][b][:, :, sl, :] = k[pos].permute(2, 1, 0, 3)
+            base["v_window"][b][:, :, sl, :] = v[pos].permute(2, 1, 0, 3)
+            if b == 0:
+                # the page to encode in each step: the next 8 tokens of sequence 0
+                self.page_k, self.page_v = k[Lb:Lb + PAGE].contiguous(), v[Lb:Lb + PAGE].contiguous()
+                self.page_row = Lb
+            del k, v
         torch.cuda.synchronize()
-        self.ctx = torch.tensor([L] * B, dtype=torch.int32, device=dev)
+        self.ctx = torch.tensor(lengths, dtype=torch.int32, device=dev)
         self.out = base["out"]
         self.ws = base["workspace"]
         copy_bytes = (base["k_index"].numel() * 2 + base["k_window"].numel() * 4)
@@ -109,9 +126,9 @@ class Setup:
         for r in range(self.rotate):
             c = {key: base[key].clone() for key in ("k_index", "v_index", "k_window", "v_window")}
             self.copies.append(c)
-        del base, k, v
+        del base
         torch.cuda.synchronize()
-        self.calls = [lv.PreparedDecode(self.cfg, self.ctx, L, c["k_index"], c["v_index"],
+        self.calls = [lv.PreparedDecode(self.cfg, self.ctx, self.L, c["k_index"], c["v_index"],
                                         self.kcb, self.vcb, c["k_window"], c["v_window"],
                                         self.ws, self.out) for c in self.copies]
         self.lv = lv
@@ -122,17 +139,19 @@ class Setup:
         self.n_call += 1
         call(t, self.q[tok, t])
 
-    def step(self):
+    def step(self, decode_only=False):
         for tok in range(PAGE):
             for t in range(self.Tc):
                 self.decode(tok, t)
+        if decode_only:
+            return
         c = self.copies[self.n_call % self.rotate]
-        self.lv.lvq_encode(self.cfg, self.page_k, self.kcb, c["k_index"], 0, self.L)
-        self.lv.lvq_encode(self.cfg, self.page_v, self.vcb, c["v_index"], 0, self.L)
+        self.lv.lvq_encode(self.cfg, self.page_k, self.kcb, c["k_index"], 0, self.page_row)
+        self.lv.lvq_encode(self.cfg, self.page_v, self.vcb, c["v_index"], 0, self.page_row)
 
     @property
     def tokens_steps_per_step(self):
-        return PAGE * self.Tc * self.B * self.L
+        return PAGE * self.Tc * sum(self.lengths)
 
 
 class PrefillEncode:
@@ -229,6 +248,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = auto, >= 2x LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time the 32 decode calls of a step without the page encode")
     ap.add_argument("--profile-decode", type=int, default=0,
                     help="only run N decode launches (for rocprofv3 runs) and exit")
     ap.add_argument("--profile-encode", type=int, default=0,
@@ -251,7 +272,7 @@ def main():
     log(f"workload {args.workload}: setup")
     setup = Setup(lv, synth, torch, args.workload, args.rotate)
     log(f"rotation over {setup.rotate} cache copies, "
-        f"{lv.lvq_decode_splits(setup.cfg, setup.L)} VQ splits per head")
+        f"{lv.lvq_decode_splits(setup.cfg, setup.L)} workgroups per (sequence, head)")
 
     if args.profile_decode or args.profile_encode:
         if args.copy_calibrate:
@@ -274,7 +295,7 @@ def main():
 
     # warmup (eager), then capture one step in a graph
     for _ in range(max(1, args.warmup)):
-        setup.step()
+        setup.step(args.decode_only)
     torch.cuda.synchronize()
     graph = None
     if not args.no_graph:
@@ -285,7 +306,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for _ in range(n_steps_graph):
-                setup.step()
+                setup.step(args.decode_only)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
@@ -302,7 +323,7 @@ def main():
         if graph is not None:
             graph.replay()
         else:
-            setup.step()
+            setup.step(args.decode_only)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end)
@@ -311,7 +332,7 @@ def main():
     log(f"{steps} steps in {ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step)")
 
     mean_ms, med_ms = decode_kernel_time_ms(setup, torch)
-    bpl = cache_bytes(setup.H, setup.d, setup.Tc, setup.G, setup.L)
+    bpl = cache_bytes(setup.H, setup.d, setup.Tc, setup.G, setup.lengths)
     achieved = bpl / (mean_ms / 1e3) / 1e9
     log(f"decode launch: mean {mean_ms * 1e3:.2f} us, median {med_ms * 1e3:.2f} us, "
         f"{achieved:.0f} GB/s on {bpl} cache bytes")
@@ -333,8 +354,10 @@ def main():
         "config": {
             "workload": args.workload,
             "batch": setup.B, "heads": setup.H, "head_dim": setup.d, "loop_steps": setup.Tc,
-            "group": setup.G, "context": setup.L, "n_sink": N_SINK, "n_recent": N_RECENT,
-            "step": "8 tokens x 4 loop-step decodes + 8-token page encode (K, V)",
+            "group": setup.G, "context": setup.L if setup.B == 1 else sum(setup.lengths),
+            "n_sink": N_SINK, "n_recent": N_RECENT,
+            "step": ("8 tokens x 4 loop-step decodes" if args.decode_only else
+                     "8 tokens x 4 loop-step decodes + 8-token page encode (K, V)"),
             "cache_copies": setup.rotate, "graph": graph is not None,
         },
         "roofline": {

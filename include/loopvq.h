@@ -24,9 +24,11 @@
  *
  * Storage layouts (all row-major, innermost last):
  *   x (encoder input) bf16  [n_tokens][H][Tc][d]  (or strided, see lvq_encode)
- *   codebook          f32 or bf16 [Tc][H][S][256][cg]: entry i = t*cg + c of
- *                     codeword k of (head h, sub-vector j) at [t][h][j][k][c],
- *                     so slice t of every codebook is contiguous
+ *   codebook          f32 or bf16 [Tc][H][256][S][cg]: entry i = t*cg + c of
+ *                     codeword k of (head h, sub-vector j) at [t][h][k][j][c]:
+ *                     slice t of a head is contiguous, and its row k holds
+ *                     code k of every sub-vector (the table row a decode
+ *                     gather reads)
  *   index cache       uint8 [B][H][max_tokens][S]; row p holds token p
  *                     (absolute position); rows of bf16 tokens are unused
  *   window buffers    bf16 [B][Tc][H][n_sink + n_recent][d]: sink token p
@@ -174,7 +176,8 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  * k_codebook, v_codebook  16-byte aligned.
  * workspace  device, >= layout.workspace_bytes, 256-byte aligned; zero-filled
  *            once after allocation; every completed call leaves it valid for
- *            the next (its arrival counters return to zero).
+ *            the next (it holds per-(b, h) arrival words that count calls and
+ *            split partials tagged with the call).
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
  * outside [0, Tc), max_tokens < 1, max_ctx_len outside [0, max_tokens],

@@ -63,7 +63,7 @@ def _bind(path):
 def _load():
     global _lib
     if _lib is None:
-        if not _LIB_PATH.exists():
+        if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
             build(force=True)
         _lib = _bind(_LIB_PATH)
     return _lib
@@ -159,7 +159,7 @@ def decode_attn(*, loop_step, q, ctx_len, k_index, v_index, k_codebook, v_codebo
                 k_window, v_window, n_sink, n_recent, group, sm_scale=1.0, vq_len=None,
                 want_p=False, heads=None, threads=None):
     """fp64 decode attention (D1-D5).  Shapes: q bf16 [B][H][d]; ctx_len int32 [B];
-    index uint8 [B][H][t_max][S]; codebooks [Tc][H][S][256][cg]; windows bf16
+    index uint8 [B][H][t_max][S]; codebooks [Tc][H][256][S][cg]; windows bf16
     [B][Tc][H][n_sink+n_recent][d].  Returns out fp64 [B][H][d] (and p fp64
     [B][H][t_max] when ``want_p``)."""
     qa = _np(q, np.uint16)

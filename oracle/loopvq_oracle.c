@@ -33,8 +33,8 @@
  * here independently):
  *  x        bf16  [n_tokens][H][Tc][d] with element strides (tok, head, step),
  *                 channel stride 1
- *  codebook f32/bf16 [Tc][H][S][256][cg], cg = G/Tc, S = d/cg; codeword k of
- *                 (h, j) has entry i = t*cg + c at [t][h][j][k][c]
+ *  codebook f32/bf16 [Tc][H][256][S][cg], cg = G/Tc, S = d/cg; codeword k of
+ *                 (h, j) has entry i = t*cg + c at [t][h][k][j][c]
  *  index    u8    [B][H][T_max][S]; row = absolute token position
  *  window   bf16  [B][Tc][H][n_sink + n_recent][d]; sink token p in slot p,
  *                 recent token p in slot n_sink + ((p - n_sink) mod n_recent)
@@ -66,7 +66,7 @@ static float codeword_entry(const void *cb, int cb_bf16, int H, int S, int cg,
                             int h, int j, int k, int i)
 {
     int t = i / cg, c = i % cg;
-    size_t off = ((((size_t)t * H + h) * S + j) * LVQO_CODES + k) * cg + c;
+    size_t off = ((((size_t)t * H + h) * LVQO_CODES + k) * S + j) * cg + c;
     if (cb_bf16)
         return bf16_bits_to_float(((const uint16_t *)cb)[off]);
     return ((const float *)cb)[off];

@@ -5,26 +5,44 @@
 // are read from shared 8-bit indices through codebook slice t, and the result
 // is merged with bf16 attention over the sink and recent tokens.
 //
-// One launch, n_split * H * B workgroups of 512 threads.  Workgroup s of (b, h) takes
-// VQ tokens [n_s + s*chunk, ...) and window slots [s*W/n_split, ...).  It
-// stages two tables of (h, t) in LDS:
-//     T[j][k] = log2(e) * sm_scale * sum_c q[j*cg + c] * Bk_t[j][k][c]  (fp32)
-//     V[j][k] = Bv_t[j][k][0..cg)  (fp16 for bf16 codebooks, else fp32)
-// A token's score is sum_j T[j][idxK[n][j]] (S gathers) and its value row is
-// gathered as V[j][idxV[n][j]] (S gathers of cg entries).  R = S/8 lanes
-// share a token, each owning 8 sub-vectors (8*cg output channels).  Every
-// wave keeps its own running max, weight sum and accumulators (online
-// softmax, base 2), so the token loop has no barrier; cross-lane reductions
-// use DPP, never the LDS crossbar, which the gathers saturate.  Token weights
-// p = 2^(s - m) enter the value sum as fp16 p * 2^14 through v_dot2_f32_f16,
-// and the weight sum adds the same rounded values, so the result is an exact
-// weighted average with weights perturbed by at most 2^-11 relative.
+// One launch, n_split * H * B workgroups of 512 threads.  Workgroup s of
+// (b, h) takes VQ tokens [n_s + s*chunk, ...) and window slots
+// [s*W/n_split, ...).  It stages two tables of (h, t) in LDS, both with one
+// 256-byte row per code k (the codebook slice is stored code-major, so row k
+// is a contiguous read):
+//     score table  [0, 64K):   row k = sm_scale * log2(e) * q_j . Bk_t[k][j]
+//                              for j < S, fp32, repeated 64/S times
+//     value table  [64K, 128K): row k = Bv_t[k][j][0..cg) for j < S (fp16 for
+//                              bf16 codebooks, else fp32), repeated to fill
+// R = S/8 lanes share a token, each owning 8 sub-vectors.  Lane (token slot
+// tk, part r) visits its sub-vectors in an order rotated by tk (and, with a
+// replica and read-order choice, offset per lane), so at every step the 32
+// lanes of a half-wave read 32 distinct LDS banks: the gathers run without
+// bank conflicts.  A gather address is one v_perm_b32 of the code byte and a
+// per-lane offset byte: 256*k + offset.
+// Every wave keeps its own running max, weight sum and accumulators (online
+// softmax, base 2), so the token loop has no barrier; per-token score sums
+// use DPP.  Token weights p = 2^(s - m) enter the value sum as fp16
+// p * 2^14, and the weight sum adds the same rounded values, so the result is
+// an exact weighted average with weights perturbed by at most 2^-11 relative.
+// Where the R lanes of a token fill whole 4-lane blocks and a gather is 4
+// fp16 channels (S = 32, cg = 4: the 0.5-bit head_dim-128 cache), the value
+// sums run on the matrix cores: v_mfma_f32_4x4x4_16b_f16 with A = the 4
+// gathered rows of a block and B = p' times a one-hot column accumulates
+// channel n of all 4 rows in lane n, exactly as p' * v summed in fp32
+// (bf16 window values use the fp32 4x4x1 form, so they stay exact).
+// Otherwise v_dot2_f32_f16 does them on the vector ALUs.
 // Index rows stream from HBM through a three-deep register ring; the first
-// two batches are issued before the tables are staged.
-// Each workgroup stores (m, l, o[d]) and takes a ticket; the last arrival of
-// (b, h) merges the partials (log-sum-exp) into out and resets the ticket.
-// Partials and tickets travel through agent-scope atomics only (no L2
-// writeback or invalidation).
+// two batches are issued before the tables are staged.  At the end the lanes
+// write their (rotated) accumulators to the freed table space at their
+// channel positions and the workgroup sums them there.
+// Every workgroup publishes (m, l, o[d]) as 64-bit (value, call tag) pairs,
+// then takes an arrival ticket of (b, h) without waiting for its stores to
+// complete.  The last arrival polls the other pairs until every tag is the
+// current call's (their stores were issued before their tickets, so the wait
+// is short), merges (log-sum-exp) into out and advances the arrival word to
+// the next call.  Everything crosses workgroups through agent-scope atomics
+// (no L2 writeback or invalidation); each pair is one 64-bit access.
 #include "kernels.h"
 
 #include <math.h>
@@ -37,37 +55,55 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 4;                     // token passes per batch
-constexpr int kRing = 3;                       // batches in flight
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPScale = 16384.f;             // p' = p * 2^14 (normal in fp16 down to p ~ 4e-9)
 constexpr int kLdsLimit = 160 * 1024;
+constexpr int kMergeChunk = 16;                // partial slots loaded per poll
+constexpr int kMaxPolls = 1 << 22;             // bound of the merger's wait
+constexpr int kVTab = 65536;                   // LDS byte offset of the value table
+constexpr int kTabBytes = 131072;              // both tables
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// 2^x by the hardware instruction (results below 2^-126 flush to zero,
+// which no weight here can tell apart from zero)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-template <typename CB>
-__device__ __forceinline__ float cb_at(const CB *p, int i);
-template <>
-__device__ __forceinline__ float cb_at<float>(const float *p, int i) { return p[i]; }
-template <>
-__device__ __forceinline__ float cb_at<uint16_t>(const uint16_t *p, int i) { return bf16f(p[i]); }
-
 template <int S, int CG, typename CB>
 struct Shape {
     static constexpr int D = S * CG;
-    static constexpr int R = S / 8;            // lanes per token
-    static constexpr int TPW = 64 / R;         // tokens per wave pass
-    static constexpr int CL = 8 * CG;          // output channels per lane
+    static constexpr int R = S / 8;                   // lanes per token
+    static constexpr int TPW = 64 / R;                // tokens per wave pass
+    static constexpr int CL = 8 * CG;                 // output channels per lane
     static constexpr bool kF16V = std::is_same<CB, uint16_t>::value;
-    static constexpr int VB = kF16V ? 2 : 4;   // bytes per value-table entry
-    static constexpr int kLut = S * 256;       // floats
-    static constexpr int kVtabWords = S * 256 * CG * VB / 4;
-    static constexpr int kScratch = kWaves * (2 + 4 * D);
-    static constexpr int kLds = 4 * (kLut + kVtabWords + kScratch + D) + 64;
-    static_assert(S >= 8 && S % 8 == 0, "8 sub-vectors per lane");
+    static constexpr int VB = kF16V ? 2 : 4;          // bytes per value-table element
+    static constexpr int EB = CG * VB;                // bytes per value-table entry
+    static constexpr int RB = EB <= 4 ? EB : 8;       // bytes per value read (b32 or b64)
+    static constexpr int NRD = EB / RB;               // reads per value gather
+    static constexpr int CPR = RB / VB;               // channels per read
+    static constexpr int KCOP = 64 / S;               // score-table replicas per row
+    static constexpr int VCOP = 256 / (S * EB);       // value-table replicas per row
+    static constexpr int SRCB = CG * (int)sizeof(CB); // codebook bytes per entry
+    static constexpr int UNIT = SRCB > 16 ? SRCB : 16;   // staging load bytes
+    static constexpr int EPU = UNIT / SRCB;           // entries per staging unit
+    static constexpr int UPT = S * 256 / EPU / kThreads;   // staging units per thread
+    static constexpr int NACC = 8 * CG;               // accumulators per lane
+    // Value sums on the matrix cores: the 4 lanes of a 4x4x4 MFMA block are
+    // parts of one token (R a multiple of 4) and a gather is 4 fp16 channels.
+    static constexpr bool kMfma = kF16V && EB == 8 && R % 4 == 0;
+    static constexpr int G = kThreads / D;            // reduction groups per channel
+    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16;
+    static constexpr int kLds = kTabBytes + kExtra;
+    static_assert(S >= 8 && S <= 64 && (S & (S - 1)) == 0, "8 sub-vectors per lane");
+    static_assert(S * EB <= 256, "a value-table row holds every sub-vector");
+    static_assert(UPT * EPU * kThreads == S * 256, "staging tiles the tables");
+    static_assert(kWaves * TPW * D * 4 <= kTabBytes, "the lane dump fits the tables");
+    static_assert(kThreads % D == 0 && TPW % G == 0, "reduction tiling");
 };
 
 struct Windows {
@@ -118,16 +154,6 @@ __device__ __forceinline__ float token_sum(float v) {
     return v;
 }
 
-// sum over the lanes of a 16-lane row that share lane % R
-template <int R>
-__device__ __forceinline__ float row_sum_same_r(float v) {
-    if constexpr (R <= 1) v += dppf<kXor1>(v);
-    if constexpr (R <= 2) v += dppf<kXor2>(v);
-    if constexpr (R <= 4) v += dppf<kRor4>(v);
-    v += dppf<kRor8>(v);
-    return v;
-}
-
 // wave-uniform maximum / sum
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dppf<kXor1>(v));
@@ -144,8 +170,83 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
+// one 64-bit (value, tag) pair of a published partial
+__device__ __forceinline__ void publish(uint64_t *p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// bytes of the 64-bit value (hi:lo) picked by the four selector bytes of sel
+// (0-3: bytes of lo, 4-7: bytes of hi, 12: zero)
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Per-lane gather constants.  At step i (0..7) lane (tk, r) handles
+// sub-vector j_i = 8r + ((i + rot) mod 8).  Its score read is at byte
+// 256k + offK_i, offK_i = 4 (S*copyK + j_i); its value reads at
+// 64K + 256k + offV_i (xor 8h for the h-th 8-byte read of an entry).  The
+// offsets sit one per byte in offK / offV words (offV words also carry the
+// 64K bit), so that one v_perm_b32 of (offset word, index word) is the address.
+template <int S, int CG, typename CB>
+struct Lanes {
+    using Sh = Shape<S, CG, CB>;
+    uint32_t rotA, rotB;         // selectors: index bytes in step order
+    uint32_t offK[2], offV[4];
+    uint32_t bmask0, bmask1;     // MFMA B operand: the lane's column in a 4-lane block
+    int rot, sw, r;
+
+    __device__ __forceinline__ void init(int lane) {
+        const int tk = lane / Sh::R;
+        r = lane % Sh::R;
+        rot = (tk + 4 * (r >> 2)) & 7;
+        const int n = r & 3;
+        bmask0 = n == 0 ? 0x0000ffffu : n == 1 ? 0xffff0000u : 0u;
+        bmask1 = n == 2 ? 0x0000ffffu : n == 3 ? 0xffff0000u : 0u;
+        const int copyK = (tk >> 3) % Sh::KCOP;
+        const int copyV = (tk >> 3) % Sh::VCOP;
+        sw = (tk / (8 * Sh::VCOP)) % Sh::NRD;
+        rotA = rotB = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            rotA |= (uint32_t)((rot + b) & 7) << (8 * b);
+            rotB |= (uint32_t)((rot + 4 + b) & 7) << (8 * b);
+        }
+        offK[0] = offK[1] = 0;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) offV[m] = 1u << 16;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = 8 * r + ((i + rot) & 7);
+            offK[i >> 2] |= (uint32_t)(4 * (S * copyK + j)) << (8 * (i & 3));
+            const uint32_t ov = Sh::EB <= 4 ? 4u * (S * copyV + j)
+                                            : 8u * (Sh::NRD * (S * copyV + j) + sw);
+            offV[i >> 1] |= ov << (8 * (i & 1));
+        }
+    }
+    // channel of read h of step i (output position of its first element)
+    __device__ __forceinline__ int channel(int i, int h) const {
+        return (8 * r + ((i + rot) & 7)) * CG + Sh::CPR * (h ^ sw);
+    }
+    // MFMA layout: channel held by accumulator element e of step i
+    // (row e of the lane's 4-lane block, column r mod 4)
+    __device__ __forceinline__ int mfma_channel(int i, int e) const {
+        return (8 * ((r & ~3) + e) + ((i + rot) & 7)) * CG + (r & 3);
+    }
+};
+
+// perm selectors: byte 0 = offset byte, byte 1 = index byte, then zero
+// (score) or the 64K byte of the offset word and zero (value)
+__device__ __forceinline__ constexpr uint32_t sel_k(int i) {
+    return 0x0c0c0000u | ((uint32_t)(i & 3) << 8) | (uint32_t)(4 + (i & 3));
+}
+__device__ __forceinline__ constexpr uint32_t sel_v(int i) {
+    return 0x0c060000u | ((uint32_t)(i & 3) << 8) | (uint32_t)(4 + (i & 1));
+}
+
 // Per-wave online-softmax state: running max m (base 2), weight sum l (scaled
-// by 2^14; lanes with r == 0 count each token once) and accumulators.
+// by 2^14; every lane of a token adds its weight, so the wave sum counts each
+// token R times) and accumulators.
 template <int NACC>
 struct Online {
     float m = -INFINITY;
@@ -159,7 +260,10 @@ struct Online {
     // raise the running max to at least `mx` (wave-uniform)
     __device__ __forceinline__ void raise(float mx) {
         if (mx > m) {
-            const float sc = exp2f(m - mx);   // 0 when m = -inf
+            // a real (wave-uniform) branch: the rescale is rare after the first
+            // batches, and the compiler would otherwise execute it every time
+            __asm__ volatile("");
+            const float sc = ex2(m - mx);     // 0 when m = -inf
             l *= sc;
 #pragma unroll
             for (int i = 0; i < NACC; ++i) acc[i] *= sc;
@@ -169,119 +273,120 @@ struct Online {
 };
 
 // ---------------------------------------------------------------------------
-// Table staging: score table and value table of (h, loop step t) into LDS.
-// ---------------------------------------------------------------------------
 // Table staging for (h, loop step t), in two phases so that the loads can be
-// issued before q is known: load() reads the K and V slices into registers,
-// finish() writes the score table and the value table into LDS.
+// issued before q is known: load() reads the K and V slices ([256][S][cg],
+// code-major) into registers, finish() writes both tables into LDS.
+// ---------------------------------------------------------------------------
 template <int S, int CG, typename CB>
 struct Stage {
     using Sh = Shape<S, CG, CB>;
-    static constexpr int PER = Sh::kLut / kThreads;               // score entries per thread
-    static constexpr int KW = CG * (int)sizeof(CB) / 4;           // 32-bit words per entry
-    static constexpr int VGROUPS = Sh::kLut * CG * (int)sizeof(CB) / 16;
-    static constexpr int VPER = VGROUPS / kThreads;               // 16-byte V groups per thread
-    static_assert(Sh::kLut % kThreads == 0 && VGROUPS % kThreads == 0, "tables must tile");
-    uint32_t kw[PER][KW];
-    uint4 vv[VPER];
+    static constexpr int UW = Sh::UNIT / 4;           // 32-bit words per unit
+    uint32_t kw[Sh::UPT][UW], vw[Sh::UPT][UW];
 
-    // kcb, vcb: the (h, t) slices, [S][256][cg]
-    __device__ __forceinline__ void load(const CB *kcb, const CB *vcb_) {
-        const uint4 *vcb = reinterpret_cast<const uint4 *>(vcb_);
+    __device__ __forceinline__ void load(const CB *kcb, const CB *vcb) {
         const int tid = threadIdx.x;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const uint32_t *src =
-                reinterpret_cast<const uint32_t *>(kcb + (size_t)(tid + u * kThreads) * CG);
-            if constexpr (KW == 1) {
-                kw[u][0] = src[0];
-            } else if constexpr (KW == 2) {
-                const uint2 t = *reinterpret_cast<const uint2 *>(src);
-                kw[u][0] = t.x;
-                kw[u][1] = t.y;
-            } else {
+        for (int u = 0; u < Sh::UPT; ++u) {
+            const size_t c = (size_t)(tid + u * kThreads) * Sh::UNIT;
+            const uint4 *ks = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(kcb) + c);
+            const uint4 *vs = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vcb) + c);
 #pragma unroll
-                for (int i = 0; i < KW; i += 4) {
-                    const uint4 t = *reinterpret_cast<const uint4 *>(src + i);
-                    kw[u][i] = t.x;
-                    kw[u][i + 1] = t.y;
-                    kw[u][i + 2] = t.z;
-                    kw[u][i + 3] = t.w;
-                }
+            for (int w = 0; w < UW; w += 4) {
+                const uint4 x = ks[w / 4], y = vs[w / 4];
+                kw[u][w] = x.x; kw[u][w + 1] = x.y; kw[u][w + 2] = x.z; kw[u][w + 3] = x.w;
+                vw[u][w] = y.x; vw[u][w + 1] = y.y; vw[u][w + 2] = y.z; vw[u][w + 3] = y.w;
             }
         }
-#pragma unroll
-        for (int u = 0; u < VPER; ++u) vv[u] = vcb[tid + u * kThreads];
     }
 
-    __device__ __forceinline__ void finish(const float *qs, float *lut, uint32_t *vtab) const {
+    __device__ __forceinline__ float elem(const uint32_t *w, int i) const {
+        if constexpr (Sh::kF16V) return (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
+        else return __uint_as_float(w[i]);
+    }
+
+    __device__ __forceinline__ void finish(const float *qs, unsigned char *smem) const {
         const int tid = threadIdx.x;
+        float *lutk = reinterpret_cast<float *>(smem);
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int e = tid + u * kThreads;
-            const int j = e >> 8;
-            float acc = 0.f;
+        for (int u = 0; u < Sh::UPT; ++u) {
+            const int e0 = (tid + u * kThreads) * Sh::EPU;   // first entry of the unit
+            const int k = e0 / S, j0 = e0 % S;
 #pragma unroll
-            for (int c = 0; c < CG; ++c) {
-                float v;
-                if constexpr (Sh::kF16V)
-                    v = (c & 1) ? bf16hi(kw[u][c >> 1]) : bf16lo(kw[u][c >> 1]);
-                else
-                    v = __uint_as_float(kw[u][c]);
-                acc += qs[j * CG + c] * v;
+            for (int e = 0; e < Sh::EPU; ++e) {
+                const int j = j0 + e;
+                float acc = 0.f;
+#pragma unroll
+                for (int c = 0; c < CG; ++c) acc += qs[j * CG + c] * elem(kw[u], e * CG + c);
+#pragma unroll
+                for (int cp = 0; cp < Sh::KCOP; ++cp) lutk[k * 64 + S * cp + j] = acc;
             }
-            lut[e] = acc;
-        }
+            // value entries of the unit, converted, into every replica of row k
+            uint32_t o[UW];
 #pragma unroll
-        for (int u = 0; u < VPER; ++u) {
-            if constexpr (Sh::kF16V) {
-                // 8 bf16 -> 8 fp16 at the same element offset
-                const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-                uint32_t o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const half2_t hp = {(_Float16)bf16lo(w[i]), (_Float16)bf16hi(w[i])};
-                    o[i] = __builtin_bit_cast(uint32_t, hp);
+            for (int w = 0; w < UW; ++w) {
+                if constexpr (Sh::kF16V) {
+                    const half2_t hp = {(_Float16)bf16lo(vw[u][w]), (_Float16)bf16hi(vw[u][w])};
+                    o[w] = __builtin_bit_cast(uint32_t, hp);
+                } else {
+                    o[w] = vw[u][w];
                 }
-                reinterpret_cast<uint4 *>(vtab)[tid + u * kThreads] = make_uint4(o[0], o[1], o[2], o[3]);
-            } else {
-                reinterpret_cast<uint4 *>(vtab)[tid + u * kThreads] = vv[u];
+            }
+#pragma unroll
+            for (int cp = 0; cp < Sh::VCOP; ++cp) {
+                uint4 *dst = reinterpret_cast<uint4 *>(smem + kVTab + k * 256 + (S * cp + j0) * Sh::EB);
+#pragma unroll
+                for (int w = 0; w < UW; w += 4) dst[w / 4] = make_uint4(o[w], o[w + 1], o[w + 2], o[w + 3]);
             }
         }
     }
 };
 
 // ---------------------------------------------------------------------------
-// Dense bf16 window slots [s0, s1): R lanes per slot, each owning CL channels.
-// Rows of one pass are loaded by `load`, then folded in by `fold`.
+// Dense bf16 window slots [s0, s1): R lanes per slot.  The key dot product
+// uses the lane's contiguous CL channels; the value row is read in the
+// lane's gather order so that it lands on the same accumulators.
 // ---------------------------------------------------------------------------
 template <int S, int CG, typename CB>
 struct WindowPass {
     using Sh = Shape<S, CG, CB>;
-    static constexpr int CL = Sh::CL;
-    uint32_t k[CL / 2], v[CL / 2];
+    static constexpr int CL = Sh::CL, NRD = Sh::NRD, CPR = Sh::CPR;
+    uint32_t k[CL / 2];
+    uint32_t v[8 * NRD][CPR / 2];
     bool ok;
 
-    // kw, vw: the [W][d] window rows of (b, t, h), offset to this lane's channels
+    // kw, vw: the [W][d] window rows of (b, t, h)
     __device__ __forceinline__ void load(const uint16_t *kw, const uint16_t *vw, const Windows &w,
-                                         int slot, int s1, int n_sink, int n_recent) {
+                                         int slot, int s1, int n_sink, int n_recent,
+                                         const Lanes<S, CG, CB> &ln) {
         constexpr int D = Sh::D;
         ok = slot < s1 && slot_valid(slot, w, n_sink, n_recent);
         const int sl = min(slot, n_sink + n_recent - 1);   // unconditional, in-bounds load
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)sl * D);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(vw + (size_t)sl * D);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)sl * D + ln.r * CL);
 #pragma unroll
         for (int i = 0; i < CL / 8; ++i) {
-            const uint4 kk = kp[i], vv = vp[i];
+            const uint4 kk = kp[i];
             k[4 * i] = kk.x; k[4 * i + 1] = kk.y; k[4 * i + 2] = kk.z; k[4 * i + 3] = kk.w;
-            v[4 * i] = vv.x; v[4 * i + 1] = vv.y; v[4 * i + 2] = vv.z; v[4 * i + 3] = vv.w;
+        }
+        const uint16_t *vrow = vw + (size_t)sl * D;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int h = 0; h < NRD; ++h) {
+                const uint16_t *p = vrow + ln.channel(i, h);
+                if constexpr (CPR == 4) {
+                    const uint2 t = *reinterpret_cast<const uint2 *>(p);
+                    v[i * NRD + h][0] = t.x;
+                    v[i * NRD + h][1] = t.y;
+                } else {
+                    v[i * NRD + h][0] = *reinterpret_cast<const uint32_t *>(p);
+                }
+            }
         }
     }
 
     template <typename OnlineT>
-    __device__ __forceinline__ void fold(const float *qs, OnlineT &st) {
+    __device__ __forceinline__ void fold(const float *qs, OnlineT &st, int r) {
         constexpr int R = Sh::R;
-        const int r = (threadIdx.x & 63) % R;
         float dot = 0.f;
         if (ok) {
 #pragma unroll
@@ -295,26 +400,40 @@ struct WindowPass {
         const float mx = wave_max(s);
         if (mx == -INFINITY) return;              // wave-uniform
         st.raise(mx);
-        if (ok) {
-            const float p = exp2f(s - st.m) * kPScale;
-            if (r == 0) st.l += p;
+        const float p = ok ? ex2(s - st.m) * kPScale : 0.f;
+        st.l += p;
+        if constexpr (Sh::kMfma) {
+            // column c of the block gets p; rows are the 4 lanes' values
+            const int n = r & 3;
+            float bc[4];
 #pragma unroll
-            for (int i = 0; i < CL / 2; ++i) {
-                st.acc[2 * i] += p * bf16lo(v[i]);
-                st.acc[2 * i + 1] += p * bf16hi(v[i]);
+            for (int c = 0; c < 4; ++c) bc[c] = n == c ? p : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float4_t d = {st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]};
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16lo(v[i][0]), bc[0], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16hi(v[i][0]), bc[1], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16lo(v[i][1]), bc[2], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16hi(v[i][1]), bc[3], d, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.acc[4 * i + e] = d[e];
+            }
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < 8 * NRD; ++q) {
+#pragma unroll
+            for (int e = 0; e < CPR / 2; ++e) {
+                st.acc[q * CPR + 2 * e] += p * bf16lo(v[q][e]);
+                st.acc[q * CPR + 2 * e + 1] += p * bf16hi(v[q][e]);
             }
         }
     }
 };
 
-template <int S>
-__device__ __forceinline__ int byte_of(const uint2 &w, int jj) {
-    return ((jj < 4 ? w.x : w.y) >> ((jj & 3) * 8)) & 0xff;
-}
-
 // ---------------------------------------------------------------------------
 // VQ tokens: a batch is kUnroll wave passes of index rows (8 bytes of the K
-// row and 8 of the V row per lane); batches are double-buffered.
+// row and 8 of the V row per lane); batches rotate through a 3-deep ring.
 // ---------------------------------------------------------------------------
 struct Batch {
     uint2 k[kUnroll], v[kUnroll];
@@ -328,32 +447,36 @@ __device__ __forceinline__ void load_batch(const uint8_t *kidx, const uint8_t *v
                                            int last_row, Batch &bt) {
     using Sh = Shape<S, CG, CB>;
     constexpr int STEP = kWaves * Sh::TPW;
-    const int tg = (threadIdx.x & 63) / Sh::R;
+    const int tk = (threadIdx.x & 63) / Sh::R;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int n = min(base + u * STEP + tg, last_row);
+        const int n = min(base + u * STEP + tk, last_row);
         bt.k[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
         bt.v[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
     }
 }
 
 template <int S, int CG, typename CB, typename OnlineT>
-__device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1, const float *lut_r,
-                                           const uint32_t *vt_r, OnlineT &st) {
+__device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
+                                           const unsigned char *smem,
+                                           const Lanes<S, CG, CB> &ln, OnlineT &st) {
     using Sh = Shape<S, CG, CB>;
-    constexpr int R = Sh::R, STEP = kWaves * Sh::TPW;
-    constexpr int VW = CG * Sh::VB / 4;                 // 32-bit words per value entry
-    const int lane = threadIdx.x & 63;
-    const int r = lane % R, tg = lane / R;
+    constexpr int R = Sh::R, STEP = kWaves * Sh::TPW, NRD = Sh::NRD, CPR = Sh::CPR;
+    const int tk = (threadIdx.x & 63) / R;
     float s[kUnroll];
     bool ok[kUnroll];
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        ok[u] = base + u * STEP + tg < t1;
+        ok[u] = base + u * STEP + tk < t1;
+        const uint32_t w0 = perm(bt.k[u].y, bt.k[u].x, ln.rotA);   // index bytes in step order
+        const uint32_t w1 = perm(bt.k[u].y, bt.k[u].x, ln.rotB);
         float acc = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc += lut_r[jj * 256 + byte_of<S>(bt.k[u], jj)];
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ad = perm(ln.offK[i >> 2], i < 4 ? w0 : w1, sel_k(i));
+            acc += *reinterpret_cast<const float *>(smem + ad);
+        }
         acc = token_sum<R>(acc);
         s[u] = ok[u] ? acc : -INFINITY;
         mx = fmaxf(mx, s[u]);
@@ -361,44 +484,63 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1, co
     st.raise(wave_max(mx));
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        if (!ok[u]) continue;
-        if constexpr (Sh::kF16V) {
-            const _Float16 ph = (_Float16)(exp2f(s[u] - st.m) * kPScale);
-            if (r == 0) st.l += (float)ph;
+        // tokens past the range take weight 0 (their clamped rows are valid codes)
+        const uint32_t w0 = perm(bt.v[u].y, bt.v[u].x, ln.rotA);
+        const uint32_t w1 = perm(bt.v[u].y, bt.v[u].x, ln.rotB);
+        if constexpr (Sh::kMfma) {
+            const _Float16 ph = (_Float16)(ok[u] ? ex2(s[u] - st.m) * kPScale : 0.f);
+            st.l += (float)ph;
+            const uint32_t ph2 = (uint32_t)__builtin_bit_cast(uint16_t, ph) * 0x00010001u;
+            const half4_t bop = __builtin_bit_cast(half4_t, make_uint2(ph2 & ln.bmask0, ph2 & ln.bmask1));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t ad = perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i));
+                const half4_t aop = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(smem + ad));
+                float4_t d = {st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]};
+                d = __builtin_amdgcn_mfma_f32_4x4x4f16(aop, bop, d, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.acc[4 * i + e] = d[e];
+            }
+        } else if constexpr (Sh::kF16V) {
+            const _Float16 ph = (_Float16)(ok[u] ? ex2(s[u] - st.m) * kPScale : 0.f);
+            st.l += (float)ph;
             const half2_t plo = {ph, (_Float16)0.f};
             const half2_t phi = {(_Float16)0.f, ph};
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const uint32_t *e = vt_r + (jj * 256 + byte_of<S>(bt.v[u], jj)) * VW;
-                uint32_t wv[VW];
-                if constexpr (VW == 1) {
-                    wv[0] = e[0];
-                } else {
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t ad = perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i));
 #pragma unroll
-                    for (int i = 0; i < VW; i += 2) {
-                        const uint2 t = *reinterpret_cast<const uint2 *>(e + i);
-                        wv[i] = t.x;
-                        wv[i + 1] = t.y;
+                for (int h = 0; h < NRD; ++h) {
+                    float *acc = st.acc + (i * NRD + h) * CPR;
+                    if constexpr (CPR == 4) {
+                        const uint2 e = *reinterpret_cast<const uint2 *>(smem + (ad ^ (8u * h)));
+                        const half2_t e0 = __builtin_bit_cast(half2_t, e.x);
+                        const half2_t e1 = __builtin_bit_cast(half2_t, e.y);
+                        acc[0] = __builtin_amdgcn_fdot2(e0, plo, acc[0], false);
+                        acc[1] = __builtin_amdgcn_fdot2(e0, phi, acc[1], false);
+                        acc[2] = __builtin_amdgcn_fdot2(e1, plo, acc[2], false);
+                        acc[3] = __builtin_amdgcn_fdot2(e1, phi, acc[3], false);
+                    } else {
+                        const half2_t e0 =
+                            __builtin_bit_cast(half2_t, *reinterpret_cast<const uint32_t *>(smem + ad));
+                        acc[0] = __builtin_amdgcn_fdot2(e0, plo, acc[0], false);
+                        acc[1] = __builtin_amdgcn_fdot2(e0, phi, acc[1], false);
                     }
-                }
-#pragma unroll
-                for (int i = 0; i < VW; ++i) {
-                    const half2_t hv = __builtin_bit_cast(half2_t, wv[i]);
-                    st.acc[jj * CG + 2 * i] =
-                        __builtin_amdgcn_fdot2(hv, plo, st.acc[jj * CG + 2 * i], false);
-                    st.acc[jj * CG + 2 * i + 1] =
-                        __builtin_amdgcn_fdot2(hv, phi, st.acc[jj * CG + 2 * i + 1], false);
                 }
             }
         } else {
-            const float p = exp2f(s[u] - st.m) * kPScale;
-            if (r == 0) st.l += p;
+            const float p = ok[u] ? ex2(s[u] - st.m) * kPScale : 0.f;
+            st.l += p;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float *e = reinterpret_cast<const float *>(vt_r) +
-                                 (jj * 256 + byte_of<S>(bt.v[u], jj)) * CG;
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t ad = perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i));
 #pragma unroll
-                for (int c = 0; c < CG; ++c) st.acc[jj * CG + c] += p * e[c];
+                for (int h = 0; h < NRD; ++h) {
+                    const float2 e = *reinterpret_cast<const float2 *>(smem + (ad ^ (8u * h)));
+                    float *acc = st.acc + (i * NRD + h) * CPR;
+                    acc[0] += p * e.x;
+                    acc[1] += p * e.y;
+                }
             }
         }
     }
@@ -407,16 +549,18 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1, co
 template <int S, int CG, typename CB>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     using Sh = Shape<S, CG, CB>;
-    constexpr int D = Sh::D, R = Sh::R, CL = Sh::CL, TPW = Sh::TPW;
+    constexpr int D = Sh::D, R = Sh::R, TPW = Sh::TPW;
+    constexpr int NRD = Sh::NRD, CPR = Sh::CPR, G = Sh::G;
     constexpr int BSTEP = kWaves * TPW * kUnroll;   // tokens per batch of the workgroup
     static_assert(Sh::kLds <= kLdsLimit, "LDS budget");
     static_assert(D <= kThreads, "one thread per output channel");
-    static_assert(kMaxSplits * (D + 2) <= Sh::kVtabWords, "merge reuses the value table");
-    __shared__ float lut[Sh::kLut];
-    __shared__ __align__(16) uint32_t vtab[Sh::kVtabWords];
-    __shared__ float scratch[Sh::kScratch];
-    __shared__ float qs[D];
-    __shared__ int is_last;
+    // The only LDS object: tables at byte 0 and 64K, then q, wave stats,
+    // reduction partials and the arrival word.
+    __shared__ __align__(16) unsigned char smem[Sh::kLds];
+    float *qs = reinterpret_cast<float *>(smem + kTabBytes);
+    float *wstat = qs + D;                      // [kWaves][m, l]
+    float *red = wstat + 2 * kWaves;            // [G][D]
+    uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);
 
     // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
     // that consecutive logical workgroups (the splits of one head) share an
@@ -426,7 +570,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int split = (int)(L % a.n_split);
     const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int tg = lane / R, r = lane % R;
+    const int tk = lane / R;
+    Lanes<S, CG, CB> ln;
+    ln.init(lane);
+    const int r = ln.r;
 
     // Everything derived from the arguments, computed once up front so that
     // the argument and length loads form a single round trip.
@@ -435,15 +582,15 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int Lraw = a.ctx_len[b];
     const int vqraw = a.vq_len ? a.vq_len[b] : -1;
     const size_t bh = (size_t)b * a.H + h;
-    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)h * Sh::kLut * CG;
-    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)h * Sh::kLut * CG;
-    const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D + r * CL;
+    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)h * 256 * S * CG;
+    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)h * 256 * S * CG;
+    const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D;
     const uint16_t *kw = a.kwin_t + wbase;
     const uint16_t *vw = a.vwin_t + wbase;
     const uint8_t *kidx = a.k_index + bh * (size_t)t_max * S + 8 * r;
     const uint8_t *vidx = a.v_index + bh * (size_t)t_max * S + 8 * r;
-    float *part = a.partials + (bh * kSlots + split) * (D + 2);
-    const float *parts = a.partials + bh * kSlots * (D + 2);
+    uint64_t *part = a.partials + (bh * kSlots + split) * (D + 2);
+    const uint64_t *parts = a.partials + bh * kSlots * (D + 2);
     uint32_t *ticket = a.tickets + bh;
     float *outp = a.out + bh * D;
     const float scale = a.scale_log2;
@@ -452,6 +599,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
     const uint32_t qraw = a.q[bh * D + min(tid, D - 1)];
+    // The call counter of (b, h) cannot change before this workgroup arrives,
+    // so it is read now, overlapped with the prologue; it tags the partials.
+    uint32_t arrival_word = 0;
+    if (tid == 0) arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
     stg.load(kcb, vcb);
 
@@ -472,129 +623,189 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int s0 = (int)((int64_t)W * split / n_split);
     const int s1 = (int)((int64_t)W * (split + 1) / n_split);
 
-    // window slots: wave w takes s0 + w + kWaves * (tg + pass * TPW)
+    // window slots: wave w takes s0 + w + kWaves * (tk + pass * TPW)
     using Win = WindowPass<S, CG, CB>;
     int wslot = s0 + wave;
     Win win;
-    win.load(kw, vw, w, wslot + kWaves * tg, s1, n_sink, n_recent);
+    win.load(kw, vw, w, wslot + kWaves * tk, s1, n_sink, n_recent, ln);
 
     const float qv = bf16f((uint16_t)qraw);
     if (tid < D) qs[tid] = qv * scale;
+    if (tid == 0) *arrival = arrival_word;
     __syncthreads();
-    stg.finish(qs, lut, vtab);
+    stg.finish(qs, smem);
     __syncthreads();
 
-    Online<CL> st;
+    Online<Sh::NACC> st;
     st.init();
     while (wslot < s1) {                         // wave-uniform
-        win.fold(qs, st);
+        win.fold(qs, st, r);
         wslot += kWaves * TPW;
-        if (wslot < s1) win.load(kw, vw, w, wslot + kWaves * tg, s1, n_sink, n_recent);
+        if (wslot < s1) win.load(kw, vw, w, wslot + kWaves * tk, s1, n_sink, n_recent, ln);
     }
-    const float *lut_r = lut + r * 8 * 256;
-    const uint32_t *vt_r = vtab + (size_t)r * 8 * 256 * (CG * Sh::VB / 4);
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
         load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r2);
-        fold_batch<S, CG, CB>(r0, base, t1, lut_r, vt_r, st);
+        fold_batch<S, CG, CB>(r0, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r0);
-        fold_batch<S, CG, CB>(r1, base, t1, lut_r, vt_r, st);
+        fold_batch<S, CG, CB>(r1, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r1);
-        fold_batch<S, CG, CB>(r2, base, t1, lut_r, vt_r, st);
+        fold_batch<S, CG, CB>(r2, base, t1, smem, ln, st);
         base += BSTEP;
     }
 
-    // wave partial: per 16-lane row, sum the lanes that own the same channels
+    // Lane accumulators to the freed table space: row (wave, tk), natural
+    // channel order.  Then wave (m, l).
+    const float lw = wave_sum(st.l) * (1.f / R);     // every token was counted R times
+    __syncthreads();                             // every wave is done with the tables
+    float *dump = reinterpret_cast<float *>(smem);
+    float *mine = dump + (size_t)(wave * TPW + tk) * D;
+    if constexpr (Sh::kMfma) {
 #pragma unroll
-    for (int i = 0; i < CL; ++i) st.acc[i] = row_sum_same_r<R>(st.acc[i]);
-    const float lw = wave_sum(st.l);
-    float *mine = scratch + wave * (2 + 4 * D);
-    const int row = lane >> 4, lr = lane & 15;
-    if (lr < R) {
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int i = 0; i < CL; ++i) mine[2 + row * D + lr * CL + i] = st.acc[i];
+            for (int e = 0; e < 4; ++e) mine[ln.mfma_channel(i, e)] = st.acc[4 * i + e];
+    } else
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int hh = 0; hh < NRD; ++hh) {
+            const float *acc = st.acc + (i * NRD + hh) * CPR;
+            float *dst = mine + ln.channel(i, hh);
+            if constexpr (CPR == 4)
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            else
+                *reinterpret_cast<float2 *>(dst) = make_float2(acc[0], acc[1]);
+        }
     }
     if (lane == 0) {
-        mine[0] = st.m;
-        mine[1] = lw;
+        wstat[2 * wave] = st.m;
+        wstat[2 * wave + 1] = lw;
     }
     __syncthreads();
 
-    // Workgroup partial (m, l, o) to the workspace, then the arrival ticket.
-    // The partial is written with agent-scope atomic stores, which are
-    // coherent across the XCDs' L2 caches, and every thread waits for its
-    // stores to complete before the ticket is taken; the merging workgroup
-    // reads them back with agent-scope atomic loads.  This publishes the
-    // partials without an L2 writeback (a device-scope release fence costs
-    // ~15 us when every workgroup issues one).
+    // Workgroup partial: scale every wave to the common max (empty waves have
+    // l == 0 and zero accumulators) and sum the dumped rows.
+    float mw[kWaves], lv[kWaves], ew[kWaves];
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        mw[v] = wstat[2 * v];
+        lv[v] = wstat[2 * v + 1];
+    }
     float M = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-        if (scratch[v * (2 + 4 * D) + 1] > 0.f) M = fmaxf(M, scratch[v * (2 + 4 * D)]);
+    for (int v = 0; v < kWaves; ++v) M = lv[v] > 0.f ? fmaxf(M, mw[v]) : M;
+    float lt = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+        ew[v] = lv[v] > 0.f ? ex2(mw[v] - M) : 0.f;
+        lt += lv[v] * ew[v];
+    }
+    {
+        const int ch = tid % D, g = tid / D;
+        float acc = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            float sv = 0.f;
+#pragma unroll
+            for (int q = 0; q < TPW / G; ++q) sv += dump[(size_t)(v * TPW + g + q * G) * D + ch];
+            acc += sv * ew[v];
+        }
+        red[g * D + ch] = acc;
+    }
+    __syncthreads();
+    float o = 0.f;
     if (tid < D) {
-        float o = 0.f;
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const float *pv = scratch + v * (2 + 4 * D);
-            if (pv[1] > 0.f)
-                o += ((pv[2 + tid] + pv[2 + D + tid]) + (pv[2 + 2 * D + tid] + pv[2 + 3 * D + tid])) *
-                     exp2f(pv[0] - M);
-        }
-        __hip_atomic_store(&part[2 + tid], o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int g = 0; g < G; ++g) o += red[g * D + tid];
     }
-    if (tid == 0) {
-        float lt = 0.f;
-#pragma unroll
-        for (int v = 0; v < kWaves; ++v) {
-            const float *pv = scratch + v * (2 + 4 * D);
-            if (pv[1] > 0.f) lt += pv[1] * exp2f(pv[0] - M);
-        }
-        __hip_atomic_store(&part[0], M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&part[1], lt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_waitcnt(0);               // this thread's stores have completed
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned prev =
-            __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = prev == (unsigned)(n_split - 1);
-    }
-    __syncthreads();
-    if (!is_last) return;
 
-    // merge all partials of (b, h), loaded in parallel into the value-table LDS
+    const uint32_t epoch = *arrival >> 8;
+    const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
     const int n = n_split;
-    float *pv = reinterpret_cast<float *>(vtab);
-    for (int i = tid; i < n * (D + 2); i += kThreads)
-        pv[i] = __hip_atomic_load(&parts[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    float Mg = -INFINITY;
-    for (int i = 0; i < n; ++i)
-        if (pv[i * (D + 2) + 1] > 0.f) Mg = fmaxf(Mg, pv[i * (D + 2)]);
-    if (tid < D) {
-        float num = 0.f, den = 0.f;
-        for (int i = 0; i < n; ++i) {
-            const float *pi = pv + i * (D + 2);
-            if (pi[1] > 0.f) {
-                const float e = exp2f(pi[0] - Mg);
-                num += pi[2 + tid] * e;
-                den += pi[1] * e;
+    if (n > 1) {
+        if (tid < D) publish(&part[2 + tid], o, tag);
+        if (tid == 0) {
+            publish(&part[0], M, tag);
+            publish(&part[1], lt, tag);
+        }
+        __syncthreads();                             // every thread has issued its stores
+        if (tid == 0)
+            *arrival = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if ((int)(*arrival & 0xffu) != n - 1) return;
+    }
+
+    // Last arrival: every other workgroup of (b, h) has issued its pairs;
+    // poll them (slot `split` is this workgroup's own).
+    if (tid >= D) return;
+    float Mg = lt > 0.f ? M : -INFINITY;
+    float num = o, den = lt;
+    bool failed = false;
+    for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
+        uint64_t po[kMergeChunk], pm[kMergeChunk], pl[kMergeChunk];
+        int poll = 0;
+        while (true) {
+#pragma unroll
+            for (int i = 0; i < kMergeChunk; ++i) {
+                const size_t sl = (size_t)min(c0 + i, n - 1) * (D + 2);
+                po[i] = __hip_atomic_load(&parts[sl + 2 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pm[i] = __hip_atomic_load(&parts[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pl[i] = __hip_atomic_load(&parts[sl + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            bool ok = true;
+#pragma unroll
+            for (int i = 0; i < kMergeChunk; ++i) {
+                const int s = c0 + i;
+                if (s < n && s != split)
+                    ok = ok && (uint32_t)(po[i] >> 32) == tag && (uint32_t)(pm[i] >> 32) == tag &&
+                         (uint32_t)(pl[i] >> 32) == tag;
+            }
+            if (__all(ok)) break;
+            if (++poll >= kMaxPolls) {
+                failed = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(4);
+        }
+        float mc = Mg;
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+            const int s = c0 + i;
+            const float li = __uint_as_float((uint32_t)pl[i]);
+            if (s < n && s != split && li > 0.f) mc = fmaxf(mc, __uint_as_float((uint32_t)pm[i]));
+        }
+        if (mc > Mg) {                               // Mg = -inf gives 0 * 0
+            const float sc = Mg == -INFINITY ? 0.f : ex2(Mg - mc);
+            num *= sc;
+            den *= sc;
+            Mg = mc;
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeChunk; ++i) {
+            const int s = c0 + i;
+            const float li = __uint_as_float((uint32_t)pl[i]);
+            if (s < n && s != split && li > 0.f) {
+                const float e = ex2(__uint_as_float((uint32_t)pm[i]) - Mg);
+                num += __uint_as_float((uint32_t)po[i]) * e;
+                den += li * e;
             }
         }
-        outp[tid] = den > 0.f ? num / den : 0.f;
     }
-    if (tid == 0)
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    outp[tid] = failed ? NAN : (den > 0.f ? num / den : 0.f);
+    if (tid == 0 && n > 1)
+        __hip_atomic_store(ticket, (epoch + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int S, int CG, typename CB>
 constexpr bool fits() {
-    return Shape<S, CG, CB>::kLds <= kLdsLimit;
+    if constexpr (S * CG * (std::is_same<CB, uint16_t>::value ? 2 : 4) > 256) return false;
+    else return Shape<S, CG, CB>::kLds <= kLdsLimit;
 }
 
 template <int S, int CG>

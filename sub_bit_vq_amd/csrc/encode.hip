@@ -71,12 +71,12 @@ __device__ __forceinline__ float cb_at<float>(const float *p, size_t i) { return
 template <>
 __device__ __forceinline__ float cb_at<uint16_t>(const uint16_t *p, size_t i) { return bf16f(p[i]); }
 
-// entry i = t*CG + c of codeword k of (h, j): codebook [Tc][H][S][256][CG]
+// entry i = t*CG + c of codeword k of (h, j): codebook [Tc][H][256][S][CG]
 template <int CG, typename CB>
 __device__ __forceinline__ float codeword(const EncodeArgs &a, const CB *cb, int h, int j, int k,
                                           int i) {
     const int t = i / CG, c = i % CG;
-    return cb_at(cb, ((((size_t)t * a.H + h) * a.S + j) * 256 + k) * CG + c);
+    return cb_at(cb, ((((size_t)t * a.H + h) * 256 + k) * a.S + j) * CG + c);
 }
 
 // sub-vector entries x_0..x_{G-1} of (token n, head h, sub-vector j)

@@ -7,15 +7,17 @@
 namespace lvq {
 
 // Workspace of lvq_decode_attn: per (b, h), kSlots partial slots of
-// (m, l, o[d]) floats, one per split, then one uint32 arrival ticket per
-// (b, h) (zero between calls: the merging workgroup resets it).
+// (m, l, o[d]), one per split, each value stored as a 64-bit (float bits,
+// call tag) pair, then one uint32 arrival word per (b, h): bits 0-7 count the
+// workgroups of the current call that have arrived, bits 8-31 count calls.
+// Between calls the count is zero (the merging workgroup advances the word).
 constexpr int kMaxSplits = 64;
 constexpr int kSlots = kMaxSplits;
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 inline uint64_t partial_bytes(int64_t B, int64_t H, int64_t d) {
-    return align_up((uint64_t)B * H * kSlots * (d + 2) * sizeof(float), 256);
+    return align_up((uint64_t)B * H * kSlots * (d + 2) * sizeof(uint64_t), 256);
 }
 inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
     return partial_bytes(B, H, d) + align_up((uint64_t)B * H * sizeof(uint32_t), 256);
@@ -33,19 +35,19 @@ struct DecodeArgs {
     const int32_t *vq_len;      // [B] or null
     const uint8_t *k_index;     // [B][H][t_max][S]
     const uint8_t *v_index;
-    const void *k_cb;           // [Tc][H][S][256][cg]
+    const void *k_cb;           // [Tc][H][256][S][cg]
     const void *v_cb;
     const uint16_t *k_win;      // [B][Tc][H][W][d]
     const uint16_t *v_win;
     float sm_scale;
     // derived by the host for the loop step of the call
-    const void *kcb_t;          // codebook slices of step t: [H][S][256][cg]
+    const void *kcb_t;          // codebook slices of step t: [H][256][S][cg]
     const void *vcb_t;
     const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [H][W][d]
     const uint16_t *vwin_t;
     int64_t win_bstride;        // elements between sequences of a window buffer
     float scale_log2;           // sm_scale * log2(e)
-    float *partials;            // [B][H][kSlots][d + 2]
+    uint64_t *partials;         // [B][H][kSlots][d + 2] (value, tag) pairs
     uint32_t *tickets;          // [B][H]
     float *out;                 // [B][H][d]
 };
@@ -56,7 +58,7 @@ struct EncodeArgs {
     const uint16_t *x;
     int64_t sx_tok, sx_head, sx_step;   // element strides of x
     int64_t n_tokens;
-    const void *cb;             // [Tc][H][S][256][cg]
+    const void *cb;             // [Tc][H][256][S][cg]
     uint8_t *index;             // [B][H][t_max][S]
     int64_t t_max;
     int64_t seq;

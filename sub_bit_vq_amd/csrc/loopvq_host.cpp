@@ -98,7 +98,7 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
     const int64_t idx_shape[4] = {B, H, c->max_tokens, S};
     set_tensor(&o->k_index, 4, idx_shape, 1);
     set_tensor(&o->v_index, 4, idx_shape, 1);
-    const int64_t cb_shape[5] = {Tc, H, S, LVQ_CODES, cg};
+    const int64_t cb_shape[5] = {Tc, H, LVQ_CODES, S, cg};
     set_tensor(&o->k_codebook, 5, cb_shape, cbe);
     set_tensor(&o->v_codebook, 5, cb_shape, cbe);
     const int64_t win_shape[5] = {B, Tc, H, W, d};
@@ -237,7 +237,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
         a.win_bstride = (int64_t)c->loop_steps * c->n_heads * W * c->head_dim;
         a.scale_log2 = sm_scale * 1.4426950408889634f;
     }
-    a.partials = static_cast<float *>(workspace);
+    a.partials = static_cast<uint64_t *>(workspace);
     a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
                                              lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
     a.out = out;

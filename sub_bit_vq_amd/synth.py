@@ -53,20 +53,21 @@ def loop_correlated_kv(n_tokens: int, n_heads: int, loop_steps: int, head_dim: i
 
 def codebooks(n_heads: int, head_dim: int, loop_steps: int, group: int, seed: int,
               dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
-    """Codebooks in the slice-major storage layout
-    ``[loop_steps][n_heads][n_sub][256][group // loop_steps]``.
+    """Codebooks in the slice-major, code-major storage layout
+    ``[loop_steps][n_heads][256][n_sub][group // loop_steps]``.
 
     Codeword k of (head h, sub-vector j) has ``group`` entries; entry
     ``i = t * cg + c`` (``cg = group // loop_steps``) is stored at
-    ``[t][h][j][k][c]`` so that the part read at loop step t is contiguous.
-    Draw order is the natural one, ``[h][j][k][i]``.
+    ``[t][h][k][j][c]``: the part read at loop step t is contiguous, and within
+    it row k holds code k of every sub-vector.  Draw order is the natural one,
+    ``[h][j][k][i]``.
     """
     cg = group // loop_steps
     n_sub = head_dim // cg
     g = _gen(seed, device)
     nat = torch.randn((n_heads, n_sub, N_CODES, loop_steps, cg), generator=g,
                       device=device, dtype=torch.float32)
-    return nat.to(dtype).permute(3, 0, 1, 2, 4).contiguous()
+    return nat.to(dtype).permute(3, 0, 2, 1, 4).contiguous()
 
 
 def queries(batch: int, n_heads: int, head_dim: int, loop_steps: int, seed: int,

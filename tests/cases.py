@@ -19,9 +19,9 @@ N_SINK, N_RECENT = 64, 256
 
 
 def natural_codebook(cb: torch.Tensor) -> torch.Tensor:
-    """[Tc][H][S][256][cg] storage -> [H][S][256][G] with entry i = t*cg + c."""
-    Tc, H, S, K, cg = cb.shape
-    return cb.permute(1, 2, 3, 0, 4).reshape(H, S, K, Tc * cg)
+    """[Tc][H][256][S][cg] storage -> [H][S][256][G] with entry i = t*cg + c."""
+    Tc, H, K, S, cg = cb.shape
+    return cb.permute(1, 3, 2, 0, 4).reshape(H, S, K, Tc * cg)
 
 
 def natural_subvectors(x: torch.Tensor, group: int) -> torch.Tensor:
@@ -36,12 +36,12 @@ def natural_subvectors(x: torch.Tensor, group: int) -> torch.Tensor:
 def kv_from_codewords(idx: torch.Tensor, cb: torch.Tensor) -> torch.Tensor:
     """Tokens whose every sub-vector is exactly a codeword.
 
-    idx uint8 [n][H][S]; cb [Tc][H][S][256][cg] -> x [n][H][Tc][d] (cb dtype)."""
-    Tc, H, S, K, cg = cb.shape
+    idx uint8 [n][H][S]; cb [Tc][H][256][S][cg] -> x [n][H][Tc][d] (cb dtype)."""
+    Tc, H, K, S, cg = cb.shape
     n = idx.shape[0]
     hh = torch.arange(H).view(1, H, 1)
     jj = torch.arange(S).view(1, 1, S)
-    rows = [cb[t][hh, jj, idx.long()] for t in range(Tc)]      # each [n][H][S][cg]
+    rows = [cb[t][hh, idx.long(), jj] for t in range(Tc)]      # each [n][H][S][cg]
     return torch.stack(rows, dim=2).reshape(n, H, Tc, S * cg)
 
 
@@ -75,7 +75,7 @@ class Cache:
     v_tokens: list
     k_index: torch.Tensor      # uint8 [B][H][t_max][S]
     v_index: torch.Tensor
-    k_codebook: torch.Tensor   # [Tc][H][S][256][cg]
+    k_codebook: torch.Tensor   # [Tc][H][256][S][cg]
     v_codebook: torch.Tensor
     k_window: torch.Tensor     # bf16 [B][Tc][H][n_sink+n_recent][d]
     v_window: torch.Tensor

@@ -51,7 +51,7 @@ def test_layout_shapes(name):
     S = d // cg
     assert lay["n_sub"] == S and lay["sub_channels"] == cg and lay["n_codes"] == 256
     assert lay["k_index"]["shape"] == (B, H, T, S) and lay["k_index"]["bytes"] == B * H * T * S
-    assert lay["k_codebook"]["shape"] == (Tc, H, S, 256, cg)
+    assert lay["k_codebook"]["shape"] == (Tc, H, 256, S, cg)
     assert lay["k_codebook"]["bytes"] == Tc * H * S * 256 * cg * (2 if dt == lv.LVQ_BF16 else 4)
     assert lay["k_window"]["shape"] == (B, Tc, H, 64 + 256, d)
     assert lay["query"]["shape"] == (B, H, d) and lay["output"]["bytes"] == B * H * d * 4

@@ -105,7 +105,7 @@ def _tie_codebook(H, d, Tc, G, seed):
     cg = G // Tc
     S = d // cg
     nat = torch.randint(-2, 3, (H, S, 256, Tc, cg), generator=g).float()
-    return nat.permute(3, 0, 1, 2, 4).contiguous()
+    return nat.permute(3, 0, 2, 1, 4).contiguous()
 
 
 @pytest.mark.parametrize("cb_dtype", [torch.bfloat16, torch.float32])

@@ -53,14 +53,14 @@ def check_exact_ties(seed=2):
         for k in tie:                           # tied codes: squared norm exactly 4
             nat[0, 0, k] = 0.0
             nat[0, 0, k, (k * 5) % G] = 2.0 if k % 2 else -2.0
-        cb = nat.reshape(H, 1, 256, Tc, G // Tc).permute(3, 0, 1, 2, 4).contiguous()
+        cb = nat.reshape(H, 1, 256, Tc, G // Tc).permute(3, 0, 2, 1, 4).contiguous()
         x = torch.zeros((1, H, Tc, d), dtype=torch.bfloat16)
         got = int(_enc(x, cb, H, d, Tc, G)[0, 0, 0, 0])
         assert got == min(tie), (tie, got)
     # a codeword tied with itself repeated at a lower index: lowest index wins
     nat = torch.randint(-3, 4, (H, 1, 256, G), generator=g).float()
     nat[0, 0, 77] = nat[0, 0, 200]
-    cb = nat.reshape(H, 1, 256, Tc, G // Tc).permute(3, 0, 1, 2, 4).contiguous()
+    cb = nat.reshape(H, 1, 256, Tc, G // Tc).permute(3, 0, 2, 1, 4).contiguous()
     x = nat[0, 0, 200].reshape(1, H, Tc, G // Tc).to(torch.bfloat16)
     assert int(_enc(x, cb, H, d, Tc, G)[0, 0, 0, 0]) == 77
 
@@ -94,7 +94,7 @@ def check_row_permutation(H=1, d=64, Tc=4, G=16, n=64, seed=4):
     base = _enc(x, cb, H, d, Tc, G)[0, 0]                              # [n][S]
     perm = torch.randperm(256, generator=torch.Generator().manual_seed(seed))
     inv = torch.argsort(perm)
-    got = _enc(x, cb[:, :, :, perm].contiguous(), H, d, Tc, G)[0, 0]
+    got = _enc(x, cb[:, :, perm].contiguous(), H, d, Tc, G)[0, 0]
     # new row r holds old code perm[r]: the old code k is now at row inv[k]
     assert torch.equal(got.long(), inv[base.long()])
 

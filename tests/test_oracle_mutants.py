@@ -28,8 +28,8 @@ MUTANTS = {
     "abs_instead_of_square": ("float sq = e * e;", "float sq = e < 0 ? -e : e;"),
     "subvector_channels_transposed": ("xv[t * cg + c] = bf16_bits_to_float(",
                                       "xv[c * Tc + t] = bf16_bits_to_float("),
-    "codebook_head_sub_swapped": ("((((size_t)t * H + h) * S + j) * LVQO_CODES + k)",
-                                  "((((size_t)t * S + j) * H + h) * LVQO_CODES + k)"),
+    "codebook_code_sub_swapped": ("((((size_t)t * H + h) * LVQO_CODES + k) * S + j)",
+                                  "((((size_t)t * H + h) * S + j) * LVQO_CODES + k)"),
     "index_row_ignores_first_token": ("* t_max + first_token + n) * S + j]", "* t_max + n) * S + j]"),
     "dequant_reads_slice_0": ("ck, t * cg + c);", "ck, 0 * cg + c);"),
     "value_dequant_uses_key_codebook": ("codeword_entry(v_cb, cb_bf16, H, S, cg, h, j, cv,",
