@@ -181,11 +181,10 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
  * outside [0, Tc), max_tokens < 1, max_ctx_len outside [0, max_tokens],
- * sm_scale not finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64}, cg not in
- * {2, 4, 8}, or the score table (4*S*256 bytes) plus the value table
- * (S*256*cg entries of 2 bytes for bf16, 4 for fp32 codebooks) of one
- * (head, loop step) above ~150 KiB of LDS: e.g. d = 256 at G = 16),
- * LVQ_ERR_WORKSPACE, LVQ_ERR_HIP.
+ * sm_scale not finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64},
+ * cg not in {2, 4, 8}, a value-table row (S*cg entries of 2 bytes for bf16,
+ * 4 for fp32 codebooks) above 256 bytes: e.g. d = 256 at G = 16, or
+ * max_tokens * S near 2^31), LVQ_ERR_WORKSPACE, LVQ_ERR_HIP.
  */
 lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void *q,
                            const int32_t *ctx_len, const int32_t *vq_len,

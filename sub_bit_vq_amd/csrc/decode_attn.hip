@@ -11,7 +11,7 @@
 // 256-byte row per code k (the codebook slice is stored code-major, so row k
 // is a contiguous read):
 //     score table  [0, 64K):   row k = sm_scale * log2(e) * q_j . Bk_t[k][j]
-//                              for j < S, fp32, repeated 64/S times
+//                              for j < S, fp32, repeated max(1, 32/S) times
 //     value table  [64K, 128K): row k = Bv_t[k][j][0..cg) for j < S (fp16 for
 //                              bf16 codebooks, else fp32), repeated to fill
 // R = S/8 lanes share a token, each owning 8 sub-vectors.  Lane (token slot
@@ -32,17 +32,18 @@
 // channel n of all 4 rows in lane n, exactly as p' * v summed in fp32
 // (bf16 window values use the fp32 4x4x1 form, so they stay exact).
 // Otherwise v_dot2_f32_f16 does them on the vector ALUs.
-// Index rows stream from HBM through a three-deep register ring; the first
-// two batches are issued before the tables are staged.  At the end the lanes
+// Index rows stream from HBM through a three-deep register ring of buffer
+// loads; the first two batches are issued before the tables are staged.  At the end the lanes
 // write their (rotated) accumulators to the freed table space at their
 // channel positions and the workgroup sums them there.
-// Every workgroup publishes (m, l, o[d]) as 64-bit (value, call tag) pairs,
-// then takes an arrival ticket of (b, h) without waiting for its stores to
-// complete.  The last arrival polls the other pairs until every tag is the
-// current call's (their stores were issued before their tickets, so the wait
-// is short), merges (log-sum-exp) into out and advances the arrival word to
-// the next call.  Everything crosses workgroups through agent-scope atomics
-// (no L2 writeback or invalidation); each pair is one 64-bit access.
+// A workgroup takes an arrival ticket of (b, h) as soon as its tokens are
+// done (the round trip overlaps its own reduction), then publishes
+// (m, l, o[d]) as 64-bit (value, call tag) pairs.  Every workgroup but the
+// last leaves; the last polls the others' pairs until every tag is the
+// current call's, merges (log-sum-exp) into out and advances the arrival
+// word to the next call.  Everything crosses workgroups through agent-scope atomics (no L2
+// writeback or invalidation); each pair is one 64-bit access, so no store
+// needs a completion wait.
 #include "kernels.h"
 
 #include <math.h>
@@ -86,7 +87,9 @@ struct Shape {
     static constexpr int RB = EB <= 4 ? EB : 8;       // bytes per value read (b32 or b64)
     static constexpr int NRD = EB / RB;               // reads per value gather
     static constexpr int CPR = RB / VB;               // channels per read
-    static constexpr int KCOP = 64 / S;               // score-table replicas per row
+    // score-table replicas per 64-float row: enough for the lanes of a
+    // half-wave to read distinct banks (a row is 256 bytes either way)
+    static constexpr int KCOP = S >= 32 ? 1 : 32 / S;
     static constexpr int VCOP = 256 / (S * EB);       // value-table replicas per row
     static constexpr int SRCB = CG * (int)sizeof(CB); // codebook bytes per entry
     static constexpr int UNIT = SRCB > 16 ? SRCB : 16;   // staging load bytes
@@ -360,7 +363,18 @@ struct WindowPass {
                                          const Lanes<S, CG, CB> &ln) {
         constexpr int D = Sh::D;
         ok = slot < s1 && slot_valid(slot, w, n_sink, n_recent);
-        const int sl = min(slot, n_sink + n_recent - 1);   // unconditional, in-bounds load
+        // rows are read only for slots that hold a token (most lanes of a
+        // pass have none when a workgroup owns few slots)
+        if (!ok) {
+#pragma unroll
+            for (int i = 0; i < CL / 2; ++i) k[i] = 0u;
+#pragma unroll
+            for (int i = 0; i < 8 * NRD; ++i)
+#pragma unroll
+                for (int e = 0; e < CPR / 2; ++e) v[i][e] = 0u;
+            return;
+        }
+        const int sl = slot;
         const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)sl * D + ln.r * CL);
 #pragma unroll
         for (int i = 0; i < CL / 8; ++i) {
@@ -439,20 +453,24 @@ struct Batch {
     uint2 k[kUnroll], v[kUnroll];
 };
 
-// Loads are unconditional: rows past t1 are clamped to the last row of the
-// cache (never used), which keeps the number of loads in flight a compile-time
-// constant, so waits on earlier loads never degrade to a full drain.
+// The index rows of one (b, h) as buffer resources: a read past the last row
+// returns zeros (code 0, masked later), so loads need neither clamps nor
+// 64-bit address arithmetic, and every batch issues the same number of loads.
+constexpr int kBufferWord3 = 0x00020000;       // raw buffer, gfx9 family
+struct IndexRows {
+    __amdgpu_buffer_rsrc_t k, v;
+    uint32_t lane;                              // byte offset of the lane: tk*S + 8r
+};
+
 template <int S, int CG, typename CB>
-__device__ __forceinline__ void load_batch(const uint8_t *kidx, const uint8_t *vidx, int base,
-                                           int last_row, Batch &bt) {
+__device__ __forceinline__ void load_batch(const IndexRows &ir, int base, Batch &bt) {
     using Sh = Shape<S, CG, CB>;
     constexpr int STEP = kWaves * Sh::TPW;
-    const int tk = (threadIdx.x & 63) / Sh::R;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int n = min(base + u * STEP + tk, last_row);
-        bt.k[u] = *reinterpret_cast<const uint2 *>(kidx + (size_t)n * S);
-        bt.v[u] = *reinterpret_cast<const uint2 *>(vidx + (size_t)n * S);
+        const uint32_t off = ir.lane + (uint32_t)(base + u * STEP) * S;
+        bt.k[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ir.k, off, 0, 0));
+        bt.v[u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ir.v, off, 0, 0));
     }
 }
 
@@ -587,8 +605,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D;
     const uint16_t *kw = a.kwin_t + wbase;
     const uint16_t *vw = a.vwin_t + wbase;
-    const uint8_t *kidx = a.k_index + bh * (size_t)t_max * S + 8 * r;
-    const uint8_t *vidx = a.v_index + bh * (size_t)t_max * S + 8 * r;
+    IndexRows ir;
+    ir.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k_index + bh * (size_t)t_max * S),
+                                            (short)0, (int)(t_max * S), kBufferWord3);
+    ir.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v_index + bh * (size_t)t_max * S),
+                                            (short)0, (int)(t_max * S), kBufferWord3);
+    ir.lane = (uint32_t)(tk * S + 8 * r);
     uint64_t *part = a.partials + (bh * kSlots + split) * (D + 2);
     const uint64_t *parts = a.partials + bh * kSlots * (D + 2);
     uint32_t *ticket = a.tickets + bh;
@@ -608,13 +630,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // The first two index batches are addressed from host-known values: a
     // sequence with any VQ token has L > n_sink + ..., so its VQ range starts
-    // at n_sink.  Rows are clamped in-bounds and masked later by the true
-    // range, so these loads need not wait for the context length.
+    // at n_sink.  Rows outside the range are masked later by the true range,
+    // so these loads need not wait for the context length.
     const int vq0 = n_sink + split * a.chunk;
-    const int last_row = (int)t_max - 1;       // the host guarantees t_max >= 1
     Batch r0, r1, r2;
-    load_batch<S, CG, CB>(kidx, vidx, vq0 + wave * TPW, last_row, r0);
-    load_batch<S, CG, CB>(kidx, vidx, vq0 + wave * TPW + BSTEP, last_row, r1);
+    load_batch<S, CG, CB>(ir, vq0 + wave * TPW, r0);
+    load_batch<S, CG, CB>(ir, vq0 + wave * TPW + BSTEP, r1);
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
@@ -633,28 +654,37 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     if (tid < D) qs[tid] = qv * scale;
     if (tid == 0) *arrival = arrival_word;
     __syncthreads();
-    stg.finish(qs, smem);
-    __syncthreads();
 
+    // The window tokens need no table: where registers allow, fold them while
+    // the table slices are still arriving, then build the tables.
+    constexpr bool kWindowFirst = Sh::NACC <= 32;
     Online<Sh::NACC> st;
     st.init();
+    if constexpr (!kWindowFirst) {
+        stg.finish(qs, smem);
+        __syncthreads();
+    }
     while (wslot < s1) {                         // wave-uniform
         win.fold(qs, st, r);
         wslot += kWaves * TPW;
         if (wslot < s1) win.load(kw, vw, w, wslot + kWaves * tk, s1, n_sink, n_recent, ln);
     }
+    if constexpr (kWindowFirst) {
+        stg.finish(qs, smem);
+        __syncthreads();
+    }
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r2);
+        load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r2);
         fold_batch<S, CG, CB>(r0, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r0);
+        load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r0);
         fold_batch<S, CG, CB>(r1, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
-        load_batch<S, CG, CB>(kidx, vidx, base + 2 * BSTEP, last_row, r1);
+        load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r1);
         fold_batch<S, CG, CB>(r2, base, t1, smem, ln, st);
         base += BSTEP;
     }
@@ -662,7 +692,17 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // Lane accumulators to the freed table space: row (wave, tk), natural
     // channel order.  Then wave (m, l).
     const float lw = wave_sum(st.l) * (1.f / R);     // every token was counted R times
+    const uint32_t epoch = *arrival >> 8;
+    const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
+    const int n = n_split;
     __syncthreads();                             // every wave is done with the tables
+    // This workgroup's arrival: the last to finish its tokens merges.  The
+    // ticket travels while the partial is reduced.  Every thread takes part
+    // (thread 0 adds 1, the rest 0; the compiler folds each wave into one
+    // atomic), so no branch forces an early wait for the result.
+    uint32_t ticket_word = 0;
+    if (tid == 0 && n > 1)
+        ticket_word = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float *dump = reinterpret_cast<float *>(smem);
     float *mine = dump + (size_t)(wave * TPW + tk) * D;
     if constexpr (Sh::kMfma) {
@@ -724,25 +764,21 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) o += red[g * D + tid];
     }
-
-    const uint32_t epoch = *arrival >> 8;
-    const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
-    const int n = n_split;
+    // Every workgroup publishes at once (before it knows whether it is last,
+    // so the others' pairs are already on their way when the last one looks).
     if (n > 1) {
         if (tid < D) publish(&part[2 + tid], o, tag);
         if (tid == 0) {
             publish(&part[0], M, tag);
             publish(&part[1], lt, tag);
+            *arrival = ticket_word;
         }
-        __syncthreads();                             // every thread has issued its stores
-        if (tid == 0)
-            *arrival = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         if ((int)(*arrival & 0xffu) != n - 1) return;
     }
 
-    // Last arrival: every other workgroup of (b, h) has issued its pairs;
-    // poll them (slot `split` is this workgroup's own).
+    // Last arrival: every other workgroup of (b, h) has finished its tokens;
+    // poll their pairs (slot `split` is this workgroup's own).
     if (tid >= D) return;
     float Mg = lt > 0.f ? M : -INFINITY;
     float num = o, den = lt;

@@ -190,6 +190,8 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     const int S = c->head_dim / cg;
     if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16))
         return LVQ_ERR_UNSUPPORTED;
+    // the index rows of one (b, h) are addressed with 32-bit byte offsets
+    if ((int64_t)c->max_tokens * S > 0x7fffffff - 65536LL * S) return LVQ_ERR_UNSUPPORTED;
     const uint64_t need = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
     if (!workspace || workspace_bytes < need) return LVQ_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
