@@ -65,16 +65,21 @@ def kernel_source_hash(name):
     return hashlib.sha256((ROOT / "sub_bit_vq_amd" / "csrc" / name).read_bytes()).hexdigest()[:16]
 
 
-def counters_traffic(workload, bytes_per_launch):
-    """HBM traffic per decode launch from the committed rocprofv3 counter
-    summary, or None when missing or taken on a different kernel source."""
-    p = ROOT / "profiles" / f"decode_attn_{workload}_counters.json"
+def counters_traffic(workload):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy), or None when it is
+    missing or was taken on a different kernel source."""
+    p = ROOT / "profiles" / f"decode_attn_{workload}.md"
     if not p.exists():
         return None
-    rec = json.loads(p.read_text())
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash("decode_attn.hip"):
+    fields = {}
+    for line in p.read_text().splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("decode_attn.hip sha256[:16]") != kernel_source_hash("decode_attn.hip"):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(fields["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in fields else None
 
 
 class Setup:
@@ -185,21 +190,26 @@ def spin_cycles_for(torch, ms):
     return int(per_ms * ms)
 
 
-def decode_kernel_time_ms(setup, torch, n=256):
-    """Mean duration of one decode launch from HIP events on the launch stream.
-    A spin kernel first lets the host enqueue every launch ahead of the GPU."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)]
-    cycles = spin_cycles_for(torch, 50.0)
+def decode_kernel_time_ms(setup, torch, n=64, reps=8):
+    """Mean duration of one decode launch: HIP events on the launch stream
+    around replays of a graph of ``n`` back-to-back launches (rotating over the
+    cache copies), so the interval holds launches and nothing else."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for i in range(n):
+            setup.decode(i % PAGE, i % setup.Tc)
     torch.cuda.synchronize()
-    torch.cuda._sleep(cycles)
-    for i in range(n):
-        evs[i][0].record()
-        setup.decode(i % PAGE, i % setup.Tc)
-        evs[i][1].record()
+    graph.replay()
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ts) / n, ts[n // 2]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (n * reps)
 
 
 def cpu_baseline(setup, torch, budget_s=15.0):
@@ -331,11 +341,10 @@ def main():
     value = setup.tokens_steps_per_step / (ms_per_step / 1e3)
     log(f"{steps} steps in {ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step)")
 
-    mean_ms, med_ms = decode_kernel_time_ms(setup, torch)
+    mean_ms = decode_kernel_time_ms(setup, torch)
     bpl = cache_bytes(setup.H, setup.d, setup.Tc, setup.G, setup.lengths)
     achieved = bpl / (mean_ms / 1e3) / 1e9
-    log(f"decode launch: mean {mean_ms * 1e3:.2f} us, median {med_ms * 1e3:.2f} us, "
-        f"{achieved:.0f} GB/s on {bpl} cache bytes")
+    log(f"decode launch: mean {mean_ms * 1e3:.2f} us, {achieved:.0f} GB/s on {bpl} cache bytes")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch)
     rec = {
@@ -362,16 +371,15 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("lvq_decode_attn = decode_main<%d,%d,bf16> + decode_merge<%d>"
-                       % (setup.d // (setup.G // setup.Tc), setup.G // setup.Tc, setup.d)),
+            "kernel": ("lvq_decode_attn: decode_main<S=%d,cg=%d,bf16>, one launch per call"
+                       % (setup.d // (setup.G // setup.Tc), setup.G // setup.Tc)),
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": counters_traffic(args.workload, bpl),
+            "traffic": counters_traffic(args.workload),
             "bytes_per_launch": bpl,
             "mean_launch_us": mean_ms * 1e3,
-            "median_launch_us": med_ms * 1e3,
         },
         "cpu_baseline": cpu,
     }

@@ -453,13 +453,24 @@ struct Batch {
     uint2 k[kUnroll], v[kUnroll];
 };
 
-// The index rows of one (b, h) as buffer resources: a read past the last row
-// returns zeros (code 0, masked later), so loads need neither clamps nor
-// 64-bit address arithmetic, and every batch issues the same number of loads.
+// The index rows of one (b, h) as buffer resources that end at the last row
+// the workgroup may use: a read past it returns zeros (code 0, masked later)
+// without touching memory, so loads need neither clamps nor 64-bit address
+// arithmetic, every batch issues the same number of loads, and the ring's
+// run-ahead past the range costs no HBM traffic.
 constexpr int kBufferWord3 = 0x00020000;       // raw buffer, gfx9 family
 struct IndexRows {
     __amdgpu_buffer_rsrc_t k, v;
     uint32_t lane;                              // byte offset of the lane: tk*S + 8r
+
+    __device__ __forceinline__ void init(const uint8_t *kbase, const uint8_t *vbase, int rows,
+                                         uint32_t lane_off, int S) {
+        k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(kbase), (short)0, rows * S,
+                                              kBufferWord3);
+        v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(vbase), (short)0, rows * S,
+                                              kBufferWord3);
+        lane = lane_off;
+    }
 };
 
 template <int S, int CG, typename CB>
@@ -605,12 +616,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D;
     const uint16_t *kw = a.kwin_t + wbase;
     const uint16_t *vw = a.vwin_t + wbase;
-    IndexRows ir;
-    ir.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.k_index + bh * (size_t)t_max * S),
-                                            (short)0, (int)(t_max * S), kBufferWord3);
-    ir.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(a.v_index + bh * (size_t)t_max * S),
-                                            (short)0, (int)(t_max * S), kBufferWord3);
-    ir.lane = (uint32_t)(tk * S + 8 * r);
+    const uint8_t *kidx = a.k_index + bh * (size_t)t_max * S;
+    const uint8_t *vidx = a.v_index + bh * (size_t)t_max * S;
+    const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
     uint64_t *part = a.partials + (bh * kSlots + split) * (D + 2);
     const uint64_t *parts = a.partials + bh * kSlots * (D + 2);
     uint32_t *ticket = a.tickets + bh;
@@ -633,14 +641,18 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // at n_sink.  Rows outside the range are masked later by the true range,
     // so these loads need not wait for the context length.
     const int vq0 = n_sink + split * a.chunk;
+    IndexRows ir0;                              // rows up to the end of the split's chunk
+    ir0.init(kidx, vidx, (int)min((int64_t)vq0 + a.chunk, t_max), lane_off, S);
     Batch r0, r1, r2;
-    load_batch<S, CG, CB>(ir, vq0 + wave * TPW, r0);
-    load_batch<S, CG, CB>(ir, vq0 + wave * TPW + BSTEP, r1);
+    load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
+    load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
     const int t1 = min(t0 + a.chunk, w.n_s + w.n_v);
     int base = t0 + wave * TPW;
+    IndexRows ir;                               // rows up to the end of the split's range
+    ir.init(kidx, vidx, max(t1, 0), lane_off, S);
     const int s0 = (int)((int64_t)W * split / n_split);
     const int s1 = (int)((int64_t)W * (split + 1) / n_split);
 
