@@ -79,7 +79,7 @@ typedef struct {
     int32_t n_recent;       /* bf16 recent tokens, >= 1 (256 on the pages)    */
     int32_t max_tokens;     /* rows of the index cache per (b, h)             */
     int32_t codebook_dtype; /* lvq_dtype                                      */
-    int32_t decode_splits;  /* VQ splits per (b, h) for lvq_decode_attn;
+    int32_t decode_splits;  /* workgroups per (b, h) for lvq_decode_attn;
                                0 = chosen by the library; 1..LVQ_MAX_SPLITS.
                                Changes only the rounding of the result.        */
 } lvq_config;

@@ -5,9 +5,11 @@
 // are read from shared 8-bit indices through codebook slice t, and the result
 // is merged with bf16 attention over the sink and recent tokens.
 //
-// One launch, n_split * H * B workgroups of 512 threads.  Workgroup s of
-// (b, h) takes VQ tokens [n_s + s*chunk, ...) and window slots
-// [s*W/n_split, ...).  It stages two tables of (h, t) in LDS, both with one
+// One launch, n_split * H * B workgroups of 512 threads.  When the grid fits
+// the chip, workgroup s < n_split - 1 of (b, h) takes VQ tokens
+// [n_s + s*chunk, ...) and the last one every bf16 window slot; otherwise
+// workgroup s takes a VQ chunk and window slots [s*W/n_split, ...).
+// A workgroup with VQ tokens stages two tables of (h, t) in LDS, both with one
 // 256-byte row per code k (the codebook slice is stored code-major, so row k
 // is a contiguous read):
 //     score table  [0, 64K):   row k = sm_scale * log2(e) * q_j . Bk_t[k][j]
@@ -61,6 +63,7 @@ constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMergeChunk = 16;                // partial slots loaded per poll
 constexpr int kMaxPolls = 1 << 22;             // bound of the merger's wait
 constexpr int kVTab = 65536;                   // LDS byte offset of the value table
+constexpr int kBufferWord3 = 0x00020000;       // raw buffer resource, gfx9 family
 constexpr int kTabBytes = 131072;              // both tables
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -286,16 +289,17 @@ struct Stage {
     static constexpr int UW = Sh::UNIT / 4;           // 32-bit words per unit
     uint32_t kw[Sh::UPT][UW], vw[Sh::UPT][UW];
 
-    __device__ __forceinline__ void load(const CB *kcb, const CB *vcb) {
-        const int tid = threadIdx.x;
+    // kr, vr: the slices as buffer resources (a zero-length one reads zeros
+    // and moves no data: workgroups without VQ tokens issue the same loads)
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr) {
+        const uint32_t off = threadIdx.x * Sh::UNIT;
 #pragma unroll
         for (int u = 0; u < Sh::UPT; ++u) {
-            const size_t c = (size_t)(tid + u * kThreads) * Sh::UNIT;
-            const uint4 *ks = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(kcb) + c);
-            const uint4 *vs = reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(vcb) + c);
+            const uint32_t so = (uint32_t)(u * kThreads * Sh::UNIT);
 #pragma unroll
             for (int w = 0; w < UW; w += 4) {
-                const uint4 x = ks[w / 4], y = vs[w / 4];
+                const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, off + 4 * w, so, 0));
+                const uint4 y = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, off + 4 * w, so, 0));
                 kw[u][w] = x.x; kw[u][w + 1] = x.y; kw[u][w + 2] = x.z; kw[u][w + 3] = x.w;
                 vw[u][w] = y.x; vw[u][w + 1] = y.y; vw[u][w + 2] = y.z; vw[u][w + 3] = y.w;
             }
@@ -355,17 +359,18 @@ struct WindowPass {
     static constexpr int CL = Sh::CL, NRD = Sh::NRD, CPR = Sh::CPR;
     uint32_t k[CL / 2];
     uint32_t v[8 * NRD][CPR / 2];
-    bool ok;
+    int slot;
+    bool in;
 
-    // kw, vw: the [W][d] window rows of (b, t, h)
-    __device__ __forceinline__ void load(const uint16_t *kw, const uint16_t *vw, const Windows &w,
-                                         int slot, int s1, int n_sink, int n_recent,
+    // kw, vw: the [W][d] window rows of (b, t, h).  Rows are read only for
+    // slots of this workgroup (host-known, so the loads need not wait for the
+    // context length); whether a slot holds a token is decided at fold time.
+    __device__ __forceinline__ void load(const uint16_t *kw, const uint16_t *vw, int slot_, int s1,
                                          const Lanes<S, CG, CB> &ln) {
         constexpr int D = Sh::D;
-        ok = slot < s1 && slot_valid(slot, w, n_sink, n_recent);
-        // rows are read only for slots that hold a token (most lanes of a
-        // pass have none when a workgroup owns few slots)
-        if (!ok) {
+        slot = slot_;
+        in = slot < s1;
+        if (!in) {
 #pragma unroll
             for (int i = 0; i < CL / 2; ++i) k[i] = 0u;
 #pragma unroll
@@ -374,14 +379,13 @@ struct WindowPass {
                 for (int e = 0; e < CPR / 2; ++e) v[i][e] = 0u;
             return;
         }
-        const int sl = slot;
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)sl * D + ln.r * CL);
+        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + (size_t)slot * D + ln.r * CL);
 #pragma unroll
         for (int i = 0; i < CL / 8; ++i) {
             const uint4 kk = kp[i];
             k[4 * i] = kk.x; k[4 * i + 1] = kk.y; k[4 * i + 2] = kk.z; k[4 * i + 3] = kk.w;
         }
-        const uint16_t *vrow = vw + (size_t)sl * D;
+        const uint16_t *vrow = vw + (size_t)slot * D;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -399,8 +403,10 @@ struct WindowPass {
     }
 
     template <typename OnlineT>
-    __device__ __forceinline__ void fold(const float *qs, OnlineT &st, int r) {
+    __device__ __forceinline__ void fold(const float *qs, OnlineT &st, int r, const Windows &w,
+                                         int n_sink, int n_recent) {
         constexpr int R = Sh::R;
+        const bool ok = in && slot_valid(slot, w, n_sink, n_recent);
         float dot = 0.f;
         if (ok) {
 #pragma unroll
@@ -458,7 +464,6 @@ struct Batch {
 // without touching memory, so loads need neither clamps nor 64-bit address
 // arithmetic, every batch issues the same number of loads, and the ring's
 // run-ahead past the range costs no HBM traffic.
-constexpr int kBufferWord3 = 0x00020000;       // raw buffer, gfx9 family
 struct IndexRows {
     __amdgpu_buffer_rsrc_t k, v;
     uint32_t lane;                              // byte offset of the lane: tk*S + 8r
@@ -625,6 +630,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     float *outp = a.out + bh * D;
     const float scale = a.scale_log2;
     const int n_split = a.n_split;
+    const bool sep = a.window_wg != 0;
+    const bool vq_wg = !sep || split < n_split - 1;        // takes a VQ chunk
 
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
@@ -634,33 +641,37 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     uint32_t arrival_word = 0;
     if (tid == 0) arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
-    stg.load(kcb, vcb);
+    {
+        const int slice = vq_wg ? 256 * S * CG * (int)sizeof(CB) : 0;
+        stg.load(__builtin_amdgcn_make_buffer_rsrc(const_cast<CB *>(kcb), (short)0, slice, kBufferWord3),
+                 __builtin_amdgcn_make_buffer_rsrc(const_cast<CB *>(vcb), (short)0, slice, kBufferWord3));
+    }
 
     // The first two index batches are addressed from host-known values: a
     // sequence with any VQ token has L > n_sink + ..., so its VQ range starts
     // at n_sink.  Rows outside the range are masked later by the true range,
     // so these loads need not wait for the context length.
+    // window rows of the first pass (wave w takes slots s0 + w + kWaves * (tk + pass * TPW))
+    const int s0 = sep ? 0 : (int)((int64_t)W * split / n_split);
+    const int s1 = sep ? (split == n_split - 1 ? W : 0) : (int)((int64_t)W * (split + 1) / n_split);
+    using Win = WindowPass<S, CG, CB>;
+    int wslot = s0 + wave;
+    Win win;
+    win.load(kw, vw, wslot + kWaves * tk, s1, ln);
+
     const int vq0 = n_sink + split * a.chunk;
     IndexRows ir0;                              // rows up to the end of the split's chunk
-    ir0.init(kidx, vidx, (int)min((int64_t)vq0 + a.chunk, t_max), lane_off, S);
+    ir0.init(kidx, vidx, vq_wg ? (int)min((int64_t)vq0 + a.chunk, t_max) : 0, lane_off, S);
     Batch r0, r1, r2;
     load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
     load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
-    const int t1 = min(t0 + a.chunk, w.n_s + w.n_v);
+    const int t1 = vq_wg ? min(t0 + a.chunk, w.n_s + w.n_v) : t0;
     int base = t0 + wave * TPW;
     IndexRows ir;                               // rows up to the end of the split's range
     ir.init(kidx, vidx, max(t1, 0), lane_off, S);
-    const int s0 = (int)((int64_t)W * split / n_split);
-    const int s1 = (int)((int64_t)W * (split + 1) / n_split);
-
-    // window slots: wave w takes s0 + w + kWaves * (tk + pass * TPW)
-    using Win = WindowPass<S, CG, CB>;
-    int wslot = s0 + wave;
-    Win win;
-    win.load(kw, vw, w, wslot + kWaves * tk, s1, n_sink, n_recent, ln);
 
     const float qv = bf16f((uint16_t)qraw);
     if (tid < D) qs[tid] = qv * scale;
@@ -673,16 +684,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     Online<Sh::NACC> st;
     st.init();
     if constexpr (!kWindowFirst) {
-        stg.finish(qs, smem);
+        if (vq_wg) stg.finish(qs, smem);
         __syncthreads();
     }
     while (wslot < s1) {                         // wave-uniform
-        win.fold(qs, st, r);
+        win.fold(qs, st, r, w, n_sink, n_recent);
         wslot += kWaves * TPW;
-        if (wslot < s1) win.load(kw, vw, w, wslot + kWaves * tk, s1, n_sink, n_recent, ln);
+        if (wslot < s1) win.load(kw, vw, wslot + kWaves * tk, s1, ln);
     }
     if constexpr (kWindowFirst) {
-        stg.finish(qs, smem);
+        if (vq_wg) stg.finish(qs, smem);
         __syncthreads();
     }
     // three-deep ring, unrolled so that every batch lives in named registers

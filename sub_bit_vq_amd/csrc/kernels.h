@@ -27,8 +27,11 @@ struct DecodeArgs {
     int B, H, d, Tc, cg, S, n_sink, n_recent;
     int64_t t_max;
     int loop_step;
-    int n_split;      // workgroups per (b, h): VQ chunks and window-slot ranges
-    int chunk;        // VQ tokens per split (multiple of 64)
+    int n_split;      // workgroups per (b, h)
+    int window_wg;    // 1: the last workgroup of (b, h) takes every window slot
+                      // and the others one VQ chunk each; 0: each takes a VQ
+                      // chunk and an equal share of the window slots
+    int chunk;        // VQ tokens per chunk (multiple of 64)
     int cb_bf16;
     const uint16_t *q;          // [B][H][d]
     const int32_t *ctx_len;     // [B]

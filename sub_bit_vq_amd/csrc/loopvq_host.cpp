@@ -44,25 +44,36 @@ int64_t max_vq_tokens(const lvq_config *c, int32_t max_ctx_len, bool exact_windo
     return v > 0 ? v : 0;
 }
 
-// Splits per (b, h).  One decode workgroup fills a compute unit's LDS, so
-// aim for one workgroup per CU (256 on MI355X), keep splits at least 512
-// tokens long, and cut long ragged contexts into chunks of at most ~8K tokens
-// so that the longest sequences do not leave a tail.
-int32_t choose_splits(const lvq_config *c, int64_t max_vq) {
-    if (max_vq <= 0) return 1;
+// Workgroups per (b, h) and where the bf16 window slots go.  One decode
+// workgroup fills a compute unit's LDS, so aim for one workgroup per CU (256
+// on MI355X), keep token splits at least 512 tokens long, and cut long ragged
+// contexts into chunks of at most ~8K tokens so that the longest sequences
+// leave no tail.  When the whole grid fits the chip at once, one extra
+// workgroup per (b, h) takes every window slot (it needs no codebook tables,
+// and the token splits skip the window pass); otherwise the window slots are
+// spread over the token splits, which costs less compute-unit time.
+struct Splits {
+    int32_t n;          // workgroups per (b, h)
+    bool window_wg;     // the last one takes every window slot
+};
+constexpr int64_t kTargetGroups = 256;
+
+Splits choose_splits(const lvq_config *c, int64_t max_vq) {
+    if (max_vq <= 0) return {1, false};
+    const int64_t bh = (int64_t)c->batch * c->n_heads;
     int64_t want = c->decode_splits;
     if (want == 0) {
-        const int64_t target_groups = 256;
-        const int64_t bh = (int64_t)c->batch * c->n_heads;
-        want = (target_groups + bh - 1) / bh;
+        int64_t vq = (kTargetGroups + bh - 1) / bh - 1;
         const int64_t by_len = (max_vq + 511) / 512;
-        if (want > by_len) want = by_len;
+        if (vq > by_len) vq = by_len;
         const int64_t by_chunk = (max_vq + 8191) / 8192;
-        if (want < by_chunk) want = by_chunk;
+        if (vq < by_chunk) vq = by_chunk;
+        if (vq < 1) vq = 1;
+        want = bh * (vq + 1) <= kTargetGroups ? vq + 1 : vq;
     }
     if (want < 1) want = 1;
     if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
-    return (int32_t)want;
+    return {(int32_t)want, want > 1 && bh * want <= kTargetGroups};
 }
 
 }  // namespace
@@ -113,7 +124,7 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
 
 int32_t lvq_decode_splits(const lvq_config *c, int32_t max_ctx_len) {
     if (!config_ok(c) || max_ctx_len < 0 || max_ctx_len > c->max_tokens) return 0;
-    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true));
+    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true)).n;
 }
 
 lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strides,
@@ -197,9 +208,11 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
 
     const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
-    const int32_t n_split = choose_splits(c, max_vq);
+    const Splits sp = choose_splits(c, max_vq);
+    const int32_t n_split = sp.n;
     if ((int64_t)n_split * c->batch * c->n_heads > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
-    int64_t chunk = (max_vq + n_split - 1) / n_split;
+    const int64_t n_vq = sp.window_wg ? n_split - 1 : n_split;
+    int64_t chunk = (max_vq + n_vq - 1) / n_vq;
     chunk = (chunk + 63) / 64 * 64;
     if (chunk < 64) chunk = 64;
 
@@ -215,6 +228,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.t_max = c->max_tokens;
     a.loop_step = loop_step;
     a.n_split = n_split;
+    a.window_wg = sp.window_wg ? 1 : 0;
     a.chunk = (int)chunk;
     a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
     a.q = static_cast<const uint16_t *>(q);

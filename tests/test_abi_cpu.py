@@ -92,10 +92,12 @@ def test_layout_rejects_bad_config(bad):
 
 def test_decode_splits():
     cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
-    assert lv.lvq_decode_splits(cfg, 32768) == 16        # 256 workgroups over 16 heads
-    assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded
-    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 3    # >= 512 tokens per split
+    # grid within the chip: VQ token chunks + one window workgroup per (b, h)
+    assert lv.lvq_decode_splits(cfg, 32768) == 16        # 15 chunks + windows, 256 workgroups
+    assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded: windows only
+    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 4    # 3 chunks of <= 512 tokens + windows
     assert lv.lvq_decode_splits(cfg, 40000) == 0         # beyond max_tokens
+    # larger grids: windows spread over the chunks
     cfg3 = _cfg(*WORKLOADS["batch64_ragged_0p5bit"])
     assert lv.lvq_decode_splits(cfg3, 18432) == 3        # chunks of at most ~8K tokens
     assert lv.lvq_decode_splits(_cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, decode_splits=7),
