@@ -500,41 +500,62 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
     float s[kUnroll];
     bool ok[kUnroll];
     float mx = -INFINITY;
+    // all score gathers of the batch go out before any is summed (the LDS
+    // latency then overlaps), and each token's 8 values are summed as a tree
+    float g[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t w0 = perm(bt.k[u].y, bt.k[u].x, ln.rotA);   // index bytes in step order
+        const uint32_t w1 = perm(bt.k[u].y, bt.k[u].x, ln.rotB);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            g[u][i] = *reinterpret_cast<const float *>(smem + perm(ln.offK[i >> 2], i < 4 ? w0 : w1, sel_k(i)));
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         ok[u] = base + u * STEP + tk < t1;
-        const uint32_t w0 = perm(bt.k[u].y, bt.k[u].x, ln.rotA);   // index bytes in step order
-        const uint32_t w1 = perm(bt.k[u].y, bt.k[u].x, ln.rotB);
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t ad = perm(ln.offK[i >> 2], i < 4 ? w0 : w1, sel_k(i));
-            acc += *reinterpret_cast<const float *>(smem + ad);
-        }
+        float acc = ((g[u][0] + g[u][1]) + (g[u][2] + g[u][3])) + ((g[u][4] + g[u][5]) + (g[u][6] + g[u][7]));
         acc = token_sum<R>(acc);
         s[u] = ok[u] ? acc : -INFINITY;
         mx = fmaxf(mx, s[u]);
     }
     st.raise(wave_max(mx));
+    if constexpr (Sh::kMfma) {
+        // value gathers of pass u + 1 go out before the MFMAs of pass u
+        uint2 av[2][8];
+        auto gather = [&](int u, uint2 *dst) {
+            const uint32_t w0 = perm(bt.v[u].y, bt.v[u].x, ln.rotA);
+            const uint32_t w1 = perm(bt.v[u].y, bt.v[u].x, ln.rotB);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-        // tokens past the range take weight 0 (their clamped rows are valid codes)
-        const uint32_t w0 = perm(bt.v[u].y, bt.v[u].x, ln.rotA);
-        const uint32_t w1 = perm(bt.v[u].y, bt.v[u].x, ln.rotB);
-        if constexpr (Sh::kMfma) {
+            for (int i = 0; i < 8; ++i)
+                dst[i] = *reinterpret_cast<const uint2 *>(smem + perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i)));
+        };
+        gather(0, av[0]);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (u + 1 < kUnroll) gather(u + 1, av[(u + 1) & 1]);
+            // tokens past the range take weight 0 (out-of-range rows read code 0)
             const _Float16 ph = (_Float16)(ok[u] ? ex2(s[u] - st.m) * kPScale : 0.f);
             st.l += (float)ph;
             const uint32_t ph2 = (uint32_t)__builtin_bit_cast(uint16_t, ph) * 0x00010001u;
             const half4_t bop = __builtin_bit_cast(half4_t, make_uint2(ph2 & ln.bmask0, ph2 & ln.bmask1));
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const uint32_t ad = perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i));
-                const half4_t aop = __builtin_bit_cast(half4_t, *reinterpret_cast<const uint2 *>(smem + ad));
                 float4_t d = {st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]};
-                d = __builtin_amdgcn_mfma_f32_4x4x4f16(aop, bop, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, av[u & 1][i]), bop, d, 0, 0, 0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) st.acc[4 * i + e] = d[e];
             }
+        }
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        // tokens past the range take weight 0 (out-of-range rows read code 0)
+        const uint32_t w0 = perm(bt.v[u].y, bt.v[u].x, ln.rotA);
+        const uint32_t w1 = perm(bt.v[u].y, bt.v[u].x, ln.rotB);
+        if constexpr (Sh::kMfma) {
+            // handled below, one pass ahead
         } else if constexpr (Sh::kF16V) {
             const _Float16 ph = (_Float16)(ok[u] ? ex2(s[u] - st.m) * kPScale : 0.f);
             st.l += (float)ph;
@@ -817,27 +838,31 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                 pm[i] = __hip_atomic_load(&parts[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 pl[i] = __hip_atomic_load(&parts[sl + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            bool ok = true;
+            // branch-free: a slot counts if it exists and is not this workgroup's
+            uint32_t ok = 1u;
 #pragma unroll
             for (int i = 0; i < kMergeChunk; ++i) {
-                const int s = c0 + i;
-                if (s < n && s != split)
-                    ok = ok && (uint32_t)(po[i] >> 32) == tag && (uint32_t)(pm[i] >> 32) == tag &&
-                         (uint32_t)(pl[i] >> 32) == tag;
+                const uint32_t want = (uint32_t)(c0 + i < n) & (uint32_t)(c0 + i != split);
+                const uint32_t cur = (uint32_t)((uint32_t)(po[i] >> 32) == tag) &
+                                     (uint32_t)((uint32_t)(pm[i] >> 32) == tag) &
+                                     (uint32_t)((uint32_t)(pl[i] >> 32) == tag);
+                ok &= cur | (want ^ 1u);
             }
-            if (__all(ok)) break;
+            if (__all(ok != 0u)) break;
             if (++poll >= kMaxPolls) {
                 failed = true;
                 break;
             }
-            __builtin_amdgcn_s_sleep(4);
+            __builtin_amdgcn_s_sleep(1);
         }
+        float mi[kMergeChunk], li[kMergeChunk];
         float mc = Mg;
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) {
-            const int s = c0 + i;
-            const float li = __uint_as_float((uint32_t)pl[i]);
-            if (s < n && s != split && li > 0.f) mc = fmaxf(mc, __uint_as_float((uint32_t)pm[i]));
+            const bool use = (c0 + i < n) & (c0 + i != split) & (__uint_as_float((uint32_t)pl[i]) > 0.f);
+            li[i] = use ? __uint_as_float((uint32_t)pl[i]) : 0.f;
+            mi[i] = use ? __uint_as_float((uint32_t)pm[i]) : -INFINITY;
+            mc = fmaxf(mc, mi[i]);
         }
         if (mc > Mg) {                               // Mg = -inf gives 0 * 0
             const float sc = Mg == -INFINITY ? 0.f : ex2(Mg - mc);
@@ -847,13 +872,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < kMergeChunk; ++i) {
-            const int s = c0 + i;
-            const float li = __uint_as_float((uint32_t)pl[i]);
-            if (s < n && s != split && li > 0.f) {
-                const float e = ex2(__uint_as_float((uint32_t)pm[i]) - Mg);
-                num += __uint_as_float((uint32_t)po[i]) * e;
-                den += li * e;
-            }
+            const float e = li[i] > 0.f ? ex2(mi[i] - Mg) : 0.f;
+            num += __uint_as_float((uint32_t)po[i]) * e;
+            den += li[i] * e;
         }
     }
     outp[tid] = failed ? NAN : (den > 0.f ? num / den : 0.f);
