@@ -35,17 +35,18 @@
 // (bf16 window values use the fp32 4x4x1 form, so they stay exact).
 // Otherwise v_dot2_f32_f16 does them on the vector ALUs.
 // Index rows stream from HBM through a three-deep register ring of buffer
-// loads; the first two batches are issued before the tables are staged.  At the end the lanes
-// write their (rotated) accumulators to the freed table space at their
-// channel positions and the workgroup sums them there.
-// A workgroup takes an arrival ticket of (b, h) as soon as its tokens are
-// done (the round trip overlaps its own reduction), then publishes
-// (m, l, o[d]) as 64-bit (value, call tag) pairs.  Every workgroup but the
-// last leaves; the last polls the others' pairs until every tag is the
-// current call's, merges (log-sum-exp) into out and advances the arrival
-// word to the next call.  Everything crosses workgroups through agent-scope atomics (no L2
-// writeback or invalidation); each pair is one 64-bit access, so no store
-// needs a completion wait.
+// loads; the first two batches are issued before the tables are staged.  At
+// the end the lanes write their (rotated) accumulators to the freed table
+// space at their channel positions and the workgroup sums them there.
+// Every workgroup but the merger of (b, h) publishes (m, l, o[d]) as 64-bit
+// (value, call tag) pairs and leaves.  The merger is the window workgroup
+// when there is one (its peers were dispatched before it), else the last to
+// take an arrival ticket once its tokens are done (the round trip overlaps
+// its own reduction).  It polls the others' pairs until every tag is the
+// current call's, merges (log-sum-exp) into out and advances the call word
+// to the next call.  Everything crosses workgroups through agent-scope
+// atomics (no L2 writeback or invalidation); each pair is one 64-bit access,
+// so no store needs a completion wait.
 #include "kernels.h"
 
 #include <math.h>
@@ -740,12 +741,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
     const int n = n_split;
     __syncthreads();                             // every wave is done with the tables
-    // This workgroup's arrival: the last to finish its tokens merges.  The
-    // ticket travels while the partial is reduced.  Every thread takes part
-    // (thread 0 adds 1, the rest 0; the compiler folds each wave into one
-    // atomic), so no branch forces an early wait for the result.
+    // Who merges.  With a window workgroup (the grid fits the chip) it is that
+    // workgroup: it has the highest index of its (b, h), so its peers were
+    // dispatched before it, and it is done early, so it simply waits for
+    // their partials.  Otherwise the last workgroup to take an arrival ticket
+    // merges; the ticket travels while the partial is reduced.
     uint32_t ticket_word = 0;
-    if (tid == 0 && n > 1)
+    if (tid == 0 && n > 1 && !sep)
         ticket_word = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float *dump = reinterpret_cast<float *>(smem);
     float *mine = dump + (size_t)(wave * TPW + tk) * D;
@@ -810,7 +812,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     }
     // Every workgroup publishes at once (before it knows whether it is last,
     // so the others' pairs are already on their way when the last one looks).
-    if (n > 1) {
+    if (n > 1 && sep) {
+        if (split != n - 1) {                    // token splits publish and leave
+            if (tid < D) publish(&part[2 + tid], o, tag);
+            if (tid == 0) {
+                publish(&part[0], M, tag);
+                publish(&part[1], lt, tag);
+            }
+            return;
+        }
+    } else if (n > 1) {
         if (tid < D) publish(&part[2 + tid], o, tag);
         if (tid == 0) {
             publish(&part[0], M, tag);
@@ -821,8 +832,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         if ((int)(*arrival & 0xffu) != n - 1) return;
     }
 
-    // Last arrival: every other workgroup of (b, h) has finished its tokens;
-    // poll their pairs (slot `split` is this workgroup's own).
+    // The merger: every other workgroup of (b, h) has started (and will
+    // publish); poll their pairs (slot `split` is this workgroup's own).
     if (tid >= D) return;
     float Mg = lt > 0.f ? M : -INFINITY;
     float num = o, den = lt;
