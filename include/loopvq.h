@@ -139,14 +139,16 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  *            x_strides == NULL means the dense [n_tokens][H][Tc][d] layout.
  *            Strides are in elements; channels must be contiguous and every
  *            stride a multiple of cg.
- * codebook   device, cfg->codebook_dtype, layout above (one call encodes one
- *            tensor: call once with the K codebook and once with the V one)
+ * codebook   device, cfg->codebook_dtype, layout above, 16-byte aligned (one
+ *            call encodes one tensor: call once with the K codebook and once
+ *            with the V one)
  * index_cache device uint8 [B][H][max_tokens][S]; rows
  *            [first_token, first_token + n_tokens) of sequence seq are written
  * n_tokens   may be 0 (nothing launched)
- * Errors: LVQ_ERR_INVALID_ARG (null pointers, seq or rows out of range,
- * bad strides), LVQ_ERR_UNSUPPORTED (G not in {8, 16, 32}, cg not in
- * {2, 4, 8}, or fp32 codebooks with G = 32), LVQ_ERR_HIP.
+ * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned x or codebook, seq
+ * or rows out of range, bad strides), LVQ_ERR_UNSUPPORTED (G not in
+ * {8, 16, 32}, cg not in {2, 4, 8}, S = d/cg not a multiple of 4, or fp32
+ * codebooks with G = 32), LVQ_ERR_HIP.
  */
 lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_strides,
                       int64_t n_tokens, const void *codebook, uint8_t *index_cache,
@@ -157,7 +159,7 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  * Attend from indices"): for every (b, h),
  *   out = sum_n softmax_n(sm_scale * q . K_n) V_n
  * over all L_b tokens, where VQ tokens use K_n[j*cg + c] =
- * k_codebook[t][h][j][k_index[b][h][n][j]][c] (likewise V) and sink/recent
+ * k_codebook[t][h][k_index[b][h][n][j]][j][c] (likewise V) and sink/recent
  * tokens use the bf16 window buffers of step t.  fp32 accumulation; VQ value
  * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
  * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).

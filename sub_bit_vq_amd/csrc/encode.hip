@@ -8,6 +8,11 @@
 //     argmin_k D_k,  D_k = sum_i (x_i - c_{k,i})^2
 // in IEEE fp32 (separate subtract, square, add; ascending i), lowest k on ties.
 //
+// Layout of the work.  A workgroup owns 4 sub-vectors j (one wave each) of one
+// head and a chunk of tokens.  It first stages the 4 codebooks (all Tc
+// slices, all 256 codes; the storage is code-major, so each (slice, code) row
+// piece is one contiguous read) in LDS, with their squared norms.
+//
 // Screen (MFMA).  The screen value S_k = |c_k|^2 - 2 x.c_k differs from D_k by
 // |x|^2, the same for every k.  One v_mfma_f32_16x16x32_bf16 multiplies 16
 // codes (rows) by 16 tokens (columns) over an augmented K axis:
@@ -16,19 +21,24 @@
 // where b0 + b1 + b2 = fl32(|c_k|^2) in bf16 parts (and, for fp32 codebooks,
 // c = c0 + c1 + c2 in bf16 parts, P = 3).  Products of bf16 values are exact
 // in fp32, so the only screen errors are the accumulation roundings.  Each
-// wave keeps its (h, j) codebook resident in registers as MFMA A operands and
-// streams 16-token tiles through it; every lane tracks the smallest and
-// second-smallest screen value of its 64 codes, and 4 lanes combine.
+// wave keeps its codebook in registers as MFMA A operands and streams 16-token
+// tiles through it.  Each lane tracks the two smallest screen values of its 64
+// codes, a pair (a, b) at a time: the smallest is min3(m1, a, b) and the
+// second smallest min(m2, med3(m1, a, b)).  The low 6 bits of each value are
+// replaced by its slot among the lane's 64 codes, so the smallest value also
+// names its code (the lane supplies the rest of the index).
 //
-// Exactness.  If the two smallest screen values are more than
-//     eps = 2^-14 (|x| + max_k |c_k|)^2
-// apart, the screen winner is the exact winner: eps exceeds twice the sum of
-// the fp32 error of D_k (at most (G+2) 2^-24 D_k) and of the screen (at most
-// F (P*G+3) 2^-24 (|c|^2 + 2|x||c|) for an accumulation F times worse than a
-// sequential fp32 sum), for F up to 13 at G = 32 and P = 1.  Otherwise the
-// wave re-scores all 256 codes of that sub-vector exactly as defined above (64
-// lanes x 4 codes, strict < per lane in ascending k, then a lowest-index
-// argmin across lanes), which reproduces the definition bit for bit.
+// Exactness.  With R = |x| + max_k |c_k|, the 6 bits written into a value
+// move it by at most 2^-17 R^2; the fp32 error of D_k is at most
+// (G+2) 2^-24 R^2 and that of the screen at most F (P*G+3) 2^-24 R^2 for an
+// accumulation F times worse than a sequential fp32 sum.  If the two smallest
+// (marked) screen values are more than eps = 2^-14 R^2 apart, eps exceeds
+// twice the sum of these (for F up to 10 at G = 32, P = 1 and up to 7 at
+// G = 16, P = 3), so the screen
+// winner is the exact winner.  Otherwise the wave re-scores all 256 codes of
+// that sub-vector exactly as defined above from the staged codebook (64 lanes
+// x 4 codes, strict < per lane in ascending k, then a lowest-index argmin
+// across lanes), which reproduces the definition bit for bit.
 #include "kernels.h"
 
 #include <math.h>
@@ -42,6 +52,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;     // 4 waves, one sub-vector index j each
+constexpr int kJW = 4;            // sub-vectors per workgroup
 constexpr int kTokChunk = 1024;   // tokens per workgroup
 constexpr float kEpsScale = 6.103515625e-05f;  // 2^-14
 
@@ -65,93 +76,153 @@ __device__ __forceinline__ float split_part(float v, int p) {
 }
 
 template <typename CB>
-__device__ __forceinline__ float cb_at(const CB *p, size_t i);
+__device__ __forceinline__ float to_f(CB v);
 template <>
-__device__ __forceinline__ float cb_at<float>(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <>
-__device__ __forceinline__ float cb_at<uint16_t>(const uint16_t *p, size_t i) { return bf16f(p[i]); }
+__device__ __forceinline__ float to_f<uint16_t>(uint16_t v) { return bf16f(v); }
 
-// entry i = t*CG + c of codeword k of (h, j): codebook [Tc][H][256][S][CG]
-template <int CG, typename CB>
-__device__ __forceinline__ float codeword(const EncodeArgs &a, const CB *cb, int h, int j, int k,
-                                          int i) {
-    const int t = i / CG, c = i % CG;
-    return cb_at(cb, ((((size_t)t * a.H + h) * 256 + k) * a.S + j) * CG + c);
+// Cross-lane exchanges without LDS.  After pair16(x, a, b), {a, b} of every
+// lane hold x of that lane and of lane ^ 16 (pair32: lane ^ 32), so any
+// symmetric combination of a and b is the pairwise result in both lanes.
+__device__ __forceinline__ void pair16(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
 }
 
-// sub-vector entries x_0..x_{G-1} of (token n, head h, sub-vector j)
-template <int G, int CG>
-__device__ __forceinline__ void load_subvector(const EncodeArgs &a, int64_t n, int h, int j,
-                                               float (&xv)[G]) {
-    const uint16_t *base = a.x + n * a.sx_tok + h * a.sx_head + (int64_t)j * CG;
+// minimum over the 64 lanes, in every lane: DPP xor 1, xor 2, half-row and
+// row mirrors within 16 lanes, then the two lane swaps
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = min(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return min(r[0], r[1]);
+}
+
+template <int G, int CG, int P, typename CB>
+struct EncShape {
+    static constexpr int T = G / CG;                       // loop steps
+    static constexpr int KAUG = (P * G + 3 + 31) / 32 * 32;
+    static constexpr int NCH = KAUG / 32;                  // MFMAs per 16 codes x 16 tokens
+    static constexpr int EB = (int)sizeof(CB);
+    static constexpr int ROWB = kJW * CG * EB;             // bytes of one (slice, code) row piece
+    static constexpr int EC = 16 / EB;                     // elements per 16-byte chunk
+    static constexpr int CHUNKS = T * 256 * ROWB / 16;     // staging chunks
+    static_assert(ROWB % 16 == 0 && CHUNKS % kThreads == 0, "staging tiles");
+    static_assert(G % 8 == 0 && (P * G) % 8 == 0, "operand blocks of 8");
+};
+
+// One 16-token tile of x as MFMA B-operand words: lane (row, kq) holds, for
+// each K chunk ch, the 4 words (8 bf16) of entries kk = ch*32 + kq*8 .. +7 of
+// token n0 + row (zero where kk is not an x entry or the token is past the end).
+template <int NCH>
+struct XTile {
+    uint32_t w[NCH][4];
+};
+
+constexpr uint32_t kOob = 0xffffff00u;            // offset past any buffer: loads return 0
+constexpr int kBufferWord3 = 0x00020000;          // raw buffer resource, gfx9 family
+
+template <int CG, int NCH>
+__device__ __forceinline__ void load_tile(XTile<NCH> &t, __amdgpu_buffer_rsrc_t rs,
+                                          const uint32_t (&off)[NCH][8 / CG > 0 ? 8 / CG : 1],
+                                          bool valid) {
+    constexpr int NLD = 8 / CG;
 #pragma unroll
-    for (int t = 0; t < G / CG; ++t) {
-        const uint16_t *p = base + t * a.sx_step;
-        if constexpr (CG == 8) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                xv[t * 8 + 2 * e] = __uint_as_float(w[e] << 16);
-                xv[t * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        for (int s = 0; s < NLD; ++s) {
+            const uint32_t o = valid ? off[ch][s] : kOob;
+            if constexpr (CG == 8) {
+                const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
+                t.w[ch][0] = v.x; t.w[ch][1] = v.y; t.w[ch][2] = v.z; t.w[ch][3] = v.w;
+            } else if constexpr (CG == 4) {
+                const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
+                t.w[ch][2 * s] = v.x; t.w[ch][2 * s + 1] = v.y;
+            } else {
+                t.w[ch][s] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
             }
-        } else if constexpr (CG == 4) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(p);
-            xv[t * 4 + 0] = __uint_as_float(v.x << 16);
-            xv[t * 4 + 1] = __uint_as_float(v.x & 0xffff0000u);
-            xv[t * 4 + 2] = __uint_as_float(v.y << 16);
-            xv[t * 4 + 3] = __uint_as_float(v.y & 0xffff0000u);
-        } else {
-            const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
-            xv[t * 2 + 0] = __uint_as_float(v << 16);
-            xv[t * 2 + 1] = __uint_as_float(v & 0xffff0000u);
         }
     }
-}
-
-// D_k exactly as defined: sequential fp32, no contraction.
-template <int G, int CG, typename CB>
-__device__ __forceinline__ float exact_distance(const EncodeArgs &a, const CB *cb, int h, int j,
-                                                int k, const float (&xv)[G]) {
-    float dist = 0.f;
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-        const float e = __fsub_rn(xv[i], codeword<CG>(a, cb, h, j, k, i));
-        dist = __fadd_rn(dist, __fmul_rn(e, e));
-    }
-    return dist;
 }
 
 template <int G, int CG, int P, typename CB>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
-    constexpr int KAUG = (P * G + 3 + 31) / 32 * 32;
-    constexpr int NCH = KAUG / 32;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    using Sh = EncShape<G, CG, P, CB>;
+    constexpr int NCH = Sh::NCH;
+    __shared__ __align__(16) CB cbs[kJW * 256 * G];    // [jl][k][i]
+    __shared__ float nrm[kJW * 256];
+    __shared__ uint16_t amb_queue[kJW][kTokChunk];     // per wave: chunk rows to re-score
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.z;
-    const int j = blockIdx.y * 4 + wave;
-    if (j >= a.S) return;
+    const int j0 = blockIdx.y * kJW, j = j0 + wave;
     const int64_t tok0 = (int64_t)blockIdx.x * kTokChunk;
     const int64_t tok_end = min(tok0 + kTokChunk, a.n_tokens);
-    const CB *cb = static_cast<const CB *>(a.cb);
     const int row = lane & 15, kq = lane >> 4;
 
-    // codebook of (h, j) as MFMA A operands; max codeword norm
-    bf16x8 afrag[16][NCH];
+    // stage the 4 codebooks: chunk c of row (t, k) piece p -> entries (jl, c) of slice t
+    {
+        const char *src = static_cast<const char *>(a.cb);
+        constexpr int PER_ROW = Sh::ROWB / 16;
+#pragma unroll
+        for (int u = 0; u < Sh::CHUNKS / kThreads; ++u) {
+            const int c = tid + u * kThreads;
+            const int r = c / PER_ROW, pc = c % PER_ROW;
+            const int t = r >> 8, k = r & 255;
+            const size_t off = ((((size_t)t * a.H + h) * 256 + k) * a.S + j0) * (CG * Sh::EB) + pc * 16;
+            const uint4 v = *reinterpret_cast<const uint4 *>(src + off);
+            const CB *e = reinterpret_cast<const CB *>(&v);
+#pragma unroll
+            for (int q = 0; q < Sh::EC; ++q) {
+                const int fe = pc * Sh::EC + q;          // element of the (t, k) row piece
+                const int jl = fe / CG, cc = fe % CG;
+                cbs[(jl * 256 + k) * G + t * CG + cc] = e[q];
+            }
+        }
+    }
+    __syncthreads();
+    // squared norms (fp64 sum, rounded once); the max over the wave's codes
+#pragma unroll
+    for (int m = 0; m < kJW; ++m) {
+        const CB *cw = cbs + (m * 256 + tid) * G;
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const double v = to_f(cw[i]);
+            s += v * v;
+        }
+        nrm[m * 256 + tid] = (float)s;
+    }
+    __syncthreads();
+    if (j >= a.S) return;
     float max_norm2 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) max_norm2 = fmaxf(max_norm2, nrm[wave * 256 + lane + 64 * r]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) max_norm2 = fmaxf(max_norm2, __shfl_xor(max_norm2, off));
+    // upper bound of max_k |c_k| (slack covers the rounding of the norm)
+    const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
+
+    // this wave's codebook as MFMA A operands: lane (row, kq) holds entries
+    // kk = ch*32 + kq*8 + e of code blk*16 + row (kq unrolled so that every
+    // register index is a constant)
+    const CB *mycb = cbs + wave * 256 * G;
+    bf16x8 afrag[16][NCH];
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
         const int code = blk * 16 + row;
-        float cw[G];
-        double n2 = 0.0;
-#pragma unroll
-        for (int i = 0; i < G; ++i) {
-            cw[i] = codeword<CG>(a, cb, h, j, code, i);
-            n2 += (double)cw[i] * (double)cw[i];
-        }
-        const float bias = (float)n2;
-        max_norm2 = fmaxf(max_norm2, bias);
-        // augmented row entries kk = ch*32 + kq*8 + e; the lane-group index
-        // kq is unrolled so that every register index is a constant
+        const CB *cw = mycb + code * G;
+        const float bias = nrm[wave * 256 + code];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (kq != q) continue;
@@ -163,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
                     const int kk = ch * 32 + q * 8 + e;
                     float v = 0.f;
                     if (kk < P * G)
-                        v = -2.f * (P == 1 ? cw[kk % G] : split_part(cw[kk % G], kk / G));
+                        v = -2.f * (P == 1 ? to_f(cw[kk % G]) : split_part(to_f(cw[kk % G]), kk / G));
                     else if (kk < P * G + 3)
                         v = split_part(bias, kk - P * G);
                     f[e] = __builtin_bit_cast(__bf16, bf16_rne(v));
@@ -172,121 +243,204 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             }
         }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) max_norm2 = fmaxf(max_norm2, __shfl_xor(max_norm2, off));
-    // upper bound of max_k |c_k| (slack covers the rounding of the norm)
-    const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
 
     uint8_t *out_rows = a.index + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token) * a.S + j;
 
-    for (int64_t n0 = tok0; n0 < tok_end; n0 += 16) {
-        const int64_t n = n0 + row;
-        const bool valid = n < tok_end;
-        float xv[G];
-        if (valid) {
-            load_subvector<G, CG>(a, n, h, j, xv);
-        } else {
+    // per-lane x offsets (bytes from the tile base) of the loads that fill the
+    // lane's B words; lanes whose K entries are not x read nothing
+    constexpr int NLD = 8 / CG;
+    uint32_t xoff[NCH][NLD];
 #pragma unroll
-            for (int i = 0; i < G; ++i) xv[i] = 0.f;
+    for (int ch = 0; ch < NCH; ++ch) {
+        const int kk0 = ch * 32 + kq * 8;
+        const int i0 = kk0 % G;
+#pragma unroll
+        for (int s = 0; s < NLD; ++s) {
+            const int64_t e = (int64_t)row * a.sx_tok + (int64_t)(i0 / CG + s) * a.sx_step +
+                              (int64_t)j * CG;
+            xoff[ch][s] = kk0 < P * G ? (uint32_t)(2 * e) : kOob;
         }
-        float xn2 = 0.f;
-#pragma unroll
-        for (int i = 0; i < G; ++i) xn2 += xv[i] * xv[i];
+    }
+    // the three ones of the bias column sit in the K chunk and lanes of kk = P*G
+    constexpr int ONES_CH = P * G / 32;
+    const bool ones_lane = kq == (P * G % 32) / 8;
+    const uint32_t ones0 = ones_lane ? 0x3f803f80u : 0u;    // bf16 1.0, 1.0
+    const uint32_t ones1 = ones_lane ? 0x00003f80u : 0u;    // bf16 1.0, 0
+    // lanes whose words are x entries i < G (counted once for |x|^2)
+    const bool norm_lane = kq * 8 < G;
 
-        bf16x8 bfrag[NCH];
+    const uint16_t *xh = a.x + h * a.sx_head;
+    auto rsrc = [&](int64_t n0) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xh + n0 * a.sx_tok), (short)0,
+                                                 0x7ffffff0, kBufferWord3);
+    };
+    uint16_t *queue = amb_queue[wave];
+    int n_amb = 0;
+
+    // tiles are processed in groups of kDepth; rows past the chunk's end (a
+    // ragged last group) load nothing and store nothing
+    constexpr int kDepth = 4;                          // tiles in flight per wave
+    const int ntok = (int)(tok_end - tok0);
+    XTile<NCH> ring[kDepth];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (kq != q) continue;
+    for (int u = 0; u < kDepth; ++u)
+        load_tile<CG, NCH>(ring[u], rsrc(tok0 + 16 * u), xoff, 16 * u + row < ntok);
+
+    for (int rb = 0; rb < ntok; rb += 16 * kDepth) {
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) {
+            const int r0 = rb + 16 * u;                // tile's first row in the chunk
+            const int64_t n0 = tok0 + r0;
+            const XTile<NCH> cur = ring[u];
+            {
+                const int rn = r0 + 16 * kDepth;
+                load_tile<CG, NCH>(ring[u], rsrc(tok0 + rn), xoff, rn + row < ntok);
+            }
+            const bool valid = r0 + row < ntok;
+
+            // B operand and |x|^2 (bf16 squares are exact; the sum only feeds a bound)
+            bf16x8 bfrag[NCH];
+            float xs = 0.f;
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) {
+                uint32_t w0 = cur.w[ch][0], w1 = cur.w[ch][1];
+                if (ch == 0) {
+                    float d = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kk = ch * 32 + q * 8 + e;
-                    float v = 0.f;
-                    if (kk < P * G)
-                        v = xv[kk % G];
-                    else if (kk < P * G + 3)
-                        v = 1.f;
-                    bfrag[ch][e] = __builtin_bit_cast(__bf16, bf16_rne(v));
+                    for (int q = 0; q < 4; ++q) {
+                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                        const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[0][q]);
+                        d = __builtin_amdgcn_fdot2_f32_bf16(v, v, d, false);
+                    }
+                    xs = norm_lane ? d : 0.f;
                 }
+                if (ch == ONES_CH) {
+                    w0 |= ones0;
+                    w1 |= ones1;
+                }
+                bfrag[ch] = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, cur.w[ch][2], cur.w[ch][3]));
             }
-        }
+            float xa, xb;
+            pair16(xs, xa, xb);
+            pair32(xa + xb, xa, xb);
+            const float xn2 = xa + xb;
 
-        float m1 = INFINITY, m2 = INFINITY;
-        int k1 = 0;
+            // two smallest marked screen values of the lane's 64 codes, taken a
+            // pair (a, b) at a time: with m1 <= m2, the second smallest of
+            // {m1, m2, a, b} is min(m2, med3(m1, a, b)) and the smallest is
+            // min3(m1, a, b)
+            // MFMAs run kPipe blocks ahead of the min tracking so that their
+            // latency overlaps it (the scheduling barriers keep that order)
+            constexpr int kPipe = 4;
+            auto screen = [&](int blk) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int blk = 0; blk < 16; ++blk) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int ch = 0; ch < NCH; ++ch)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[blk][ch], bfrag[ch], acc, 0, 0, 0);
+                return acc;
+            };
+            floatx4 accs[kPipe];
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[blk][ch], bfrag[ch], acc, 0, 0, 0);
-            // lane holds codes blk*16 + kq*4 + i of token n0 + row
+            for (int p = 0; p < kPipe; ++p) accs[p] = screen(p);
+            __builtin_amdgcn_sched_barrier(0);
+            float m1 = INFINITY, m2 = INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = acc[i];
-                if (v < m1) {
-                    m2 = m1;
-                    m1 = v;
-                    k1 = blk * 16 + kq * 4 + i;
-                } else {
-                    m2 = fminf(m2, v);
+            for (int blk = 0; blk < 16; ++blk) {
+                const floatx4 acc = accs[blk % kPipe];
+                // lane holds codes blk*16 + kq*4 + i of token n0 + row; the low
+                // 6 bits of each value become its slot blk*4 + i in the lane
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = __uint_as_float((__float_as_uint(acc[i]) & 0xffffffc0u) | (uint32_t)(blk * 4 + i));
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    m2 = fminf(m2, __builtin_amdgcn_fmed3f(m1, v[i], v[i + 1]));
+                    m1 = fminf(m1, fminf(v[i], v[i + 1]));
                 }
+                if (blk + kPipe < 16) accs[blk % kPipe] = screen(blk + kPipe);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
-        // combine the four lanes holding the same token
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float om1 = __shfl_xor(m1, off);
-            const float om2 = __shfl_xor(m2, off);
-            const int ok1 = __shfl_xor(k1, off);
-            const float nm2 = fminf(fminf(m2, om2), fmaxf(m1, om1));
-            if (om1 < m1 || (om1 == m1 && ok1 < k1)) {
-                m1 = om1;
-                k1 = ok1;
+            // combine the four lanes holding the same token; the lane whose own
+            // smallest value is the token's smallest holds the winner
+            const float own = m1;
+            {
+                float a1, b1, a2, b2;
+                pair16(m1, a1, b1);
+                pair16(m2, a2, b2);
+                m2 = fminf(fmaxf(a1, b1), fminf(a2, b2));
+                m1 = fminf(a1, b1);
+                pair32(m1, a1, b1);
+                pair32(m2, a2, b2);
+                m2 = fminf(fmaxf(a1, b1), fminf(a2, b2));
+                m1 = fminf(a1, b1);
             }
-            m2 = nm2;
-        }
-        const float rad = sqrtf(xn2) * (1.f + 1e-5f) + max_norm;
-        const float eps = kEpsScale * rad * rad;
-        const bool unique = (m2 - m1) > eps;
-        if (kq == 0 && valid && unique) out_rows[(size_t)n * a.S] = (uint8_t)k1;
+            const uint32_t slot = __float_as_uint(m1) & 63u;
+            const int k1 = (int)((slot >> 2) * 16 + kq * 4 + (slot & 3));
+            const bool holder = __float_as_uint(own) == __float_as_uint(m1);
+            // hardware square root (within 1 ulp): the slack covers it
+            const float rad = __builtin_amdgcn_sqrtf(xn2) * (1.f + 1e-5f) + max_norm;
+            const float eps = kEpsScale * rad * rad;
+            const bool unique = (m2 - m1) > eps;
+            // when the winner is unique no other lane holds an equal value (it
+            // would be the second smallest), so exactly one lane stores
+            if (holder && valid && unique) out_rows[(size_t)(n0 + row) * a.S] = (uint8_t)k1;
 
-        // exact re-score of the ambiguous sub-vectors of this tile
-        uint64_t amb = __ballot(kq == 0 && valid && !unique);
-        while (amb) {
-            const int src = __builtin_ctzll(amb);
-            amb &= amb - 1;
-            const int64_t nn = n0 + src;
-            float xe[G];
-            load_subvector<G, CG>(a, nn, h, j, xe);
-            float best = INFINITY;
-            int bk = 256;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k = lane + 64 * r;
-                const float dist = exact_distance<G, CG>(a, cb, h, j, k, xe);
-                if (dist < best) {
-                    best = dist;
-                    bk = k;
-                }
+            // queue the ambiguous sub-vectors of this tile (rows of the chunk)
+            const bool amb = kq == 0 && valid && !unique;
+            const uint64_t amb_mask = __ballot(amb);
+            if (amb) {
+                const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(amb_mask >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)amb_mask, 0));
+                queue[n_amb + pos] = (uint16_t)(r0 + row);
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ob = __shfl_xor(best, off);
-                const int ok = __shfl_xor(bk, off);
-                if (ob < best || (ob == best && ok < bk)) {
-                    best = ob;
-                    bk = ok;
-                }
-            }
-            if (lane == 0) out_rows[(size_t)nn * a.S] = (uint8_t)bk;
+            n_amb += __builtin_popcountll(amb_mask);
         }
+    }
+
+    // exact re-score of the queued sub-vectors: every lane scores 4 codes
+    // k = lane + 64 r, then the wave takes the lowest index of the smallest
+    // distance
+    float cf[4][G];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < G; ++i) cf[r][i] = to_f(mycb[(lane + 64 * r) * G + i]);
+    for (int q = 0; q < n_amb; ++q) {
+        const int rq = __builtin_amdgcn_readfirstlane(queue[q]);
+        const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
+        float xe[G];
+#pragma unroll
+        for (int t = 0; t < G / CG; ++t)
+#pragma unroll
+            for (int c = 0; c < CG; ++c) xe[t * CG + c] = bf16f(xr[t * a.sx_step + c]);
+        float best = INFINITY;
+        int bk = 256;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float dist = 0.f;
+#pragma unroll
+            for (int i = 0; i < G; ++i) {
+                // separate roundings: this file is built without contraction
+                const float e = xe[i] - cf[r][i];
+                const float sq = e * e;
+                dist = dist + sq;
+            }
+            if (dist < best) {
+                best = dist;
+                bk = lane + 64 * r;
+            }
+        }
+        // distances are >= 0, so their bit patterns order like them
+        const uint32_t dmin = wave_min_u32(__float_as_uint(best));
+        const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
+        if (lane == 0) out_rows[(size_t)(tok0 + rq) * a.S] = (uint8_t)kmin;
     }
 }
 
 template <int G, int CG>
 hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + 3) / 4, a.H);
+    const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW, a.H);
     if (a.cb_bf16) {
         hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t>), grid, dim3(kThreads), 0, st, a);
     } else {
@@ -300,10 +454,11 @@ hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
 
 }  // namespace
 
-bool encode_supported(int G, int cg, int cb_bf16) {
+bool encode_supported(int G, int cg, int S, int cb_bf16) {
     if (G != 8 && G != 16 && G != 32) return false;
     if (cg != 2 && cg != 4 && cg != 8) return false;
     if (cg > G) return false;
+    if (S % kJW != 0) return false;                    // whole workgroups of sub-vectors
     if (!cb_bf16 && G > 16) return false;
     return true;
 }

@@ -71,7 +71,7 @@ struct EncodeArgs {
 // Kernel-support predicates (host) and launchers (return the HIP error of the
 // launch).
 bool decode_supported(int d, int S, int cg, int cb_bf16);
-bool encode_supported(int G, int cg, int cb_bf16);
+bool encode_supported(int G, int cg, int S, int cb_bf16);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 

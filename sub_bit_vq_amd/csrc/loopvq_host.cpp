@@ -145,7 +145,12 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
     }
     // sub-vector runs of cg bf16 are read as one vector
     if (reinterpret_cast<uintptr_t>(x) % (2 * (uintptr_t)cg) != 0) return LVQ_ERR_INVALID_ARG;
-    if (!lvq::encode_supported(c->group, cg, c->codebook_dtype == LVQ_BF16))
+    // the codebooks are staged in 16-byte pieces
+    if (reinterpret_cast<uintptr_t>(codebook) % 16 != 0) return LVQ_ERR_INVALID_ARG;
+    // a 16-token tile of one head is addressed with 32-bit byte offsets
+    if (2 * (15 * st[0] + Tc * st[2] + d) >= 0x7ffffff0LL) return LVQ_ERR_UNSUPPORTED;
+    if (!lvq::encode_supported(c->group, cg, (int)(c->head_dim / cg),
+                               c->codebook_dtype == LVQ_BF16))
         return LVQ_ERR_UNSUPPORTED;
     if (n_tokens == 0) return LVQ_OK;
     lvq::EncodeArgs a{};

@@ -205,3 +205,44 @@ def oracle_decode(oracle_mod, c: Cache, t, sm_scale=1.0, heads=None):
                                   v_codebook=c.v_codebook, k_window=c.k_window,
                                   v_window=c.v_window, n_sink=c.n_sink, n_recent=c.n_recent,
                                   group=c.group, sm_scale=sm_scale, vq_len=c.vq_len, heads=heads)
+
+
+def rounding_order_case(H, d, Tc, G, n, cb_dtype, seed, n_base=4):
+    """Codebooks whose 256 codes of each (head, sub-vector) are permutations
+    of ``n_base`` base vectors, and inputs whose rows are constant (one level
+    per token).  The exact distances of sibling codes coincide, so the winner
+    is decided by the fp32 rounding of each term and by the summation order:
+    an implementation that fuses the square into the add, or sums in another
+    order, picks a different code on many sub-vectors.  Returns (x, cb)."""
+    g = torch.Generator().manual_seed(seed)
+    cg = G // Tc
+    S = d // cg
+    base = torch.randn((H, S, n_base, G), generator=g)
+    if cb_dtype == torch.bfloat16:
+        base = (0.25 * base).to(torch.bfloat16).float()
+    rows = base[:, :, torch.arange(256) % n_base]                       # [H][S][256][G]
+    perm = torch.argsort(torch.rand((H, S, 256, G), generator=g), dim=-1)
+    nat = torch.gather(rows, -1, perm)
+    cb = nat.reshape(H, S, 256, Tc, cg).permute(3, 0, 2, 1, 4).contiguous().to(cb_dtype)
+    if cb_dtype == torch.bfloat16:
+        levels = 1.0 + torch.arange(n, dtype=torch.float32) * 2.0 ** -7
+    else:
+        levels = torch.arange(n, dtype=torch.float32) * 2.0 ** -6
+    x = levels[:, None, None, None].expand(n, H, Tc, d).to(torch.bfloat16).contiguous()
+    return x, cb
+
+
+def fp32_sequential_argmin(xs: np.ndarray, cn: np.ndarray, fused: bool = False) -> np.ndarray:
+    """Nearest code by an independent numpy evaluation of the fp32 distance:
+    xs [..., G] float32 sub-vectors, cn [256][G] float32 codes (broadcast over
+    the leading axes of xs as [..., 256, G]).  Each step rounds to fp32;
+    ``fused=True`` instead rounds e*e + acc once (what a fused multiply-add
+    would give), to show that a case tells the two apart."""
+    acc = np.zeros(xs.shape[:-1] + (cn.shape[-2],), np.float32)
+    for i in range(xs.shape[-1]):
+        e = (xs[..., i][..., None] - cn[..., i]).astype(np.float32)
+        if fused:
+            acc = (acc.astype(np.float64) + e.astype(np.float64) ** 2).astype(np.float32)
+        else:
+            acc = (acc + (e * e).astype(np.float32)).astype(np.float32)
+    return acc.argmin(-1)          # numpy returns the first (lowest) index on ties

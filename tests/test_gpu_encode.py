@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from cases import kv_from_codewords
+from cases import kv_from_codewords, rounding_order_case
 from sub_bit_vq_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -144,6 +144,21 @@ def test_near_ties(lv):
     x = (mid + jitter).to(torch.bfloat16)
     _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
                  "near ties")
+
+
+@pytest.mark.parametrize("cb_dtype,G", [(torch.float32, 16), (torch.float32, 8),
+                                        (torch.bfloat16, 16), (torch.bfloat16, 32),
+                                        (torch.bfloat16, 8)])
+def test_rounding_order(lv, cb_dtype, G):
+    """Codes that are permutations of each other: the screen cannot separate
+    them, and the exact re-score must round every subtraction, square and add
+    separately in ascending entry order, as the oracle does (a fused
+    multiply-add picks another code on many of these sub-vectors)."""
+    _note(f"rounding order G={G} {cb_dtype}")
+    H, d, Tc = 2, 64, 4
+    x, cb = rounding_order_case(H, d, Tc, G, 300, cb_dtype, seed=80 + G)
+    _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
+                 "rounding order")
 
 
 def test_strided_input_from_window_buffer(lv):

@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import oracle
-from cases import kv_from_codewords, natural_codebook, natural_subvectors, bf16_representable_fp32
+from cases import (kv_from_codewords, natural_codebook, natural_subvectors, bf16_representable_fp32,
+                   rounding_order_case, fp32_sequential_argmin)
 from sub_bit_vq_amd import synth
 
 SHAPES = [  # (n_heads, head_dim, loop_steps, group)
@@ -114,6 +115,23 @@ def check_placement(seed=5):
     assert np.array_equal(cache, want)
 
 
+def check_rounding_order(seed=6):
+    """The distance is a sequence of separately rounded fp32 operations in
+    ascending entry order.  On codes that are permutations of each other the
+    exact distances coincide, so the winner is decided by those roundings; an
+    independent numpy evaluation step by step must agree with the oracle, and
+    a fused multiply-add evaluation must not (so the case has teeth)."""
+    for cb_dtype, (H, d, Tc, G) in ((torch.float32, (1, 64, 4, 16)), (torch.bfloat16, (1, 64, 4, 32)),
+                                    (torch.float32, (1, 32, 2, 8))):
+        x, cb = rounding_order_case(H, d, Tc, G, 48, cb_dtype, seed)
+        got = _enc(x, cb, H, d, Tc, G)[0].permute(1, 0, 2).numpy()        # [n][H][S]
+        xs = natural_subvectors(x.float(), G).numpy()
+        cn = natural_codebook(cb.float()).numpy()
+        want = fp32_sequential_argmin(xs, cn)
+        assert np.array_equal(got, want), (cb_dtype, G, int((got != want).sum()))
+        assert (fp32_sequential_argmin(xs, cn, fused=True) != want).any()
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("cb_dtype", [torch.bfloat16, torch.float32])
 def test_codeword_inputs(shape, cb_dtype):
@@ -123,6 +141,10 @@ def test_codeword_inputs(shape, cb_dtype):
 
 def test_exact_ties():
     check_exact_ties()
+
+
+def test_rounding_order():
+    check_rounding_order()
 
 
 @pytest.mark.parametrize("shape", SHAPES)

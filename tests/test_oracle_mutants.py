@@ -17,7 +17,7 @@ import test_oracle_encode as enc
 SRC = pathlib.Path(oracle.__file__).resolve().parent / "loopvq_oracle.c"
 
 ENC_PINS = [enc.check_codeword_inputs, enc.check_exact_ties, enc.check_fp64_bruteforce,
-            enc.check_row_permutation, enc.check_placement]
+            enc.check_row_permutation, enc.check_placement, enc.check_rounding_order]
 ATT_PINS = [att.check_attend_matches_sdpa, att.check_windows_only, att.check_end_to_end,
             att.check_zero_query_mean, att.check_empty_and_single, att.check_end_to_end_page_lag]
 
@@ -26,6 +26,10 @@ MUTANTS = {
     "tie_keeps_last": ("dist < best_d", "dist <= best_d"),
     "sum_instead_of_difference": ("xv[i] - codeword_entry", "xv[i] + codeword_entry"),
     "abs_instead_of_square": ("float sq = e * e;", "float sq = e < 0 ? -e : e;"),
+    "fused_square_add": ("float sq = e * e;\n                        dist = dist + sq;",
+                         "dist = fmaf(e, e, dist);"),
+    "distance_summed_descending": ("float e = xv[i] - codeword_entry(codebook, cb_bf16, H, S, cg, h, j, k, i);",
+                                   "float e = xv[G - 1 - i] - codeword_entry(codebook, cb_bf16, H, S, cg, h, j, k, G - 1 - i);"),
     "subvector_channels_transposed": ("xv[t * cg + c] = bf16_bits_to_float(",
                                       "xv[c * Tc + t] = bf16_bits_to_float("),
     "codebook_code_sub_swapped": ("((((size_t)t * H + h) * LVQO_CODES + k) * S + j)",
