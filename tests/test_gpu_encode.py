@@ -87,6 +87,19 @@ def test_shapes_multi_chunk_ragged_tail(lv, H, d, Tc, G, cb_dtype):
                  "shape")
 
 
+@pytest.mark.parametrize("n", [1, 8, 31, 32, 33, 64])
+@pytest.mark.parametrize("H,d,Tc,G,cb_dtype", SHAPES)
+def test_short_runs(lv, n, H, d, Tc, G, cb_dtype):
+    """Runs of up to 32 tokens (a page of generated tokens) take the direct
+    exact path, longer ones the MFMA screen; both sides of the switch."""
+    _note(f"short run n={n} H={H} d={d} Tc={Tc} G={G} {cb_dtype}")
+    seed = 7000 + n + H * 100 + d + Tc * 10 + G
+    x = synth.loop_correlated_kv(n, H, Tc, d, seed)
+    cb = synth.codebooks(H, d, Tc, G, seed + 1, dtype=cb_dtype)
+    _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G, T=n + 5, first=5),
+                 _oracle_encode(x, cb, H, d, Tc, G, T=n + 5, first=5), "short run")
+
+
 def test_codeword_inputs(lv):
     _note("codeword inputs")
     H, d, Tc, G = 2, 128, 4, 16
@@ -108,18 +121,19 @@ def _tie_codebook(H, d, Tc, G, seed):
     return nat.permute(3, 0, 2, 1, 4).contiguous()
 
 
+@pytest.mark.parametrize("n", [700, 24])
 @pytest.mark.parametrize("cb_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("G", [16, 32])
-def test_exact_ties(lv, cb_dtype, G):
+def test_exact_ties(lv, cb_dtype, G, n):
     """Integer codebooks and integer inputs: exact fp32 ties everywhere; the
     lowest index must win on every sub-vector."""
     if cb_dtype == torch.float32 and G == 32:
         pytest.skip("fp32 codebooks are supported for G <= 16")
-    _note(f"exact ties G={G} {cb_dtype}")
+    _note(f"exact ties G={G} {cb_dtype} n={n}")
     H, d, Tc = 2, 64, 4
     cb = _tie_codebook(H, d, Tc, G, seed=40 + G).to(cb_dtype)
     g = torch.Generator().manual_seed(41)
-    x = torch.randint(-2, 3, (700, H, Tc, d), generator=g).to(torch.bfloat16)
+    x = torch.randint(-2, 3, (n, H, Tc, d), generator=g).to(torch.bfloat16)
     _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
                  "ties")
 
@@ -149,14 +163,15 @@ def test_near_ties(lv):
 @pytest.mark.parametrize("cb_dtype,G", [(torch.float32, 16), (torch.float32, 8),
                                         (torch.bfloat16, 16), (torch.bfloat16, 32),
                                         (torch.bfloat16, 8)])
-def test_rounding_order(lv, cb_dtype, G):
+@pytest.mark.parametrize("n", [300, 30])
+def test_rounding_order(lv, cb_dtype, G, n):
     """Codes that are permutations of each other: the screen cannot separate
     them, and the exact re-score must round every subtraction, square and add
     separately in ascending entry order, as the oracle does (a fused
     multiply-add picks another code on many of these sub-vectors)."""
-    _note(f"rounding order G={G} {cb_dtype}")
+    _note(f"rounding order G={G} {cb_dtype} n={n}")
     H, d, Tc = 2, 64, 4
-    x, cb = rounding_order_case(H, d, Tc, G, 300, cb_dtype, seed=80 + G)
+    x, cb = rounding_order_case(H, d, Tc, G, n, cb_dtype, seed=80 + G)
     _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
                  "rounding order")
 
