@@ -34,10 +34,12 @@ sys.path.insert(0, str(ROOT))
 HBM_PEAK_GBS = 8000.0
 LLC_BYTES = 256 << 20
 WORKLOADS = {
-    # name: (B, H, d, Tc, G, context; "ragged" = 2048 + U{4096, 8192, 16384})
+    # name: (B, H, d, Tc, G, context; "ragged" = 2048 + U{4096, 8192, 16384}[, KV heads])
     "ouro1p4b_layer_32k_0p5bit": (1, 16, 128, 4, 16, 32768),
     "ouro1p4b_layer_32k_0p25bit": (1, 16, 128, 4, 32, 32768),
     "batch64_ragged_0p5bit": (64, 16, 128, 4, 16, "ragged"),
+    # grouped-query attention: 32 query heads over 8 KV heads
+    "gqa32q8kv_32k_0p5bit": (1, 32, 128, 4, 16, 32768, 8),
 }
 PAGE = 8          # tokens per eviction page
 N_SINK, N_RECENT = 64, 256
@@ -51,7 +53,8 @@ def log(msg):
 def cache_bytes(H, d, Tc, G, lengths):
     """Algorithmic bytes of one decode call: K and V index rows of every VQ
     token plus the bf16 K and V of the sink and recent tokens of the step,
-    summed over the sequences of the batch."""
+    summed over the sequences of the batch (H = KV heads: query heads that
+    share a KV head share its bytes)."""
     S = d // (G // Tc)
     total = 0
     for L in lengths:
@@ -88,24 +91,25 @@ class Setup:
     rotated over enough distinct copies to defeat the last-level cache."""
 
     def __init__(self, lv, synth, torch, workload, rotate, seed=1001):
-        B, H, d, Tc, G, L = WORKLOADS[workload]
+        B, H, d, Tc, G, L = WORKLOADS[workload][:6]
+        Hk = WORKLOADS[workload][6] if len(WORKLOADS[workload]) > 6 else H
         lengths = synth.ragged_lengths(B, seed=1003) if L == "ragged" else [L] * B
-        self.B, self.H, self.d, self.Tc, self.G = B, H, d, Tc, G
+        self.B, self.H, self.Hk, self.d, self.Tc, self.G = B, H, Hk, d, Tc, G
         self.lengths = lengths
         self.L = max(lengths)
         dev = torch.device("cuda")
         T = self.L + PAGE
         self.cfg = lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
-                             max_tokens=T)
-        self.kcb = synth.codebooks(H, d, Tc, G, seed * 10 + 1, device=dev)
-        self.vcb = synth.codebooks(H, d, Tc, G, seed * 10 + 2, device=dev)
+                             max_tokens=T, n_kv_heads=Hk if Hk != H else 0)
+        self.kcb = synth.codebooks(Hk, d, Tc, G, seed * 10 + 1, device=dev)
+        self.vcb = synth.codebooks(Hk, d, Tc, G, seed * 10 + 2, device=dev)
         # one query per (token of the page, loop step)
         self.q = torch.stack([synth.queries(B, H, d, Tc, seed * 10 + 3 + i, device=dev)
                               for i in range(PAGE)])                 # [PAGE][Tc][B][H][d]
         base = lv.allocate(self.cfg, dev)
         for b, Lb in enumerate(lengths):
-            k = synth.loop_correlated_kv(Lb + PAGE, H, Tc, d, seed * 10 + 5 + 2 * b, device=dev)
-            v = synth.loop_correlated_kv(Lb + PAGE, H, Tc, d, seed * 10 + 6 + 2 * b, device=dev)
+            k = synth.loop_correlated_kv(Lb + PAGE, Hk, Tc, d, seed * 10 + 5 + 2 * b, device=dev)
+            v = synth.loop_correlated_kv(Lb + PAGE, Hk, Tc, d, seed * 10 + 6 + 2 * b, device=dev)
             lo, hi = N_SINK, Lb - N_RECENT
             if hi > lo:
                 lv.lvq_encode(self.cfg, k[lo:hi], self.kcb, base["k_index"], b, lo)
@@ -168,9 +172,9 @@ class PrefillEncode:
     def __init__(self, lv, synth, torch, setup, seed=1004):
         dev = torch.device("cuda")
         self.lv = lv
-        self.cfg = lv.Config(batch=1, n_heads=setup.H, head_dim=setup.d, loop_steps=setup.Tc,
+        self.cfg = lv.Config(batch=1, n_heads=setup.Hk, head_dim=setup.d, loop_steps=setup.Tc,
                              group=setup.G, max_tokens=self.N)
-        self.x = synth.loop_correlated_kv(self.N, setup.H, setup.Tc, setup.d, seed, device=dev)
+        self.x = synth.loop_correlated_kv(self.N, setup.Hk, setup.Tc, setup.d, seed, device=dev)
         self.cb = setup.kcb
         self.idx = lv.allocate(self.cfg, dev)["k_index"]
 
@@ -233,7 +237,7 @@ def cpu_baseline(setup, torch, budget_s=15.0):
         calls += 1
     t_dec = (time.perf_counter() - t0) / calls
     t1 = time.perf_counter()
-    oracle.encode(setup.page_k.cpu(), kcb, n_heads=setup.H, head_dim=setup.d,
+    oracle.encode(setup.page_k.cpu(), kcb, n_heads=setup.Hk, head_dim=setup.d,
                   loop_steps=setup.Tc, group=setup.G, threads=threads)
     t_enc = time.perf_counter() - t1
     t_step = PAGE * setup.Tc * t_dec + 2 * t_enc
@@ -242,7 +246,7 @@ def cpu_baseline(setup, torch, budget_s=15.0):
         "unit": "ctx-token*loop-steps/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{calls} whole decode calls (16 heads, 32768-token context, loop step 0, "
+        "sample": (f"{calls} whole decode calls ({setup.H} heads, {setup.L}-token context, loop step 0, "
                    f"{t_dec * 1e3:.1f} ms each) and one 8-token page encode ({t_enc * 1e3:.1f} ms, "
                    f"counted for K and V), combined as one step of 32 decodes + 2 encodes; "
                    f"OpenMP threads {threads} of {os.cpu_count()} logical CPUs"),
@@ -342,7 +346,7 @@ def main():
     log(f"{steps} steps in {ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step)")
 
     mean_ms = decode_kernel_time_ms(setup, torch)
-    bpl = cache_bytes(setup.H, setup.d, setup.Tc, setup.G, setup.lengths)
+    bpl = cache_bytes(setup.Hk, setup.d, setup.Tc, setup.G, setup.lengths)
     achieved = bpl / (mean_ms / 1e3) / 1e9
     log(f"decode launch: mean {mean_ms * 1e3:.2f} us, {achieved:.0f} GB/s on {bpl} cache bytes")
 
@@ -362,7 +366,8 @@ def main():
         "data": "synthetic (seeded loop-correlated K/V, N(0,1) codebooks)",
         "config": {
             "workload": args.workload,
-            "batch": setup.B, "heads": setup.H, "head_dim": setup.d, "loop_steps": setup.Tc,
+            "batch": setup.B, "heads": setup.H, "kv_heads": setup.Hk, "head_dim": setup.d,
+            "loop_steps": setup.Tc,
             "group": setup.G, "context": setup.L if setup.B == 1 else sum(setup.lengths),
             "n_sink": N_SINK, "n_recent": N_RECENT,
             "step": ("8 tokens x 4 loop-step decodes" if args.decode_only else

@@ -17,21 +17,22 @@
  *  - same page, "Results -- Long-context retrieval": n_sink = 64 and
  *    n_recent = 256.
  *
- * Notation: B sequences, H heads (query heads = KV heads), d = head_dim,
- * Tc = loop_steps, G = group (elements per sub-vector), cg = G / Tc channels
- * per loop step, S = d / cg sub-vectors per token per head, 256 codes.
- * bits per cached element = 8 / G.
+ * Notation: B sequences, H query heads, Hk KV heads (Hk = H for multi-head
+ * attention; Hk dividing H for grouped-query attention, where query head h
+ * reads KV head h / (H / Hk)), d = head_dim, Tc = loop_steps, G = group
+ * (elements per sub-vector), cg = G / Tc channels per loop step, S = d / cg
+ * sub-vectors per token per head, 256 codes.  bits per cached element = 8 / G.
  *
  * Storage layouts (all row-major, innermost last):
- *   x (encoder input) bf16  [n_tokens][H][Tc][d]  (or strided, see lvq_encode)
- *   codebook          f32 or bf16 [Tc][H][256][S][cg]: entry i = t*cg + c of
+ *   x (encoder input) bf16  [n_tokens][Hk][Tc][d]  (or strided, see lvq_encode)
+ *   codebook          f32 or bf16 [Tc][Hk][256][S][cg]: entry i = t*cg + c of
  *                     codeword k of (head h, sub-vector j) at [t][h][k][j][c]:
  *                     slice t of a head is contiguous, and its row k holds
  *                     code k of every sub-vector (the table row a decode
  *                     gather reads)
- *   index cache       uint8 [B][H][max_tokens][S]; row p holds token p
+ *   index cache       uint8 [B][Hk][max_tokens][S]; row p holds token p
  *                     (absolute position); rows of bf16 tokens are unused
- *   window buffers    bf16 [B][Tc][H][n_sink + n_recent][d]: sink token p
+ *   window buffers    bf16 [B][Tc][Hk][n_sink + n_recent][d]: sink token p
  *                     (p < n_sink) in slot p; recent token p (p >= n_sink) in
  *                     slot n_sink + ((p - n_sink) mod n_recent)  (a ring)
  *   query             bf16 [B][H][d] (the query of the loop step decoded)
@@ -82,6 +83,11 @@ typedef struct {
     int32_t decode_splits;  /* workgroups per (b, h) for lvq_decode_attn;
                                0 = chosen by the library; 1..LVQ_MAX_SPLITS.
                                Changes only the rounding of the result.        */
+    int32_t n_kv_heads;     /* Hk: heads of the index caches, codebooks and
+                               windows; 0 = n_heads (multi-head attention);
+                               otherwise must divide n_heads (grouped-query
+                               attention, consecutive query heads sharing a
+                               KV head)                                        */
 } lvq_config;
 
 #define LVQ_MAX_SPLITS 64
@@ -132,17 +138,19 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  * square and add, ascending i); the lowest k wins ties.  The result is
  * bit-identical to that definition: the kernel screens all 256 codes with a
  * bf16 MFMA contraction and re-scores exactly every sub-vector whose two best
- * screen values lie within the screen's error bound.
+ * screen values lie within the screen's error bound (runs of up to 32 tokens
+ * evaluate every distance directly).
  *
  * x          device bf16; element (n, h, t, ch) at
  *            x[n*x_strides[0] + h*x_strides[1] + t*x_strides[2] + ch];
- *            x_strides == NULL means the dense [n_tokens][H][Tc][d] layout.
+ *            x_strides == NULL means the dense [n_tokens][Hk][Tc][d] layout
+ *            (the KV heads).
  *            Strides are in elements; channels must be contiguous and every
  *            stride a multiple of cg.
  * codebook   device, cfg->codebook_dtype, layout above, 16-byte aligned (one
  *            call encodes one tensor: call once with the K codebook and once
  *            with the V one)
- * index_cache device uint8 [B][H][max_tokens][S]; rows
+ * index_cache device uint8 [B][Hk][max_tokens][S]; rows
  *            [first_token, first_token + n_tokens) of sequence seq are written
  * n_tokens   may be 0 (nothing launched)
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned x or codebook, seq
@@ -163,8 +171,10 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  * tokens use the bf16 window buffers of step t.  fp32 accumulation; VQ value
  * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
  * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).
- * One kernel launch on `stream`; the last workgroup of every (b, h) merges
- * the split partials.  Results depend on the split count only through
+ * With grouped-query attention (n_kv_heads < n_heads) query head h reads the
+ * caches, codebooks and windows of KV head h / (n_heads / n_kv_heads) with
+ * its own query.  One kernel launch on `stream`; one workgroup of every
+ * (b, h) merges the split partials.  Results depend on the split count only through
  * rounding.
  *
  * q          device bf16 [B][H][d]

@@ -52,7 +52,7 @@ def _bind(path):
     lib.lvqo_attend.restype = None
     lib.lvqo_attend.argtypes = [i64, i32, vp, vp, vp, dbl, vp, vp]
     lib.lvqo_decode_attn.restype = i32
-    lib.lvqo_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
+    lib.lvqo_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp,
                                      i32, i32, i32]
     lib.lvqo_max_threads.restype = i32
@@ -159,13 +159,14 @@ def decode_attn(*, loop_step, q, ctx_len, k_index, v_index, k_codebook, v_codebo
                 k_window, v_window, n_sink, n_recent, group, sm_scale=1.0, vq_len=None,
                 want_p=False, heads=None, threads=None):
     """fp64 decode attention (D1-D5).  Shapes: q bf16 [B][H][d]; ctx_len int32 [B];
-    index uint8 [B][H][t_max][S]; codebooks [Tc][H][256][S][cg]; windows bf16
-    [B][Tc][H][n_sink+n_recent][d].  Returns out fp64 [B][H][d] (and p fp64
-    [B][H][t_max] when ``want_p``)."""
+    index uint8 [B][Hk][t_max][S]; codebooks [Tc][Hk][256][S][cg]; windows bf16
+    [B][Tc][Hk][n_sink+n_recent][d], where Hk (taken from the index cache)
+    divides H and query head h reads KV head h // (H // Hk).  Returns out fp64
+    [B][H][d] (and p fp64 [B][H][t_max] when ``want_p``)."""
     qa = _np(q, np.uint16)
     B, H, d = qa.shape
     ki, vi = _np(k_index, np.uint8), _np(v_index, np.uint8)
-    t_max = ki.shape[2]
+    Hk, t_max = ki.shape[1], ki.shape[2]
     kcb, kb = _codebook(k_codebook)
     vcb, vb = _codebook(v_codebook)
     if kb != vb:
@@ -177,7 +178,7 @@ def decode_attn(*, loop_step, q, ctx_len, k_index, v_index, k_codebook, v_codebo
     out = np.zeros((B, H, d), np.float64)
     p = np.zeros((B, H, t_max), np.float64) if want_p else None
     h0, h1 = (0, H) if heads is None else heads
-    rc = _load().lvqo_decode_attn(B, H, d, Tc, group, n_sink, n_recent, t_max, kb, loop_step,
+    rc = _load().lvqo_decode_attn(B, H, Hk, d, Tc, group, n_sink, n_recent, t_max, kb, loop_step,
                                   _ptr(qa), _ptr(cl), _ptr(vl), _ptr(ki), _ptr(vi), _ptr(kcb),
                                   _ptr(vcb), _ptr(kw), _ptr(vw), float(sm_scale), _ptr(out),
                                   _ptr(p), h0, h1, threads or max_threads())

@@ -177,11 +177,15 @@ void lvqo_attend(int64_t L, int d, const double *q, const double *K, const doubl
  *       idxK[b][h][n][j]) entry t*cg + c; likewise Vhat.  Sink and recent
  *       tokens come from the bf16 window buffers of loop step t.
  *   D3-D5  dense fp64 attention over all L tokens (lvqo_attend).
+ * Grouped-query attention: n_heads query heads, n_kv_heads heads in the index
+ * caches, codebooks and windows (n_kv_heads divides n_heads); query head h
+ * attends over the tokens of KV head h / (n_heads / n_kv_heads).  Equal
+ * counts are multi-head attention.
  * out: fp64 [B][H][d]; p_out (optional): fp64 [B][H][t_max], probability of
- * every position < L (entries >= L untouched).  Heads [h0, h1) only.
+ * every position < L (entries >= L untouched).  Query heads [h0, h1) only.
  * Returns -1 on a shape or precondition violation.
  * ------------------------------------------------------------------------- */
-int lvqo_decode_attn(int batch, int n_heads, int head_dim, int loop_steps, int group,
+int lvqo_decode_attn(int batch, int n_heads, int n_kv_heads, int head_dim, int loop_steps, int group,
                      int n_sink, int n_recent, int64_t t_max, int cb_bf16, int loop_step,
                      const uint16_t *q, const int32_t *ctx_len, const int32_t *vq_len,
                      const uint8_t *k_index, const uint8_t *v_index,
@@ -191,10 +195,11 @@ int lvqo_decode_attn(int batch, int n_heads, int head_dim, int loop_steps, int g
                      int h0, int h1, int n_threads)
 {
     if (check_shape(n_heads, head_dim, loop_steps, group)) return -1;
+    if (n_kv_heads < 1 || n_heads % n_kv_heads != 0) return -1;
     if (loop_step < 0 || loop_step >= loop_steps) return -1;
     if (n_sink < 0 || n_recent < 1 || batch < 0) return -1;
     if (h0 < 0 || h1 > n_heads || h0 > h1) return -1;
-    const int H = n_heads, d = head_dim, Tc = loop_steps, t = loop_step;
+    const int H = n_heads, Hk = n_kv_heads, d = head_dim, Tc = loop_steps, t = loop_step;
     const int cg = group / Tc, S = d / cg, W = n_sink + n_recent;
 
     for (int b = 0; b < batch; ++b) {
@@ -211,6 +216,7 @@ int lvqo_decode_attn(int batch, int n_heads, int head_dim, int loop_steps, int g
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads)
     for (int u = 0; u < units; ++u) {
         const int b = u / (h1 - h0), h = h0 + u % (h1 - h0);
+        const int hk = h / (H / Hk);          /* the KV head this query head reads */
         const int64_t L = ctx_len[b];
         const int64_t n_s = L < n_sink ? L : n_sink;
         const int64_t n_v = vq_len ? vq_len[b]
@@ -230,17 +236,17 @@ int lvqo_decode_attn(int batch, int n_heads, int head_dim, int loop_steps, int g
         for (int64_t pos = 0; pos < L; ++pos) {
             double *kr = K + pos * d, *vr = V + pos * d;
             if (pos >= n_s && pos < n_s + n_v) {
-                const size_t row = (((size_t)b * H + h) * t_max + pos) * S;
+                const size_t row = (((size_t)b * Hk + hk) * t_max + pos) * S;
                 for (int j = 0; j < S; ++j) {
                     int ck = k_index[row + j], cv = v_index[row + j];
                     for (int c = 0; c < cg; ++c) {
-                        kr[j * cg + c] = codeword_entry(k_cb, cb_bf16, H, S, cg, h, j, ck, t * cg + c);
-                        vr[j * cg + c] = codeword_entry(v_cb, cb_bf16, H, S, cg, h, j, cv, t * cg + c);
+                        kr[j * cg + c] = codeword_entry(k_cb, cb_bf16, Hk, S, cg, hk, j, ck, t * cg + c);
+                        vr[j * cg + c] = codeword_entry(v_cb, cb_bf16, Hk, S, cg, hk, j, cv, t * cg + c);
                     }
                 }
             } else {
                 int64_t slot = pos < n_sink ? pos : n_sink + (pos - n_sink) % n_recent;
-                const size_t base = ((((size_t)b * Tc + t) * H + h) * W + slot) * d;
+                const size_t base = ((((size_t)b * Tc + t) * Hk + hk) * W + slot) * d;
                 for (int ch = 0; ch < d; ++ch) {
                     kr[ch] = bf16_bits_to_float(k_win[base + ch]);
                     vr[ch] = bf16_bits_to_float(v_win[base + ch]);

@@ -637,14 +637,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int64_t t_max = a.t_max;
     const int Lraw = a.ctx_len[b];
     const int vqraw = a.vq_len ? a.vq_len[b] : -1;
-    const size_t bh = (size_t)b * a.H + h;
-    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)h * 256 * S * CG;
-    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)h * 256 * S * CG;
-    const size_t wbase = (size_t)b * a.win_bstride + ((size_t)h * W) * D;
+    const size_t bh = (size_t)b * a.H + h;             // query head: q, partials, out
+    const int hk = h / a.q_per_kv;                      // KV head: caches, codebooks, windows
+    const size_t bhk = (size_t)b * a.Hk + hk;
+    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)hk * 256 * S * CG;
+    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)hk * 256 * S * CG;
+    const size_t wbase = (size_t)b * a.win_bstride + ((size_t)hk * W) * D;
     const uint16_t *kw = a.kwin_t + wbase;
     const uint16_t *vw = a.vwin_t + wbase;
-    const uint8_t *kidx = a.k_index + bh * (size_t)t_max * S;
-    const uint8_t *vidx = a.v_index + bh * (size_t)t_max * S;
+    const uint8_t *kidx = a.k_index + bhk * (size_t)t_max * S;
+    const uint8_t *vidx = a.v_index + bhk * (size_t)t_max * S;
     const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
     uint64_t *part = a.partials + (bh * kSlots + split) * (D + 2);
     const uint64_t *parts = a.partials + bh * kSlots * (D + 2);

@@ -25,6 +25,8 @@ inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
 
 struct DecodeArgs {
     int B, H, d, Tc, cg, S, n_sink, n_recent;
+    int Hk;           // KV heads (caches, codebooks, windows)
+    int q_per_kv;     // H / Hk: query head h reads KV head h / q_per_kv
     int64_t t_max;
     int loop_step;
     int n_split;      // workgroups per (b, h)
@@ -36,17 +38,17 @@ struct DecodeArgs {
     const uint16_t *q;          // [B][H][d]
     const int32_t *ctx_len;     // [B]
     const int32_t *vq_len;      // [B] or null
-    const uint8_t *k_index;     // [B][H][t_max][S]
+    const uint8_t *k_index;     // [B][Hk][t_max][S]
     const uint8_t *v_index;
-    const void *k_cb;           // [Tc][H][256][S][cg]
+    const void *k_cb;           // [Tc][Hk][256][S][cg]
     const void *v_cb;
-    const uint16_t *k_win;      // [B][Tc][H][W][d]
+    const uint16_t *k_win;      // [B][Tc][Hk][W][d]
     const uint16_t *v_win;
     float sm_scale;
     // derived by the host for the loop step of the call
-    const void *kcb_t;          // codebook slices of step t: [H][256][S][cg]
+    const void *kcb_t;          // codebook slices of step t: [Hk][256][S][cg]
     const void *vcb_t;
-    const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [H][W][d]
+    const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [Hk][W][d]
     const uint16_t *vwin_t;
     int64_t win_bstride;        // elements between sequences of a window buffer
     float scale_log2;           // sm_scale * log2(e)

@@ -11,6 +11,9 @@
 
 namespace {
 
+// KV heads: the heads of the index caches, codebooks and windows
+int64_t kv_heads(const lvq_config *c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
+
 bool config_ok(const lvq_config *c) {
     if (!c) return false;
     if (c->batch < 1 || c->n_heads < 1 || c->head_dim < 1) return false;
@@ -22,6 +25,8 @@ bool config_ok(const lvq_config *c) {
     if (c->codebook_dtype != LVQ_F32 && c->codebook_dtype != LVQ_BF16) return false;
     if (c->decode_splits < 0 || c->decode_splits > LVQ_MAX_SPLITS) return false;
     if (c->batch > 65535 || c->n_heads > 65535) return false;
+    if (c->n_kv_heads < 0 || c->n_kv_heads > c->n_heads) return false;
+    if (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0) return false;
     return true;
 }
 
@@ -94,7 +99,7 @@ const char *lvq_status_string(lvq_status s) {
 lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
     if (!o || !config_ok(c)) return LVQ_ERR_INVALID_ARG;
     std::memset(o, 0, sizeof *o);
-    const int64_t B = c->batch, H = c->n_heads, d = c->head_dim, Tc = c->loop_steps;
+    const int64_t B = c->batch, H = c->n_heads, Hk = kv_heads(c), d = c->head_dim, Tc = c->loop_steps;
     const int64_t cg = c->group / c->loop_steps, S = d / cg, W = (int64_t)c->n_sink + c->n_recent;
     const uint64_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
     o->n_sub = (int32_t)S;
@@ -106,13 +111,13 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
     // per token and loop step: bf16 K and V read 2 * d * 2 bytes; the index
     // rows (K and V, shared by all loop steps) are re-read whole: 2 * S bytes
     o->read_reduction_per_step = (4.0 * (double)d) / (2.0 * (double)S);
-    const int64_t idx_shape[4] = {B, H, c->max_tokens, S};
+    const int64_t idx_shape[4] = {B, Hk, c->max_tokens, S};
     set_tensor(&o->k_index, 4, idx_shape, 1);
     set_tensor(&o->v_index, 4, idx_shape, 1);
-    const int64_t cb_shape[5] = {Tc, H, LVQ_CODES, S, cg};
+    const int64_t cb_shape[5] = {Tc, Hk, LVQ_CODES, S, cg};
     set_tensor(&o->k_codebook, 5, cb_shape, cbe);
     set_tensor(&o->v_codebook, 5, cb_shape, cbe);
-    const int64_t win_shape[5] = {B, Tc, H, W, d};
+    const int64_t win_shape[5] = {B, Tc, Hk, W, d};
     set_tensor(&o->k_window, 5, win_shape, 2);
     set_tensor(&o->v_window, 5, win_shape, 2);
     const int64_t q_shape[3] = {B, H, d};
@@ -135,7 +140,8 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
     if (n_tokens < 0 || seq < 0 || seq >= c->batch) return LVQ_ERR_INVALID_ARG;
     if (first_token < 0 || first_token + n_tokens > c->max_tokens) return LVQ_ERR_INVALID_ARG;
     const int cg = c->group / c->loop_steps;
-    const int64_t H = c->n_heads, d = c->head_dim, Tc = c->loop_steps;
+    // the encoder writes the index caches: one pass per KV head
+    const int64_t H = kv_heads(c), d = c->head_dim, Tc = c->loop_steps;
     int64_t st[3] = {H * Tc * d, Tc * d, d};
     if (x_strides) {
         for (int i = 0; i < 3; ++i) {
@@ -154,7 +160,7 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
         return LVQ_ERR_UNSUPPORTED;
     if (n_tokens == 0) return LVQ_OK;
     lvq::EncodeArgs a{};
-    a.H = c->n_heads;
+    a.H = (int)H;
     a.d = c->head_dim;
     a.Tc = c->loop_steps;
     a.G = c->group;
@@ -224,6 +230,8 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     lvq::DecodeArgs a{};
     a.B = c->batch;
     a.H = c->n_heads;
+    a.Hk = (int)kv_heads(c);
+    a.q_per_kv = c->n_heads / a.Hk;
     a.d = c->head_dim;
     a.Tc = c->loop_steps;
     a.cg = cg;
@@ -248,14 +256,14 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.sm_scale = sm_scale;
     {
         const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
-        const size_t slice = (size_t)loop_step * c->n_heads * S * LVQ_CODES * cg * cbe;
+        const size_t slice = (size_t)loop_step * a.Hk * S * LVQ_CODES * cg * cbe;
         a.kcb_t = static_cast<const char *>(k_codebook) + slice;
         a.vcb_t = static_cast<const char *>(v_codebook) + slice;
         const size_t W = (size_t)c->n_sink + c->n_recent;
-        const size_t step = (size_t)loop_step * c->n_heads * W * c->head_dim;
+        const size_t step = (size_t)loop_step * a.Hk * W * c->head_dim;
         a.kwin_t = static_cast<const uint16_t *>(k_window) + step;
         a.vwin_t = static_cast<const uint16_t *>(v_window) + step;
-        a.win_bstride = (int64_t)c->loop_steps * c->n_heads * W * c->head_dim;
+        a.win_bstride = (int64_t)c->loop_steps * a.Hk * W * c->head_dim;
         a.scale_log2 = sm_scale * 1.4426950408889634f;
     }
     a.partials = static_cast<uint64_t *>(workspace);

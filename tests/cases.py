@@ -61,7 +61,10 @@ def sdpa_fp64(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: float) -
 
 @dataclass
 class Cache:
-    """A complete decode-attention test case (host tensors)."""
+    """A complete decode-attention test case (host tensors).  ``n_heads`` is the
+    number of KV heads (index caches, codebooks, windows, tokens); the query has
+    ``q_heads`` heads (0: as many), query head h reading KV head
+    h // (q_heads // n_heads)."""
     batch: int
     n_heads: int
     head_dim: int
@@ -70,7 +73,7 @@ class Cache:
     t_max: int
     lengths: list
     vq_len: list | None
-    q: torch.Tensor            # bf16 [Tc][B][H][d]
+    q: torch.Tensor            # bf16 [Tc][B][Hq][d]
     k_tokens: list             # per sequence bf16 [L][H][Tc][d] (original tokens)
     v_tokens: list
     k_index: torch.Tensor      # uint8 [B][H][t_max][S]
@@ -82,6 +85,11 @@ class Cache:
     n_sink: int = N_SINK
     n_recent: int = N_RECENT
     extra: dict = field(default_factory=dict)
+    q_heads: int = 0
+
+    @property
+    def n_q_heads(self):
+        return self.q_heads or self.n_heads
 
     @property
     def n_sub(self):
@@ -94,7 +102,7 @@ class Cache:
 
 def make_cache(*, batch=1, n_heads=1, head_dim=64, loop_steps=4, group=16, lengths=(512,),
                cb_dtype=torch.bfloat16, seed=0, codeword_tokens=False, vq_len=None,
-               encode=None, t_max=None, n_sink=N_SINK, n_recent=N_RECENT) -> Cache:
+               encode=None, t_max=None, n_sink=N_SINK, n_recent=N_RECENT, q_heads=None) -> Cache:
     """Seeded cache.  VQ tokens either come from the loop-correlated generator
     and are encoded with ``encode(x, codebook, index, seq, first_token)``, or
     (``codeword_tokens=True``) are drawn as exact codewords of random indices,
@@ -108,7 +116,7 @@ def make_cache(*, batch=1, n_heads=1, head_dim=64, loop_steps=4, group=16, lengt
     vcb = synth.codebooks(n_heads, head_dim, loop_steps, group, seed * 7919 + 2, dtype=cb_dtype)
     if cb_dtype == torch.float32 and codeword_tokens:
         kcb, vcb = bf16_representable_fp32(kcb), bf16_representable_fp32(vcb)
-    q = synth.queries(batch, n_heads, head_dim, loop_steps, seed * 7919 + 3)
+    q = synth.queries(batch, q_heads or n_heads, head_dim, loop_steps, seed * 7919 + 3)
     k_index = torch.zeros((batch, n_heads, t_max, S), dtype=torch.uint8)
     v_index = torch.zeros_like(k_index)
     W = n_sink + n_recent
@@ -138,7 +146,7 @@ def make_cache(*, batch=1, n_heads=1, head_dim=64, loop_steps=4, group=16, lengt
         v_tokens.append(vt)
     return Cache(batch, n_heads, head_dim, loop_steps, group, t_max, lengths, vq_len, q,
                  k_tokens, v_tokens, k_index, v_index, kcb, vcb, k_window, v_window,
-                 n_sink, n_recent)
+                 n_sink, n_recent, q_heads=q_heads or 0)
 
 
 def oracle_encoder(oracle_mod, n_heads, head_dim, loop_steps, group):
@@ -165,7 +173,8 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
 # ---------------------------------------------------------------------------
 
 def lvq_config(lv, c: Cache, **kw):
-    return lv.Config(batch=c.batch, n_heads=c.n_heads, head_dim=c.head_dim,
+    kw.setdefault("n_kv_heads", c.n_heads if c.n_q_heads != c.n_heads else 0)
+    return lv.Config(batch=c.batch, n_heads=c.n_q_heads, head_dim=c.head_dim,
                      loop_steps=c.loop_steps, group=c.group, n_sink=c.n_sink,
                      n_recent=c.n_recent, max_tokens=c.t_max,
                      codebook_dtype=lv.LVQ_BF16 if c.k_codebook.dtype == torch.bfloat16

@@ -58,6 +58,26 @@ def test_layout_shapes(name):
     assert lay["workspace_bytes"] >= B * H * lv.LVQ_MAX_SPLITS * (d + 2) * 4
 
 
+def test_layout_grouped_query_heads():
+    """12 query heads over 4 KV heads: caches, codebooks and windows per KV
+    head; query, output and workspace per query head."""
+    B, H, Hk, d, Tc, G, T = 2, 12, 4, 128, 4, 16, 1000
+    lay = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                        max_tokens=T, n_kv_heads=Hk))
+    mha = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                        max_tokens=T))
+    S = d // (G // Tc)
+    assert lay["k_index"]["shape"] == (B, Hk, T, S)
+    assert lay["v_codebook"]["shape"] == (Tc, Hk, 256, S, G // Tc)
+    assert lay["k_window"]["shape"] == (B, Tc, Hk, 64 + 256, d)
+    assert lay["query"]["shape"] == (B, H, d) and lay["output"]["shape"] == (B, H, d)
+    assert lay["workspace_bytes"] == mha["workspace_bytes"]
+    # n_kv_heads = n_heads is multi-head attention
+    same = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                         max_tokens=T, n_kv_heads=H))
+    assert same == mha
+
+
 def test_layout_reproduces_page_bit_budgets():
     """bits/element, compression and bytes read per token and loop step, as
     the project page prints them (Highlights; Efficiency -- Latency), for the
@@ -81,6 +101,7 @@ def test_default_windows_match_pages():
     dict(batch=0), dict(n_heads=0), dict(head_dim=0), dict(loop_steps=0), dict(group=18),
     dict(group=16, head_dim=66), dict(n_sink=-1), dict(n_recent=0), dict(max_tokens=-1),
     dict(codebook_dtype=7), dict(decode_splits=65), dict(decode_splits=-1),
+    dict(n_kv_heads=-1), dict(n_kv_heads=3), dict(n_heads=6, n_kv_heads=4),
 ])
 def test_layout_rejects_bad_config(bad):
     base = dict(batch=1, n_heads=2, head_dim=64, loop_steps=4, group=16, max_tokens=100)

@@ -81,6 +81,24 @@ def test_ragged_shapes(lv, head_dim, group, cb_dtype):
         _check(dc, t)
 
 
+@pytest.mark.parametrize("q_heads,kv_heads,head_dim,group,cb_dtype", [
+    (8, 2, 128, 16, torch.bfloat16),
+    (6, 3, 64, 32, torch.bfloat16),
+    (4, 1, 64, 16, torch.float32),
+])
+def test_grouped_query_heads(lv, q_heads, kv_heads, head_dim, group, cb_dtype):
+    """Grouped-query attention: each query head attends over the index
+    stream, codebooks and windows of its KV head (h // (Hq / Hk))."""
+    _note(f"GQA {q_heads}q/{kv_heads}kv d={head_dim} G={group} {cb_dtype}")
+    lengths = (40, 320, 900, 5000)
+    c = make_cache(batch=len(lengths), n_heads=kv_heads, q_heads=q_heads, head_dim=head_dim,
+                   group=group, lengths=lengths, cb_dtype=cb_dtype, seed=400 + q_heads,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    for t in (0, 1, 3):
+        _check(dc, t)
+
+
 def test_loop_correlated_encoded_cache(lv):
     """Realistic (skewed) code histogram: loop-correlated K/V encoded by the
     oracle, 0.5-bit, 4 heads, 3000-token context."""
@@ -205,20 +223,22 @@ def test_max_ctx_len_bound(lv):
 
 # --- full-size workloads: sampled against the oracle ---------------------------
 
-def _full_size_cache(lv, H, d, G, lengths, seed, device="cuda"):
-    """Device-resident cache at full size: windows from the loop-correlated
-    generator, VQ indices drawn uniformly (drawn, so the oracle can take
-    them as input)."""
+def _full_size_cache(lv, H, d, G, lengths, seed, device="cuda", Hq=None):
+    """Device-resident cache at full size (H KV heads, Hq query heads):
+    windows from the loop-correlated generator, VQ indices drawn uniformly
+    (drawn, so the oracle can take them as input)."""
     B = len(lengths)
     Tc = 4
     cg = G // Tc
     S = d // cg
     T = max(lengths)
-    cfg = lv.Config(batch=B, n_heads=H, head_dim=d, group=G, max_tokens=T)
+    Hq = Hq or H
+    cfg = lv.Config(batch=B, n_heads=Hq, head_dim=d, group=G, max_tokens=T,
+                    n_kv_heads=H if Hq != H else 0)
     bufs = lv.allocate(cfg, device)
     kcb = synth.codebooks(H, d, Tc, G, seed + 1, device=device)
     vcb = synth.codebooks(H, d, Tc, G, seed + 2, device=device)
-    q = synth.queries(B, H, d, Tc, seed + 3, device=device)
+    q = synth.queries(B, Hq, d, Tc, seed + 3, device=device)
     for b, L in enumerate(lengths):
         ki = synth.random_indices((H, L, S), seed + 10 + 2 * b, device=device)
         vi = synth.random_indices((H, L, S), seed + 11 + 2 * b, device=device)
@@ -258,6 +278,28 @@ def test_full_32k_context(lv, G):
                                  k_codebook=kcb.cpu(), v_codebook=vcb.cpu(),
                                  k_window=bufs["k_window"].cpu(), v_window=bufs["v_window"].cpu(),
                                  n_sink=64, n_recent=256, group=G)
+        err = rel_err_rows(got, ref)
+        _note(f"  t={t} rel err {err:.2e}")
+        assert err <= TOL
+
+
+def test_full_32k_gqa(lv):
+    """32 query heads over 8 KV heads, one 32768-token sequence, 0.5 bit:
+    every query head at loop steps 1 and 2 against the oracle, in the launch
+    configuration the benchmark's GQA workload times."""
+    _note("32K GQA 32q/8kv")
+    cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 8, 128, 16, [32768], seed=500, Hq=32)
+    for t in (1, 2):
+        lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, 32768, bufs["k_index"],
+                           bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
+                           bufs["workspace"], bufs["out"])
+        torch.cuda.synchronize()
+        got = bufs["out"].double().cpu().numpy()
+        ref = oracle.decode_attn(loop_step=t, q=q[t].cpu(), ctx_len=[32768],
+                                 k_index=bufs["k_index"].cpu(), v_index=bufs["v_index"].cpu(),
+                                 k_codebook=kcb.cpu(), v_codebook=vcb.cpu(),
+                                 k_window=bufs["k_window"].cpu(), v_window=bufs["v_window"].cpu(),
+                                 n_sink=64, n_recent=256, group=16)
         err = rel_err_rows(got, ref)
         _note(f"  t={t} rel err {err:.2e}")
         assert err <= TOL

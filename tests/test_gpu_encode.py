@@ -100,6 +100,22 @@ def test_short_runs(lv, n, H, d, Tc, G, cb_dtype):
                  _oracle_encode(x, cb, H, d, Tc, G, T=n + 5, first=5), "short run")
 
 
+def test_grouped_query_config(lv):
+    """With grouped-query attention the encoder writes the KV heads' caches:
+    x has n_kv_heads heads."""
+    _note("GQA encode")
+    Hk, Hq, d, Tc, G = 2, 8, 128, 4, 16
+    for n in (8, 300):
+        x = synth.loop_correlated_kv(n, Hk, Tc, d, seed=90 + n)
+        cb = synth.codebooks(Hk, d, Tc, G, seed=91)
+        cfg = lv.Config(batch=1, n_heads=Hq, n_kv_heads=Hk, head_dim=d, loop_steps=Tc, group=G,
+                        max_tokens=n)
+        idx = torch.zeros((1, Hk, n, d // (G // Tc)), dtype=torch.uint8, device="cuda")
+        lv.lvq_encode(cfg, x.cuda(), cb.cuda(), idx)
+        torch.cuda.synchronize()
+        _assert_same(idx.cpu().numpy(), _oracle_encode(x, cb, Hk, d, Tc, G), "gqa encode")
+
+
 def test_codeword_inputs(lv):
     _note("codeword inputs")
     H, d, Tc, G = 2, 128, 4, 16

@@ -127,6 +127,29 @@ def check_empty_and_single(seed=5):
     assert np.abs(got[1, 0] - want).max() < TOL
 
 
+def check_gqa_end_to_end(seed=8):
+    """Grouped-query attention: 6 query heads over 2 KV heads.  VQ tokens are
+    exact codewords encoded by the oracle; at every loop step the decode equals
+    torch's fp64 SDPA with ``enable_gqa`` (query head h reads KV head h // 3)
+    over the original tokens, for window-only and wrapped-ring contexts."""
+    lengths = (200, 700, 1500)
+    c = make_cache(batch=3, n_heads=2, q_heads=6, head_dim=64, lengths=lengths, seed=seed,
+                   codeword_tokens=True)
+    for t in range(c.loop_steps):
+        got = _decode(c, t, 0.5)
+        for b, L in enumerate(lengths):
+            q = c.q[t, b].double()[None, :, None, :]                    # [1][6][1][d]
+            K = c.k_tokens[b][:L, :, t].double().permute(1, 0, 2)[None]  # [1][2][L][d]
+            V = c.v_tokens[b][:L, :, t].double().permute(1, 0, 2)[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q, K, V, scale=0.5, enable_gqa=True)[0, :, 0].numpy()
+            assert np.abs(got[b] - ref).max() < TOL * max(1.0, np.abs(ref).max()), (t, b)
+
+
+def test_gqa_end_to_end():
+    check_gqa_end_to_end()
+
+
 def test_attend_matches_sdpa():
     check_attend_matches_sdpa()
 

@@ -19,7 +19,8 @@ SRC = pathlib.Path(oracle.__file__).resolve().parent / "loopvq_oracle.c"
 ENC_PINS = [enc.check_codeword_inputs, enc.check_exact_ties, enc.check_fp64_bruteforce,
             enc.check_row_permutation, enc.check_placement, enc.check_rounding_order]
 ATT_PINS = [att.check_attend_matches_sdpa, att.check_windows_only, att.check_end_to_end,
-            att.check_zero_query_mean, att.check_empty_and_single, att.check_end_to_end_page_lag]
+            att.check_zero_query_mean, att.check_empty_and_single, att.check_end_to_end_page_lag,
+            att.check_gqa_end_to_end]
 
 MUTANTS = {
     "drop_last_distance_term": ("for (int i = 0; i < G; ++i) {", "for (int i = 0; i < G - 1; ++i) {"),
@@ -36,8 +37,8 @@ MUTANTS = {
                                   "((((size_t)t * H + h) * S + j) * LVQO_CODES + k)"),
     "index_row_ignores_first_token": ("* t_max + first_token + n) * S + j]", "* t_max + n) * S + j]"),
     "dequant_reads_slice_0": ("ck, t * cg + c);", "ck, 0 * cg + c);"),
-    "value_dequant_uses_key_codebook": ("codeword_entry(v_cb, cb_bf16, H, S, cg, h, j, cv,",
-                                        "codeword_entry(k_cb, cb_bf16, H, S, cg, h, j, cv,"),
+    "value_dequant_uses_key_codebook": ("codeword_entry(v_cb, cb_bf16, Hk, S, cg, hk, j, cv,",
+                                        "codeword_entry(k_cb, cb_bf16, Hk, S, cg, hk, j, cv,"),
     "ring_slot_without_sink_offset": ("n_sink + (pos - n_sink) % n_recent", "n_sink + pos % n_recent"),
     "vq_count_drops_sink": (": (L - n_sink - n_recent > 0 ? L - n_sink - n_recent : 0);\n        double",
                             ": (L - n_recent > 0 ? L - n_recent : 0);\n        double"),
@@ -46,8 +47,9 @@ MUTANTS = {
     "window_value_from_key_buffer": ("vr[ch] = bf16_bits_to_float(v_win[base + ch]);",
                                      "vr[ch] = bf16_bits_to_float(k_win[base + ch]);"),
     "query_ignores_batch": ("q[((size_t)b * H + h) * d + ch]", "q[((size_t)0 * H + h) * d + ch]"),
-    "window_reads_step_0": ("((((size_t)b * Tc + t) * H + h) * W + slot) * d",
-                            "((((size_t)b * Tc + 0) * H + h) * W + slot) * d"),
+    "window_reads_step_0": ("((((size_t)b * Tc + t) * Hk + hk) * W + slot) * d",
+                            "((((size_t)b * Tc + 0) * Hk + hk) * W + slot) * d"),
+    "gqa_kv_head_interleaved": ("const int hk = h / (H / Hk);", "const int hk = h % Hk;"),
     "key_dot_skips_last_channel": ("for (int ch = 0; ch < d; ++ch) acc += q[ch] * K[n * d + ch];",
                                    "for (int ch = 0; ch < d - 1; ++ch) acc += q[ch] * K[n * d + ch];"),
 }
