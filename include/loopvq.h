@@ -19,20 +19,26 @@
  *
  * Notation: B sequences, H query heads, Hk KV heads (Hk = H for multi-head
  * attention; Hk dividing H for grouped-query attention, where query head h
- * reads KV head h / (H / Hk)), d = head_dim, Tc = loop_steps, G = group
- * (elements per sub-vector), cg = G / Tc channels per loop step, S = d / cg
- * sub-vectors per token per head, 256 codes.  bits per cached element = 8 / G.
+ * reads KV head h / (H / Hk)), d = head_dim, Tc = loop_steps (loop steps
+ * sharing one index), R = n_loops (loop steps of the model, a multiple of Tc;
+ * R = Tc unless set), G = group (elements per sub-vector), cg = G / Tc
+ * channels per loop step, S = d / cg sub-vectors per token per head, 256
+ * codes.  bits per cached element = 8 / G.  With R > Tc a token keeps R / Tc
+ * index rows: group g serves loop steps g*Tc .. g*Tc + Tc - 1 through
+ * codebook slices g*Tc + t.
  *
  * Storage layouts (all row-major, innermost last):
- *   x (encoder input) bf16  [n_tokens][Hk][Tc][d]  (or strided, see lvq_encode)
- *   codebook          f32 or bf16 [Tc][Hk][256][S][cg]: entry i = t*cg + c of
- *                     codeword k of (head h, sub-vector j) at [t][h][k][j][c]:
- *                     slice t of a head is contiguous, and its row k holds
- *                     code k of every sub-vector (the table row a decode
- *                     gather reads)
- *   index cache       uint8 [B][Hk][max_tokens][S]; row p holds token p
- *                     (absolute position); rows of bf16 tokens are unused
- *   window buffers    bf16 [B][Tc][Hk][n_sink + n_recent][d]: sink token p
+ *   x (encoder input) bf16  [n_tokens][Hk][R][d]  (or strided, see lvq_encode)
+ *   codebook          f32 or bf16 [R][Hk][256][S][cg]: entry i = t*cg + c of
+ *                     codeword k of (group g, head h, sub-vector j) at
+ *                     [g*Tc + t][h][k][j][c]: slice r of a head is contiguous,
+ *                     and its row k holds code k of every sub-vector (the
+ *                     table row a decode gather reads)
+ *   index cache       uint8 [B][Hk][max_tokens][S] (R = Tc), or
+ *                     [R/Tc][B][Hk][max_tokens][S] (one such block per group);
+ *                     row p holds token p (absolute position); rows of bf16
+ *                     tokens are unused
+ *   window buffers    bf16 [B][R][Hk][n_sink + n_recent][d]: sink token p
  *                     (p < n_sink) in slot p; recent token p (p >= n_sink) in
  *                     slot n_sink + ((p - n_sink) mod n_recent)  (a ring)
  *   query             bf16 [B][H][d] (the query of the loop step decoded)
@@ -88,9 +94,13 @@ typedef struct {
                                otherwise must divide n_heads (grouped-query
                                attention, consecutive query heads sharing a
                                KV head)                                        */
+    int32_t n_loops;        /* R: loop steps of the model; 0 = loop_steps;
+                               otherwise a multiple of loop_steps, at most
+                               LVQ_MAX_LOOPS                                   */
 } lvq_config;
 
 #define LVQ_MAX_SPLITS 64
+#define LVQ_MAX_LOOPS 64
 #define LVQ_CODES 256
 
 typedef struct {
@@ -132,8 +142,9 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  * page, "Component 1 -- Loop-axis vector quantization" and "Serving in SGLang
  * -- Encode in pages"; the news article "How LoopVQ works").
  *
- * Sub-vector j of (token n, head h) has entries x_i = x[n][h][t][j*cg + c],
- * i = t*cg + c.  Its code is the k minimising the squared distance
+ * Sub-vector j of (token n, head h, group g) has entries
+ * x_i = x[n][h][g*Tc + t][j*cg + c], i = t*cg + c, and is coded with the
+ * codewords of group g.  Its code is the k minimising the squared distance
  * D_k = sum_i (x_i - c_{k,i})^2 evaluated in IEEE fp32 (separate subtract,
  * square and add, ascending i); the lowest k wins ties.  The result is
  * bit-identical to that definition: the kernel screens all 256 codes with a
@@ -143,8 +154,9 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  *
  * x          device bf16; element (n, h, t, ch) at
  *            x[n*x_strides[0] + h*x_strides[1] + t*x_strides[2] + ch];
- *            x_strides == NULL means the dense [n_tokens][Hk][Tc][d] layout
- *            (the KV heads).
+ *            x_strides == NULL means the dense [n_tokens][Hk][R][d] layout
+ *            (the KV heads, every loop step of the model; all R / Tc groups
+ *            are encoded).
  *            Strides are in elements; channels must be contiguous and every
  *            stride a multiple of cg.
  * codebook   device, cfg->codebook_dtype, layout above, 16-byte aligned (one
@@ -163,12 +175,13 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
                       int32_t seq, int64_t first_token, void *stream);
 
 /*
- * Decode attention of loop step t (LoopVQ project page, "Serving in SGLang --
- * Attend from indices"): for every (b, h),
+ * Decode attention of loop step r in [0, R) (LoopVQ project page, "Serving in
+ * SGLang -- Attend from indices"): for every (b, h),
  *   out = sum_n softmax_n(sm_scale * q . K_n) V_n
  * over all L_b tokens, where VQ tokens use K_n[j*cg + c] =
- * k_codebook[t][h][k_index[b][h][n][j]][j][c] (likewise V) and sink/recent
- * tokens use the bf16 window buffers of step t.  fp32 accumulation; VQ value
+ * k_codebook[r][h][k_index[g][b][h][n][j]][j][c] with g = r / Tc (likewise V;
+ * g is absent when R = Tc) and sink/recent tokens use the bf16 window buffers
+ * of step r.  fp32 accumulation; VQ value
  * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
  * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).
  * With grouped-query attention (n_kv_heads < n_heads) query head h reads the
@@ -192,7 +205,7 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
  *            split partials tagged with the call).
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
- * outside [0, Tc), max_tokens < 1, max_ctx_len outside [0, max_tokens],
+ * outside [0, R), max_tokens < 1, max_ctx_len outside [0, max_tokens],
  * sm_scale not finite), LVQ_ERR_UNSUPPORTED (S = d/cg not in {8, 16, 32, 64},
  * cg not in {2, 4, 8}, a value-table row (S*cg entries of 2 bytes for bf16,
  * 4 for fp32 codebooks) above 256 bytes: e.g. d = 256 at G = 16, or

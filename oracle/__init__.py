@@ -47,12 +47,12 @@ def _bind(path):
     lib = ctypes.CDLL(str(path))
     i32, i64, vp, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
     lib.lvqo_encode.restype = i32
-    lib.lvqo_encode.argtypes = [i32, i32, i32, i32, i32, vp, vp, i64, i64, i64, i64,
-                                vp, i64, i64, i64, i32]
+    lib.lvqo_encode.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, i64, i64, i64, i64,
+                                vp, i64, i64, i64, i64, i32]
     lib.lvqo_attend.restype = None
     lib.lvqo_attend.argtypes = [i64, i32, vp, vp, vp, dbl, vp, vp]
     lib.lvqo_decode_attn.restype = i32
-    lib.lvqo_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
+    lib.lvqo_decode_attn.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp,
                                      i32, i32, i32]
     lib.lvqo_max_threads.restype = i32
@@ -117,26 +117,32 @@ def _codebook(cb):
     raise TypeError("codebook must be bf16 (uint16 bits) or float32")
 
 
-def encode(x, codebook, *, n_heads, head_dim, loop_steps, group, index=None,
+def encode(x, codebook, *, n_heads, head_dim, loop_steps, group, n_loops=None, index=None,
            t_max=None, seq=0, first_token=0, threads=None):
-    """Encode ``x`` (bf16 ``[n][H][Tc][d]``) into ``index`` (uint8
-    ``[B][H][t_max][S]``, allocated as ``[1][H][first_token+n][S]`` if None).
-    Returns the index array."""
+    """Encode ``x`` (bf16 ``[n][H][R][d]``, R = ``n_loops`` or ``loop_steps``)
+    into ``index`` (uint8 ``[B][H][t_max][S]``, or ``[R/Tc][B][H][t_max][S]``
+    when R > Tc; allocated with B = seq + 1 and t_max = first_token + n if
+    None).  Returns the index array."""
     xa = _np(x, np.uint16)
     n = xa.shape[0]
     cb, is_bf16 = _codebook(codebook)
     cg = group // loop_steps
     S = head_dim // cg
+    R = n_loops or loop_steps
+    NG = R // loop_steps
     if index is None:
         t_max = first_token + n if t_max is None else t_max
-        index = np.zeros((seq + 1, n_heads, t_max, S), np.uint8)
+        shape = (seq + 1, n_heads, t_max, S)
+        index = np.zeros(shape if NG == 1 else (NG,) + shape, np.uint8)
     else:
         index = _np(index, np.uint8)
-        t_max = index.shape[2]
-    assert xa.shape == (n, n_heads, loop_steps, head_dim), xa.shape
-    st = (n_heads * loop_steps * head_dim, loop_steps * head_dim, head_dim)
-    rc = _load().lvqo_encode(n_heads, head_dim, loop_steps, group, is_bf16, _ptr(cb), _ptr(xa),
-                             n, st[0], st[1], st[2], _ptr(index), t_max, seq, first_token,
+        if index.ndim != (4 if NG == 1 else 5):
+            raise ValueError(f"index: expected {4 if NG == 1 else 5} dimensions")
+    batch, t_max = index.shape[-4], index.shape[-2]
+    assert xa.shape == (n, n_heads, R, head_dim), xa.shape
+    st = (n_heads * R * head_dim, R * head_dim, head_dim)
+    rc = _load().lvqo_encode(n_heads, head_dim, loop_steps, R, group, is_bf16, _ptr(cb), _ptr(xa),
+                             n, st[0], st[1], st[2], _ptr(index), batch, t_max, seq, first_token,
                              threads or max_threads())
     if rc != 0:
         raise ValueError(f"lvqo_encode rejected its arguments ({rc})")
@@ -157,28 +163,32 @@ def attend(q, K, V, sm_scale, want_p=False):
 
 def decode_attn(*, loop_step, q, ctx_len, k_index, v_index, k_codebook, v_codebook,
                 k_window, v_window, n_sink, n_recent, group, sm_scale=1.0, vq_len=None,
-                want_p=False, heads=None, threads=None):
+                want_p=False, heads=None, threads=None, loop_steps=None):
     """fp64 decode attention (D1-D5).  Shapes: q bf16 [B][H][d]; ctx_len int32 [B];
     index uint8 [B][Hk][t_max][S]; codebooks [Tc][Hk][256][S][cg]; windows bf16
     [B][Tc][Hk][n_sink+n_recent][d], where Hk (taken from the index cache)
-    divides H and query head h reads KV head h // (H // Hk).  Returns out fp64
-    [B][H][d] (and p fp64 [B][H][t_max] when ``want_p``)."""
+    divides H and query head h reads KV head h // (H // Hk).  A model with R
+    loop steps (codebooks and windows with R slices, R a multiple of
+    ``loop_steps``) has index caches [R/Tc][B][Hk][t_max][S] and decodes
+    loop_step in [0, R).  Returns out fp64 [B][H][d] (and p fp64
+    [B][H][t_max] when ``want_p``)."""
     qa = _np(q, np.uint16)
     B, H, d = qa.shape
     ki, vi = _np(k_index, np.uint8), _np(v_index, np.uint8)
-    Hk, t_max = ki.shape[1], ki.shape[2]
+    Hk, t_max = ki.shape[-3], ki.shape[-2]
     kcb, kb = _codebook(k_codebook)
     vcb, vb = _codebook(v_codebook)
     if kb != vb:
         raise TypeError("K and V codebooks must share a dtype")
-    Tc = kcb.shape[0]
+    R = kcb.shape[0]
+    Tc = loop_steps or R
     kw, vw = _np(k_window, np.uint16), _np(v_window, np.uint16)
     cl = np.ascontiguousarray(np.asarray(ctx_len, np.int32))
     vl = None if vq_len is None else np.ascontiguousarray(np.asarray(vq_len, np.int32))
     out = np.zeros((B, H, d), np.float64)
     p = np.zeros((B, H, t_max), np.float64) if want_p else None
     h0, h1 = (0, H) if heads is None else heads
-    rc = _load().lvqo_decode_attn(B, H, Hk, d, Tc, group, n_sink, n_recent, t_max, kb, loop_step,
+    rc = _load().lvqo_decode_attn(B, H, Hk, d, Tc, R, group, n_sink, n_recent, t_max, kb, loop_step,
                                   _ptr(qa), _ptr(cl), _ptr(vl), _ptr(ki), _ptr(vi), _ptr(kcb),
                                   _ptr(vcb), _ptr(kw), _ptr(vw), float(sm_scale), _ptr(out),
                                   _ptr(p), h0, h1, threads or max_threads())

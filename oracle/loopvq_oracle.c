@@ -31,12 +31,14 @@
  *
  * Data layouts (shared with the library's documented boundary, implemented
  * here independently):
- *  x        bf16  [n_tokens][H][Tc][d] with element strides (tok, head, step),
+ *  A model with R loop steps (R a multiple of Tc) keeps R / Tc index rows per
+ *  token: group g covers loop steps g*Tc .. g*Tc + Tc - 1.
+ *  x        bf16  [n_tokens][H][R][d] with element strides (tok, head, step),
  *                 channel stride 1
- *  codebook f32/bf16 [Tc][H][256][S][cg], cg = G/Tc, S = d/cg; codeword k of
- *                 (h, j) has entry i = t*cg + c at [t][h][k][j][c]
- *  index    u8    [B][H][T_max][S]; row = absolute token position
- *  window   bf16  [B][Tc][H][n_sink + n_recent][d]; sink token p in slot p,
+ *  codebook f32/bf16 [R][H][256][S][cg], cg = G/Tc, S = d/cg; codeword k of
+ *                 (g, h, j) has entry i = t*cg + c at [g*Tc + t][h][k][j][c]
+ *  index    u8    [R/Tc][B][H][T_max][S]; row = absolute token position
+ *  window   bf16  [B][R][H][n_sink + n_recent][d]; sink token p in slot p,
  *                 recent token p in slot n_sink + ((p - n_sink) mod n_recent)
  *  q        bf16  [B][H][d]
  *
@@ -60,13 +62,13 @@ static float bf16_bits_to_float(uint16_t b)
     return f;
 }
 
-/* Entry i of codeword k for (head h, sub-vector j) as fp32 (conversion of
- * bf16 to fp32 is exact). */
-static float codeword_entry(const void *cb, int cb_bf16, int H, int S, int cg,
-                            int h, int j, int k, int i)
+/* Entry i of codeword k for (group g, head h, sub-vector j) as fp32
+ * (conversion of bf16 to fp32 is exact): loop step r = g*Tc + i/cg. */
+static float codeword_entry(const void *cb, int cb_bf16, int H, int S, int cg, int Tc,
+                            int g, int h, int j, int k, int i)
 {
-    int t = i / cg, c = i % cg;
-    size_t off = ((((size_t)t * H + h) * LVQO_CODES + k) * S + j) * cg + c;
+    int r = g * Tc + i / cg, c = i % cg;
+    size_t off = ((((size_t)r * H + h) * LVQO_CODES + k) * S + j) * cg + c;
     if (cb_bf16)
         return bf16_bits_to_float(((const uint16_t *)cb)[off]);
     return ((const float *)cb)[off];
@@ -83,42 +85,47 @@ static int check_shape(int H, int d, int Tc, int G)
 /* ---------------------------------------------------------------------------
  * Encoding: nearest codeword by squared distance.
  *   E1  x and codebook entries as fp32.
- *   E2  sub-vector j of (token n, head h): x_i = X[n][h][t][j*cg + c],
- *       i = t*cg + c (loop-step-major, contiguous channels).
+ *   E2  sub-vector j of (token n, head h, group g): x_i = X[n][h][g*Tc + t][j*cg + c],
+ *       i = t*cg + c (loop-step-major, contiguous channels); its codewords
+ *       are those of group g.
  *   E3  D_k = sum_{i=0}^{G-1} (x_i - c_{k,i})^2, one fp32 op at a time.
  *   E4  scan k = 0..255, keep k when D_k < best (strict): lowest index wins.
- * Writes index[seq][h][first_token + n][j].
+ * Writes index[g][seq][h][first_token + n][j] for every group g < R/Tc; the
+ * index cache holds `batch` sequences per group.
  * ------------------------------------------------------------------------- */
-int lvqo_encode(int n_heads, int head_dim, int loop_steps, int group,
+int lvqo_encode(int n_heads, int head_dim, int loop_steps, int n_loops, int group,
                 int cb_bf16, const void *codebook,
                 const uint16_t *x, int64_t n_tokens,
                 int64_t sx_tok, int64_t sx_head, int64_t sx_step,
-                uint8_t *index, int64_t t_max, int64_t seq, int64_t first_token,
+                uint8_t *index, int64_t batch, int64_t t_max, int64_t seq, int64_t first_token,
                 int n_threads)
 {
     if (check_shape(n_heads, head_dim, loop_steps, group)) return -1;
+    if (n_loops < loop_steps || n_loops % loop_steps != 0) return -1;
+    if (seq < 0 || seq >= batch) return -1;
     if (!codebook || !x || !index || n_tokens < 0) return -1;
     if (group > 1024) return -1;
     if (first_token < 0 || first_token + n_tokens > t_max) return -1;
-    const int H = n_heads, Tc = loop_steps, G = group;
+    const int H = n_heads, Tc = loop_steps, G = group, NG = n_loops / loop_steps;
     const int cg = G / Tc, S = head_dim / cg;
     if (n_threads < 1) n_threads = 1;
 
 #pragma omp parallel for schedule(static) num_threads(n_threads)
     for (int64_t n = 0; n < n_tokens; ++n) {
         float xv[1024];
+        for (int g = 0; g < NG; ++g)
         for (int h = 0; h < H; ++h) {
             for (int j = 0; j < S; ++j) {
                 for (int t = 0; t < Tc; ++t)
                     for (int c = 0; c < cg; ++c)
                         xv[t * cg + c] = bf16_bits_to_float(
-                            x[n * sx_tok + h * sx_head + t * sx_step + j * cg + c]);
+                            x[n * sx_tok + h * sx_head + (g * Tc + t) * sx_step + j * cg + c]);
                 int best = 0;
                 float best_d = 0.0f;
                 for (int k = 0; k < LVQO_CODES; ++k) {
                     float dist = 0.0f;
                     for (int i = 0; i < G; ++i) {
-                        float e = xv[i] - codeword_entry(codebook, cb_bf16, H, S, cg, h, j, k, i);
+                        float e = xv[i] - codeword_entry(codebook, cb_bf16, H, S, cg, Tc, g, h, j, k, i);
                         float sq = e * e;
                         dist = dist + sq;
                     }
@@ -127,7 +134,7 @@ int lvqo_encode(int n_heads, int head_dim, int loop_steps, int group,
                         best_d = dist;
                     }
                 }
-                index[(((size_t)seq * H + h) * t_max + first_token + n) * S + j] = (uint8_t)best;
+                index[((((size_t)g * batch + seq) * H + h) * t_max + first_token + n) * S + j] = (uint8_t)best;
             }
         }
     }
@@ -168,7 +175,8 @@ void lvqo_attend(int64_t L, int d, const double *q, const double *K, const doubl
 }
 
 /* ---------------------------------------------------------------------------
- * Decode attention of loop step t over the LoopVQ cache.
+ * Decode attention of loop step r (0 <= r < R) over the LoopVQ cache; its
+ * index rows are those of group g = r / Tc and t = r % Tc below.
  *   D1  windows for a context of L tokens (L counts the current token):
  *       sink = [0, n_s), n_s = min(L, n_sink); VQ = [n_s, n_s + n_v) with
  *       n_v = vq_len[b] when given, else max(0, L - n_sink - n_recent);
@@ -185,7 +193,8 @@ void lvqo_attend(int64_t L, int d, const double *q, const double *K, const doubl
  * every position < L (entries >= L untouched).  Query heads [h0, h1) only.
  * Returns -1 on a shape or precondition violation.
  * ------------------------------------------------------------------------- */
-int lvqo_decode_attn(int batch, int n_heads, int n_kv_heads, int head_dim, int loop_steps, int group,
+int lvqo_decode_attn(int batch, int n_heads, int n_kv_heads, int head_dim, int loop_steps,
+                     int n_loops, int group,
                      int n_sink, int n_recent, int64_t t_max, int cb_bf16, int loop_step,
                      const uint16_t *q, const int32_t *ctx_len, const int32_t *vq_len,
                      const uint8_t *k_index, const uint8_t *v_index,
@@ -196,10 +205,12 @@ int lvqo_decode_attn(int batch, int n_heads, int n_kv_heads, int head_dim, int l
 {
     if (check_shape(n_heads, head_dim, loop_steps, group)) return -1;
     if (n_kv_heads < 1 || n_heads % n_kv_heads != 0) return -1;
-    if (loop_step < 0 || loop_step >= loop_steps) return -1;
+    if (n_loops < loop_steps || n_loops % loop_steps != 0) return -1;
+    if (loop_step < 0 || loop_step >= n_loops) return -1;
     if (n_sink < 0 || n_recent < 1 || batch < 0) return -1;
     if (h0 < 0 || h1 > n_heads || h0 > h1) return -1;
-    const int H = n_heads, Hk = n_kv_heads, d = head_dim, Tc = loop_steps, t = loop_step;
+    const int H = n_heads, Hk = n_kv_heads, d = head_dim, Tc = loop_steps, R = n_loops;
+    const int g = loop_step / Tc, t = loop_step % Tc;
     const int cg = group / Tc, S = d / cg, W = n_sink + n_recent;
 
     for (int b = 0; b < batch; ++b) {
@@ -236,17 +247,17 @@ int lvqo_decode_attn(int batch, int n_heads, int n_kv_heads, int head_dim, int l
         for (int64_t pos = 0; pos < L; ++pos) {
             double *kr = K + pos * d, *vr = V + pos * d;
             if (pos >= n_s && pos < n_s + n_v) {
-                const size_t row = (((size_t)b * Hk + hk) * t_max + pos) * S;
+                const size_t row = ((((size_t)g * batch + b) * Hk + hk) * t_max + pos) * S;
                 for (int j = 0; j < S; ++j) {
                     int ck = k_index[row + j], cv = v_index[row + j];
                     for (int c = 0; c < cg; ++c) {
-                        kr[j * cg + c] = codeword_entry(k_cb, cb_bf16, Hk, S, cg, hk, j, ck, t * cg + c);
-                        vr[j * cg + c] = codeword_entry(v_cb, cb_bf16, Hk, S, cg, hk, j, cv, t * cg + c);
+                        kr[j * cg + c] = codeword_entry(k_cb, cb_bf16, Hk, S, cg, Tc, g, hk, j, ck, t * cg + c);
+                        vr[j * cg + c] = codeword_entry(v_cb, cb_bf16, Hk, S, cg, Tc, g, hk, j, cv, t * cg + c);
                     }
                 }
             } else {
                 int64_t slot = pos < n_sink ? pos : n_sink + (pos - n_sink) % n_recent;
-                const size_t base = ((((size_t)b * Tc + t) * Hk + hk) * W + slot) * d;
+                const size_t base = ((((size_t)b * R + loop_step) * Hk + hk) * W + slot) * d;
                 for (int ch = 0; ch < d; ++ch) {
                     kr[ch] = bf16_bits_to_float(k_win[base + ch]);
                     vr[ch] = bf16_bits_to_float(v_win[base + ch]);

@@ -13,6 +13,8 @@ namespace {
 
 // KV heads: the heads of the index caches, codebooks and windows
 int64_t kv_heads(const lvq_config *c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
+// R: loop steps of the model; R / Tc index rows (groups) per token
+int64_t n_loops(const lvq_config *c) { return c->n_loops > 0 ? c->n_loops : c->loop_steps; }
 
 bool config_ok(const lvq_config *c) {
     if (!c) return false;
@@ -27,6 +29,7 @@ bool config_ok(const lvq_config *c) {
     if (c->batch > 65535 || c->n_heads > 65535) return false;
     if (c->n_kv_heads < 0 || c->n_kv_heads > c->n_heads) return false;
     if (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0) return false;
+    if (c->n_loops < 0 || c->n_loops > LVQ_MAX_LOOPS || c->n_loops % c->loop_steps != 0) return false;
     return true;
 }
 
@@ -111,13 +114,20 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
     // per token and loop step: bf16 K and V read 2 * d * 2 bytes; the index
     // rows (K and V, shared by all loop steps) are re-read whole: 2 * S bytes
     o->read_reduction_per_step = (4.0 * (double)d) / (2.0 * (double)S);
-    const int64_t idx_shape[4] = {B, Hk, c->max_tokens, S};
-    set_tensor(&o->k_index, 4, idx_shape, 1);
-    set_tensor(&o->v_index, 4, idx_shape, 1);
-    const int64_t cb_shape[5] = {Tc, Hk, LVQ_CODES, S, cg};
+    const int64_t R = n_loops(c), NG = R / Tc;
+    if (NG == 1) {
+        const int64_t idx_shape[4] = {B, Hk, c->max_tokens, S};
+        set_tensor(&o->k_index, 4, idx_shape, 1);
+        set_tensor(&o->v_index, 4, idx_shape, 1);
+    } else {
+        const int64_t idx_shape[5] = {NG, B, Hk, c->max_tokens, S};
+        set_tensor(&o->k_index, 5, idx_shape, 1);
+        set_tensor(&o->v_index, 5, idx_shape, 1);
+    }
+    const int64_t cb_shape[5] = {R, Hk, LVQ_CODES, S, cg};
     set_tensor(&o->k_codebook, 5, cb_shape, cbe);
     set_tensor(&o->v_codebook, 5, cb_shape, cbe);
-    const int64_t win_shape[5] = {B, Tc, Hk, W, d};
+    const int64_t win_shape[5] = {B, R, Hk, W, d};
     set_tensor(&o->k_window, 5, win_shape, 2);
     set_tensor(&o->v_window, 5, win_shape, 2);
     const int64_t q_shape[3] = {B, H, d};
@@ -140,9 +150,10 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
     if (n_tokens < 0 || seq < 0 || seq >= c->batch) return LVQ_ERR_INVALID_ARG;
     if (first_token < 0 || first_token + n_tokens > c->max_tokens) return LVQ_ERR_INVALID_ARG;
     const int cg = c->group / c->loop_steps;
-    // the encoder writes the index caches: one pass per KV head
-    const int64_t H = kv_heads(c), d = c->head_dim, Tc = c->loop_steps;
-    int64_t st[3] = {H * Tc * d, Tc * d, d};
+    // the encoder writes the index caches: one pass per KV head, and per group
+    // of Tc loop steps when the model has R > Tc
+    const int64_t H = kv_heads(c), d = c->head_dim, Tc = c->loop_steps, R = n_loops(c);
+    int64_t st[3] = {H * R * d, R * d, d};
     if (x_strides) {
         for (int i = 0; i < 3; ++i) {
             st[i] = x_strides[i];
@@ -159,6 +170,8 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
                                c->codebook_dtype == LVQ_BF16))
         return LVQ_ERR_UNSUPPORTED;
     if (n_tokens == 0) return LVQ_OK;
+    const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
+    const int64_t S = c->head_dim / cg;
     lvq::EncodeArgs a{};
     a.H = (int)H;
     a.d = c->head_dim;
@@ -177,8 +190,16 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
     a.t_max = c->max_tokens;
     a.seq = seq;
     a.first_token = first_token;
-    hipError_t e = lvq::launch_encode(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;
+    for (int64_t g = 0; g < R / Tc; ++g) {
+        // group g: loop steps g*Tc .. g*Tc + Tc - 1, codebook slices of those
+        // steps, and the group's index cache block
+        a.x = static_cast<const uint16_t *>(x) + g * Tc * st[2];
+        a.cb = static_cast<const char *>(codebook) + (size_t)(g * Tc * H) * LVQ_CODES * S * cg * cbe;
+        a.index = index_cache + (size_t)g * c->batch * H * c->max_tokens * S;
+        hipError_t e = lvq::launch_encode(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return LVQ_ERR_HIP;
+    }
+    return LVQ_OK;
 }
 
 lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q,
@@ -192,7 +213,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     if (!q || !ctx_len || !k_index || !v_index || !k_codebook || !v_codebook || !k_window ||
         !v_window || !out)
         return LVQ_ERR_INVALID_ARG;
-    if (loop_step < 0 || loop_step >= c->loop_steps) return LVQ_ERR_INVALID_ARG;
+    if (loop_step < 0 || loop_step >= n_loops(c)) return LVQ_ERR_INVALID_ARG;
     if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return LVQ_ERR_INVALID_ARG;
     if (c->max_tokens < 1) return LVQ_ERR_INVALID_ARG;     // the index cache has rows
     if (!std::isfinite(sm_scale)) return LVQ_ERR_INVALID_ARG;
@@ -247,8 +268,12 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     a.q = static_cast<const uint16_t *>(q);
     a.ctx_len = ctx_len;
     a.vq_len = vq_len;
-    a.k_index = k_index;
-    a.v_index = v_index;
+    {
+        // loop step r reads the index rows of group r / Tc
+        const size_t grp = (size_t)(loop_step / c->loop_steps) * c->batch * a.Hk * c->max_tokens * S;
+        a.k_index = k_index + grp;
+        a.v_index = v_index + grp;
+    }
     a.k_cb = k_codebook;
     a.v_cb = v_codebook;
     a.k_win = static_cast<const uint16_t *>(k_window);
@@ -263,7 +288,7 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
         const size_t step = (size_t)loop_step * a.Hk * W * c->head_dim;
         a.kwin_t = static_cast<const uint16_t *>(k_window) + step;
         a.vwin_t = static_cast<const uint16_t *>(v_window) + step;
-        a.win_bstride = (int64_t)c->loop_steps * a.Hk * W * c->head_dim;
+        a.win_bstride = n_loops(c) * a.Hk * W * c->head_dim;
         a.scale_log2 = sm_scale * 1.4426950408889634f;
     }
     a.partials = static_cast<uint64_t *>(workspace);

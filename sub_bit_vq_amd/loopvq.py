@@ -34,7 +34,7 @@ class LoopVQError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
-        "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads")]
+        "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops")]
 
 
 class _Tensor(ctypes.Structure):
@@ -66,10 +66,15 @@ class Config:
     codebook_dtype: int = LVQ_BF16
     decode_splits: int = 0
     n_kv_heads: int = 0          # 0: as many KV heads as query heads
+    n_loops: int = 0             # 0: the model has loop_steps loop steps
 
     @property
     def kv_heads(self) -> int:
         return self.n_kv_heads or self.n_heads
+
+    @property
+    def loops(self) -> int:
+        return self.n_loops or self.loop_steps
 
     def c(self) -> _Config:
         return _Config(*(int(getattr(self, f.name)) for f in dataclasses.fields(self)))
@@ -158,14 +163,14 @@ def _stream(stream):
 
 def lvq_encode(cfg: Config, x: torch.Tensor, codebook: torch.Tensor, index_cache: torch.Tensor,
                seq: int = 0, first_token: int = 0, stream=None) -> None:
-    """Encode bf16 ``x`` ``[n][Hk][Tc][d]`` (KV heads; any element strides with
-    contiguous channels) into rows ``[first_token, first_token + n)`` of
-    sequence ``seq``."""
+    """Encode bf16 ``x`` ``[n][Hk][R][d]`` (KV heads, every loop step of the
+    model; any element strides with contiguous channels) into rows
+    ``[first_token, first_token + n)`` of sequence ``seq`` of every group."""
     lay = lvq_cache_layout(cfg)
     if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
         raise ValueError("x must be a bf16 device tensor")
-    if x.dim() != 4 or tuple(x.shape[1:]) != (cfg.kv_heads, cfg.loop_steps, cfg.head_dim):
-        raise ValueError(f"x: expected [n][{cfg.kv_heads}][{cfg.loop_steps}][{cfg.head_dim}]")
+    if x.dim() != 4 or tuple(x.shape[1:]) != (cfg.kv_heads, cfg.loops, cfg.head_dim):
+        raise ValueError(f"x: expected [n][{cfg.kv_heads}][{cfg.loops}][{cfg.head_dim}]")
     if x.stride(3) != 1:
         raise ValueError("x: channels must be contiguous")
     strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))

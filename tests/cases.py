@@ -86,6 +86,7 @@ class Cache:
     n_recent: int = N_RECENT
     extra: dict = field(default_factory=dict)
     q_heads: int = 0
+    n_loops: int = 0          # R > loop_steps: index caches [R/Tc][B][H][t_max][S]
 
     @property
     def n_q_heads(self):
@@ -149,6 +150,24 @@ def make_cache(*, batch=1, n_heads=1, head_dim=64, loop_steps=4, group=16, lengt
                  n_sink, n_recent, q_heads=q_heads or 0)
 
 
+def merge_loop_groups(caches) -> Cache:
+    """One cache of a model with R = len(caches) * Tc loop steps from caches
+    built for Tc steps each (same shapes and lengths): tokens, queries,
+    codebooks and windows are joined along the loop axis, index caches are
+    stacked as groups [R/Tc][B][H][t_max][S]."""
+    c0 = caches[0]
+    cat = lambda key, dim: torch.cat([getattr(c, key) for c in caches], dim)  # noqa: E731
+    merged = Cache(c0.batch, c0.n_heads, c0.head_dim, c0.loop_steps, c0.group, c0.t_max,
+                   list(c0.lengths), c0.vq_len, cat("q", 0),
+                   [torch.cat([c.k_tokens[b] for c in caches], 2) for b in range(c0.batch)],
+                   [torch.cat([c.v_tokens[b] for c in caches], 2) for b in range(c0.batch)],
+                   torch.stack([c.k_index for c in caches]), torch.stack([c.v_index for c in caches]),
+                   cat("k_codebook", 0), cat("v_codebook", 0), cat("k_window", 1),
+                   cat("v_window", 1), c0.n_sink, c0.n_recent, q_heads=c0.q_heads,
+                   n_loops=len(caches) * c0.loop_steps)
+    return merged
+
+
 def oracle_encoder(oracle_mod, n_heads, head_dim, loop_steps, group):
     """encode(x, cb, index, seq, first) callback running the CPU oracle in place."""
     def enc(x, cb, index, seq, first):
@@ -174,6 +193,7 @@ def rel_err_rows(got: np.ndarray, ref: np.ndarray) -> float:
 
 def lvq_config(lv, c: Cache, **kw):
     kw.setdefault("n_kv_heads", c.n_heads if c.n_q_heads != c.n_heads else 0)
+    kw.setdefault("n_loops", c.n_loops)
     return lv.Config(batch=c.batch, n_heads=c.n_q_heads, head_dim=c.head_dim,
                      loop_steps=c.loop_steps, group=c.group, n_sink=c.n_sink,
                      n_recent=c.n_recent, max_tokens=c.t_max,
@@ -213,7 +233,8 @@ def oracle_decode(oracle_mod, c: Cache, t, sm_scale=1.0, heads=None):
                                   v_index=c.v_index, k_codebook=c.k_codebook,
                                   v_codebook=c.v_codebook, k_window=c.k_window,
                                   v_window=c.v_window, n_sink=c.n_sink, n_recent=c.n_recent,
-                                  group=c.group, sm_scale=sm_scale, vq_len=c.vq_len, heads=heads)
+                                  group=c.group, sm_scale=sm_scale, vq_len=c.vq_len, heads=heads,
+                                  loop_steps=c.loop_steps)
 
 
 def rounding_order_case(H, d, Tc, G, n, cb_dtype, seed, n_base=4):

@@ -78,6 +78,24 @@ def test_layout_grouped_query_heads():
     assert same == mha
 
 
+def test_layout_loop_groups():
+    """R = 12 loop steps over Tc = 4: three index rows per token, stored as
+    three [B][H][T][S] blocks; codebooks and windows carry all 12 steps."""
+    B, H, d, Tc, G, T, R = 2, 4, 64, 4, 16, 500, 12
+    lay = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                        max_tokens=T, n_loops=R))
+    S = d // (G // Tc)
+    assert lay["k_index"]["shape"] == (R // Tc, B, H, T, S)
+    assert lay["k_index"]["bytes"] == (R // Tc) * B * H * T * S
+    assert lay["k_codebook"]["shape"] == (R, H, 256, S, G // Tc)
+    assert lay["v_window"]["shape"] == (B, R, H, 64 + 256, d)
+    assert lay["bits_per_element"] == 8 / G
+    # R = Tc is the single-group layout
+    one = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                        max_tokens=T, n_loops=Tc))
+    assert one["k_index"]["shape"] == (B, H, T, S)
+
+
 def test_layout_reproduces_page_bit_budgets():
     """bits/element, compression and bytes read per token and loop step, as
     the project page prints them (Highlights; Efficiency -- Latency), for the
@@ -102,6 +120,7 @@ def test_default_windows_match_pages():
     dict(group=16, head_dim=66), dict(n_sink=-1), dict(n_recent=0), dict(max_tokens=-1),
     dict(codebook_dtype=7), dict(decode_splits=65), dict(decode_splits=-1),
     dict(n_kv_heads=-1), dict(n_kv_heads=3), dict(n_heads=6, n_kv_heads=4),
+    dict(n_loops=-4), dict(n_loops=6), dict(n_loops=68),
 ])
 def test_layout_rejects_bad_config(bad):
     base = dict(batch=1, n_heads=2, head_dim=64, loop_steps=4, group=16, max_tokens=100)

@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from cases import (DeviceCache, make_cache, oracle_decode, oracle_encoder, rel_err_rows)
+from cases import (DeviceCache, make_cache, merge_loop_groups, oracle_decode, oracle_encoder,
+                   rel_err_rows)
 from sub_bit_vq_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -97,6 +98,22 @@ def test_grouped_query_heads(lv, q_heads, kv_heads, head_dim, group, cb_dtype):
     dc = DeviceCache(lv, c)
     for t in (0, 1, 3):
         _check(dc, t)
+
+
+@pytest.mark.parametrize("groups,q_heads", [(2, 0), (3, 4)])
+def test_loop_groups(lv, groups, q_heads):
+    """A model with R = groups * 4 loop steps (one index row per group of 4
+    steps): every loop step r reads the rows of group r // 4, codebook slice r
+    and window step r; also under grouped-query attention."""
+    _note(f"loop groups {groups} q_heads={q_heads}")
+    lengths = (100, 800, 3000)
+    parts = [make_cache(batch=3, n_heads=2, q_heads=q_heads or None, head_dim=128, group=16,
+                        lengths=lengths, seed=600 + 17 * g, codeword_tokens=True)
+             for g in range(groups)]
+    c = merge_loop_groups(parts)
+    dc = DeviceCache(lv, c)
+    for r in range(4 * groups):
+        _check(dc, r)
 
 
 def test_loop_correlated_encoded_cache(lv):

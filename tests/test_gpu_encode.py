@@ -116,6 +116,28 @@ def test_grouped_query_config(lv):
         _assert_same(idx.cpu().numpy(), _oracle_encode(x, cb, Hk, d, Tc, G), "gqa encode")
 
 
+@pytest.mark.parametrize("n", [8, 700])
+def test_loop_groups(lv, n):
+    """R = 8 loop steps over Tc = 4: x carries all 8 steps, and both groups'
+    index blocks are written (group g from steps 4g..4g+3 and codebook
+    slices 4g..4g+3)."""
+    _note(f"loop groups encode n={n}")
+    H, d, Tc, G, R = 2, 128, 4, 16, 8
+    x = synth.loop_correlated_kv(n, H, R, d, seed=95 + n)
+    S = d // (G // Tc)
+    cb = synth.codebooks(H, d, Tc, G, seed=97)
+    cb = torch.cat([cb, synth.codebooks(H, d, Tc, G, seed=98)], 0)   # [8][H][256][S][cg]
+    cfg = lv.Config(batch=2, n_heads=H, head_dim=d, loop_steps=Tc, group=G, max_tokens=n + 3,
+                    n_loops=R)
+    idx = torch.full((R // Tc, 2, H, n + 3, S), 0x5A, dtype=torch.uint8, device="cuda")
+    lv.lvq_encode(cfg, x.cuda(), cb.cuda(), idx, 1, 3)
+    torch.cuda.synchronize()
+    ref = np.full((R // Tc, 2, H, n + 3, S), 0x5A, np.uint8)
+    oracle.encode(x, cb, n_heads=H, head_dim=d, loop_steps=Tc, group=G, n_loops=R, index=ref,
+                  seq=1, first_token=3)
+    _assert_same(idx.cpu().numpy(), ref, "loop groups encode")
+
+
 def test_codeword_inputs(lv):
     _note("codeword inputs")
     H, d, Tc, G = 2, 128, 4, 16

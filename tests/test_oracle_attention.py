@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from cases import make_cache, oracle_encoder, sdpa_fp64
+from cases import make_cache, merge_loop_groups, oracle_encoder, sdpa_fp64
 from sub_bit_vq_amd import synth
 
 TOL = 1e-10
@@ -24,7 +24,8 @@ def _decode(c, t, sm_scale=1.0, **kw):
                               v_index=c.v_index, k_codebook=c.k_codebook,
                               v_codebook=c.v_codebook, k_window=c.k_window,
                               v_window=c.v_window, n_sink=c.n_sink, n_recent=c.n_recent,
-                              group=c.group, sm_scale=sm_scale, vq_len=c.vq_len, **kw)
+                              group=c.group, sm_scale=sm_scale, vq_len=c.vq_len,
+                              loop_steps=c.loop_steps, **kw)
 
 
 def _dense_reference(c, t, sm_scale):
@@ -144,6 +145,37 @@ def check_gqa_end_to_end(seed=8):
             ref = torch.nn.functional.scaled_dot_product_attention(
                 q, K, V, scale=0.5, enable_gqa=True)[0, :, 0].numpy()
             assert np.abs(got[b] - ref).max() < TOL * max(1.0, np.abs(ref).max()), (t, b)
+
+
+def check_loop_groups_end_to_end(seed=9):
+    """A model with R = 8 loop steps over Tc = 4 (two index rows per token):
+    two independently drawn single-group caches joined along the loop axis.
+    The oracle encoder, given every loop step of the VQ tokens, must recover
+    both groups' drawn indices, and decoding loop step r = 0..7 must equal
+    fp64 SDPA over the original tokens at step r."""
+    lengths = (300, 900, 1700)
+    parts = [make_cache(batch=3, n_heads=2, head_dim=64, lengths=lengths, seed=seed + 31 * g,
+                        codeword_tokens=True) for g in range(2)]
+    c = merge_loop_groups(parts)
+    truth_k, truth_v = c.k_index.clone(), c.v_index.clone()
+    c.k_index.zero_()
+    c.v_index.zero_()
+    for b in range(c.batch):
+        r = c.vq_range(b)
+        if len(r):
+            for tok, cb, idx in ((c.k_tokens, c.k_codebook, c.k_index),
+                                 (c.v_tokens, c.v_codebook, c.v_index)):
+                oracle.encode(tok[b][r.start:r.stop], cb, n_heads=2, head_dim=64, loop_steps=4,
+                              group=16, n_loops=8, index=idx.numpy(), seq=b, first_token=r.start)
+    assert torch.equal(c.k_index, truth_k) and torch.equal(c.v_index, truth_v)
+    for step in range(8):
+        got = _decode(c, step, 0.5)
+        ref = _dense_reference(c, step, 0.5)
+        assert np.abs(got - ref).max() < TOL * max(1.0, np.abs(ref).max()), step
+
+
+def test_loop_groups_end_to_end():
+    check_loop_groups_end_to_end()
 
 
 def test_gqa_end_to_end():

@@ -20,7 +20,7 @@ ENC_PINS = [enc.check_codeword_inputs, enc.check_exact_ties, enc.check_fp64_brut
             enc.check_row_permutation, enc.check_placement, enc.check_rounding_order]
 ATT_PINS = [att.check_attend_matches_sdpa, att.check_windows_only, att.check_end_to_end,
             att.check_zero_query_mean, att.check_empty_and_single, att.check_end_to_end_page_lag,
-            att.check_gqa_end_to_end]
+            att.check_gqa_end_to_end, att.check_loop_groups_end_to_end]
 
 MUTANTS = {
     "drop_last_distance_term": ("for (int i = 0; i < G; ++i) {", "for (int i = 0; i < G - 1; ++i) {"),
@@ -29,16 +29,20 @@ MUTANTS = {
     "abs_instead_of_square": ("float sq = e * e;", "float sq = e < 0 ? -e : e;"),
     "fused_square_add": ("float sq = e * e;\n                        dist = dist + sq;",
                          "dist = fmaf(e, e, dist);"),
-    "distance_summed_descending": ("float e = xv[i] - codeword_entry(codebook, cb_bf16, H, S, cg, h, j, k, i);",
-                                   "float e = xv[G - 1 - i] - codeword_entry(codebook, cb_bf16, H, S, cg, h, j, k, G - 1 - i);"),
+    "distance_summed_descending": ("float e = xv[i] - codeword_entry(codebook, cb_bf16, H, S, cg, Tc, g, h, j, k, i);",
+                                   "float e = xv[G - 1 - i] - codeword_entry(codebook, cb_bf16, H, S, cg, Tc, g, h, j, k, G - 1 - i);"),
     "subvector_channels_transposed": ("xv[t * cg + c] = bf16_bits_to_float(",
                                       "xv[c * Tc + t] = bf16_bits_to_float("),
-    "codebook_code_sub_swapped": ("((((size_t)t * H + h) * LVQO_CODES + k) * S + j)",
-                                  "((((size_t)t * H + h) * S + j) * LVQO_CODES + k)"),
+    "codebook_code_sub_swapped": ("((((size_t)r * H + h) * LVQO_CODES + k) * S + j)",
+                                  "((((size_t)r * H + h) * S + j) * LVQO_CODES + k)"),
+    "codeword_slice_ignores_group": ("int r = g * Tc + i / cg, c = i % cg;",
+                                     "int r = i / cg, c = i % cg;"),
+    "encode_writes_group_0_rows": ("index[((((size_t)g * batch + seq) * H + h)",
+                                   "index[((((size_t)0 * batch + seq) * H + h)"),
     "index_row_ignores_first_token": ("* t_max + first_token + n) * S + j]", "* t_max + n) * S + j]"),
     "dequant_reads_slice_0": ("ck, t * cg + c);", "ck, 0 * cg + c);"),
-    "value_dequant_uses_key_codebook": ("codeword_entry(v_cb, cb_bf16, Hk, S, cg, hk, j, cv,",
-                                        "codeword_entry(k_cb, cb_bf16, Hk, S, cg, hk, j, cv,"),
+    "value_dequant_uses_key_codebook": ("codeword_entry(v_cb, cb_bf16, Hk, S, cg, Tc, g, hk, j, cv,",
+                                        "codeword_entry(k_cb, cb_bf16, Hk, S, cg, Tc, g, hk, j, cv,"),
     "ring_slot_without_sink_offset": ("n_sink + (pos - n_sink) % n_recent", "n_sink + pos % n_recent"),
     "vq_count_drops_sink": (": (L - n_sink - n_recent > 0 ? L - n_sink - n_recent : 0);\n        double",
                             ": (L - n_recent > 0 ? L - n_recent : 0);\n        double"),
@@ -47,8 +51,8 @@ MUTANTS = {
     "window_value_from_key_buffer": ("vr[ch] = bf16_bits_to_float(v_win[base + ch]);",
                                      "vr[ch] = bf16_bits_to_float(k_win[base + ch]);"),
     "query_ignores_batch": ("q[((size_t)b * H + h) * d + ch]", "q[((size_t)0 * H + h) * d + ch]"),
-    "window_reads_step_0": ("((((size_t)b * Tc + t) * Hk + hk) * W + slot) * d",
-                            "((((size_t)b * Tc + 0) * Hk + hk) * W + slot) * d"),
+    "window_reads_step_0": ("((((size_t)b * R + loop_step) * Hk + hk) * W + slot) * d",
+                            "((((size_t)b * R + 0) * Hk + hk) * W + slot) * d"),
     "gqa_kv_head_interleaved": ("const int hk = h / (H / Hk);", "const int hk = h % Hk;"),
     "key_dot_skips_last_channel": ("for (int ch = 0; ch < d; ++ch) acc += q[ch] * K[n * d + ch];",
                                    "for (int ch = 0; ch < d - 1; ++ch) acc += q[ch] * K[n * d + ch];"),
