@@ -253,6 +253,31 @@ def cpu_baseline(setup, torch, budget_s=15.0):
     }
 
 
+def loop_axis_experiment(lv, synth, torch, heads=8, d=128, n_train=8192, n_test=2048,
+                         iters=8, seed=2024):
+    """The equal-bits comparison of the LoopVQ project page ("Component 1 --
+    Loop-axis vector quantization") on the synthetic looped-model keys: k-means
+    codebooks with the HIP encoder as the assignment step, test-set error per
+    element for 4-step loop-axis grouping and for channel-only grouping."""
+    from sub_bit_vq_amd import kmeans
+    x = synth.loop_correlated_kv(n_train + n_test, heads, 4, d, seed)
+    assign = kmeans.device_assign(lv)
+    rows = []
+    for group in (16, 32):
+        t0 = time.perf_counter()
+        r = kmeans.loop_axis_comparison(x[:n_train], x[n_train:], group, iters, seed + group,
+                                        assign)
+        log(f"G={group}: loop axis {r['mse_loop_axis']:.5f}, channels only "
+            f"{r['mse_channels_only']:.5f} ({time.perf_counter() - t0:.1f} s)")
+        rows.append({k: v for k, v in r.items() if not k.startswith("train_history")}
+                    | {"group": group})
+    print(json.dumps({"experiment": "loop_axis_vs_channels_equal_bits", "heads": heads,
+                      "head_dim": d, "loop_steps": 4, "train_tokens": n_train,
+                      "test_tokens": n_test, "iterations": iters,
+                      "data": "synthetic loop-correlated keys (base N(0,1) + N(0, (0.1(l+1))^2))",
+                      "results": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +293,9 @@ def main():
                     help="only run N decode launches (for rocprofv3 runs) and exit")
     ap.add_argument("--profile-encode", type=int, default=0,
                     help="only run N prefill encodes of 32768 tokens (for rocprofv3 runs) and exit")
+    ap.add_argument("--loop-axis", action="store_true",
+                    help="instead of the benchmark: the equal-bits loop-axis vs channel-only "
+                         "k-means comparison (encoder as the assignment step); prints one JSON line")
     ap.add_argument("--copy-calibrate", action="store_true",
                     help="with --profile-*: also run plain 512 MiB device copies, whose HBM "
                          "counters give the scale of FETCH_SIZE / WRITE_SIZE")
@@ -283,6 +311,9 @@ def main():
     from sub_bit_vq_amd import synth
 
     lv.library()
+    if args.loop_axis:
+        loop_axis_experiment(lv, synth, torch)
+        return
     log(f"workload {args.workload}: setup")
     setup = Setup(lv, synth, torch, args.workload, args.rotate)
     log(f"rotation over {setup.rotate} cache copies, "
