@@ -720,21 +720,36 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         if (vq_wg) stg.finish(qs, smem);
         __syncthreads();
     }
+    // Waves w and w + 4 share a SIMD; the older one would win every issue slot
+    // and finish long before its partner.  Their priorities alternate from
+    // batch to batch instead, so both reach the reduction together.
+    int turn = __builtin_amdgcn_readfirstlane(wave >> 2);
+    auto take_turn = [&]() {
+        if (turn & 1)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
+        ++turn;
+    };
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r2);
+        take_turn();
         fold_batch<S, CG, CB>(r0, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r0);
+        take_turn();
         fold_batch<S, CG, CB>(r1, base, t1, smem, ln, st);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r1);
+        take_turn();
         fold_batch<S, CG, CB>(r2, base, t1, smem, ln, st);
         base += BSTEP;
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // Lane accumulators to the freed table space: row (wave, tk), natural
     // channel order.  Then wave (m, l).
