@@ -53,7 +53,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;     // 4 waves, one sub-vector index j each
 constexpr int kJW = 4;            // sub-vectors per workgroup
-constexpr int kTokChunk = 1024;   // tokens per workgroup
+constexpr int kTokChunk = 2048;   // tokens per workgroup (queued rows fit 16 bits)
 constexpr float kEpsScale = 6.103515625e-05f;  // 2^-14
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -78,10 +78,10 @@ SHAPES = [  # (H, d, Tc, G, cb dtype)
 
 @pytest.mark.parametrize("H,d,Tc,G,cb_dtype", SHAPES)
 def test_shapes_multi_chunk_ragged_tail(lv, H, d, Tc, G, cb_dtype):
-    """2500 tokens: three 1024-token workgroups, the last one ragged."""
+    """4500 tokens: three 2048-token workgroups, the last one ragged."""
     _note(f"shape H={H} d={d} Tc={Tc} G={G} {cb_dtype}")
     seed = H * 1000 + d + Tc * 10 + G
-    x = synth.loop_correlated_kv(2500, H, Tc, d, seed)
+    x = synth.loop_correlated_kv(4500, H, Tc, d, seed)
     cb = synth.codebooks(H, d, Tc, G, seed + 1, dtype=cb_dtype)
     _assert_same(_gpu_encode(lv, x, cb, H, d, Tc, G), _oracle_encode(x, cb, H, d, Tc, G),
                  "shape")
