@@ -155,8 +155,8 @@ class Setup:
         if decode_only:
             return
         c = self.copies[self.n_call % self.rotate]
-        self.lv.lvq_encode(self.cfg, self.page_k, self.kcb, c["k_index"], 0, self.page_row)
-        self.lv.lvq_encode(self.cfg, self.page_v, self.vcb, c["v_index"], 0, self.page_row)
+        self.lv.lvq_encode_kv(self.cfg, self.page_k, self.page_v, self.kcb, self.vcb,
+                              c["k_index"], c["v_index"], 0, self.page_row)
 
     @property
     def tokens_steps_per_step(self):
@@ -402,7 +402,7 @@ def main():
             "group": setup.G, "context": setup.L if setup.B == 1 else sum(setup.lengths),
             "n_sink": N_SINK, "n_recent": N_RECENT,
             "step": ("8 tokens x 4 loop-step decodes" if args.decode_only else
-                     "8 tokens x 4 loop-step decodes + 8-token page encode (K, V)"),
+                     "8 tokens x 4 loop-step decodes + 8-token page encode (K and V, one launch)"),
             "cache_copies": setup.rotate, "graph": graph is not None,
         },
         "roofline": {

@@ -175,6 +175,22 @@ lvq_status lvq_encode(const lvq_config *cfg, const void *x, const int64_t *x_str
                       int32_t seq, int64_t first_token, void *stream);
 
 /*
+ * The K and V of one run of tokens in a single launch (LoopVQ project page,
+ * "Serving in SGLang -- Encode in pages": every page evicted from the recent
+ * window is encoded into the K and the V index caches).  Identical to
+ * lvq_encode(k_x, k_codebook, k_index) followed by lvq_encode(v_x,
+ * v_codebook, v_index) with the same cfg, x_strides, n_tokens, seq and
+ * first_token, but both tensors are encoded by one kernel launch (per group
+ * of Tc loop steps), so a page costs one launch instead of two.  Arguments,
+ * layouts, alignment and errors as for lvq_encode; nothing is launched unless
+ * both tensors' arguments are valid.
+ */
+lvq_status lvq_encode_kv(const lvq_config *cfg, const void *k_x, const void *v_x,
+                         const int64_t *x_strides, int64_t n_tokens, const void *k_codebook,
+                         const void *v_codebook, uint8_t *k_index, uint8_t *v_index,
+                         int32_t seq, int64_t first_token, void *stream);
+
+/*
  * Decode attention of loop step r in [0, R) (LoopVQ project page, "Serving in
  * SGLang -- Attend from indices"): for every (b, h),
  *   out = sum_n softmax_n(sm_scale * q . K_n) V_n

@@ -164,7 +164,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     __shared__ float nrm[kJW * 256];
     __shared__ uint16_t amb_queue[kJW][kTokChunk];     // per wave: chunk rows to re-score
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int h = blockIdx.z;
+    // grid z = tensor * H + head (a launch may encode two tensors, e.g. K and V)
+    const int tz = (int)blockIdx.z / a.H;
+    const int h = (int)blockIdx.z - tz * a.H;
+    const uint16_t *xin = tz ? a.x_b : a.x;
+    const void *cbin = tz ? a.cb_b : a.cb;
+    uint8_t *idxout = tz ? a.index_b : a.index;
     const int j0 = blockIdx.y * kJW, j = j0 + wave;
     const int64_t tok0 = (int64_t)blockIdx.x * kTokChunk;
     const int64_t tok_end = min(tok0 + kTokChunk, a.n_tokens);
@@ -172,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 
     // stage the 4 codebooks: chunk c of row (t, k) piece p -> entries (jl, c) of slice t
     {
-        const char *src = static_cast<const char *>(a.cb);
+        const char *src = static_cast<const char *>(cbin);
         constexpr int PER_ROW = Sh::ROWB / 16;
 #pragma unroll
         for (int u = 0; u < Sh::CHUNKS / kThreads; ++u) {
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
         }
     }
 
-    uint8_t *out_rows = a.index + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token) * a.S + j;
+    uint8_t *out_rows = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token) * a.S + j;
 
     // per-lane x offsets (bytes from the tile base) of the loads that fill the
     // lane's B words; lanes whose K entries are not x read nothing
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     // lanes whose words are x entries i < G (counted once for |x|^2)
     const bool norm_lane = kq * 8 < G;
 
-    const uint16_t *xh = a.x + h * a.sx_head;
+    const uint16_t *xh = xin + h * a.sx_head;
     auto rsrc = [&](int64_t n0) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xh + n0 * a.sx_tok), (short)0,
                                                  0x7ffffff0, kBufferWord3);
@@ -453,14 +458,16 @@ __global__ __launch_bounds__(256) void encode_small(EncodeArgs a) {
     __shared__ float xs[kSmallTokens][G];
     __shared__ uint32_t wave_d[4][kSmallTokens], wave_k[4][kSmallTokens];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = blockIdx.x, h = blockIdx.y;
+    const int j = blockIdx.x, h = blockIdx.y;           // grid z = tensor
+    const uint16_t *xin = blockIdx.z ? a.x_b : a.x;
+    uint8_t *idxout = blockIdx.z ? a.index_b : a.index;
     const int n = (int)a.n_tokens;
     for (int e = tid; e < n * G; e += 256) {
         const int tok = e / G, i = e % G;
-        xs[tok][i] = bf16f(a.x[tok * a.sx_tok + h * a.sx_head + (i / CG) * a.sx_step + (int64_t)j * CG + i % CG]);
+        xs[tok][i] = bf16f(xin[tok * a.sx_tok + h * a.sx_head + (i / CG) * a.sx_step + (int64_t)j * CG + i % CG]);
     }
     // code k = tid of (h, j); slice t holds entries t*CG .. t*CG + CG - 1
-    const CB *cb = static_cast<const CB *>(a.cb);
+    const CB *cb = static_cast<const CB *>(blockIdx.z ? a.cb_b : a.cb);
     float cw[G];
 #pragma unroll
     for (int t = 0; t < G / CG; ++t)
@@ -493,14 +500,14 @@ __global__ __launch_bounds__(256) void encode_small(EncodeArgs a) {
                 bk = wave_k[w][tid];
             }
         }
-        a.index[(((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tid) * a.S + j] = (uint8_t)bk;
+        idxout[(((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tid) * a.S + j] = (uint8_t)bk;
     }
 }
 
 template <int G, int CG>
 hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
     if (a.n_tokens <= kSmallTokens) {
-        const dim3 grid(a.S, a.H);
+        const dim3 grid(a.S, a.H, a.n_tensors);
         if (a.cb_bf16)
             hipLaunchKernelGGL((encode_small<G, CG, uint16_t>), grid, dim3(256), 0, st, a);
         else if constexpr (G <= 16)
@@ -509,7 +516,8 @@ hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW, a.H);
+    const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW,
+                    a.H * a.n_tensors);
     if (a.cb_bf16) {
         hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t>), grid, dim3(kThreads), 0, st, a);
     } else {

@@ -60,11 +60,15 @@ struct DecodeArgs {
 struct EncodeArgs {
     int H, d, Tc, G, cg, S;
     int cb_bf16;
+    int n_tensors;              // 1, or 2: a second tensor of the same shape
     const uint16_t *x;
-    int64_t sx_tok, sx_head, sx_step;   // element strides of x
+    int64_t sx_tok, sx_head, sx_step;   // element strides of x (and x_b)
     int64_t n_tokens;
     const void *cb;             // [Tc][H][256][S][cg]
     uint8_t *index;             // [B][H][t_max][S]
+    const uint16_t *x_b;        // the second tensor (n_tensors == 2): its input,
+    const void *cb_b;           // codebook and index cache
+    uint8_t *index_b;
     int64_t t_max;
     int64_t seq;
     int64_t first_token;

@@ -84,6 +84,76 @@ Splits choose_splits(const lvq_config *c, int64_t max_vq) {
     return {(int32_t)want, want > 1 && bh * want <= kTargetGroups};
 }
 
+// Encode n tensors of one shape (1: lvq_encode; 2: the K and V of a page in one
+// launch per group).  Every argument is checked before anything is launched.
+lvq_status encode_tensors(const lvq_config *c, int n, const void *const *x, const int64_t *x_strides,
+                          int64_t n_tokens, const void *const *codebook, uint8_t *const *index_cache,
+                          int32_t seq, int64_t first_token, void *stream) {
+    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i)
+        if (!x[i] || !codebook[i] || !index_cache[i]) return LVQ_ERR_INVALID_ARG;
+    if (n_tokens < 0 || seq < 0 || seq >= c->batch) return LVQ_ERR_INVALID_ARG;
+    if (first_token < 0 || first_token + n_tokens > c->max_tokens) return LVQ_ERR_INVALID_ARG;
+    const int cg = c->group / c->loop_steps;
+    // the encoder writes the index caches: one pass per KV head, and per group
+    // of Tc loop steps when the model has R > Tc
+    const int64_t H = kv_heads(c), d = c->head_dim, Tc = c->loop_steps, R = n_loops(c);
+    int64_t st[3] = {H * R * d, R * d, d};
+    if (x_strides) {
+        for (int i = 0; i < 3; ++i) {
+            st[i] = x_strides[i];
+            if (st[i] < 0 || st[i] % cg != 0) return LVQ_ERR_INVALID_ARG;
+        }
+    }
+    for (int i = 0; i < n; ++i) {
+        // sub-vector runs of cg bf16 are read as one vector
+        if (reinterpret_cast<uintptr_t>(x[i]) % (2 * (uintptr_t)cg) != 0) return LVQ_ERR_INVALID_ARG;
+        // the codebooks are staged in 16-byte pieces
+        if (reinterpret_cast<uintptr_t>(codebook[i]) % 16 != 0) return LVQ_ERR_INVALID_ARG;
+    }
+    // a 16-token tile of one head is addressed with 32-bit byte offsets
+    if (2 * (15 * st[0] + Tc * st[2] + d) >= 0x7ffffff0LL) return LVQ_ERR_UNSUPPORTED;
+    if (!lvq::encode_supported(c->group, cg, (int)(c->head_dim / cg),
+                               c->codebook_dtype == LVQ_BF16))
+        return LVQ_ERR_UNSUPPORTED;
+    if (n_tokens == 0) return LVQ_OK;
+    const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
+    const int64_t S = c->head_dim / cg;
+    lvq::EncodeArgs a{};
+    a.H = (int)H;
+    a.d = c->head_dim;
+    a.Tc = c->loop_steps;
+    a.G = c->group;
+    a.cg = cg;
+    a.S = c->head_dim / cg;
+    a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
+    a.n_tensors = n;
+    a.sx_tok = st[0];
+    a.sx_head = st[1];
+    a.sx_step = st[2];
+    a.n_tokens = n_tokens;
+    a.t_max = c->max_tokens;
+    a.seq = seq;
+    a.first_token = first_token;
+    for (int64_t g = 0; g < R / Tc; ++g) {
+        // group g: loop steps g*Tc .. g*Tc + Tc - 1, codebook slices of those
+        // steps, and the group's index cache block
+        const size_t cb_off = (size_t)(g * Tc * H) * LVQ_CODES * S * cg * cbe;
+        const size_t idx_off = (size_t)g * c->batch * H * c->max_tokens * S;
+        a.x = static_cast<const uint16_t *>(x[0]) + g * Tc * st[2];
+        a.cb = static_cast<const char *>(codebook[0]) + cb_off;
+        a.index = index_cache[0] + idx_off;
+        if (n == 2) {
+            a.x_b = static_cast<const uint16_t *>(x[1]) + g * Tc * st[2];
+            a.cb_b = static_cast<const char *>(codebook[1]) + cb_off;
+            a.index_b = index_cache[1] + idx_off;
+        }
+        hipError_t e = lvq::launch_encode(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return LVQ_ERR_HIP;
+    }
+    return LVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -145,61 +215,20 @@ int32_t lvq_decode_splits(const lvq_config *c, int32_t max_ctx_len) {
 lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strides,
                       int64_t n_tokens, const void *codebook, uint8_t *index_cache,
                       int32_t seq, int64_t first_token, void *stream) {
-    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
-    if (!x || !codebook || !index_cache) return LVQ_ERR_INVALID_ARG;
-    if (n_tokens < 0 || seq < 0 || seq >= c->batch) return LVQ_ERR_INVALID_ARG;
-    if (first_token < 0 || first_token + n_tokens > c->max_tokens) return LVQ_ERR_INVALID_ARG;
-    const int cg = c->group / c->loop_steps;
-    // the encoder writes the index caches: one pass per KV head, and per group
-    // of Tc loop steps when the model has R > Tc
-    const int64_t H = kv_heads(c), d = c->head_dim, Tc = c->loop_steps, R = n_loops(c);
-    int64_t st[3] = {H * R * d, R * d, d};
-    if (x_strides) {
-        for (int i = 0; i < 3; ++i) {
-            st[i] = x_strides[i];
-            if (st[i] < 0 || st[i] % cg != 0) return LVQ_ERR_INVALID_ARG;
-        }
-    }
-    // sub-vector runs of cg bf16 are read as one vector
-    if (reinterpret_cast<uintptr_t>(x) % (2 * (uintptr_t)cg) != 0) return LVQ_ERR_INVALID_ARG;
-    // the codebooks are staged in 16-byte pieces
-    if (reinterpret_cast<uintptr_t>(codebook) % 16 != 0) return LVQ_ERR_INVALID_ARG;
-    // a 16-token tile of one head is addressed with 32-bit byte offsets
-    if (2 * (15 * st[0] + Tc * st[2] + d) >= 0x7ffffff0LL) return LVQ_ERR_UNSUPPORTED;
-    if (!lvq::encode_supported(c->group, cg, (int)(c->head_dim / cg),
-                               c->codebook_dtype == LVQ_BF16))
-        return LVQ_ERR_UNSUPPORTED;
-    if (n_tokens == 0) return LVQ_OK;
-    const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
-    const int64_t S = c->head_dim / cg;
-    lvq::EncodeArgs a{};
-    a.H = (int)H;
-    a.d = c->head_dim;
-    a.Tc = c->loop_steps;
-    a.G = c->group;
-    a.cg = cg;
-    a.S = c->head_dim / cg;
-    a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
-    a.x = static_cast<const uint16_t *>(x);
-    a.sx_tok = st[0];
-    a.sx_head = st[1];
-    a.sx_step = st[2];
-    a.n_tokens = n_tokens;
-    a.cb = codebook;
-    a.index = index_cache;
-    a.t_max = c->max_tokens;
-    a.seq = seq;
-    a.first_token = first_token;
-    for (int64_t g = 0; g < R / Tc; ++g) {
-        // group g: loop steps g*Tc .. g*Tc + Tc - 1, codebook slices of those
-        // steps, and the group's index cache block
-        a.x = static_cast<const uint16_t *>(x) + g * Tc * st[2];
-        a.cb = static_cast<const char *>(codebook) + (size_t)(g * Tc * H) * LVQ_CODES * S * cg * cbe;
-        a.index = index_cache + (size_t)g * c->batch * H * c->max_tokens * S;
-        hipError_t e = lvq::launch_encode(a, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return LVQ_ERR_HIP;
-    }
-    return LVQ_OK;
+    const void *xs[1] = {x};
+    const void *cbs[1] = {codebook};
+    uint8_t *idx[1] = {index_cache};
+    return encode_tensors(c, 1, xs, x_strides, n_tokens, cbs, idx, seq, first_token, stream);
+}
+
+lvq_status lvq_encode_kv(const lvq_config *c, const void *k_x, const void *v_x,
+                         const int64_t *x_strides, int64_t n_tokens, const void *k_codebook,
+                         const void *v_codebook, uint8_t *k_index, uint8_t *v_index, int32_t seq,
+                         int64_t first_token, void *stream) {
+    const void *xs[2] = {k_x, v_x};
+    const void *cbs[2] = {k_codebook, v_codebook};
+    uint8_t *idx[2] = {k_index, v_index};
+    return encode_tensors(c, 2, xs, x_strides, n_tokens, cbs, idx, seq, first_token, stream);
 }
 
 lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q,

@@ -21,8 +21,8 @@ LVQ_F32, LVQ_BF16 = 0, 1
 LVQ_MAX_SPLITS = 64
 N_CODES = 256
 
-EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_decode_attn", "lvq_decode_splits",
-           "lvq_status_string")
+EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
+           "lvq_decode_splits", "lvq_status_string")
 
 
 class LoopVQError(RuntimeError):
@@ -100,6 +100,9 @@ def library() -> ctypes.CDLL:
         lib.lvq_cache_layout.argtypes = [cfgp, ctypes.POINTER(_Layout)]
         lib.lvq_encode.restype = i32
         lib.lvq_encode.argtypes = [cfgp, vp, ctypes.POINTER(i64), i64, vp, vp, i32, i64, vp]
+        lib.lvq_encode_kv.restype = i32
+        lib.lvq_encode_kv.argtypes = [cfgp, vp, vp, ctypes.POINTER(i64), i64, vp, vp, vp, vp,
+                                      i32, i64, vp]
         lib.lvq_decode_attn.restype = i32
         lib.lvq_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_float, vp, u64, vp, vp]
@@ -167,20 +170,44 @@ def lvq_encode(cfg: Config, x: torch.Tensor, codebook: torch.Tensor, index_cache
     model; any element strides with contiguous channels) into rows
     ``[first_token, first_token + n)`` of sequence ``seq`` of every group."""
     lay = lvq_cache_layout(cfg)
-    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
-        raise ValueError("x must be a bf16 device tensor")
-    if x.dim() != 4 or tuple(x.shape[1:]) != (cfg.kv_heads, cfg.loops, cfg.head_dim):
-        raise ValueError(f"x: expected [n][{cfg.kv_heads}][{cfg.loops}][{cfg.head_dim}]")
-    if x.stride(3) != 1:
-        raise ValueError("x: channels must be contiguous")
+    xp = _encode_input(cfg, x, "x")
     strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
     cbp = _dev_ptr(codebook, "codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"])
     ip = _dev_ptr(index_cache, "index_cache", torch.uint8, lay["k_index"]["shape"])
-    st = library().lvq_encode(ctypes.byref(cfg.c()), ctypes.c_void_p(x.data_ptr()), strides,
-                              int(x.shape[0]), cbp, ip, int(seq), int(first_token),
-                              _stream(stream))
+    st = library().lvq_encode(ctypes.byref(cfg.c()), xp, strides, int(x.shape[0]), cbp, ip,
+                              int(seq), int(first_token), _stream(stream))
     if st != LVQ_OK:
         raise LoopVQError("lvq_encode", st)
+
+
+def _encode_input(cfg: Config, x: torch.Tensor, name: str):
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda" or x.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be a bf16 device tensor")
+    if x.dim() != 4 or tuple(x.shape[1:]) != (cfg.kv_heads, cfg.loops, cfg.head_dim):
+        raise ValueError(f"{name}: expected [n][{cfg.kv_heads}][{cfg.loops}][{cfg.head_dim}]")
+    if x.stride(3) != 1:
+        raise ValueError(f"{name}: channels must be contiguous")
+    return ctypes.c_void_p(x.data_ptr())
+
+
+def lvq_encode_kv(cfg: Config, k_x: torch.Tensor, v_x: torch.Tensor, k_codebook: torch.Tensor,
+                  v_codebook: torch.Tensor, k_index: torch.Tensor, v_index: torch.Tensor,
+                  seq: int = 0, first_token: int = 0, stream=None) -> None:
+    """Encode the K and V of one run of tokens in one launch (same shapes and
+    strides for both inputs, as for a page of the bf16 window buffers)."""
+    lay = lvq_cache_layout(cfg)
+    kx, vx = _encode_input(cfg, k_x, "k_x"), _encode_input(cfg, v_x, "v_x")
+    if tuple(k_x.shape) != tuple(v_x.shape) or k_x.stride() != v_x.stride():
+        raise ValueError("k_x and v_x must have the same shape and strides")
+    strides = (ctypes.c_int64 * 3)(k_x.stride(0), k_x.stride(1), k_x.stride(2))
+    args = [_dev_ptr(k_codebook, "k_codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"]),
+            _dev_ptr(v_codebook, "v_codebook", cfg.torch_codebook_dtype, lay["v_codebook"]["shape"]),
+            _dev_ptr(k_index, "k_index", torch.uint8, lay["k_index"]["shape"]),
+            _dev_ptr(v_index, "v_index", torch.uint8, lay["v_index"]["shape"])]
+    st = library().lvq_encode_kv(ctypes.byref(cfg.c()), kx, vx, strides, int(k_x.shape[0]), *args,
+                                 int(seq), int(first_token), _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_encode_kv", st)
 
 
 def lvq_decode_attn(cfg: Config, loop_step: int, q: torch.Tensor, ctx_len: torch.Tensor,

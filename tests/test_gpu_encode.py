@@ -233,6 +233,41 @@ def test_strided_input_from_window_buffer(lv):
     _assert_same(got, ref, "strided")
 
 
+@pytest.mark.parametrize("n", [8, 300])
+def test_encode_kv_one_launch(lv, n):
+    """lvq_encode_kv (K and V of a page in one launch, here from the strided
+    window buffers) writes exactly what two lvq_encode calls and the oracle
+    write, on both sides of the short-run switch."""
+    _note(f"encode_kv n={n}")
+    H, d, Tc, G, B = 2, 128, 4, 16, 2
+    W = max(320, n)
+    kwin = synth.loop_correlated_kv(B * W, H, Tc, d, seed=62).view(B, W, H, Tc, d)
+    vwin = synth.loop_correlated_kv(B * W, H, Tc, d, seed=63).view(B, W, H, Tc, d)
+    kwin = kwin.permute(0, 3, 2, 1, 4).contiguous().cuda()       # [B][Tc][H][W][d]
+    vwin = vwin.permute(0, 3, 2, 1, 4).contiguous().cuda()
+    kcb = synth.codebooks(H, d, Tc, G, seed=64).cuda()
+    vcb = synth.codebooks(H, d, Tc, G, seed=65).cuda()
+    T, first = n + 400, 400
+    cfg = lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G, max_tokens=T)
+    S = d // (G // Tc)
+    kx = kwin[1][:, :, :n, :].permute(2, 1, 0, 3)                  # [n][H][Tc][d] views
+    vx = vwin[1][:, :, :n, :].permute(2, 1, 0, 3)
+    ki = torch.full((B, H, T, S), 0xAB, dtype=torch.uint8, device="cuda")
+    vi = torch.full_like(ki, 0xCD)
+    lv.lvq_encode_kv(cfg, kx, vx, kcb, vcb, ki, vi, 1, first)
+    ki2, vi2 = torch.full_like(ki, 0xAB), torch.full_like(vi, 0xCD)
+    lv.lvq_encode(cfg, kx, kcb, ki2, 1, first)
+    lv.lvq_encode(cfg, vx, vcb, vi2, 1, first)
+    torch.cuda.synchronize()
+    assert torch.equal(ki, ki2) and torch.equal(vi, vi2)
+    ref_k = _oracle_encode(kx.cpu().contiguous(), kcb.cpu(), H, d, Tc, G, T=T, B=B, seq=1,
+                           first=first, fill=0xAB)
+    ref_v = _oracle_encode(vx.cpu().contiguous(), vcb.cpu(), H, d, Tc, G, T=T, B=B, seq=1,
+                           first=first, fill=0xCD)
+    _assert_same(ki.cpu().numpy(), ref_k, "encode_kv K")
+    _assert_same(vi.cpu().numpy(), ref_v, "encode_kv V")
+
+
 def test_placement_and_untouched_rows(lv):
     _note("placement")
     H, d, Tc, G = 2, 64, 4, 16
