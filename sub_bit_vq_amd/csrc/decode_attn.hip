@@ -851,61 +851,95 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // The merger: every other workgroup of (b, h) has started (and will
     // publish); poll their pairs (slot `split` is this workgroup's own).
-    if (tid >= D) return;
+    // Threads below D own a channel; at least 32 take part (the per-slot
+    // m and l pairs are read by lanes 0..31).
+    if (tid >= (D > 32 ? D : 32)) return;
+    const int ch = tid < D ? tid : 0;
     float Mg = lt > 0.f ? M : -INFINITY;
     float num = o, den = lt;
     bool failed = false;
+    // A poll reads this channel of every slot of a chunk, and one (m or l)
+    // pair per lane: lane i of a 32-lane half reads m of slot i (i < 16) or l
+    // of slot i - 16.  Two polls are kept in flight, so the last partial is
+    // seen about half a round trip after it lands rather than one.
+    struct Poll {
+        uint64_t po[kMergeChunk];
+        uint64_t ml;
+    };
+    const int hl = tid & 31;
     for (int c0 = 0; c0 < n; c0 += kMergeChunk) {
-        uint64_t po[kMergeChunk], pm[kMergeChunk], pl[kMergeChunk];
-        int poll = 0;
-        while (true) {
+        auto issue = [&](Poll &pp) {
 #pragma unroll
             for (int i = 0; i < kMergeChunk; ++i) {
                 const size_t sl = (size_t)min(c0 + i, n - 1) * (D + 2);
-                po[i] = __hip_atomic_load(&parts[sl + 2 + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                pm[i] = __hip_atomic_load(&parts[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                pl[i] = __hip_atomic_load(&parts[sl + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pp.po[i] = __hip_atomic_load(&parts[sl + 2 + ch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            // branch-free: a slot counts if it exists and is not this workgroup's
+            const size_t sl = (size_t)min(c0 + (hl & 15), n - 1) * (D + 2);
+            pp.ml = __hip_atomic_load(&parts[sl + (hl >> 4)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        // branch-free: a slot counts if it exists and is not this workgroup's
+        auto current = [&](const Poll &pp) {
             uint32_t ok = 1u;
 #pragma unroll
             for (int i = 0; i < kMergeChunk; ++i) {
                 const uint32_t want = (uint32_t)(c0 + i < n) & (uint32_t)(c0 + i != split);
-                const uint32_t cur = (uint32_t)((uint32_t)(po[i] >> 32) == tag) &
-                                     (uint32_t)((uint32_t)(pm[i] >> 32) == tag) &
-                                     (uint32_t)((uint32_t)(pl[i] >> 32) == tag);
-                ok &= cur | (want ^ 1u);
+                ok &= (uint32_t)((uint32_t)(pp.po[i] >> 32) == tag) | (want ^ 1u);
             }
-            if (__all(ok != 0u)) break;
-            if (++poll >= kMaxPolls) {
+            const int si = c0 + (hl & 15);
+            const uint32_t want = (uint32_t)(si < n) & (uint32_t)(si != split);
+            ok &= (uint32_t)((uint32_t)(pp.ml >> 32) == tag) | (want ^ 1u);
+            return __all(ok != 0u);
+        };
+        // merge a chunk from the poll that saw every pair current (only its
+        // registers are read, so the other poll's loads need not land)
+        auto merge = [&](const Poll &pp) {
+            float mi[kMergeChunk], li[kMergeChunk];
+            float mc = Mg;
+            const uint32_t mlv = (uint32_t)pp.ml;
+#pragma unroll
+            for (int i = 0; i < kMergeChunk; ++i) {
+                const float lraw = __uint_as_float(__builtin_amdgcn_readlane(mlv, 16 + i));
+                const float mraw = __uint_as_float(__builtin_amdgcn_readlane(mlv, i));
+                const bool use = (c0 + i < n) & (c0 + i != split) & (lraw > 0.f);
+                li[i] = use ? lraw : 0.f;
+                mi[i] = use ? mraw : -INFINITY;
+                mc = fmaxf(mc, mi[i]);
+            }
+            if (mc > Mg) {                           // Mg = -inf gives 0 * 0
+                const float sc = Mg == -INFINITY ? 0.f : ex2(Mg - mc);
+                num *= sc;
+                den *= sc;
+                Mg = mc;
+            }
+#pragma unroll
+            for (int i = 0; i < kMergeChunk; ++i) {
+                const float e = li[i] > 0.f ? ex2(mi[i] - Mg) : 0.f;
+                num += __uint_as_float((uint32_t)pp.po[i]) * e;
+                den += li[i] * e;
+            }
+        };
+        Poll pa, pb;
+        issue(pa);
+        int poll = 0;
+        while (true) {
+            issue(pb);
+            if (current(pa)) {
+                merge(pa);
+                break;
+            }
+            issue(pa);
+            if (current(pb)) {
+                merge(pb);
+                break;
+            }
+            poll += 2;
+            if (poll >= kMaxPolls) {
                 failed = true;
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
-        }
-        float mi[kMergeChunk], li[kMergeChunk];
-        float mc = Mg;
-#pragma unroll
-        for (int i = 0; i < kMergeChunk; ++i) {
-            const bool use = (c0 + i < n) & (c0 + i != split) & (__uint_as_float((uint32_t)pl[i]) > 0.f);
-            li[i] = use ? __uint_as_float((uint32_t)pl[i]) : 0.f;
-            mi[i] = use ? __uint_as_float((uint32_t)pm[i]) : -INFINITY;
-            mc = fmaxf(mc, mi[i]);
-        }
-        if (mc > Mg) {                               // Mg = -inf gives 0 * 0
-            const float sc = Mg == -INFINITY ? 0.f : ex2(Mg - mc);
-            num *= sc;
-            den *= sc;
-            Mg = mc;
-        }
-#pragma unroll
-        for (int i = 0; i < kMergeChunk; ++i) {
-            const float e = li[i] > 0.f ? ex2(mi[i] - Mg) : 0.f;
-            num += __uint_as_float((uint32_t)po[i]) * e;
-            den += li[i] * e;
         }
     }
-    outp[tid] = failed ? NAN : (den > 0.f ? num / den : 0.f);
+    if (tid < D) outp[tid] = failed ? NAN : (den > 0.f ? num / den : 0.f);
     if (tid == 0 && n > 1)
         __hip_atomic_store(ticket, (epoch + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
