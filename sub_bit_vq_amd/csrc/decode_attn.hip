@@ -679,9 +679,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int s0 = sep ? 0 : (int)((int64_t)W * split / n_split);
     const int s1 = sep ? (split == n_split - 1 ? W : 0) : (int)((int64_t)W * (split + 1) / n_split);
     using Win = WindowPass<S, CG, CB>;
+    // With at most 4 channels per sub-vector step a second pass's rows fit
+    // the registers: pass p + 1 is in flight while pass p is folded.
+    constexpr bool kWinDB = CG <= 4;
+    constexpr int WP = kWaves * TPW;             // window slots per pass
     int wslot = s0 + wave;
-    Win win;
+    Win win, win2;
     win.load(kw, vw, wslot + kWaves * tk, s1, ln);
+    if constexpr (kWinDB) {
+        if (wslot + WP < s1) win2.load(kw, vw, wslot + WP + kWaves * tk, s1, ln);
+    }
 
     const int vq0 = n_sink + split * a.chunk;
     IndexRows ir0;                              // rows up to the end of the split's chunk
@@ -711,10 +718,22 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         if (vq_wg) stg.finish(qs, smem);
         __syncthreads();
     }
-    while (wslot < s1) {                         // wave-uniform
-        win.fold(qs, st, r, w, n_sink, n_recent);
-        wslot += kWaves * TPW;
-        if (wslot < s1) win.load(kw, vw, wslot + kWaves * tk, s1, ln);
+    if constexpr (kWinDB) {
+        while (wslot < s1) {                     // wave-uniform
+            win.fold(qs, st, r, w, n_sink, n_recent);
+            wslot += WP;
+            if (wslot + WP < s1) win.load(kw, vw, wslot + WP + kWaves * tk, s1, ln);
+            if (wslot >= s1) break;
+            win2.fold(qs, st, r, w, n_sink, n_recent);
+            wslot += WP;
+            if (wslot + WP < s1) win2.load(kw, vw, wslot + WP + kWaves * tk, s1, ln);
+        }
+    } else {
+        while (wslot < s1) {                     // wave-uniform
+            win.fold(qs, st, r, w, n_sink, n_recent);
+            wslot += WP;
+            if (wslot < s1) win.load(kw, vw, wslot + kWaves * tk, s1, ln);
+        }
     }
     if constexpr (kWindowFirst) {
         if (vq_wg) stg.finish(qs, smem);
