@@ -319,14 +319,30 @@ struct Stage {
         for (int u = 0; u < Sh::UPT; ++u) {
             const int e0 = (tid + u * kThreads) * Sh::EPU;   // first entry of the unit
             const int k = e0 / S, j0 = e0 % S;
+            float accs[Sh::EPU];
 #pragma unroll
             for (int e = 0; e < Sh::EPU; ++e) {
                 const int j = j0 + e;
                 float acc = 0.f;
 #pragma unroll
                 for (int c = 0; c < CG; ++c) acc += qs[j * CG + c] * elem(kw[u], e * CG + c);
+                accs[e] = acc;
+            }
+            // a unit's entries are adjacent in the row: written together
 #pragma unroll
-                for (int cp = 0; cp < Sh::KCOP; ++cp) lutk[k * 64 + S * cp + j] = acc;
+            for (int cp = 0; cp < Sh::KCOP; ++cp) {
+                float *row = lutk + k * 64 + S * cp + j0;
+                if constexpr (Sh::EPU % 4 == 0) {
+#pragma unroll
+                    for (int e = 0; e < Sh::EPU; e += 4)
+                        *reinterpret_cast<float4 *>(row + e) = make_float4(accs[e], accs[e + 1], accs[e + 2], accs[e + 3]);
+                } else if constexpr (Sh::EPU % 2 == 0) {
+#pragma unroll
+                    for (int e = 0; e < Sh::EPU; e += 2)
+                        *reinterpret_cast<float2 *>(row + e) = make_float2(accs[e], accs[e + 1]);
+                } else {
+                    row[0] = accs[0];
+                }
             }
             // value entries of the unit, converted, into every replica of row k
             uint32_t o[UW];
