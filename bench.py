@@ -216,6 +216,23 @@ def decode_kernel_time_ms(setup, torch, n=64, reps=8):
     return a.elapsed_time(b) / (n * reps)
 
 
+def prefill_encode_time_ms(lv, synth, torch, setup, n=10):
+    """Mean duration of one 32768-token prefill encode (one tensor): HIP events
+    around ``n`` back-to-back launches on the current stream, after ten
+    untimed ones (the clock ramps up over the first few)."""
+    enc = PrefillEncode(lv, synth, torch, setup)
+    for _ in range(10):
+        enc.run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        enc.run()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def cpu_baseline(setup, torch, budget_s=15.0):
     """The C oracle on a bounded sample of the same workload: whole decode
     calls (all heads, loop step 0) repeated for about ``budget_s`` seconds, and
@@ -380,6 +397,13 @@ def main():
     bpl = cache_bytes(setup.Hk, setup.d, setup.Tc, setup.G, setup.lengths)
     achieved = bpl / (mean_ms / 1e3) / 1e9
     log(f"decode launch: mean {mean_ms * 1e3:.2f} us, {achieved:.0f} GB/s on {bpl} cache bytes")
+
+    if setup.B == 1:
+        enc_ms = prefill_encode_time_ms(lv, synth, torch, setup)
+        enc_bytes = PrefillEncode.N * setup.Hk * setup.Tc * setup.d * 2 + \
+            PrefillEncode.N * setup.Hk * (setup.d // (setup.G // setup.Tc))
+        log(f"prefill encode ({PrefillEncode.N} tokens, one tensor): mean {enc_ms * 1e3:.1f} us, "
+            f"{enc_bytes / (enc_ms / 1e3) / 1e9:.0f} GB/s on {enc_bytes} bytes")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch)
     rec = {
