@@ -56,9 +56,9 @@
 namespace lvq {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
-constexpr int kUnroll = 4;                     // token passes per batch
+constexpr int kUnroll = kDecodeUnroll;         // token passes per batch
 constexpr float kPScale = 16384.f;             // p' = p * 2^14 (normal in fp16 down to p ~ 4e-9)
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMergeChunk = 16;                // partial slots loaded per poll
@@ -111,6 +111,7 @@ struct Shape {
     static_assert(UPT * EPU * kThreads == S * 256, "staging tiles the tables");
     static_assert(kWaves * TPW * D * 4 <= kTabBytes, "the lane dump fits the tables");
     static_assert(kThreads % D == 0 && TPW % G == 0, "reduction tiling");
+    static_assert(kWaves * TPW * kUnroll == decode_batch_tokens(S), "the host plans with this batch");
 };
 
 struct Windows {

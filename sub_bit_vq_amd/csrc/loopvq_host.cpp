@@ -52,36 +52,54 @@ int64_t max_vq_tokens(const lvq_config *c, int32_t max_ctx_len, bool exact_windo
     return v > 0 ? v : 0;
 }
 
-// Workgroups per (b, h) and where the bf16 window slots go.  One decode
-// workgroup fills a compute unit's LDS, so aim for one workgroup per CU (256
-// on MI355X), keep token splits at least 512 tokens long, and cut long ragged
-// contexts into chunks of at most ~8K tokens so that the longest sequences
-// leave no tail.  When the whole grid fits the chip at once, one extra
-// workgroup per (b, h) takes every window slot (it needs no codebook tables,
-// and the token splits skip the window pass); otherwise the window slots are
-// spread over the token splits, which costs less compute-unit time.
+// Workgroups per (b, h) and where the bf16 window slots go, from a cost model
+// of the launch.  One decode workgroup fills a compute unit's LDS, so the grid
+// runs in ceil(B*H*n / 256) rounds on MI355X's 256 CUs.  A workgroup costs a
+// fixed start-up (codebook staging and first loads under a loaded memory
+// system, about kFixedBatches token batches' worth) plus its VQ tokens, which
+// it folds in whole batches of decode_batch_tokens(S), plus its share of the
+// bf16 window rows (a window token reads as many bytes as 8 VQ tokens).
+// Every sequence is costed at the longest one's length.  When a grid with two
+// workgroups per (b, h) fits the chip, only one-round grids are considered,
+// and one extra workgroup per (b, h) takes every window slot (it needs no
+// codebook tables, and it merges the others' partials while they finish).
+// Splits stay at least 512 tokens long; ties go to fewer workgroups.
 struct Splits {
     int32_t n;          // workgroups per (b, h)
     bool window_wg;     // the last one takes every window slot
 };
 constexpr int64_t kTargetGroups = 256;
+constexpr int64_t kFixedBatches = 6;
 
 Splits choose_splits(const lvq_config *c, int64_t max_vq) {
     if (max_vq <= 0) return {1, false};
     const int64_t bh = (int64_t)c->batch * c->n_heads;
-    int64_t want = c->decode_splits;
-    if (want == 0) {
-        int64_t vq = (kTargetGroups + bh - 1) / bh - 1;
-        const int64_t by_len = (max_vq + 511) / 512;
-        if (vq > by_len) vq = by_len;
-        const int64_t by_chunk = (max_vq + 8191) / 8192;
-        if (vq < by_chunk) vq = by_chunk;
-        if (vq < 1) vq = 1;
-        want = bh * (vq + 1) <= kTargetGroups ? vq + 1 : vq;
+    if (c->decode_splits != 0) {
+        int64_t want = c->decode_splits;
+        if (want < 1) want = 1;
+        if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
+        return {(int32_t)want, want > 1 && bh * want <= kTargetGroups};
     }
-    if (want < 1) want = 1;
-    if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
-    return {(int32_t)want, want > 1 && bh * want <= kTargetGroups};
+    const int S = c->head_dim / (c->group / c->loop_steps);
+    const int64_t step = lvq::decode_batch_tokens(S);
+    const int64_t W = (int64_t)c->n_sink + c->n_recent;
+    int64_t best_cost = -1, best_n = 1;
+    // small grids: one round with a window workgroup per (b, h)
+    const bool win = bh * 2 <= kTargetGroups;
+    for (int64_t n_vq = 1; n_vq < LVQ_MAX_SPLITS; ++n_vq) {
+        const int64_t chunk = (max_vq + n_vq - 1) / n_vq;
+        if (n_vq > 1 && chunk < 512) break;
+        if (win && bh * (n_vq + 1) > kTargetGroups) break;
+        const int64_t n = win ? n_vq + 1 : n_vq;
+        const int64_t rounds = (bh * n + kTargetGroups - 1) / kTargetGroups;
+        const int64_t per_wg = ((chunk + step - 1) / step + kFixedBatches) * step + (win ? 0 : 8 * W / n);
+        const int64_t cost = rounds * per_wg;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_n = n;
+        }
+    }
+    return {(int32_t)best_n, win && best_n > 1};
 }
 
 // Encode n tensors of one shape (1: lvq_encode; 2: the K and V of a page in one

@@ -132,14 +132,20 @@ def test_layout_rejects_bad_config(bad):
 
 def test_decode_splits():
     cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
-    # grid within the chip: VQ token chunks + one window workgroup per (b, h)
-    assert lv.lvq_decode_splits(cfg, 32768) == 16        # 15 chunks + windows, 256 workgroups
+    # Grid within the chip: VQ token chunks + one window workgroup per (b, h),
+    # the fewest chunks that keep the fewest 512-token batches per workgroup:
+    # 32448 VQ tokens in 13 chunks of 2496 take 5 batches each, as 15 chunks of
+    # 2176 would; 12 chunks of 2704 would take 6.
+    assert lv.lvq_decode_splits(cfg, 32768) == 14
     assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded: windows only
-    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 4    # 3 chunks of <= 512 tokens + windows
+    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 3    # 2 chunks of 550 (one batch less than 1)
+    assert lv.lvq_decode_splits(cfg, 320 + 600) == 2     # splits stay >= 512 tokens
     assert lv.lvq_decode_splits(cfg, 40000) == 0         # beyond max_tokens
-    # larger grids: windows spread over the chunks
+    # Larger grids (1024 heads over 256 CUs): every split costs a workgroup
+    # start-up in every round, so one workgroup per (b, h) takes its whole
+    # context and its window slots.
     cfg3 = _cfg(*WORKLOADS["batch64_ragged_0p5bit"])
-    assert lv.lvq_decode_splits(cfg3, 18432) == 3        # chunks of at most ~8K tokens
+    assert lv.lvq_decode_splits(cfg3, 18432) == 1
     assert lv.lvq_decode_splits(_cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, decode_splits=7),
                                 32768) == 7
 
