@@ -896,8 +896,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     bool failed = false;
     // A poll reads this channel of every slot of a chunk, and one (m or l)
     // pair per lane: lane i of a 32-lane half reads m of slot i (i < 16) or l
-    // of slot i - 16.  Two polls are kept in flight, so the last partial is
-    // seen about half a round trip after it lands rather than one.
+    // of slot i - 16.  One poll is in flight at a time: a second one, issued
+    // half a round trip later, sees the last partial sooner, but the wave
+    // cannot end before its loads land, so the call would not end sooner.
     struct Poll {
         uint64_t po[kMergeChunk];
         uint64_t ml;
@@ -926,8 +927,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             ok &= (uint32_t)((uint32_t)(pp.ml >> 32) == tag) | (want ^ 1u);
             return __all(ok != 0u);
         };
-        // merge a chunk from the poll that saw every pair current (only its
-        // registers are read, so the other poll's loads need not land)
+        // merge a chunk from the poll that saw every pair current
         auto merge = [&](const Poll &pp) {
             float mi[kMergeChunk], li[kMergeChunk];
             float mc = Mg;
@@ -954,22 +954,15 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                 den += li[i] * e;
             }
         };
-        Poll pa, pb;
-        issue(pa);
+        Poll pa;
         int poll = 0;
         while (true) {
-            issue(pb);
+            issue(pa);
             if (current(pa)) {
                 merge(pa);
                 break;
             }
-            issue(pa);
-            if (current(pb)) {
-                merge(pb);
-                break;
-            }
-            poll += 2;
-            if (poll >= kMaxPolls) {
+            if (++poll >= kMaxPolls) {
                 failed = true;
                 break;
             }
