@@ -968,7 +968,11 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             }
         }
     }
-    if (tid < D) outp[tid] = failed ? NAN : (den > 0.f ? num / den : 0.f);
+    // (a timed-out merge writes quiet-NaN bits: an integer select, so that the
+    // no-NaN arithmetic this file is built with cannot fold it away)
+    if (tid < D)
+        reinterpret_cast<uint32_t *>(outp)[tid] =
+            failed ? 0x7fc00000u : __float_as_uint(den > 0.f ? num / den : 0.f);
     if (tid == 0 && n > 1)
         __hip_atomic_store(ticket, (epoch + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
