@@ -258,6 +258,16 @@ def cpu_baseline(setup, torch, budget_s=15.0):
                   loop_steps=setup.Tc, group=setup.G, threads=threads)
     t_enc = time.perf_counter() - t1
     t_step = PAGE * setup.Tc * t_dec + 2 * t_enc
+    # the same on one core: one whole decode call and the page encode
+    t2 = time.perf_counter()
+    oracle.decode_attn(loop_step=0, q=q, ctx_len=[setup.L] * setup.B, k_index=kidx,
+                       v_index=vidx, k_codebook=kcb, v_codebook=vcb, k_window=kw,
+                       v_window=vw, n_sink=N_SINK, n_recent=N_RECENT, group=setup.G, threads=1)
+    t_dec1 = time.perf_counter() - t2
+    t3 = time.perf_counter()
+    oracle.encode(setup.page_k.cpu(), kcb, n_heads=setup.Hk, head_dim=setup.d,
+                  loop_steps=setup.Tc, group=setup.G, threads=1)
+    t_enc1 = time.perf_counter() - t3
     return {
         "value": setup.tokens_steps_per_step / t_step,
         "unit": "ctx-token*loop-steps/s",
@@ -267,7 +277,34 @@ def cpu_baseline(setup, torch, budget_s=15.0):
                    f"{t_dec * 1e3:.1f} ms each) and one 8-token page encode ({t_enc * 1e3:.1f} ms, "
                    f"counted for K and V), combined as one step of 32 decodes + 2 encodes; "
                    f"OpenMP threads {threads} of {os.cpu_count()} logical CPUs"),
+        "value_1core": setup.tokens_steps_per_step / (PAGE * setup.Tc * t_dec1 + 2 * t_enc1),
+        "sample_1core": (f"one whole decode call ({t_dec1 * 1e3:.0f} ms) and one page encode "
+                         f"({t_enc1 * 1e3:.1f} ms) on one thread, combined the same way"),
     }
+
+
+def stream_rates(torch, reps=10):
+    """HBM rates of plain torch kernels on this GPU, for reference beside the
+    roofline: a read-bound reduction over 1 GiB of fp32 (bytes read per
+    second) and a 512 MiB device copy (bytes read + written per second)."""
+    big = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    src = torch.ones(1 << 29, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("read_GBps", lambda: big.sum(), big.numel() * 4),
+                             ("copy_GBps", lambda: dst.copy_(src), 2 * src.numel())):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del big, src, dst
+    return out
 
 
 def loop_axis_experiment(lv, synth, torch, heads=8, d=128, n_train=8192, n_test=2048,
@@ -405,6 +442,10 @@ def main():
         log(f"prefill encode ({PrefillEncode.N} tokens, one tensor): mean {enc_ms * 1e3:.1f} us, "
             f"{enc_bytes / (enc_ms / 1e3) / 1e9:.0f} GB/s on {enc_bytes} bytes")
 
+    streams = stream_rates(torch)
+    cb_bytes = 2 * setup.Hk * 256 * setup.d * 2     # the K and V slices of step t, bf16
+    log(f"stream rates on this GPU: read {streams['read_GBps']:.0f} GB/s, copy {streams['copy_GBps']:.0f} GB/s")
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch)
     rec = {
         "metric": METRIC,
@@ -440,6 +481,13 @@ def main():
             "traffic": counters_traffic(args.workload),
             "bytes_per_launch": bpl,
             "mean_launch_us": mean_ms * 1e3,
+            # secondary: with the codebook slices of step t counted, and
+            # against the HBM rates of plain torch kernels measured here (a
+            # device copy moves the most bytes per second of the two)
+            "achieved_with_codebook_slices": (bpl + cb_bytes) / (mean_ms / 1e3) / 1e9,
+            "measured_read_GBps": streams["read_GBps"],
+            "measured_copy_GBps": streams["copy_GBps"],
+            "frac_of_measured_copy": achieved / streams["copy_GBps"],
         },
         "cpu_baseline": cpu,
     }
