@@ -194,10 +194,12 @@ def spin_cycles_for(torch, ms):
     return int(per_ms * ms)
 
 
-def decode_kernel_time_ms(setup, torch, n=64, reps=8):
+def decode_kernel_time_ms(setup, torch, n=64, reps=8, spread=None):
     """Mean duration of one decode launch: HIP events on the launch stream
     around replays of a graph of ``n`` back-to-back launches (rotating over the
-    cache copies), so the interval holds launches and nothing else."""
+    cache copies), so the interval holds launches and nothing else.  With a
+    dict ``spread``, each replay is also timed on its own and the median and
+    minimum per-launch times of the replays are stored there."""
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
@@ -207,13 +209,17 @@ def decode_kernel_time_ms(setup, torch, n=64, reps=8):
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         graph.replay()
-    b.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / (n * reps)
+    if spread is not None:
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) / n for i in range(reps))
+        spread["median_ms"] = per[len(per) // 2] if reps % 2 else 0.5 * (per[reps // 2 - 1] + per[reps // 2])
+        spread["min_ms"] = per[0]
+    return ev[0].elapsed_time(ev[reps]) / (n * reps)
 
 
 def prefill_encode_time_ms(lv, synth, torch, setup, n=10):
@@ -430,10 +436,12 @@ def main():
     value = setup.tokens_steps_per_step / (ms_per_step / 1e3)
     log(f"{steps} steps in {ms:.3f} ms ({ms_per_step * 1e3:.1f} us/step)")
 
-    mean_ms = decode_kernel_time_ms(setup, torch)
+    spread = {}
+    mean_ms = decode_kernel_time_ms(setup, torch, spread=spread)
     bpl = cache_bytes(setup.Hk, setup.d, setup.Tc, setup.G, setup.lengths)
     achieved = bpl / (mean_ms / 1e3) / 1e9
-    log(f"decode launch: mean {mean_ms * 1e3:.2f} us, {achieved:.0f} GB/s on {bpl} cache bytes")
+    log(f"decode launch: mean {mean_ms * 1e3:.2f} us (replay median {spread['median_ms'] * 1e3:.2f}, "
+        f"min {spread['min_ms'] * 1e3:.2f}), {achieved:.0f} GB/s on {bpl} cache bytes")
 
     if setup.B == 1:
         enc_ms = prefill_encode_time_ms(lv, synth, torch, setup)
@@ -481,6 +489,8 @@ def main():
             "traffic": counters_traffic(args.workload),
             "bytes_per_launch": bpl,
             "mean_launch_us": mean_ms * 1e3,
+            "median_launch_us": spread["median_ms"] * 1e3,     # over the timed replays
+            "min_launch_us": spread["min_ms"] * 1e3,
             # secondary: with the codebook slices of step t counted, and
             # against the HBM rates of plain torch kernels measured here (a
             # device copy moves the most bytes per second of the two)
