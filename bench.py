@@ -313,6 +313,93 @@ def stream_rates(torch, reps=10):
     return out
 
 
+def layers_experiment(lv, synth, torch, workload, n_layers, reps=8, n_calls=16):
+    """Decode attention of ``n_layers`` layers per launch (lvq_decode_attn_layers)
+    against one layer per launch, on the same caches: each layer is one of
+    the workload's rotated cache copies with its own codebooks and query;
+    sets of layers rotate so that every call reads cold caches.  Prints one
+    JSON line."""
+    B, H, d, Tc, G, L = WORKLOADS[workload][:6]
+    Hk = WORKLOADS[workload][6] if len(WORKLOADS[workload]) > 6 else H
+    T = (max(synth.ragged_lengths(B, seed=1003)) if L == "ragged" else L) + PAGE
+    lay0 = lv.lvq_cache_layout(lv.Config(batch=B, n_heads=H, head_dim=d, loop_steps=Tc, group=G,
+                                         max_tokens=T, n_kv_heads=Hk if Hk != H else 0))
+    per_copy = 2 * lay0["k_index"]["bytes"] + 2 * lay0["k_window"]["bytes"]
+    sets = max(2, math.ceil(2 * LLC_BYTES / (per_copy * n_layers)))
+    setup = Setup(lv, synth, torch, workload, sets * n_layers)
+    dev = torch.device("cuda")
+    lay = lv.lvq_cache_layout(setup.cfg)
+    layers = []
+    for i, c in enumerate(setup.copies):
+        layers.append(dict(
+            q=setup.q[0, i % setup.Tc].clone(), k_index=c["k_index"], v_index=c["v_index"],
+            k_codebook=synth.codebooks(setup.Hk, setup.d, setup.Tc, setup.G, 9000 + 2 * i, device=dev),
+            v_codebook=synth.codebooks(setup.Hk, setup.d, setup.Tc, setup.G, 9001 + 2 * i, device=dev),
+            k_window=c["k_window"], v_window=c["v_window"],
+            out=torch.empty(lay["output"]["shape"], dtype=torch.float32, device=dev)))
+    ws = torch.zeros(n_layers * lay["workspace_bytes"], dtype=torch.uint8, device=dev)
+
+    def timed(call):
+        """mean per-call time over graph replays of n_calls calls"""
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for k in range(n_calls):
+                call(k)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * n_calls)
+
+    def multi(k):
+        s = (k % sets) * n_layers
+        lv.lvq_decode_attn_layers(setup.cfg, k % setup.Tc, layers[s:s + n_layers], setup.ctx,
+                                  setup.L, ws)
+
+    def single(k):
+        ly = layers[k % len(layers)]
+        lv.lvq_decode_attn(setup.cfg, k % setup.Tc, ly["q"], setup.ctx, setup.L, ly["k_index"],
+                           ly["v_index"], ly["k_codebook"], ly["v_codebook"], ly["k_window"],
+                           ly["v_window"], ws, ly["out"])
+
+    for _ in range(3):
+        multi(0)
+        single(0)
+    torch.cuda.synchronize()
+    ms_multi = timed(multi)
+    ms_single = timed(single)
+    bpl = cache_bytes(setup.Hk, setup.d, setup.Tc, setup.G, setup.lengths)
+    per_layer_us = ms_multi * 1e3 / n_layers
+    achieved = bpl / (per_layer_us * 1e-6) / 1e9
+    log(f"{n_layers} layers per launch: {ms_multi * 1e3:.2f} us per call, {per_layer_us:.2f} us "
+        f"per layer ({achieved:.0f} GB/s); one layer per launch: {ms_single * 1e3:.2f} us")
+    rec = {
+        "metric": f"VQ-KV decode attn, {n_layers} layers per launch: context-token*loop-steps/s",
+        "value": sum(setup.lengths) * n_layers / (ms_multi / 1e3),
+        "unit": "ctx-token*loop-steps/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": "fp32",
+        "data": "synthetic (seeded loop-correlated K/V encoded by the HIP encoder, N(0,1) codebooks per layer)",
+        "config": {"workload": workload, "layers_per_call": n_layers, "cache_sets": sets,
+                   "heads": setup.H, "head_dim": setup.d, "group": setup.G,
+                   "context": sum(setup.lengths)},
+        "per_call_us": ms_multi * 1e3,
+        "per_layer_us": per_layer_us,
+        "single_layer_call_us": ms_single * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "bytes_per_layer": bpl},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def loop_axis_experiment(lv, synth, torch, heads=8, d=128, n_train=8192, n_test=2048,
                          iters=8, seed=2024):
     """The equal-bits comparison of the LoopVQ project page ("Component 1 --
@@ -353,6 +440,9 @@ def main():
                     help="only run N decode launches (for rocprofv3 runs) and exit")
     ap.add_argument("--profile-encode", type=int, default=0,
                     help="only run N prefill encodes of 32768 tokens (for rocprofv3 runs) and exit")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="time lvq_decode_attn_layers with this many layers per launch "
+                         "(prints its own JSON line)")
     ap.add_argument("--loop-axis", action="store_true",
                     help="instead of the benchmark: the equal-bits loop-axis vs channel-only "
                          "k-means comparison (encoder as the assignment step); prints one JSON line")
@@ -373,6 +463,9 @@ def main():
     lv.library()
     if args.loop_axis:
         loop_axis_experiment(lv, synth, torch)
+        return
+    if args.layers:
+        layers_experiment(lv, synth, torch, args.workload, args.layers)
         return
     log(f"workload {args.workload}: setup")
     setup = Setup(lv, synth, torch, args.workload, args.rotate)

@@ -101,6 +101,7 @@ typedef struct {
 
 #define LVQ_MAX_SPLITS 64
 #define LVQ_MAX_LOOPS 64
+#define LVQ_MAX_LAYERS 4096
 #define LVQ_CODES 256
 
 typedef struct {
@@ -234,6 +235,42 @@ lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void 
                            const void *v_codebook, const void *k_window,
                            const void *v_window, float sm_scale, void *workspace,
                            uint64_t workspace_bytes, float *out, void *stream);
+
+/* The operands of one layer of lvq_decode_attn_layers: the device buffers
+ * that lvq_decode_attn takes, with the same layouts and alignments. */
+typedef struct {
+    const void *q;              /* bf16 [B][H][d]                               */
+    const uint8_t *k_index;     /* index caches of the layer                    */
+    const uint8_t *v_index;
+    const void *k_codebook;     /* codebooks of the layer                       */
+    const void *v_codebook;
+    const void *k_window;       /* bf16 window buffers of the layer             */
+    const void *v_window;
+    float *out;                 /* fp32 [B][H][d]                               */
+} lvq_decode_layer;
+
+/* lvq_decode_attn for n_layers layers that share the config, the sequence
+ * lengths and the loop step (several layers' caches attended at once, e.g.
+ * independent requests that reach the same step; one launch per 16 layers,
+ * so the launch and the split merge are paid once for all of them).  Each
+ * layer computes exactly what lvq_decode_attn computes for its buffers (the
+ * operation of the LoopVQ project page, "Serving in SGLang -- Attend from
+ * indices"); results differ from separate calls only by rounding, through
+ * the split count.
+ *
+ * layers     host array [n_layers], 1 <= n_layers <= LVQ_MAX_LAYERS; every
+ *            pointer as for lvq_decode_attn.
+ * workspace  device, >= n_layers * layout.workspace_bytes, 256-byte aligned,
+ *            zero-filled once after allocation; layer l uses the single-layer
+ *            workspace layout at workspace + l * layout.workspace_bytes, so
+ *            layer 0 and lvq_decode_attn may share one workspace.
+ * Other arguments and errors as for lvq_decode_attn (LVQ_ERR_INVALID_ARG also
+ * for n_layers outside [1, LVQ_MAX_LAYERS] or a null layers array).
+ */
+lvq_status lvq_decode_attn_layers(const lvq_config *cfg, int32_t n_layers, int32_t loop_step,
+                                  const lvq_decode_layer *layers, const int32_t *ctx_len,
+                                  const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
+                                  void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* Number of workgroups per (b, h) that lvq_decode_attn launches for
  * max_ctx_len with exact windows (vq_len == NULL); host arithmetic only; 0 on

@@ -639,9 +639,14 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // that consecutive logical workgroups (the splits of one head) share an
     // XCD and its L2, which then serves their table slices once.
     const unsigned total = gridDim.x, p = blockIdx.x;
-    const unsigned L = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
+    const unsigned Lg = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
+    // layers outermost: the workgroups of one (layer, b, h) stay consecutive
+    const unsigned per_layer = (unsigned)a.n_split * a.H * a.B;
+    const int layer = (int)(Lg / per_layer);
+    const unsigned L = Lg % per_layer;
     const int split = (int)(L % a.n_split);
     const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
+    const DecodeLayer &lp = a.layer[layer];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tk = lane / R;
     Lanes<S, CG, CB> ln;
@@ -657,18 +662,20 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const size_t bh = (size_t)b * a.H + h;             // query head: q, partials, out
     const int hk = h / a.q_per_kv;                      // KV head: caches, codebooks, windows
     const size_t bhk = (size_t)b * a.Hk + hk;
-    const CB *kcb = static_cast<const CB *>(a.kcb_t) + (size_t)hk * 256 * S * CG;
-    const CB *vcb = static_cast<const CB *>(a.vcb_t) + (size_t)hk * 256 * S * CG;
+    const CB *kcb = static_cast<const CB *>(lp.kcb_t) + (size_t)hk * 256 * S * CG;
+    const CB *vcb = static_cast<const CB *>(lp.vcb_t) + (size_t)hk * 256 * S * CG;
     const size_t wbase = (size_t)b * a.win_bstride + ((size_t)hk * W) * D;
-    const uint16_t *kw = a.kwin_t + wbase;
-    const uint16_t *vw = a.vwin_t + wbase;
-    const uint8_t *kidx = a.k_index + bhk * (size_t)t_max * S;
-    const uint8_t *vidx = a.v_index + bhk * (size_t)t_max * S;
+    const uint16_t *kw = lp.kwin_t + wbase;
+    const uint16_t *vw = lp.vwin_t + wbase;
+    const uint8_t *kidx = lp.k_index + bhk * (size_t)t_max * S;
+    const uint8_t *vidx = lp.v_index + bhk * (size_t)t_max * S;
     const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
-    uint64_t *part = a.partials + (bh * kSlots + split) * (D + 2);
-    const uint64_t *parts = a.partials + bh * kSlots * (D + 2);
-    uint32_t *ticket = a.tickets + bh;
-    float *outp = a.out + bh * D;
+    char *wsl = a.ws + (size_t)layer * a.ws_stride;
+    uint64_t *partials = reinterpret_cast<uint64_t *>(wsl);
+    uint64_t *part = partials + (bh * kSlots + split) * (D + 2);
+    const uint64_t *parts = partials + bh * kSlots * (D + 2);
+    uint32_t *ticket = reinterpret_cast<uint32_t *>(wsl + a.ws_tickets) + bh;
+    float *outp = lp.out + bh * D;
     const float scale = a.scale_log2;
     const int n_split = a.n_split;
     const bool sep = a.window_wg != 0;
@@ -676,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
-    const uint32_t qraw = a.q[bh * D + min(tid, D - 1)];
+    const uint32_t qraw = lp.q[bh * D + min(tid, D - 1)];
     // The call counter of (b, h) cannot change before this workgroup arrives,
     // so it is read now, overlapped with the prologue; it tags the partials.
     uint32_t arrival_word = 0;
@@ -985,7 +992,7 @@ constexpr bool fits() {
 
 template <int S, int CG>
 hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)a.n_split * a.H * a.B);
+    const dim3 grid((unsigned)a.n_split * a.H * a.B * a.n_layers);
     if (a.cb_bf16) {
         if constexpr (fits<S, CG, uint16_t>())
             hipLaunchKernelGGL((decode_main<S, CG, uint16_t>), grid, dim3(kThreads), 0, st, a);

@@ -30,38 +30,42 @@ inline uint64_t workspace_bytes(int64_t B, int64_t H, int64_t d) {
     return partial_bytes(B, H, d) + align_up((uint64_t)B * H * sizeof(uint32_t), 256);
 }
 
+// Operands of one layer of a decode launch, derived by the host for the
+// call's loop step.
+struct DecodeLayer {
+    const uint16_t *q;          // [B][H][d]
+    const uint8_t *k_index;     // [B][Hk][t_max][S] of the step's index group
+    const uint8_t *v_index;
+    const void *kcb_t;          // codebook slices of step t: [Hk][256][S][cg]
+    const void *vcb_t;
+    const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [Hk][W][d]
+    const uint16_t *vwin_t;
+    float *out;                 // [B][H][d]
+};
+constexpr int kMaxLayersPerLaunch = 16;
+
 struct DecodeArgs {
-    int B, H, d, Tc, cg, S, n_sink, n_recent;
+    int B, H, d, cg, S, n_sink, n_recent;
     int Hk;           // KV heads (caches, codebooks, windows)
     int q_per_kv;     // H / Hk: query head h reads KV head h / q_per_kv
     int64_t t_max;
-    int loop_step;
-    int n_split;      // workgroups per (b, h)
+    int n_split;      // workgroups per (layer, b, h)
     int window_wg;    // 1: the last workgroup of (b, h) takes every window slot
                       // and the others one VQ chunk each; 0: each takes a VQ
                       // chunk and an equal share of the window slots
     int chunk;        // VQ tokens per chunk (multiple of 64)
     int cb_bf16;
-    const uint16_t *q;          // [B][H][d]
-    const int32_t *ctx_len;     // [B]
+    int n_layers;     // layers of this launch, 1..kMaxLayersPerLaunch
+    const int32_t *ctx_len;     // [B], shared by the layers
     const int32_t *vq_len;      // [B] or null
-    const uint8_t *k_index;     // [B][Hk][t_max][S]
-    const uint8_t *v_index;
-    const void *k_cb;           // [Tc][Hk][256][S][cg]
-    const void *v_cb;
-    const uint16_t *k_win;      // [B][Tc][Hk][W][d]
-    const uint16_t *v_win;
-    float sm_scale;
-    // derived by the host for the loop step of the call
-    const void *kcb_t;          // codebook slices of step t: [Hk][256][S][cg]
-    const void *vcb_t;
-    const uint16_t *kwin_t;     // windows of step t: b * win_bstride + [Hk][W][d]
-    const uint16_t *vwin_t;
     int64_t win_bstride;        // elements between sequences of a window buffer
     float scale_log2;           // sm_scale * log2(e)
-    uint64_t *partials;         // [B][H][kSlots][d + 2] (value, tag) pairs
-    uint32_t *tickets;          // [B][H]
-    float *out;                 // [B][H][d]
+    // Workspace of layer l: the single-layer layout at ws + l * ws_stride,
+    // partials [B][H][kSlots][d + 2] (value, tag) pairs, then tickets [B][H].
+    char *ws;
+    uint64_t ws_stride;
+    uint64_t ws_tickets;        // byte offset of the tickets in a layer's workspace
+    DecodeLayer layer[kMaxLayersPerLaunch];
 };
 
 struct EncodeArgs {

@@ -3,6 +3,7 @@
 // arithmetic, so every error path returns before any HIP call.
 #include "../../include/loopvq.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -71,9 +72,9 @@ struct Splits {
 constexpr int64_t kTargetGroups = 256;
 constexpr int64_t kFixedBatches = 6;
 
-Splits choose_splits(const lvq_config *c, int64_t max_vq) {
+Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1) {
     if (max_vq <= 0) return {1, false};
-    const int64_t bh = (int64_t)c->batch * c->n_heads;
+    const int64_t bh = n_layers * c->batch * c->n_heads;
     if (c->decode_splits != 0) {
         int64_t want = c->decode_splits;
         if (want < 1) want = 1;
@@ -249,6 +250,108 @@ lvq_status lvq_encode_kv(const lvq_config *c, const void *k_x, const void *v_x,
     return encode_tensors(c, 2, xs, x_strides, n_tokens, cbs, idx, seq, first_token, stream);
 }
 
+namespace {
+
+// Every check of a decode call, then one launch per kMaxLayersPerLaunch
+// layers.  Layer l uses the single-layer workspace layout at workspace +
+// l * workspace_bytes(B, H, d).
+lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_step,
+                         const lvq_decode_layer *layers, const int32_t *ctx_len,
+                         const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
+                         void *workspace, uint64_t workspace_bytes, void *stream) {
+    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
+    if (n_layers < 1 || n_layers > LVQ_MAX_LAYERS || !layers || !ctx_len) return LVQ_ERR_INVALID_ARG;
+    if (loop_step < 0 || loop_step >= n_loops(c)) return LVQ_ERR_INVALID_ARG;
+    if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return LVQ_ERR_INVALID_ARG;
+    if (c->max_tokens < 1) return LVQ_ERR_INVALID_ARG;     // the index cache has rows
+    if (!std::isfinite(sm_scale)) return LVQ_ERR_INVALID_ARG;
+    const int cg = c->group / c->loop_steps;
+    const int S = c->head_dim / cg;
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const lvq_decode_layer &L = layers[l];
+        if (!L.q || !L.k_index || !L.v_index || !L.k_codebook || !L.v_codebook || !L.k_window ||
+            !L.v_window || !L.out)
+            return LVQ_ERR_INVALID_ARG;
+        // index rows and window rows are read with 8- or 16-byte vector loads
+        const uintptr_t ia = S >= 16 ? 16 : 8;
+        if (reinterpret_cast<uintptr_t>(L.k_index) % ia || reinterpret_cast<uintptr_t>(L.v_index) % ia)
+            return LVQ_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(L.k_window) % 16 || reinterpret_cast<uintptr_t>(L.v_window) % 16)
+            return LVQ_ERR_INVALID_ARG;
+        if (reinterpret_cast<uintptr_t>(L.k_codebook) % 16 ||
+            reinterpret_cast<uintptr_t>(L.v_codebook) % 16)
+            return LVQ_ERR_INVALID_ARG;
+    }
+    if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16))
+        return LVQ_ERR_UNSUPPORTED;
+    // the index rows of one (b, h) are addressed with 32-bit byte offsets
+    if ((int64_t)c->max_tokens * S > 0x7fffffff - 65536LL * S) return LVQ_ERR_UNSUPPORTED;
+    const uint64_t per_layer = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
+    if (!workspace || workspace_bytes / per_layer < (uint64_t)n_layers) return LVQ_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
+
+    const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
+    const int64_t Hk = kv_heads(c);
+    const size_t W = (size_t)c->n_sink + c->n_recent;
+    for (int32_t l0 = 0; l0 < n_layers; l0 += lvq::kMaxLayersPerLaunch) {
+        const int32_t nl = std::min<int32_t>(lvq::kMaxLayersPerLaunch, n_layers - l0);
+        const Splits sp = choose_splits(c, max_vq, nl);
+        const int32_t n_split = sp.n;
+        if ((int64_t)n_split * c->batch * c->n_heads * nl > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
+        const int64_t n_vq = sp.window_wg ? n_split - 1 : n_split;
+        int64_t chunk = (max_vq + n_vq - 1) / n_vq;
+        chunk = (chunk + 63) / 64 * 64;
+        if (chunk < 64) chunk = 64;
+
+        lvq::DecodeArgs a{};
+        a.B = c->batch;
+        a.H = c->n_heads;
+        a.Hk = (int)Hk;
+        a.q_per_kv = c->n_heads / a.Hk;
+        a.d = c->head_dim;
+        a.cg = cg;
+        a.S = S;
+        a.n_sink = c->n_sink;
+        a.n_recent = c->n_recent;
+        a.t_max = c->max_tokens;
+        a.n_split = n_split;
+        a.window_wg = sp.window_wg ? 1 : 0;
+        a.chunk = (int)chunk;
+        a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
+        a.n_layers = nl;
+        a.ctx_len = ctx_len;
+        a.vq_len = vq_len;
+        a.win_bstride = n_loops(c) * a.Hk * W * c->head_dim;
+        a.scale_log2 = sm_scale * 1.4426950408889634f;
+        a.ws = static_cast<char *>(workspace) + (size_t)l0 * per_layer;
+        a.ws_stride = per_layer;
+        a.ws_tickets = lvq::partial_bytes(c->batch, c->n_heads, c->head_dim);
+        // loop step r reads the index rows of group r / Tc, codebook slice r
+        // and window buffers of step r
+        const size_t grp = (size_t)(loop_step / c->loop_steps) * c->batch * Hk * c->max_tokens * S;
+        const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
+        const size_t slice = (size_t)loop_step * Hk * S * LVQ_CODES * cg * cbe;
+        const size_t wstep = (size_t)loop_step * Hk * W * c->head_dim;
+        for (int32_t i = 0; i < nl; ++i) {
+            const lvq_decode_layer &L = layers[l0 + i];
+            lvq::DecodeLayer &d = a.layer[i];
+            d.q = static_cast<const uint16_t *>(L.q);
+            d.k_index = L.k_index + grp;
+            d.v_index = L.v_index + grp;
+            d.kcb_t = static_cast<const char *>(L.k_codebook) + slice;
+            d.vcb_t = static_cast<const char *>(L.v_codebook) + slice;
+            d.kwin_t = static_cast<const uint16_t *>(L.k_window) + wstep;
+            d.vwin_t = static_cast<const uint16_t *>(L.v_window) + wstep;
+            d.out = L.out;
+        }
+        const hipError_t e = lvq::launch_decode(a, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return LVQ_ERR_HIP;
+    }
+    return LVQ_OK;
+}
+
+}  // namespace
+
 lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q,
                            const int32_t *ctx_len, const int32_t *vq_len,
                            int32_t max_ctx_len, const uint8_t *k_index,
@@ -256,94 +359,17 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
                            const void *v_codebook, const void *k_window,
                            const void *v_window, float sm_scale, void *workspace,
                            uint64_t workspace_bytes, float *out, void *stream) {
-    if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
-    if (!q || !ctx_len || !k_index || !v_index || !k_codebook || !v_codebook || !k_window ||
-        !v_window || !out)
-        return LVQ_ERR_INVALID_ARG;
-    if (loop_step < 0 || loop_step >= n_loops(c)) return LVQ_ERR_INVALID_ARG;
-    if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return LVQ_ERR_INVALID_ARG;
-    if (c->max_tokens < 1) return LVQ_ERR_INVALID_ARG;     // the index cache has rows
-    if (!std::isfinite(sm_scale)) return LVQ_ERR_INVALID_ARG;
-    // index rows and window rows are read with 8- or 16-byte vector loads
-    {
-        const int cg0 = c->group / c->loop_steps, S0 = c->head_dim / cg0;
-        const uintptr_t ia = S0 >= 16 ? 16 : 8;
-        if (reinterpret_cast<uintptr_t>(k_index) % ia || reinterpret_cast<uintptr_t>(v_index) % ia)
-            return LVQ_ERR_INVALID_ARG;
-        if (reinterpret_cast<uintptr_t>(k_window) % 16 || reinterpret_cast<uintptr_t>(v_window) % 16)
-            return LVQ_ERR_INVALID_ARG;
-        if (reinterpret_cast<uintptr_t>(k_codebook) % 16 ||
-            reinterpret_cast<uintptr_t>(v_codebook) % 16)
-            return LVQ_ERR_INVALID_ARG;
-    }
-    const int cg = c->group / c->loop_steps;
-    const int S = c->head_dim / cg;
-    if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16))
-        return LVQ_ERR_UNSUPPORTED;
-    // the index rows of one (b, h) are addressed with 32-bit byte offsets
-    if ((int64_t)c->max_tokens * S > 0x7fffffff - 65536LL * S) return LVQ_ERR_UNSUPPORTED;
-    const uint64_t need = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
-    if (!workspace || workspace_bytes < need) return LVQ_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
+    const lvq_decode_layer layer{q, k_index, v_index, k_codebook, v_codebook, k_window, v_window, out};
+    return decode_layers(c, 1, loop_step, &layer, ctx_len, vq_len, max_ctx_len, sm_scale, workspace,
+                         workspace_bytes, stream);
+}
 
-    const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
-    const Splits sp = choose_splits(c, max_vq);
-    const int32_t n_split = sp.n;
-    if ((int64_t)n_split * c->batch * c->n_heads > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
-    const int64_t n_vq = sp.window_wg ? n_split - 1 : n_split;
-    int64_t chunk = (max_vq + n_vq - 1) / n_vq;
-    chunk = (chunk + 63) / 64 * 64;
-    if (chunk < 64) chunk = 64;
-
-    lvq::DecodeArgs a{};
-    a.B = c->batch;
-    a.H = c->n_heads;
-    a.Hk = (int)kv_heads(c);
-    a.q_per_kv = c->n_heads / a.Hk;
-    a.d = c->head_dim;
-    a.Tc = c->loop_steps;
-    a.cg = cg;
-    a.S = S;
-    a.n_sink = c->n_sink;
-    a.n_recent = c->n_recent;
-    a.t_max = c->max_tokens;
-    a.loop_step = loop_step;
-    a.n_split = n_split;
-    a.window_wg = sp.window_wg ? 1 : 0;
-    a.chunk = (int)chunk;
-    a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
-    a.q = static_cast<const uint16_t *>(q);
-    a.ctx_len = ctx_len;
-    a.vq_len = vq_len;
-    {
-        // loop step r reads the index rows of group r / Tc
-        const size_t grp = (size_t)(loop_step / c->loop_steps) * c->batch * a.Hk * c->max_tokens * S;
-        a.k_index = k_index + grp;
-        a.v_index = v_index + grp;
-    }
-    a.k_cb = k_codebook;
-    a.v_cb = v_codebook;
-    a.k_win = static_cast<const uint16_t *>(k_window);
-    a.v_win = static_cast<const uint16_t *>(v_window);
-    a.sm_scale = sm_scale;
-    {
-        const size_t cbe = c->codebook_dtype == LVQ_BF16 ? 2 : 4;
-        const size_t slice = (size_t)loop_step * a.Hk * S * LVQ_CODES * cg * cbe;
-        a.kcb_t = static_cast<const char *>(k_codebook) + slice;
-        a.vcb_t = static_cast<const char *>(v_codebook) + slice;
-        const size_t W = (size_t)c->n_sink + c->n_recent;
-        const size_t step = (size_t)loop_step * a.Hk * W * c->head_dim;
-        a.kwin_t = static_cast<const uint16_t *>(k_window) + step;
-        a.vwin_t = static_cast<const uint16_t *>(v_window) + step;
-        a.win_bstride = n_loops(c) * a.Hk * W * c->head_dim;
-        a.scale_log2 = sm_scale * 1.4426950408889634f;
-    }
-    a.partials = static_cast<uint64_t *>(workspace);
-    a.tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) +
-                                             lvq::partial_bytes(c->batch, c->n_heads, c->head_dim));
-    a.out = out;
-    hipError_t e = lvq::launch_decode(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? LVQ_OK : LVQ_ERR_HIP;
+lvq_status lvq_decode_attn_layers(const lvq_config *c, int32_t n_layers, int32_t loop_step,
+                                  const lvq_decode_layer *layers, const int32_t *ctx_len,
+                                  const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
+                                  void *workspace, uint64_t workspace_bytes, void *stream) {
+    return decode_layers(c, n_layers, loop_step, layers, ctx_len, vq_len, max_ctx_len, sm_scale,
+                         workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

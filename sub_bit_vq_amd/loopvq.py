@@ -19,10 +19,11 @@ LIB_PATH = _HERE / "libloopvq.so"
 LVQ_OK, LVQ_ERR_INVALID_ARG, LVQ_ERR_UNSUPPORTED, LVQ_ERR_WORKSPACE, LVQ_ERR_HIP = range(5)
 LVQ_F32, LVQ_BF16 = 0, 1
 LVQ_MAX_SPLITS = 64
+LVQ_MAX_LAYERS = 4096
 N_CODES = 256
 
 EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
-           "lvq_decode_splits", "lvq_status_string")
+           "lvq_decode_attn_layers", "lvq_decode_splits", "lvq_status_string")
 
 
 class LoopVQError(RuntimeError):
@@ -35,6 +36,11 @@ class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
         "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops")]
+
+
+class _DecodeLayer(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "q", "k_index", "v_index", "k_codebook", "v_codebook", "k_window", "v_window", "out")]
 
 
 class _Tensor(ctypes.Structure):
@@ -106,6 +112,9 @@ def library() -> ctypes.CDLL:
         lib.lvq_decode_attn.restype = i32
         lib.lvq_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_float, vp, u64, vp, vp]
+        lib.lvq_decode_attn_layers.restype = i32
+        lib.lvq_decode_attn_layers.argtypes = [cfgp, i32, i32, ctypes.POINTER(_DecodeLayer), vp, vp,
+                                               i32, ctypes.c_float, vp, u64, vp]
         lib.lvq_decode_splits.restype = i32
         lib.lvq_decode_splits.argtypes = [cfgp, i32]
         lib.lvq_status_string.restype = ctypes.c_char_p
@@ -236,6 +245,46 @@ def lvq_decode_attn(cfg: Config, loop_step: int, q: torch.Tensor, ctx_len: torch
     st = library().lvq_decode_attn(ctypes.byref(cfg.c()), int(loop_step), *args, _stream(stream))
     if st != LVQ_OK:
         raise LoopVQError("lvq_decode_attn", st)
+
+
+LAYER_KEYS = ("q", "k_index", "v_index", "k_codebook", "v_codebook", "k_window", "v_window", "out")
+
+
+def _layers_array(cfg: Config, layers):
+    lay = lvq_cache_layout(cfg)
+    specs = {"q": (torch.bfloat16, lay["query"]["shape"]),
+             "k_index": (torch.uint8, lay["k_index"]["shape"]),
+             "v_index": (torch.uint8, lay["v_index"]["shape"]),
+             "k_codebook": (cfg.torch_codebook_dtype, lay["k_codebook"]["shape"]),
+             "v_codebook": (cfg.torch_codebook_dtype, lay["v_codebook"]["shape"]),
+             "k_window": (torch.bfloat16, lay["k_window"]["shape"]),
+             "v_window": (torch.bfloat16, lay["v_window"]["shape"]),
+             "out": (torch.float32, lay["output"]["shape"])}
+    arr = (_DecodeLayer * max(1, len(layers)))()
+    for i, ly in enumerate(layers):
+        for key in LAYER_KEYS:
+            dt, shape = specs[key]
+            setattr(arr[i], key, _dev_ptr(ly[key], f"layers[{i}].{key}", dt, shape))
+    return arr
+
+
+def lvq_decode_attn_layers(cfg: Config, loop_step: int, layers, ctx_len: torch.Tensor,
+                           max_ctx_len: int, workspace: torch.Tensor, sm_scale: float = 1.0,
+                           vq_len: torch.Tensor | None = None, stream=None) -> None:
+    """Decode attention of ``loop_step`` for several layers at once: each entry
+    of ``layers`` maps the keys of ``LAYER_KEYS`` to that layer's buffers (as
+    :func:`lvq_decode_attn` takes them); ``workspace`` holds at least
+    ``len(layers)`` single-layer workspaces."""
+    arr = _layers_array(cfg, layers)
+    B = cfg.batch
+    st = library().lvq_decode_attn_layers(
+        ctypes.byref(cfg.c()), len(layers), int(loop_step), arr,
+        _dev_ptr(ctx_len, "ctx_len", torch.int32, (B,)),
+        _dev_ptr(vq_len, "vq_len", torch.int32, (B,), allow_none=True), int(max_ctx_len),
+        ctypes.c_float(sm_scale), _dev_ptr(workspace, "workspace"),
+        ctypes.c_uint64(workspace.numel() * workspace.element_size()), _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_decode_attn_layers", st)
 
 
 def allocate(cfg: Config, device="cuda") -> dict:

@@ -193,6 +193,45 @@ def test_decode_validation():
                                         ctypes.c_uint64(1 << 30), P, None) == INV
 
 
+def _decode_layers(cfg, n_layers=3, layer_over=None, **over):
+    lay = lv.lvq_cache_layout(cfg)
+    arr = (lv._DecodeLayer * max(1, n_layers))()
+    for i in range(n_layers):
+        for key in lv.LAYER_KEYS:
+            setattr(arr[i], key, P)
+    for (i, key), v in (layer_over or {}).items():
+        setattr(arr[i], key, v)
+    a = dict(n_layers=n_layers, layers=arr, loop_step=0, ctx_len=P, vq_len=None,
+             max_ctx_len=cfg.max_tokens, sm_scale=1.0, ws=P,
+             ws_bytes=n_layers * lay["workspace_bytes"])
+    a.update(over)
+    return lv.library().lvq_decode_attn_layers(
+        ctypes.byref(cfg.c()), a["n_layers"], a["loop_step"], a["layers"], a["ctx_len"],
+        a["vq_len"], a["max_ctx_len"], ctypes.c_float(a["sm_scale"]), a["ws"],
+        ctypes.c_uint64(a["ws_bytes"]), None)
+
+
+def test_decode_layers_validation():
+    """Every argument of the multi-layer call is checked before any launch:
+    the layer count, each layer's buffers and the workspace of all layers."""
+    cfg = _cfg(1, 2, 64, 4, 16, 1024, lv.LVQ_BF16)
+    INV, UNS, WS = lv.LVQ_ERR_INVALID_ARG, lv.LVQ_ERR_UNSUPPORTED, lv.LVQ_ERR_WORKSPACE
+    per = lv.lvq_cache_layout(cfg)["workspace_bytes"]
+    assert _decode_layers(cfg, n_layers=0) == INV
+    assert _decode_layers(cfg, n_layers=lv.LVQ_MAX_LAYERS + 1) == INV
+    assert _decode_layers(cfg, layers=None) == INV
+    assert _decode_layers(cfg, ctx_len=None) == INV
+    for key in lv.LAYER_KEYS:                                           # any layer, any buffer
+        assert _decode_layers(cfg, layer_over={(2, key): None}) == INV, key
+    assert _decode_layers(cfg, layer_over={(1, "k_window"): P.value + 8}) == INV   # misaligned
+    assert _decode_layers(cfg, layer_over={(0, "v_codebook"): P.value + 8}) == INV
+    assert _decode_layers(cfg, loop_step=4) == INV
+    assert _decode_layers(cfg, sm_scale=float("inf")) == INV
+    assert _decode_layers(cfg, ws_bytes=3 * per - 1) == WS              # one workspace per layer
+    assert _decode_layers(cfg, ws=None) == WS
+    assert _decode_layers(_cfg(1, 2, 384, 4, 16, 1024, lv.LVQ_BF16)) == UNS
+
+
 def _encode(cfg, **over):
     a = dict(x=P, strides=None, n=16, cb=P, index=P, seq=0, first=0)
     a.update(over)
