@@ -619,7 +619,10 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
     }
 }
 
-template <int S, int CG, typename CB>
+// kMulti: the launch holds several layers (the layer index comes from the
+// workgroup index); a single-layer launch reads layer 0's operands at fixed
+// argument offsets, in the first round of argument loads.
+template <int S, int CG, typename CB, bool kMulti>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     using Sh = Shape<S, CG, CB>;
     constexpr int D = Sh::D, R = Sh::R, TPW = Sh::TPW;
@@ -641,9 +644,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const unsigned total = gridDim.x, p = blockIdx.x;
     const unsigned Lg = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
     // layers outermost: the workgroups of one (layer, b, h) stay consecutive
-    const unsigned per_layer = (unsigned)a.n_split * a.H * a.B;
-    const int layer = (int)(Lg / per_layer);
-    const unsigned L = Lg % per_layer;
+    const unsigned per_layer = kMulti ? (unsigned)a.n_split * a.H * a.B : 1u;
+    const int layer = kMulti ? (int)(Lg / per_layer) : 0;
+    const unsigned L = kMulti ? Lg % per_layer : Lg;
     const int split = (int)(L % a.n_split);
     const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
     const DecodeLayer &lp = a.layer[layer];
@@ -670,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint8_t *kidx = lp.k_index + bhk * (size_t)t_max * S;
     const uint8_t *vidx = lp.v_index + bhk * (size_t)t_max * S;
     const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
-    char *wsl = a.ws + (size_t)layer * a.ws_stride;
+    char *wsl = kMulti ? a.ws + (size_t)layer * a.ws_stride : a.ws;
     uint64_t *partials = reinterpret_cast<uint64_t *>(wsl);
     uint64_t *part = partials + (bh * kSlots + split) * (D + 2);
     const uint64_t *parts = partials + bh * kSlots * (D + 2);
@@ -993,16 +996,25 @@ constexpr bool fits() {
 template <int S, int CG>
 hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)a.n_split * a.H * a.B * a.n_layers);
+    const bool multi = a.n_layers > 1;
     if (a.cb_bf16) {
-        if constexpr (fits<S, CG, uint16_t>())
-            hipLaunchKernelGGL((decode_main<S, CG, uint16_t>), grid, dim3(kThreads), 0, st, a);
-        else
+        if constexpr (fits<S, CG, uint16_t>()) {
+            if (multi)
+                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, true>), grid, dim3(kThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, false>), grid, dim3(kThreads), 0, st, a);
+        } else {
             return hipErrorInvalidValue;
+        }
     } else {
-        if constexpr (fits<S, CG, float>())
-            hipLaunchKernelGGL((decode_main<S, CG, float>), grid, dim3(kThreads), 0, st, a);
-        else
+        if constexpr (fits<S, CG, float>()) {
+            if (multi)
+                hipLaunchKernelGGL((decode_main<S, CG, float, true>), grid, dim3(kThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((decode_main<S, CG, float, false>), grid, dim3(kThreads), 0, st, a);
+        } else {
             return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
