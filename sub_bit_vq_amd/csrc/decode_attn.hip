@@ -5,10 +5,12 @@
 // are read from shared 8-bit indices through codebook slice t, and the result
 // is merged with bf16 attention over the sink and recent tokens.
 //
-// One launch, n_split * H * B workgroups of 512 threads.  When the grid fits
-// the chip, workgroup s < n_split - 1 of (b, h) takes VQ tokens
-// [n_s + s*chunk, ...) and the last one every bf16 window slot; otherwise
-// workgroup s takes a VQ chunk and window slots [s*W/n_split, ...).
+// One launch, n_split * H * B workgroups of 512 threads per layer (a launch
+// may hold several layers' buffers: layers are the outermost workgroup
+// index).  When the grid fits the chip, workgroup s < n_split - 1 of (b, h)
+// takes VQ tokens [n_s + s*chunk, ...) and the last one every bf16 window
+// slot; otherwise workgroup s takes a VQ chunk and window slots
+// [s*W/n_split, ...).  The host picks n_split and chunk.
 // A workgroup with VQ tokens stages two tables of (h, t) in LDS, both with one
 // 256-byte row per code k (the codebook slice is stored code-major, so row k
 // is a contiguous read):

@@ -15,10 +15,10 @@ constexpr int kMaxSplits = 64;
 constexpr int kSlots = kMaxSplits;
 
 // Shape of a decode workgroup, shared with the host's split planning: 512
-// threads (8 waves); a wave folds 64 / (S/8) tokens per pass and 4 passes per
-// batch, so a workgroup steps through its VQ tokens 16384 / S at a time.
+// threads (8 waves); a wave folds 64 / (S/8) tokens per pass and 3 passes per
+// batch, so a workgroup steps through its VQ tokens 12288 / S at a time.
 constexpr int kDecodeThreads = 512;
-constexpr int kDecodeUnroll = 4;
+constexpr int kDecodeUnroll = 3;
 constexpr int decode_batch_tokens(int S) { return kDecodeThreads / 64 * (64 / (S / 8)) * kDecodeUnroll; }
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }

@@ -133,10 +133,10 @@ def test_layout_rejects_bad_config(bad):
 def test_decode_splits():
     cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
     # Grid within the chip: VQ token chunks + one window workgroup per (b, h),
-    # the fewest chunks that keep the fewest 512-token batches per workgroup:
-    # 32448 VQ tokens in 13 chunks of 2496 take 5 batches each, as 15 chunks of
-    # 2176 would; 12 chunks of 2704 would take 6.
-    assert lv.lvq_decode_splits(cfg, 32768) == 14
+    # the fewest chunks that keep the fewest 384-token batches per workgroup:
+    # 32448 VQ tokens in 15 chunks of 2164 take 6 batches each; 14 chunks of
+    # 2318 would take 7.
+    assert lv.lvq_decode_splits(cfg, 32768) == 16
     assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded: windows only
     assert lv.lvq_decode_splits(cfg, 320 + 1100) == 3    # 2 chunks of 550 (one batch less than 1)
     assert lv.lvq_decode_splits(cfg, 320 + 600) == 2     # splits stay >= 512 tokens
