@@ -205,9 +205,9 @@ def test_sm_scale(lv):
 
 def test_empty_context_and_repeat(lv):
     """L = 0 gives zeros; repeated calls on one workspace stay correct (the
-    merge tickets reset themselves).  Repeats agree to rounding only: the
-    value-weight histogram is accumulated with LDS float atomics whose order
-    varies from run to run."""
+    merge tickets reset themselves).  Repeats agree to rounding only: where
+    the last workgroup to arrive merges the partials, which one that is (and
+    with it the order of the merge's sums) can change from run to run."""
     _note("empty + repeat")
     c = make_cache(batch=3, n_heads=2, head_dim=64, group=16, lengths=(1, 900, 1), seed=16,
                    codeword_tokens=True)
