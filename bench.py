@@ -64,14 +64,23 @@ def cache_bytes(H, d, Tc, G, lengths):
     return total
 
 
-def kernel_source_hash(name):
-    return hashlib.sha256((ROOT / "sub_bit_vq_amd" / "csrc" / name).read_bytes()).hexdigest()[:16]
+# everything the decode kernel's code depends on: its source, the header it
+# shares with the host (workgroup shape, argument layout) and the build flags
+DECODE_SOURCES = ("sub_bit_vq_amd/csrc/decode_attn.hip", "sub_bit_vq_amd/csrc/kernels.h",
+                  "sub_bit_vq_amd/build.py")
+
+
+def kernel_source_hash(paths=DECODE_SOURCES):
+    h = hashlib.sha256()
+    for rel in paths:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
 
 
 def counters_traffic(workload):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE scaled by a plain copy), or None when it is
-    missing or was taken on a different kernel source."""
+    missing or was taken on different kernel sources (DECODE_SOURCES)."""
     p = ROOT / "profiles" / f"decode_attn_{workload}.md"
     if not p.exists():
         return None
@@ -80,7 +89,7 @@ def counters_traffic(workload):
         if line.startswith("- ") and ": " in line:
             k, v = line[2:].split(": ", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("decode_attn.hip sha256[:16]") != kernel_source_hash("decode_attn.hip"):
+    if fields.get("decode kernel sources (decode_attn.hip, kernels.h, build.py) sha256[:16]") != kernel_source_hash():
         return None
     return int(fields["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in fields else None
 
