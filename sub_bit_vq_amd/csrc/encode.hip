@@ -443,75 +443,149 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     }
 }
 
-// Direct path for short runs (a page of generated tokens, up to kSmallTokens):
-// one workgroup per (sub-vector j, head h) and one thread per code k.  Every
-// distance is evaluated exactly as defined; for each token the wave takes the
+// Direct path for short runs (a page of generated tokens, up to kSmallTokens).
+// A workgroup takes kJW adjacent sub-vectors j of one head h and all 256
+// codes: lane (c, jj) of wave w (c = lane % 16, jj = lane / 16) scores codes
+// k = (16 w + c) R + r, r < R, for sub-vector j0 + jj, so the 16 lanes of a
+// row share one sub-vector and each code row is read as kJW adjacent slice
+// entries (one contiguous piece of a cache line, not one entry per line).
+// Every distance is evaluated exactly as defined; a lane keeps its lowest
+// code of the smallest distance (strict < in ascending k), the row takes the
 // smallest distance (distances are >= 0, so their bit patterns order like
-// them) and the lowest code holding it, and the lowest wave (lowest codes)
-// wins ties across waves.  No screen, so nothing is re-scored.  Measured at
-// 16 heads, d 128, G 16: 7.5 us for 8 tokens, about 0.33 us more per token,
-// against about 15 us for the screen path's smallest launch.
+// them) and then the lowest code holding it, and the lowest wave (lowest
+// codes) wins ties across waves.  No screen, so nothing is re-scored.
 constexpr int kSmallTokens = 32;
+constexpr int kSmallThreads = 1024;
+
+template <int CG, typename CB>
+__device__ __forceinline__ void load_entries(const CB *src, float *out) {
+    constexpr int NB = CG * (int)sizeof(CB);           // bytes of one slice entry
+    uint32_t w[NB / 4];
+    if constexpr (NB >= 16) {
+#pragma unroll
+        for (int q = 0; q < NB / 16; ++q) {
+            const uint4 v = reinterpret_cast<const uint4 *>(src)[q];
+            w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+        }
+    } else if constexpr (NB == 8) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(src);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(src);
+    }
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+        if constexpr (sizeof(CB) == 2)
+            out[c] = __uint_as_float((c & 1) ? (w[c >> 1] & 0xffff0000u) : (w[c >> 1] << 16));
+        else
+            out[c] = __uint_as_float(w[c]);
+    }
+}
+
+// minimum over the 16 lanes of a row, in every lane of it (DPP only)
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v) {
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xf, 0xf, false));  // row_ror 8
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xf, 0xf, false));  // row_ror 4
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));   // xor 2
+    return min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false)); // xor 1
+}
 
 template <int G, int CG, typename CB>
-__global__ __launch_bounds__(256) void encode_small(EncodeArgs a) {
-    __shared__ float xs[kSmallTokens][G];
-    __shared__ uint32_t wave_d[4][kSmallTokens], wave_k[4][kSmallTokens];
+__global__ __launch_bounds__(kSmallThreads) void encode_small(EncodeArgs a) {
+    constexpr int NW = kSmallThreads / 64;
+    constexpr int R = 256 / (NW * 16);                 // codes per lane
+    constexpr int XR = G + 4;                          // padded row: conflict-free 16-B reads
+    __shared__ __align__(16) float xs[kSmallTokens][kJW][XR];
+    __shared__ uint32_t wave_d[NW][kSmallTokens][kJW], wave_k[NW][kSmallTokens][kJW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int j = blockIdx.x, h = blockIdx.y;           // grid z = tensor
-    const uint16_t *xin = blockIdx.z ? a.x_b : a.x;
-    uint8_t *idxout = blockIdx.z ? a.index_b : a.index;
+    const int c = lane & 15, jj = lane >> 4;
+    // the workgroups of one (head, tensor) read the same code rows: keep them
+    // on one XCD (workgroups are dealt to the 8 XCDs in turn)
+    const int nj = a.S / kJW;
+    const int n_wg = nj * a.H * a.n_tensors;
+    int L = blockIdx.x;
+    if (n_wg % 8 == 0) L = (L % 8) * (n_wg / 8) + L / 8;
+    const int jb = L % nj, h = (L / nj) % a.H, z = L / (nj * a.H);
+    const int j0 = jb * kJW;
+    const uint16_t *xin = z ? a.x_b : a.x;
+    uint8_t *idxout = z ? a.index_b : a.index;
     const int n = (int)a.n_tokens;
-    for (int e = tid; e < n * G; e += 256) {
-        const int tok = e / G, i = e % G;
-        xs[tok][i] = bf16f(xin[tok * a.sx_tok + h * a.sx_head + (i / CG) * a.sx_step + (int64_t)j * CG + i % CG]);
+    for (int e = tid; e < n * kJW * G; e += kSmallThreads) {
+        const int tok = e / (kJW * G), q = (e / G) % kJW, i = e % G;
+        xs[tok][q][i] = bf16f(xin[tok * a.sx_tok + h * a.sx_head + (i / CG) * a.sx_step +
+                                  (int64_t)(j0 + q) * CG + i % CG]);
     }
-    // code k = tid of (h, j); slice t holds entries t*CG .. t*CG + CG - 1
-    const CB *cb = static_cast<const CB *>(blockIdx.z ? a.cb_b : a.cb);
-    float cw[G];
+    const CB *cb = static_cast<const CB *>(z ? a.cb_b : a.cb);
+    const int k0 = (wave * 16 + c) * R;
+    float cw[R][G];
 #pragma unroll
-    for (int t = 0; t < G / CG; ++t)
+    for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int c = 0; c < CG; ++c)
-            cw[t * CG + c] = to_f(cb[(((size_t)t * a.H + h) * 256 + tid) * a.S * CG + (size_t)j * CG + c]);
+        for (int t = 0; t < G / CG; ++t)
+            load_entries<CG, CB>(cb + ((((size_t)t * a.H + h) * 256 + k0 + r) * a.S + j0 + jj) * CG,
+                                 &cw[r][t * CG]);
     __syncthreads();
-    for (int tok = 0; tok < n; ++tok) {
-        float dist = 0.f;
+    for (int t0 = 0; t0 < n; t0 += 4) {
+        uint32_t best[4], bk[4];
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const float e = xs[tok][i] - cw[i];
-            const float sq = e * e;
-            dist = dist + sq;
-        }
-        const uint32_t dmin = wave_min_u32(__float_as_uint(dist));
-        const uint32_t kmin = wave_min_u32(__float_as_uint(dist) == dmin ? (uint32_t)tid : 256u);
-        if (lane == 0) {
-            wave_d[wave][tok] = dmin;
-            wave_k[wave][tok] = kmin;
-        }
-    }
-    __syncthreads();
-    if (tid < n) {
-        uint32_t bd = wave_d[0][tid], bk = wave_k[0][tid];
+        for (int q = 0; q < 4; ++q) {
+            const int tok = min(t0 + q, n - 1);
+            float xv[G];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) {
-            if (wave_d[w][tid] < bd) {
-                bd = wave_d[w][tid];
-                bk = wave_k[w][tid];
+            for (int i = 0; i < G; i += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(&xs[tok][jj][i]);
+                xv[i] = v.x; xv[i + 1] = v.y; xv[i + 2] = v.z; xv[i + 3] = v.w;
+            }
+            best[q] = 0xffffffffu;
+            bk[q] = 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                float dd = 0.f;
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const float e = xv[i] - cw[r][i];
+                    const float sq = e * e;
+                    dd = dd + sq;
+                }
+                if (__float_as_uint(dd) < best[q]) {
+                    best[q] = __float_as_uint(dd);
+                    bk[q] = k0 + r;
+                }
             }
         }
-        idxout[(((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tid) * a.S + j] = (uint8_t)bk;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t dmin = row_min_u32(best[q]);
+            const uint32_t kmin = row_min_u32(best[q] == dmin ? bk[q] : 256u);
+            if (c == 0 && t0 + q < n) {
+                wave_d[wave][t0 + q][jj] = dmin;
+                wave_k[wave][t0 + q][jj] = kmin;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < n * kJW) {
+        const int tok = tid / kJW, q = tid % kJW;
+        uint32_t bd = wave_d[0][tok][q], bkk = wave_k[0][tok][q];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            if (wave_d[w][tok][q] < bd) {
+                bd = wave_d[w][tok][q];
+                bkk = wave_k[w][tok][q];
+            }
+        }
+        idxout[(((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok) * a.S + j0 + q] = (uint8_t)bkk;
     }
 }
 
 template <int G, int CG>
 hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
     if (a.n_tokens <= kSmallTokens) {
-        const dim3 grid(a.S, a.H, a.n_tensors);
+        const dim3 grid((unsigned)(a.S / kJW * a.H * a.n_tensors));
         if (a.cb_bf16)
-            hipLaunchKernelGGL((encode_small<G, CG, uint16_t>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((encode_small<G, CG, uint16_t>), grid, dim3(kSmallThreads), 0, st, a);
         else if constexpr (G <= 16)
-            hipLaunchKernelGGL((encode_small<G, CG, float>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((encode_small<G, CG, float>), grid, dim3(kSmallThreads), 0, st, a);
         else
             return hipErrorInvalidValue;
         return hipGetLastError();
