@@ -164,6 +164,20 @@ __device__ __forceinline__ float token_sum(float v) {
     return v;
 }
 
+// maximum / sum over the 16 lanes of a row, in every lane of it
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dppf<kXor1>(v));
+    v = fmaxf(v, dppf<kXor2>(v));
+    v = fmaxf(v, dppf<kRor4>(v));
+    return fmaxf(v, dppf<kRor8>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dppf<kXor1>(v);
+    v += dppf<kXor2>(v);
+    v += dppf<kRor4>(v);
+    return v + dppf<kRor8>(v);
+}
+
 // wave-uniform maximum / sum
 __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dppf<kXor1>(v));
@@ -911,6 +925,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // of slot i - 16.  One poll is in flight at a time: a second one, issued
     // half a round trip later, sees the last partial sooner, but the wave
     // cannot end before its loads land, so the call would not end sooner.
+    static_assert(kMergeChunk == 16, "a chunk's m and l pairs fill one 32-lane half");
     struct Poll {
         uint64_t po[kMergeChunk];
         uint64_t ml;
@@ -939,32 +954,29 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             ok &= (uint32_t)((uint32_t)(pp.ml >> 32) == tag) | (want ^ 1u);
             return __all(ok != 0u);
         };
-        // merge a chunk from the poll that saw every pair current
+        // merge a chunk from the poll that saw every pair current.  The slot
+        // weights are computed one slot per lane: lane i of a 32-lane half
+        // holds m of slot c0 + i (i < 16), lane i + 16 its l; after the
+        // exchange every 16-lane row holds all 16 slots, so row reductions
+        // (however many rows are active) give the chunk's max and weight sum.
         auto merge = [&](const Poll &pp) {
-            float mi[kMergeChunk], li[kMergeChunk];
-            float mc = Mg;
-            const uint32_t mlv = (uint32_t)pp.ml;
-#pragma unroll
-            for (int i = 0; i < kMergeChunk; ++i) {
-                const float lraw = __uint_as_float(__builtin_amdgcn_readlane(mlv, 16 + i));
-                const float mraw = __uint_as_float(__builtin_amdgcn_readlane(mlv, i));
-                const bool use = (c0 + i < n) & (c0 + i != split) & (lraw > 0.f);
-                li[i] = use ? lraw : 0.f;
-                mi[i] = use ? mraw : -INFINITY;
-                mc = fmaxf(mc, mi[i]);
-            }
+            const float v = __uint_as_float((uint32_t)pp.ml);
+            const float vo = __shfl_xor(v, 16);
+            const int si = c0 + (hl & 15);
+            const float ms = hl < 16 ? v : vo, ls = hl < 16 ? vo : v;
+            const bool use = (si < n) & (si != split) & (ls > 0.f);
+            const float mi = use ? ms : -INFINITY;
+            const float mc = fmaxf(Mg, row_max(mi));
             if (mc > Mg) {                           // Mg = -inf gives 0 * 0
                 const float sc = Mg == -INFINITY ? 0.f : ex2(Mg - mc);
                 num *= sc;
                 den *= sc;
                 Mg = mc;
             }
+            const float e = use ? ex2(mi - Mg) : 0.f;
+            den += row_sum(use ? ls * e : 0.f);
 #pragma unroll
-            for (int i = 0; i < kMergeChunk; ++i) {
-                const float e = li[i] > 0.f ? ex2(mi[i] - Mg) : 0.f;
-                num += __uint_as_float((uint32_t)pp.po[i]) * e;
-                den += li[i] * e;
-            }
+            for (int i = 0; i < kMergeChunk; ++i) num += __uint_as_float((uint32_t)pp.po[i]) * lane_f(e, i);
         };
         Poll pa;
         int poll = 0;
