@@ -479,7 +479,8 @@ def main():
     log(f"workload {args.workload}: setup")
     setup = Setup(lv, synth, torch, args.workload, args.rotate)
     log(f"rotation over {setup.rotate} cache copies, "
-        f"{lv.lvq_decode_splits(setup.cfg, setup.L)} workgroups per (sequence, head)")
+        f"{lv.lvq_decode_splits(setup.cfg, setup.L)} workgroups per (sequence, head), "
+        f"{lv.lvq_decode_window_groups(setup.cfg, setup.L)} of them on the window slots")
 
     if args.profile_decode or args.profile_encode:
         if args.copy_calibrate:

@@ -97,9 +97,17 @@ typedef struct {
     int32_t n_loops;        /* R: loop steps of the model; 0 = loop_steps;
                                otherwise a multiple of loop_steps, at most
                                LVQ_MAX_LOOPS                                   */
+    int32_t decode_window_groups; /* with decode_splits = n > 1 on a grid of
+                               at most 256 workgroups: how many of the n split
+                               the bf16 window slots (the others take VQ
+                               chunks); 0 = 1; otherwise 1..min(n - 1,
+                               LVQ_MAX_WINDOW_GROUPS).  Must be 0 when
+                               decode_splits is 0.  Changes only the rounding
+                               of the result.                                   */
 } lvq_config;
 
 #define LVQ_MAX_SPLITS 64
+#define LVQ_MAX_WINDOW_GROUPS 4
 #define LVQ_MAX_LOOPS 64
 #define LVQ_MAX_LAYERS 4096
 #define LVQ_CODES 256
@@ -276,6 +284,12 @@ lvq_status lvq_decode_attn_layers(const lvq_config *cfg, int32_t n_layers, int32
  * max_ctx_len with exact windows (vq_len == NULL); host arithmetic only; 0 on
  * an invalid config. */
 int32_t lvq_decode_splits(const lvq_config *cfg, int32_t max_ctx_len);
+
+/* How many of those workgroups take the bf16 window slots instead of a VQ
+ * chunk (0: every workgroup takes a VQ chunk and a share of the window
+ * slots); same arguments and conventions as lvq_decode_splits, -1 on an
+ * invalid config. */
+int32_t lvq_decode_window_groups(const lvq_config *cfg, int32_t max_ctx_len);
 
 /* Static, NUL-terminated description of a status code. */
 const char *lvq_status_string(lvq_status status);

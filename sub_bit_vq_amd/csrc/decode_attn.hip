@@ -7,10 +7,10 @@
 //
 // One launch, n_split * H * B workgroups of 512 threads per layer (a launch
 // may hold several layers' buffers: layers are the outermost workgroup
-// index).  When the grid fits the chip, workgroup s < n_split - 1 of (b, h)
-// takes VQ tokens [n_s + s*chunk, ...) and the last one every bf16 window
-// slot; otherwise workgroup s takes a VQ chunk and window slots
-// [s*W/n_split, ...).  The host picks n_split and chunk.
+// index).  When the grid fits the chip, workgroup s < n_split - w of (b, h)
+// takes VQ tokens [n_s + s*chunk, ...) and the last w split the bf16 window
+// slots into w equal ranges; otherwise workgroup s takes a VQ chunk and
+// window slots [s*W/n_split, ...).  The host picks n_split, w and chunk.
 // A workgroup with VQ tokens stages two tables of (h, t) in LDS, both with one
 // 256-byte row per code k (the codebook slice is stored code-major, so row k
 // is a contiguous read):
@@ -697,8 +697,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     float *outp = lp.out + bh * D;
     const float scale = a.scale_log2;
     const int n_split = a.n_split;
-    const bool sep = a.window_wg != 0;
-    const bool vq_wg = !sep || split < n_split - 1;        // takes a VQ chunk
+    const int n_win = a.window_wg;
+    const bool sep = n_win != 0;
+    const int wi = split - (n_split - n_win);              // window workgroup index (sep)
+    const bool vq_wg = !sep || wi < 0;                     // takes a VQ chunk
 
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
@@ -719,8 +721,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // at n_sink.  Rows outside the range are masked later by the true range,
     // so these loads need not wait for the context length.
     // window rows of the first pass (wave w takes slots s0 + w + kWaves * (tk + pass * TPW))
-    const int s0 = sep ? 0 : (int)((int64_t)W * split / n_split);
-    const int s1 = sep ? (split == n_split - 1 ? W : 0) : (int)((int64_t)W * (split + 1) / n_split);
+    const int s0 = sep ? (vq_wg ? 0 : (int)((int64_t)W * wi / n_win)) : (int)((int64_t)W * split / n_split);
+    const int s1 = sep ? (vq_wg ? 0 : (int)((int64_t)W * (wi + 1) / n_win))
+                       : (int)((int64_t)W * (split + 1) / n_split);
     using Win = WindowPass<S, CG, CB>;
     // With at most 4 channels per sub-vector step a second pass's rows fit
     // the registers: pass p + 1 is in flight while pass p is folded.
@@ -820,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
     const int n = n_split;
     __syncthreads();                             // every wave is done with the tables
-    // Who merges.  With a window workgroup (the grid fits the chip) it is that
-    // workgroup: it has the highest index of its (b, h), so its peers were
+    // Who merges.  With window workgroups (the grid fits the chip) it is the
+    // last of them: it has the highest index of its (b, h), so its peers were
     // dispatched before it, and it is done early, so it simply waits for
     // their partials.  Otherwise the last workgroup to take an arrival ticket
     // merges; the ticket travels while the partial is reduced.

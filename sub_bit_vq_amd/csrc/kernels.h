@@ -50,9 +50,10 @@ struct DecodeArgs {
     int q_per_kv;     // H / Hk: query head h reads KV head h / q_per_kv
     int64_t t_max;
     int n_split;      // workgroups per (layer, b, h)
-    int window_wg;    // 1: the last workgroup of (b, h) takes every window slot
-                      // and the others one VQ chunk each; 0: each takes a VQ
-                      // chunk and an equal share of the window slots
+    int window_wg;    // w > 0: the last w workgroups of (b, h) split the window
+                      // slots into w equal ranges and the others take one VQ
+                      // chunk each; 0: each takes a VQ chunk and an equal
+                      // share of the window slots
     int chunk;        // VQ tokens per chunk (multiple of 64)
     int cb_bf16;
     int n_layers;     // layers of this launch, 1..kMaxLayersPerLaunch

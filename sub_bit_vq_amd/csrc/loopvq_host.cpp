@@ -27,6 +27,8 @@ bool config_ok(const lvq_config *c) {
     if (c->n_sink < 0 || c->n_recent < 1 || c->max_tokens < 0) return false;
     if (c->codebook_dtype != LVQ_F32 && c->codebook_dtype != LVQ_BF16) return false;
     if (c->decode_splits < 0 || c->decode_splits > LVQ_MAX_SPLITS) return false;
+    if (c->decode_window_groups < 0 || c->decode_window_groups > LVQ_MAX_WINDOW_GROUPS) return false;
+    if (c->decode_window_groups > 0 && c->decode_window_groups >= c->decode_splits) return false;
     if (c->batch > 65535 || c->n_heads > 65535) return false;
     if (c->n_kv_heads < 0 || c->n_kv_heads > c->n_heads) return false;
     if (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0) return false;
@@ -57,50 +59,64 @@ int64_t max_vq_tokens(const lvq_config *c, int32_t max_ctx_len, bool exact_windo
 // of the launch.  One decode workgroup fills a compute unit's LDS, so the grid
 // runs in ceil(B*H*n / 256) rounds on MI355X's 256 CUs.  A workgroup costs a
 // fixed start-up (codebook staging and first loads under a loaded memory
-// system, about kFixedBatches token batches' worth) plus its VQ tokens, which
-// it folds in whole batches of decode_batch_tokens(S), plus its share of the
-// bf16 window rows (a window token reads as many bytes as 8 VQ tokens).
-// Every sequence is costed at the longest one's length.  When a grid with two
-// workgroups per (b, h) fits the chip, only one-round grids are considered,
-// and one extra workgroup per (b, h) takes every window slot (it needs no
-// codebook tables, and it merges the others' partials while they finish).
-// Splits stay at least 512 tokens long; ties go to fewer workgroups.
+// system, about kFixedBatches token batches' worth) plus the bytes it reads,
+// counted in VQ tokens: its VQ tokens, which it folds in whole batches of
+// decode_batch_tokens(S), and its bf16 window rows (a window slot reads
+// 2 * 2d bytes against 2S for a VQ token: 2d/S VQ tokens).  Every sequence is
+// costed at the longest one's length.  When a grid with two workgroups per
+// (b, h) fits the chip, only one-round grids are considered, and w extra
+// workgroups per (b, h) split the window slots (they need no codebook tables,
+// and the last of them merges the others' partials while they finish); a
+// round costs its slowest workgroup.  Splits stay at least 512 tokens long;
+// ties go to fewer workgroups.
 struct Splits {
     int32_t n;          // workgroups per (b, h)
-    bool window_wg;     // the last one takes every window slot
+    int32_t n_win;      // the last n_win of them split the window slots (0: none)
 };
 constexpr int64_t kTargetGroups = 256;
 constexpr int64_t kFixedBatches = 6;
+constexpr int64_t kMaxWindowGroups = LVQ_MAX_WINDOW_GROUPS;
 
 Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1) {
-    if (max_vq <= 0) return {1, false};
+    if (max_vq <= 0) return {1, 0};
     const int64_t bh = n_layers * c->batch * c->n_heads;
     if (c->decode_splits != 0) {
         int64_t want = c->decode_splits;
         if (want < 1) want = 1;
         if (want > LVQ_MAX_SPLITS) want = LVQ_MAX_SPLITS;
-        return {(int32_t)want, want > 1 && bh * want <= kTargetGroups};
+        const int32_t w = c->decode_window_groups > 0 ? c->decode_window_groups : 1;
+        return {(int32_t)want, want > 1 && bh * want <= kTargetGroups ? w : 0};
     }
     const int S = c->head_dim / (c->group / c->loop_steps);
     const int64_t step = lvq::decode_batch_tokens(S);
     const int64_t W = (int64_t)c->n_sink + c->n_recent;
-    int64_t best_cost = -1, best_n = 1;
-    // small grids: one round with a window workgroup per (b, h)
+    const int64_t wslot = 2 * (int64_t)c->head_dim / S;    // VQ tokens per window slot
+    int64_t best_cost = -1, best_n = 1, best_win = 0;
+    auto consider = [&](int64_t cost, int64_t n, int64_t n_win) {
+        if (best_cost < 0 || cost < best_cost || (cost == best_cost && n < best_n)) {
+            best_cost = cost;
+            best_n = n;
+            best_win = n_win;
+        }
+    };
+    // small grids: one round with window workgroups
     const bool win = bh * 2 <= kTargetGroups;
     for (int64_t n_vq = 1; n_vq < LVQ_MAX_SPLITS; ++n_vq) {
         const int64_t chunk = (max_vq + n_vq - 1) / n_vq;
         if (n_vq > 1 && chunk < 512) break;
-        if (win && bh * (n_vq + 1) > kTargetGroups) break;
-        const int64_t n = win ? n_vq + 1 : n_vq;
-        const int64_t rounds = (bh * n + kTargetGroups - 1) / kTargetGroups;
-        const int64_t per_wg = ((chunk + step - 1) / step + kFixedBatches) * step + (win ? 0 : 8 * W / n);
-        const int64_t cost = rounds * per_wg;
-        if (best_cost < 0 || cost < best_cost) {
-            best_cost = cost;
-            best_n = n;
+        const int64_t vq_cost = ((chunk + step - 1) / step + kFixedBatches) * step;
+        if (win) {
+            if (bh * (n_vq + 1) > kTargetGroups) break;
+            for (int64_t w = 1; w <= kMaxWindowGroups && bh * (n_vq + w) <= kTargetGroups; ++w) {
+                const int64_t win_cost = kFixedBatches * step + wslot * ((W + w - 1) / w);
+                consider(std::max(vq_cost, win_cost), n_vq + w, w);
+            }
+        } else {
+            const int64_t rounds = (bh * n_vq + kTargetGroups - 1) / kTargetGroups;
+            consider(rounds * (vq_cost + wslot * W / n_vq), n_vq, 0);
         }
     }
-    return {(int32_t)best_n, win && best_n > 1};
+    return {(int32_t)best_n, best_n > 1 ? (int32_t)best_win : 0};
 }
 
 // Encode n tensors of one shape (1: lvq_encode; 2: the K and V of a page in one
@@ -231,6 +247,11 @@ int32_t lvq_decode_splits(const lvq_config *c, int32_t max_ctx_len) {
     return choose_splits(c, max_vq_tokens(c, max_ctx_len, true)).n;
 }
 
+int32_t lvq_decode_window_groups(const lvq_config *c, int32_t max_ctx_len) {
+    if (!config_ok(c) || max_ctx_len < 0 || max_ctx_len > c->max_tokens) return -1;
+    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true)).n_win;
+}
+
 lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strides,
                       int64_t n_tokens, const void *codebook, uint8_t *index_cache,
                       int32_t seq, int64_t first_token, void *stream) {
@@ -298,7 +319,7 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         const Splits sp = choose_splits(c, max_vq, nl);
         const int32_t n_split = sp.n;
         if ((int64_t)n_split * c->batch * c->n_heads * nl > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
-        const int64_t n_vq = sp.window_wg ? n_split - 1 : n_split;
+        const int64_t n_vq = n_split - sp.n_win;
         int64_t chunk = (max_vq + n_vq - 1) / n_vq;
         chunk = (chunk + 63) / 64 * 64;
         if (chunk < 64) chunk = 64;
@@ -315,7 +336,7 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         a.n_recent = c->n_recent;
         a.t_max = c->max_tokens;
         a.n_split = n_split;
-        a.window_wg = sp.window_wg ? 1 : 0;
+        a.window_wg = sp.n_win;
         a.chunk = (int)chunk;
         a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
         a.n_layers = nl;

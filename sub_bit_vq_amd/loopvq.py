@@ -19,11 +19,13 @@ LIB_PATH = _HERE / "libloopvq.so"
 LVQ_OK, LVQ_ERR_INVALID_ARG, LVQ_ERR_UNSUPPORTED, LVQ_ERR_WORKSPACE, LVQ_ERR_HIP = range(5)
 LVQ_F32, LVQ_BF16 = 0, 1
 LVQ_MAX_SPLITS = 64
+LVQ_MAX_WINDOW_GROUPS = 4
 LVQ_MAX_LAYERS = 4096
 N_CODES = 256
 
 EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
-           "lvq_decode_attn_layers", "lvq_decode_splits", "lvq_status_string")
+           "lvq_decode_attn_layers", "lvq_decode_splits", "lvq_decode_window_groups",
+           "lvq_status_string")
 
 
 class LoopVQError(RuntimeError):
@@ -35,7 +37,8 @@ class LoopVQError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
-        "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops")]
+        "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops",
+        "decode_window_groups")]
 
 
 class _DecodeLayer(ctypes.Structure):
@@ -73,6 +76,7 @@ class Config:
     decode_splits: int = 0
     n_kv_heads: int = 0          # 0: as many KV heads as query heads
     n_loops: int = 0             # 0: the model has loop_steps loop steps
+    decode_window_groups: int = 0  # with decode_splits: workgroups taking window slots
 
     @property
     def kv_heads(self) -> int:
@@ -117,6 +121,8 @@ def library() -> ctypes.CDLL:
                                                i32, ctypes.c_float, vp, u64, vp]
         lib.lvq_decode_splits.restype = i32
         lib.lvq_decode_splits.argtypes = [cfgp, i32]
+        lib.lvq_decode_window_groups.restype = i32
+        lib.lvq_decode_window_groups.argtypes = [cfgp, i32]
         lib.lvq_status_string.restype = ctypes.c_char_p
         lib.lvq_status_string.argtypes = [i32]
         _lib = lib
@@ -149,6 +155,10 @@ def lvq_cache_layout(cfg: Config) -> dict:
 
 def lvq_decode_splits(cfg: Config, max_ctx_len: int) -> int:
     return int(library().lvq_decode_splits(ctypes.byref(cfg.c()), int(max_ctx_len)))
+
+
+def lvq_decode_window_groups(cfg: Config, max_ctx_len: int) -> int:
+    return int(library().lvq_decode_window_groups(ctypes.byref(cfg.c()), int(max_ctx_len)))
 
 
 def _dev_ptr(t, name, dtype=None, shape=None, allow_none=False):

@@ -121,6 +121,8 @@ def test_default_windows_match_pages():
     dict(codebook_dtype=7), dict(decode_splits=65), dict(decode_splits=-1),
     dict(n_kv_heads=-1), dict(n_kv_heads=3), dict(n_heads=6, n_kv_heads=4),
     dict(n_loops=-4), dict(n_loops=6), dict(n_loops=68),
+    dict(decode_window_groups=1), dict(decode_splits=8, decode_window_groups=-1),
+    dict(decode_splits=8, decode_window_groups=5), dict(decode_splits=3, decode_window_groups=3),
 ])
 def test_layout_rejects_bad_config(bad):
     base = dict(batch=1, n_heads=2, head_dim=64, loop_steps=4, group=16, max_tokens=100)
@@ -132,22 +134,43 @@ def test_layout_rejects_bad_config(bad):
 
 def test_decode_splits():
     cfg = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p5bit"])
-    # Grid within the chip: VQ token chunks + one window workgroup per (b, h),
-    # the fewest chunks that keep the fewest 384-token batches per workgroup:
-    # 32448 VQ tokens in 15 chunks of 2164 take 6 batches each; 14 chunks of
-    # 2318 would take 7.
-    assert lv.lvq_decode_splits(cfg, 32768) == 16
-    assert lv.lvq_decode_splits(cfg, 320) == 1           # nothing VQ-coded: windows only
-    assert lv.lvq_decode_splits(cfg, 320 + 1100) == 3    # 2 chunks of 550 (one batch less than 1)
-    assert lv.lvq_decode_splits(cfg, 320 + 600) == 2     # splits stay >= 512 tokens
-    assert lv.lvq_decode_splits(cfg, 40000) == 0         # beyond max_tokens
+    splits = lambda c, L: (lv.lvq_decode_splits(c, L), lv.lvq_decode_window_groups(c, L))  # noqa: E731
+    # Grid within the chip: VQ token chunks + window workgroups per (b, h).
+    # A round costs its slowest workgroup: a VQ chunk in whole 384-token
+    # batches, or a window range at 8 VQ tokens per slot (512 B against 64 B),
+    # each plus a fixed start-up of 6 batches.  32448 VQ tokens in 15 chunks
+    # of 2164 take 6 batches (4608 token-equivalents); one window workgroup
+    # reads 320 slots (2304 + 2560 = 4864) and sets the round; 14 chunks of
+    # 2318 would take 7 batches (4992).
+    assert splits(cfg, 32768) == (16, 1)
+    assert splits(cfg, 320) == (1, 0)                   # nothing VQ-coded: windows only
+    # short contexts: the window rows outweigh the VQ chunks, so they are
+    # split: 2 chunks of 550 (2 batches, 3072) and 4 window ranges of 80 slots
+    # (2304 + 640)
+    assert splits(cfg, 320 + 1100) == (6, 4)
+    assert splits(cfg, 320 + 600) == (5, 4)            # splits stay >= 512 tokens
+    assert splits(cfg, 2048) == (7, 4)                  # 3 chunks of 576
+    assert lv.lvq_decode_splits(cfg, 40000) == 0        # beyond max_tokens
+    assert lv.lvq_decode_window_groups(cfg, 40000) == -1
+    # 0.25 bit (S = 16, 768-token batches, a window slot weighs 16 VQ tokens):
+    # one window workgroup would cost 4608 + 5120; two cost 4608 + 2560, below
+    # the 4 batches of any chunk count from 11 (2950 tokens) to 14 (2318), and
+    # ties go to the fewest workgroups
+    cfg2 = _cfg(*WORKLOADS["ouro1p4b_layer_32k_0p25bit"])
+    assert splits(cfg2, 32768) == (13, 2)
     # Larger grids (1024 heads over 256 CUs): every split costs a workgroup
     # start-up in every round, so one workgroup per (b, h) takes its whole
     # context and its window slots.
     cfg3 = _cfg(*WORKLOADS["batch64_ragged_0p5bit"])
-    assert lv.lvq_decode_splits(cfg3, 18432) == 1
-    assert lv.lvq_decode_splits(_cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, decode_splits=7),
-                                32768) == 7
+    assert splits(cfg3, 18432) == (1, 0)
+    # forced plans: decode_splits alone takes one window workgroup when the
+    # grid fits, decode_window_groups sets the count; a grid beyond the chip
+    # spreads the window slots
+    forced = lambda **kw: _cfg(1, 16, 128, 4, 16, 32768, lv.LVQ_BF16, **kw)  # noqa: E731
+    assert splits(forced(decode_splits=7), 32768) == (7, 1)
+    assert splits(forced(decode_splits=7, decode_window_groups=3), 32768) == (7, 3)
+    assert splits(forced(decode_splits=17, decode_window_groups=3), 32768) == (17, 0)
+    assert splits(forced(decode_splits=1), 32768) == (1, 0)
 
 
 # --- argument validation: every case fails before any HIP call ---------------

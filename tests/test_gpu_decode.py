@@ -146,6 +146,28 @@ def test_split_count_invariance(lv):
         assert rel_err_rows(o, outs[0]) <= 5e-4
 
 
+def test_window_group_counts(lv):
+    """The bf16 window slots split over 1..4 window workgroups (forced plans
+    and the library's own for short and long contexts, 0.5 and 0.25 bit):
+    every plan against the oracle and against the others.  320 slots split
+    into 80/107/160-slot ranges, so the ranges' ends fall inside the sink
+    window, the recent ring and passes of each wave."""
+    for G, lengths in ((16, (2048, 700)), (32, (5000, 1500))):
+        _note(f"window groups G={G}")
+        c = make_cache(batch=2, n_heads=2, head_dim=128, group=G, lengths=lengths, seed=21 + G,
+                       codeword_tokens=True)
+        dc = DeviceCache(lv, c)
+        for t in (0, 3):
+            ref = oracle_decode(oracle, c, t)
+            base = dc.decode(t)
+            assert rel_err_rows(base, ref) <= TOL, (G, t)
+            for splits, w in ((2, 1), (5, 2), (5, 3), (6, 4), (9, 4)):
+                cfg = dataclasses.replace(dc.cfg, decode_splits=splits, decode_window_groups=w)
+                got = dc.decode(t, cfg=cfg)
+                assert rel_err_rows(got, ref) <= TOL, (G, t, splits, w)
+                assert rel_err_rows(got, base) <= 5e-4, (G, t, splits, w)
+
+
 def test_token_permutation_invariance(lv):
     """Permuting the VQ tokens (their K and V index rows together) changes
     only the rounding."""
