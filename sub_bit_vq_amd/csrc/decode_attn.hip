@@ -72,6 +72,7 @@ constexpr int kTabBytes = 131072;              // both tables
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // 2^x by the hardware instruction (results below 2^-126 flush to zero,
 // which no weight here can tell apart from zero)
@@ -106,7 +107,7 @@ struct Shape {
     // parts of one token (R a multiple of 4) and a gather is 4 fp16 channels.
     static constexpr bool kMfma = kF16V && EB == 8 && R % 4 == 0;
     static constexpr int G = kThreads / D;            // reduction groups per channel
-    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16;
+    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16 + 2 * D;
     static constexpr int kLds = kTabBytes + kExtra;
     static_assert(S >= 8 && S <= 64 && (S & (S - 1)) == 0, "8 sub-vectors per lane");
     static_assert(S * EB <= 256, "a value-table row holds every sub-vector");
@@ -329,7 +330,9 @@ struct Stage {
         else return __uint_as_float(w[i]);
     }
 
-    __device__ __forceinline__ void finish(const float *qs, unsigned char *smem) const {
+    // qs: the scaled query (fp32); qw: the raw bf16 query, two channels a word
+    __device__ __forceinline__ void finish(const float *qs, const uint32_t *qw, float scale,
+                                           unsigned char *smem) const {
         const int tid = threadIdx.x;
         float *lutk = reinterpret_cast<float *>(smem);
 #pragma unroll
@@ -341,8 +344,19 @@ struct Stage {
             for (int e = 0; e < Sh::EPU; ++e) {
                 const int j = j0 + e;
                 float acc = 0.f;
+                if constexpr (Sh::kF16V) {
+                    // bf16 pairs: exact products, then one scaling
+                    constexpr int WPE = CG / 2;
 #pragma unroll
-                for (int c = 0; c < CG; ++c) acc += qs[j * CG + c] * elem(kw[u], e * CG + c);
+                    for (int m = 0; m < WPE; ++m)
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[j * WPE + m]),
+                                                              __builtin_bit_cast(bf16x2_t, kw[u][e * WPE + m]),
+                                                              acc, false);
+                    acc *= scale;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) acc += qs[j * CG + c] * elem(kw[u], e * CG + c);
+                }
                 accs[e] = acc;
             }
             // a unit's entries are adjacent in the row: written together
@@ -366,8 +380,9 @@ struct Stage {
 #pragma unroll
             for (int w = 0; w < UW; ++w) {
                 if constexpr (Sh::kF16V) {
-                    const half2_t hp = {(_Float16)bf16lo(vw[u][w]), (_Float16)bf16hi(vw[u][w])};
-                    o[w] = __builtin_bit_cast(uint32_t, hp);
+                    // bf16 -> fp16 is exact within fp16's range, so the
+                    // rounding mode of the packed conversion does not matter
+                    o[w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16lo(vw[u][w]), bf16hi(vw[u][w])));
                 } else {
                     o[w] = vw[u][w];
                 }
@@ -653,6 +668,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     float *wstat = qs + D;                      // [kWaves][m, l]
     float *red = wstat + 2 * kWaves;            // [G][D]
     uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);
+    uint16_t *qh = reinterpret_cast<uint16_t *>(smem + kTabBytes + 4 * (D + 2 * kWaves + kThreads) + 16);
 
     // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
     // that consecutive logical workgroups (the splits of one head) share an
@@ -751,7 +767,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     ir.init(kidx, vidx, max(t1, 0), lane_off, S);
 
     const float qv = bf16f((uint16_t)qraw);
-    if (tid < D) qs[tid] = qv * scale;
+    if (tid < D) {
+        qs[tid] = qv * scale;
+        qh[tid] = (uint16_t)qraw;
+    }
     if (tid == 0) *arrival = arrival_word;
     __syncthreads();
 
@@ -761,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     Online<Sh::NACC> st;
     st.init();
     if constexpr (!kWindowFirst) {
-        if (vq_wg) stg.finish(qs, smem);
+        if (vq_wg) stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
         __syncthreads();
     }
     if constexpr (kWinDB) {
@@ -782,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
     }
     if constexpr (kWindowFirst) {
-        if (vq_wg) stg.finish(qs, smem);
+        if (vq_wg) stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
         __syncthreads();
     }
     // Waves w and w + 4 share a SIMD; the older one would win every issue slot
