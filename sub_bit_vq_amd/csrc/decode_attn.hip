@@ -37,7 +37,7 @@
 // (bf16 window values use the fp32 4x4x1 form, so they stay exact).
 // Otherwise v_dot2_f32_f16 does them on the vector ALUs.
 // Index rows stream from HBM through a three-deep register ring of buffer
-// loads; the first two batches are issued before the tables are staged.  At
+// loads; the first batch is issued before the tables are staged.  At
 // the end the lanes write their (rotated) accumulators to the freed table
 // space at their channel positions and the workgroup sums them there.
 // Every workgroup but the merger of (b, h) publishes (m, l, o[d]) as 64-bit
@@ -757,7 +757,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     ir0.init(kidx, vidx, vq_wg ? (int)min((int64_t)vq0 + a.chunk, t_max) : 0, lane_off, S);
     Batch r0, r1, r2;
     load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
-    load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+    // The second batch waits: at start-up every workgroup's first loads queue
+    // for HBM together, and the table slices, which gate the token loop, get
+    // through sooner with fewer rows ahead of them.  With the longer rows of
+    // S >= 32 it goes out once the tables are built, otherwise after the
+    // first barrier (measured).
+    constexpr bool kSecondAfterTables = S >= 32;
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
@@ -773,6 +778,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     }
     if (tid == 0) *arrival = arrival_word;
     __syncthreads();
+    if constexpr (!kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 
     // The window tokens need no table: where registers allow, fold them while
     // the table slices are still arriving, then build the tables.
@@ -815,6 +821,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             __builtin_amdgcn_s_setprio(0);
         ++turn;
     };
+    if constexpr (kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
