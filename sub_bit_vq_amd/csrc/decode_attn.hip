@@ -41,8 +41,8 @@
 // the end the lanes write their (rotated) accumulators to the freed table
 // space at their channel positions and the workgroup sums them there.
 // Every workgroup but the merger of (b, h) publishes (m, l, o[d]) as 64-bit
-// (value, call tag) pairs and leaves.  The merger is the window workgroup
-// when there is one (its peers were dispatched before it), else the last to
+// (value, call tag) pairs and leaves.  The merger is the last window
+// workgroup when there are any (its peers were dispatched before it), else the last to
 // take an arrival ticket once its tokens are done (the round trip overlaps
 // its own reduction).  It polls the others' pairs until every tag is the
 // current call's, merges (log-sum-exp) into out and advances the call word
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                  __builtin_amdgcn_make_buffer_rsrc(const_cast<CB *>(vcb), (short)0, slice, kBufferWord3));
     }
 
-    // The first two index batches are addressed from host-known values: a
+    // The first index batches are addressed from host-known values: a
     // sequence with any VQ token has L > n_sink + ..., so its VQ range starts
     // at n_sink.  Rows outside the range are masked later by the true range,
     // so these loads need not wait for the context length.
