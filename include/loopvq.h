@@ -207,8 +207,10 @@ lvq_status lvq_encode_kv(const lvq_config *cfg, const void *k_x, const void *v_x
  * k_codebook[r][h][k_index[g][b][h][n][j]][j][c] with g = r / Tc (likewise V;
  * g is absent when R = Tc) and sink/recent tokens use the bf16 window buffers
  * of step r.  fp32 accumulation; VQ value
- * rows enter as fp16 (exact for bf16 codebook entries below 65504 in
- * magnitude) weighted by fp16-rounded softmax weights (relative 2^-11).
+ * rows enter as fp16 (exact for bf16 codebook entries of magnitude in
+ * [2^-14, 65504], truncated toward zero below, by less than 2^-24; larger
+ * entries are outside the supported range) weighted by fp16-rounded softmax
+ * weights (relative 2^-11).
  * With grouped-query attention (n_kv_heads < n_heads) query head h reads the
  * caches, codebooks and windows of KV head h / (n_heads / n_kv_heads) with
  * its own query.  One kernel launch on `stream`; one workgroup of every
