@@ -11,6 +11,8 @@
 // takes VQ tokens [n_s + s*chunk, ...) and the last w split the bf16 window
 // slots into w equal ranges; otherwise workgroup s takes a VQ chunk and
 // window slots [s*W/n_split, ...).  The host picks n_split, w and chunk.
+// With one workgroup per (b, h) over several rounds, workgroups take the
+// sequences longest first, in dispatch order.
 // A workgroup with VQ tokens stages two tables of (h, t) in LDS, both with one
 // 256-byte row per code k (the codebook slice is stored code-major, so row k
 // is a contiguous read):
@@ -661,6 +663,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     constexpr int BSTEP = kWaves * TPW * kUnroll;   // tokens per batch of the workgroup
     static_assert(Sh::kLds <= kLdsLimit, "LDS budget");
     static_assert(D <= kThreads, "one thread per output channel");
+    static_assert(2 * kMaxOrderedBatch <= kThreads, "the length ranking fits the reduction space");
     // The only LDS object: tables at byte 0 and 64K, then q, wave stats,
     // reduction partials and the arrival word.
     __shared__ __align__(16) unsigned char smem[Sh::kLds];
@@ -680,9 +683,31 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int layer = kMulti ? (int)(Lg / per_layer) : 0;
     const unsigned L = kMulti ? Lg % per_layer : Lg;
     const int split = (int)(L % a.n_split);
-    const int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
-    const DecodeLayer &lp = a.layer[layer];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
+    if (!kMulti && a.by_length) {
+        // One workgroup per (b, h) over several rounds: the longest
+        // sequences go first (in dispatch order), so the last round holds the
+        // shortest ones.  Rank by (length descending, index ascending), a
+        // permutation whatever the lengths are.
+        h = (int)(p % a.H);
+        int *lens = reinterpret_cast<int *>(red);
+        int *order = lens + kMaxOrderedBatch;
+        if (tid < a.B) lens[tid] = a.ctx_len[tid];
+        __syncthreads();
+        if (tid < a.B) {
+            const int mine = lens[tid];
+            int rank = 0;
+            for (int i = 0; i < a.B; ++i) {
+                const int li = lens[i];
+                rank += (li > mine) | ((li == mine) & (i < tid));
+            }
+            order[rank] = tid;
+        }
+        __syncthreads();
+        b = order[p / a.H];
+    }
+    const DecodeLayer &lp = a.layer[layer];
     const int tk = lane / R;
     Lanes<S, CG, CB> ln;
     ln.init(lane);

@@ -43,6 +43,7 @@ struct DecodeLayer {
     float *out;                 // [B][H][d]
 };
 constexpr int kMaxLayersPerLaunch = 16;
+constexpr int kMaxOrderedBatch = 256;
 
 struct DecodeArgs {
     int B, H, d, cg, S, n_sink, n_recent;
@@ -55,6 +56,9 @@ struct DecodeArgs {
                       // chunk each; 0: each takes a VQ chunk and an equal
                       // share of the window slots
     int chunk;        // VQ tokens per chunk (multiple of 64)
+    int by_length;    // 1 (one workgroup per (b, h), 2 <= B <= kMaxOrderedBatch,
+                      // one layer): workgroups take sequences longest first
+                      // in dispatch order
     int cb_bf16;
     int n_layers;     // layers of this launch, 1..kMaxLayersPerLaunch
     const int32_t *ctx_len;     // [B], shared by the layers

@@ -338,6 +338,7 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         a.n_split = n_split;
         a.window_wg = sp.n_win;
         a.chunk = (int)chunk;
+        a.by_length = n_split == 1 && nl == 1 && c->batch > 1 && c->batch <= lvq::kMaxOrderedBatch;
         a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
         a.n_layers = nl;
         a.ctx_len = ctx_len;

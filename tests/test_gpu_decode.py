@@ -168,6 +168,23 @@ def test_window_group_counts(lv):
                 assert rel_err_rows(got, base) <= 5e-4, (G, t, splits, w)
 
 
+def test_longest_first_order(lv):
+    """One workgroup per (b, h) (forced single split): workgroups take the
+    sequences longest first, ranked by (length, index), including ties and
+    window-only sequences.  Every row against the oracle, so a wrong or
+    repeated rank shows as a wrong row."""
+    _note("longest-first order")
+    c = make_cache(batch=7, n_heads=3, head_dim=64, group=16,
+                   lengths=(700, 3000, 700, 1500, 3000, 64, 2200), seed=41, codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    cfg = dataclasses.replace(dc.cfg, decode_splits=1)
+    for t in (0, 2):
+        ref = oracle_decode(oracle, c, t)
+        got = dc.decode(t, cfg=cfg)
+        assert rel_err_rows(got, ref) <= TOL, t
+        assert rel_err_rows(got, dc.decode(t)) <= 5e-4, t
+
+
 def test_token_permutation_invariance(lv):
     """Permuting the VQ tokens (their K and V index rows together) changes
     only the rounding."""
