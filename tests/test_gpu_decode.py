@@ -168,6 +168,20 @@ def test_window_group_counts(lv):
                 assert rel_err_rows(got, base) <= 5e-4, (G, t, splits, w)
 
 
+def test_window_groups_small_windows(lv):
+    """Window ranges that are empty or a single slot: 5 window slots (2 sink,
+    3 recent) over 4 window workgroups, and 1 slot over 3; the merger's own
+    range may be empty."""
+    for n_sink, n_recent, splits, w in ((2, 3, 6, 4), (0, 1, 5, 3), (1, 2, 3, 2)):
+        _note(f"small windows {n_sink}+{n_recent}, {splits} splits, {w} window groups")
+        c = make_cache(batch=2, n_heads=2, head_dim=64, group=16, lengths=(1800, 900), seed=51 + w,
+                       codeword_tokens=True, n_sink=n_sink, n_recent=n_recent)
+        dc = DeviceCache(lv, c)
+        cfg = dataclasses.replace(dc.cfg, decode_splits=splits, decode_window_groups=w)
+        for t in (1, 3):
+            assert rel_err_rows(dc.decode(t, cfg=cfg), oracle_decode(oracle, c, t)) <= TOL, (n_sink, n_recent, t)
+
+
 def test_longest_first_order(lv):
     """One workgroup per (b, h) (forced single split): workgroups take the
     sequences longest first, ranked by (length, index), including ties and
