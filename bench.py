@@ -163,6 +163,10 @@ class Setup:
                 self.decode(tok, t)
         if decode_only:
             return
+        self.page_encode()
+
+    def page_encode(self):
+        """The K and V page encode of a step (8 tokens, one launch)."""
         c = self.copies[self.n_call % self.rotate]
         self.lv.lvq_encode_kv(self.cfg, self.page_k, self.page_v, self.kcb, self.vcb,
                               c["k_index"], c["v_index"], 0, self.page_row)
@@ -449,6 +453,9 @@ def main():
                     help="only run N decode launches (for rocprofv3 runs) and exit")
     ap.add_argument("--profile-encode", type=int, default=0,
                     help="only run N prefill encodes of 32768 tokens (for rocprofv3 runs) and exit")
+    ap.add_argument("--profile-page", type=int, default=0,
+                    help="only run N page encodes (8 tokens, K and V in one launch; for "
+                         "rocprofv3 runs) and exit")
     ap.add_argument("--layers", type=int, default=0,
                     help="time lvq_decode_attn_layers with this many layers per launch "
                          "(prints its own JSON line)")
@@ -482,7 +489,7 @@ def main():
         f"{lv.lvq_decode_splits(setup.cfg, setup.L)} workgroups per (sequence, head), "
         f"{lv.lvq_decode_window_groups(setup.cfg, setup.L)} of them on the window slots")
 
-    if args.profile_decode or args.profile_encode:
+    if args.profile_decode or args.profile_encode or args.profile_page:
         if args.copy_calibrate:
             src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
@@ -497,8 +504,11 @@ def main():
             enc = PrefillEncode(lv, synth, torch, setup)
             for _ in range(args.profile_encode):
                 enc.run()
+        for _ in range(args.profile_page):
+            setup.page_encode()
         torch.cuda.synchronize()
-        log(f"ran {args.profile_decode} decode launches, {args.profile_encode} prefill encodes")
+        log(f"ran {args.profile_decode} decode launches, {args.profile_encode} prefill encodes, "
+            f"{args.profile_page} page encodes")
         return
 
     # warmup (eager), then capture one step in a graph
