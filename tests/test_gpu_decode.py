@@ -199,6 +199,22 @@ def test_longest_first_order(lv):
         assert rel_err_rows(got, dc.decode(t)) <= 5e-4, t
 
 
+@pytest.mark.parametrize("batch", [256, 257])
+def test_longest_first_order_limit(lv, batch):
+    """256 sequences (the largest batch ranked by length) and 257 (dispatch
+    order), one workgroup per (b, h): ragged short contexts, every row
+    against the oracle."""
+    _note(f"longest-first limit, batch {batch}")
+    rng = np.random.default_rng(batch)
+    lengths = tuple(int(x) for x in rng.integers(1, 1500, size=batch))
+    c = make_cache(batch=batch, n_heads=1, head_dim=64, group=16, lengths=lengths, seed=61,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c)
+    assert lv.lvq_decode_splits(dc.cfg, max(lengths)) == 1
+    ref = oracle_decode(oracle, c, 1)
+    assert rel_err_rows(dc.decode(1), ref) <= TOL
+
+
 def test_token_permutation_invariance(lv):
     """Permuting the VQ tokens (their K and V index rows together) changes
     only the rounding."""
