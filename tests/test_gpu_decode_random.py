@@ -2,10 +2,12 @@
 the CPU oracle (MI355X).
 
 Every case draws a supported shape (head_dim, G, codebook dtype), a batch of
-ragged lengths mixing window-only, short and multi-split sequences, a
-grouped-query ratio, a loop-group count, an optional page lag (vq_len), an
-optional explicit split count, sm_scale, the loop step and, for some cases,
-two layers in one call.  Indices are drawn (exact codewords), so the oracle
+ragged lengths mixing window-only, short and multi-split sequences (for some
+cases 45-89 sequences, a grid beyond the chip taken one workgroup per (b, h)
+in longest-first order), a grouped-query ratio, a loop-group count, an
+optional page lag (vq_len), an optional explicit split count and window
+workgroup count, sm_scale, the loop step and, for some cases, two layers in
+one call.  Indices are drawn (exact codewords), so the oracle
 takes the same cache.  Bar: per (b, h) row, max_ch |gpu - oracle| /
 max_ch |oracle| <= 2e-3.
 """
@@ -21,7 +23,7 @@ from cases import DeviceCache, make_cache, merge_loop_groups, oracle_decode, rel
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
-N_CASES = 24
+N_CASES = 32
 SHAPES = [  # (head_dim, G, codebook dtype): every supported sub-vector shape
     (32, 8, torch.bfloat16), (32, 16, torch.bfloat16), (32, 16, torch.float32),
     (64, 8, torch.bfloat16), (64, 8, torch.float32), (64, 16, torch.bfloat16),
@@ -42,12 +44,13 @@ def lv():
 def _draw(seed):
     rng = np.random.default_rng(seed)
     d, G, dt = SHAPES[int(rng.integers(len(SHAPES)))]
-    B = int(rng.integers(1, 5))
-    kinds = rng.integers(0, 4, size=B)            # window-only, short, medium, long
+    big = seed % 8 == 5                           # a grid beyond the chip: one workgroup per (b, h)
+    B = int(rng.integers(45, 90)) if big else int(rng.integers(1, 5))
+    kinds = rng.integers(0, 3 if big else 4, size=B)   # window-only, short, medium, long
     bounds = [(1, 320), (321, 900), (901, 4000), (4001, 9000)]
     lengths = [int(rng.integers(*bounds[k])) for k in kinds]
-    Hk = int(rng.integers(1, 4))
-    qpk = int(rng.choice([1, 2, 4]))
+    Hk = 3 if big else int(rng.integers(1, 4))
+    qpk = 1 if big else int(rng.choice([1, 2, 4]))
     groups = int(rng.choice([1, 1, 2]))
     lag = bool(rng.integers(0, 4) == 0)
     vq = None
@@ -55,10 +58,12 @@ def _draw(seed):
         vq = [max(0, L - 320) + (int(rng.integers(0, 9)) if L > 320 else 0) for L in lengths]
         vq = [min(v, max(0, L - min(L, 64))) for v, L in zip(vq, lengths)]
     splits = int(rng.choice([0, 0, 0, int(rng.integers(1, 21))]))
+    # with a forced split count, sometimes a forced number of window workgroups
+    wgroups = int(rng.integers(1, min(4, splits - 1) + 1)) if splits > 1 and rng.integers(0, 2) else 0
     sm = float(rng.choice([1.0, 1.0 / np.sqrt(d)]))
     layers = int(rng.choice([1, 1, 2]))
     return dict(d=d, G=G, dt=dt, B=B, lengths=lengths, Hk=Hk, qpk=qpk, groups=groups, vq=vq,
-                splits=splits, sm=sm, layers=layers, t=int(rng.integers(0, 4 * groups)))
+                splits=splits, wgroups=wgroups, sm=sm, layers=layers, t=int(rng.integers(0, 4 * groups)))
 
 
 def _cache(p, seed):
@@ -77,7 +82,7 @@ def test_random_decode(lv, case):
     dcs = [DeviceCache(lv, c) for c in caches]
     cfg = dcs[0].cfg
     if p["splits"]:
-        cfg = dataclasses.replace(cfg, decode_splits=p["splits"])
+        cfg = dataclasses.replace(cfg, decode_splits=p["splits"], decode_window_groups=p["wgroups"])
     t, L = p["t"], max(p["lengths"])
     if p["layers"] == 1:
         got = [dcs[0].decode(t, p["sm"], cfg=cfg)]
