@@ -104,6 +104,11 @@ typedef struct {
                                LVQ_MAX_WINDOW_GROUPS).  Must be 0 when
                                decode_splits is 0.  Changes only the rounding
                                of the result.                                   */
+    int32_t decode_poll_limit; /* >= 0: how many times the workgroup that merges
+                               the split partials of a (b, h) polls for them
+                               before it gives up (writes NaN for that row and
+                               sets LVQ_STATUS_MERGE_TIMEOUT); 0 = the default,
+                               2^22 polls (seconds)                              */
 } lvq_config;
 
 #define LVQ_MAX_SPLITS 64
@@ -111,6 +116,16 @@ typedef struct {
 #define LVQ_MAX_LOOPS 64
 #define LVQ_MAX_LAYERS 4096
 #define LVQ_CODES 256
+
+/* Flags of the workspace status word (lvq_decode_status). */
+#define LVQ_STATUS_MERGE_TIMEOUT 1u /* a merge gave up waiting for a split
+                                       partial: that (b, h) row of out holds
+                                       NaN; zero-fill the workspace before
+                                       its next use                          */
+#define LVQ_STATUS_VALUE_RANGE 2u   /* a bf16 value codebook entry read by a
+                                       decode lies outside fp16's finite range
+                                       (|v| >= 65536, or not finite): the value
+                                       sums clamped it                       */
 
 typedef struct {
     int32_t ndim;
@@ -228,8 +243,12 @@ lvq_status lvq_encode_kv(const lvq_config *cfg, const void *k_x, const void *v_x
  * k_codebook, v_codebook  16-byte aligned.
  * workspace  device, >= layout.workspace_bytes, 256-byte aligned; zero-filled
  *            once after allocation; every completed call leaves it valid for
- *            the next (it holds per-(b, h) arrival words that count calls and
- *            split partials tagged with the call).
+ *            the next, whatever batch, head count, layer count or head_dim
+ *            the next call has (as long as it is large enough for it): a
+ *            status word, then per (layer, b, h) a block on a fixed grid
+ *            holding an arrival word (a call epoch) and split partials
+ *            tagged with that epoch.  Calls that share a workspace must not
+ *            overlap in time (one stream, or ordered streams).
  * out        device fp32 [B][H][d]
  * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned buffers, loop_step
  * outside [0, R), max_tokens < 1, max_ctx_len outside [0, max_tokens],
@@ -271,9 +290,10 @@ typedef struct {
  * layers     host array [n_layers], 1 <= n_layers <= LVQ_MAX_LAYERS; every
  *            pointer as for lvq_decode_attn.
  * workspace  device, >= n_layers * layout.workspace_bytes, 256-byte aligned,
- *            zero-filled once after allocation; layer l uses the single-layer
- *            workspace layout at workspace + l * layout.workspace_bytes, so
- *            layer 0 and lvq_decode_attn may share one workspace.
+ *            zero-filled once after allocation; the status word is shared and
+ *            layer l uses the blocks of (l * B + b) * H + h, so layer 0 uses
+ *            exactly the blocks of lvq_decode_attn and the two may share one
+ *            workspace.
  * Other arguments and errors as for lvq_decode_attn (LVQ_ERR_INVALID_ARG also
  * for n_layers outside [1, LVQ_MAX_LAYERS] or a null layers array).
  */
@@ -281,6 +301,28 @@ lvq_status lvq_decode_attn_layers(const lvq_config *cfg, int32_t n_layers, int32
                                   const lvq_decode_layer *layers, const int32_t *ctx_len,
                                   const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
                                   void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Status flags that decode calls have set in a workspace (LVQ_STATUS_*; 0
+ * when every call completed normally), for callers that check for a merge
+ * that timed out (a workgroup never ran, e.g. on a device shared with a
+ * kernel that holds compute units) or for value codebook entries outside the
+ * supported range.  Unlike every other call this one synchronises: it waits
+ * for `stream`, copies the word to *flags and, when `clear` is nonzero,
+ * zeroes it.  Errors: LVQ_ERR_INVALID_ARG (null or misaligned workspace,
+ * null flags), LVQ_ERR_HIP. */
+lvq_status lvq_decode_status(void *workspace, uint32_t *flags, int32_t clear, void *stream);
+
+/* Which (layer, sequence, query head) and which split role workgroup
+ * `workgroup` of a decode launch of n_layers (1..16) layers takes, for
+ * max_ctx_len with exact windows (host arithmetic: the mapping the kernel
+ * computes from its dispatch index).  Roles 0 .. n-1 of a (layer, b, h) are
+ * ordered by dispatch index; where the launch merges by window workgroups,
+ * role n-1 merges, so it is the member of its group dispatched last.  With
+ * one workgroup per (b, h) and 2 <= B <= 256 the kernel assigns sequences
+ * by length at run time, and `seq` is then a position in that order.
+ * Returns the role, or -1 for an invalid config or workgroup index. */
+int32_t lvq_decode_role(const lvq_config *cfg, int32_t n_layers, int32_t max_ctx_len,
+                        int32_t workgroup, int32_t *layer, int32_t *seq, int32_t *head);
 
 /* Number of workgroups per (b, h) that lvq_decode_attn launches for
  * max_ctx_len with exact windows (vq_len == NULL); host arithmetic only; 0 on

@@ -44,13 +44,15 @@
 // space at their channel positions and the workgroup sums them there.
 // Every workgroup but the merger of (b, h) publishes (m, l, o[d]) as 64-bit
 // (value, call tag) pairs and leaves.  The merger is the last window
-// workgroup when there are any (its peers were dispatched before it), else the last to
-// take an arrival ticket once its tokens are done (the round trip overlaps
-// its own reduction).  It polls the others' pairs until every tag is the
-// current call's, merges (log-sum-exp) into out and advances the call word
-// to the next call.  Everything crosses workgroups through agent-scope
-// atomics (no L2 writeback or invalidation); each pair is one 64-bit access,
-// so no store needs a completion wait.
+// workgroup when there are any (the member of its group dispatched last, so
+// its peers were dispatched before it), else the last to take an arrival
+// ticket once its tokens are done (the round trip overlaps its own
+// reduction).  It polls the others' pairs until every tag is the current
+// call's, merges (log-sum-exp, slots in ascending order, its own from
+// registers, so the result does not depend on which workgroup merges) into
+// out and advances the block's epoch to the next call.  Everything crosses
+// workgroups through agent-scope atomics (no L2 writeback or invalidation);
+// each pair is one 64-bit access, so no store needs a completion wait.
 #include "kernels.h"
 
 #include <math.h>
@@ -66,7 +68,6 @@ constexpr int kUnroll = kDecodeUnroll;         // token passes per batch
 constexpr float kPScale = 16384.f;             // p' = p * 2^14 (normal in fp16 down to p ~ 4e-9)
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMergeChunk = 16;                // partial slots loaded per poll
-constexpr int kMaxPolls = 1 << 22;             // bound of the merger's wait
 constexpr int kVTab = 65536;                   // LDS byte offset of the value table
 constexpr int kBufferWord3 = 0x00020000;       // raw buffer resource, gfx9 family
 constexpr int kTabBytes = 131072;              // both tables
@@ -75,6 +76,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 // 2^x by the hardware instruction (results below 2^-126 flush to zero,
 // which no weight here can tell apart from zero)
@@ -330,6 +332,26 @@ struct Stage {
     __device__ __forceinline__ float elem(const uint32_t *w, int i) const {
         if constexpr (Sh::kF16V) return (i & 1) ? bf16hi(w[i >> 1]) : bf16lo(w[i >> 1]);
         else return __uint_as_float(w[i]);
+    }
+
+    // Whether a bf16 value entry of the staged units falls outside fp16's
+    // finite range (|v| >= 2^16, or not finite; no bf16 value lies in
+    // (65280, 65536)).  The workgroups of a head stage the same slice, so
+    // they share the check: a workgroup of VQ role `role` among `nvq` looks
+    // at the units u with u = role (mod nvq).
+    __device__ __forceinline__ bool value_range_bad(int role, int nvq) const {
+        uint32_t mx = 0;
+        if constexpr (Sh::kF16V) {
+#pragma unroll
+            for (int u = 0; u < Sh::UPT; ++u) {
+                if ((u - role) % nvq != 0) continue;      // wave-uniform
+#pragma unroll
+                for (int w = 0; w < UW; ++w)
+                    mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                        __builtin_bit_cast(ushort2_t, mx), __builtin_bit_cast(ushort2_t, vw[u][w] & 0x7fff7fffu)));
+            }
+        }
+        return (mx & 0xffffu) >= 0x4780u || (mx >> 16) >= 0x4780u;
     }
 
     // qs: the scaled query (fp32); qw: the raw bf16 query, two channels a word
@@ -673,18 +695,17 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);
     uint16_t *qh = reinterpret_cast<uint16_t *>(smem + kTabBytes + 4 * (D + 2 * kWaves + kThreads) + 16);
 
-    // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
-    // that consecutive logical workgroups (the splits of one head) share an
-    // XCD and its L2, which then serves their table slices once.
-    const unsigned total = gridDim.x, p = blockIdx.x;
-    const unsigned Lg = (total % 8 == 0) ? (p % 8) * (total / 8) + p / 8 : p;
-    // layers outermost: the workgroups of one (layer, b, h) stay consecutive
-    const unsigned per_layer = kMulti ? (unsigned)a.n_split * a.H * a.B : 1u;
-    const int layer = kMulti ? (int)(Lg / per_layer) : 0;
-    const unsigned L = kMulti ? Lg % per_layer : Lg;
-    const int split = (int)(L % a.n_split);
+    // The splits of one (layer, b, h) share an XCD (and its L2, which then
+    // serves their table slices once); within the group, roles follow the
+    // dispatch order (decode_role).  Layers are outermost.
+    const unsigned p = blockIdx.x;
+    const WgRole wr = decode_role(p, gridDim.x, (unsigned)a.n_split);
+    const unsigned groups_per_layer = (unsigned)a.H * a.B;
+    const int layer = kMulti ? (int)(wr.group / groups_per_layer) : 0;
+    const unsigned gq = kMulti ? wr.group % groups_per_layer : wr.group;
+    const int split = wr.role;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int h = (int)((L / a.n_split) % a.H), b = (int)(L / a.n_split / a.H);
+    int h = (int)(gq % a.H), b = (int)(gq / a.H);
     if (!kMulti && a.by_length) {
         // One workgroup per (b, h) over several rounds: the longest
         // sequences go first (in dispatch order), so the last round holds the
@@ -730,11 +751,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint8_t *kidx = lp.k_index + bhk * (size_t)t_max * S;
     const uint8_t *vidx = lp.v_index + bhk * (size_t)t_max * S;
     const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
-    char *wsl = kMulti ? a.ws + (size_t)layer * a.ws_stride : a.ws;
-    uint64_t *partials = reinterpret_cast<uint64_t *>(wsl);
-    uint64_t *part = partials + (bh * kSlots + split) * (D + 2);
-    const uint64_t *parts = partials + bh * kSlots * (D + 2);
-    uint32_t *ticket = reinterpret_cast<uint32_t *>(wsl + a.ws_tickets) + bh;
+    char *blk = a.blocks + ((size_t)layer * a.B * a.H + bh) * kBlockBytes;
+    uint64_t *ticket = reinterpret_cast<uint64_t *>(blk);          // arrival word
+    const uint64_t *parts = reinterpret_cast<const uint64_t *>(blk + kSlotBase);
+    uint64_t *part = reinterpret_cast<uint64_t *>(blk + kSlotBase) + (size_t)split * (D + 2);
     float *outp = lp.out + bh * D;
     const float scale = a.scale_log2;
     const int n_split = a.n_split;
@@ -746,9 +766,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
     const uint32_t qraw = lp.q[bh * D + min(tid, D - 1)];
-    // The call counter of (b, h) cannot change before this workgroup arrives,
-    // so it is read now, overlapped with the prologue; it tags the partials.
-    uint32_t arrival_word = 0;
+    // The block's epoch cannot change before this workgroup arrives, so it is
+    // read now, overlapped with the prologue; it tags the partials.
+    uint64_t arrival_word = 0;
     if (tid == 0) arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
     {
@@ -801,7 +821,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         qs[tid] = qv * scale;
         qh[tid] = (uint16_t)qraw;
     }
-    if (tid == 0) *arrival = arrival_word;
+    if (tid == 0) *arrival = (uint32_t)(arrival_word >> 32);
     __syncthreads();
     if constexpr (!kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 
@@ -810,8 +830,20 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     constexpr bool kWindowFirst = Sh::NACC <= 32;
     Online<Sh::NACC> st;
     st.init();
+    // a value entry outside fp16's range is flagged in the status word
+    const int n_vq_wg = n_split - n_win;
+    auto check_range = [&]() {
+        if constexpr (Sh::kF16V) {
+            const bool bad = __ballot(stg.value_range_bad(split % 8, n_vq_wg < 8 ? n_vq_wg : 8)) != 0;
+            if (bad && lane == 0)
+                __hip_atomic_fetch_or(a.status, kStatusValueRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
     if constexpr (!kWindowFirst) {
-        if (vq_wg) stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
+        if (vq_wg) {
+            check_range();
+            stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
+        }
         __syncthreads();
     }
     if constexpr (kWinDB) {
@@ -832,7 +864,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
     }
     if constexpr (kWindowFirst) {
-        if (vq_wg) stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
+        if (vq_wg) {
+            check_range();
+            stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem);
+        }
         __syncthreads();
     }
     // Waves w and w + 4 share a SIMD; the older one would win every issue slot
@@ -870,8 +905,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // Lane accumulators to the freed table space: row (wave, tk), natural
     // channel order.  Then wave (m, l).
     const float lw = wave_sum(st.l) * (1.f / R);     // every token was counted R times
-    const uint32_t epoch = *arrival >> 8;
-    const uint32_t tag = epoch % 0xffffffu + 1u;     // never 0 (zero-filled slots)
+    const uint32_t epoch = *arrival;                 // 0 .. kEpochWrap - 1
+    const uint32_t tag = epoch + 1u;                 // never 0 (zero-filled slots)
     const int n = n_split;
     __syncthreads();                             // every wave is done with the tables
     // Who merges.  With window workgroups (the grid fits the chip) it is the
@@ -879,9 +914,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // dispatched before it, and it is done early, so it simply waits for
     // their partials.  Otherwise the last workgroup to take an arrival ticket
     // merges; the ticket travels while the partial is reduced.
-    uint32_t ticket_word = 0;
+    uint64_t ticket_word = 0;
     if (tid == 0 && n > 1 && !sep)
-        ticket_word = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket_word = __hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float *dump = reinterpret_cast<float *>(smem);
     float *mine = dump + (size_t)(wave * TPW + tk) * D;
     if constexpr (Sh::kMfma) {
@@ -959,10 +994,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         if (tid == 0) {
             publish(&part[0], M, tag);
             publish(&part[1], lt, tag);
-            *arrival = ticket_word;
+            *arrival = (uint32_t)ticket_word;            // arrivals before this one
         }
         __syncthreads();
-        if ((int)(*arrival & 0xffu) != n - 1) return;
+        if ((int)*arrival != n - 1) return;
     }
 
     // The merger: every other workgroup of (b, h) has started (and will
@@ -971,8 +1006,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // m and l pairs are read by lanes 0..31).
     if (tid >= (D > 32 ? D : 32)) return;
     const int ch = tid < D ? tid : 0;
-    float Mg = lt > 0.f ? M : -INFINITY;
-    float num = o, den = lt;
+    // slots in ascending order, this workgroup's own (slot `split`) from its
+    // registers: the same sum whichever workgroup merges
+    float Mg = -INFINITY;
+    float num = 0.f, den = 0.f;
     bool failed = false;
     // A poll reads this channel of every slot of a chunk, and one (m or l)
     // pair per lane: lane i of a 32-lane half reads m of slot i (i < 16) or l
@@ -1017,8 +1054,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             const float v = __uint_as_float((uint32_t)pp.ml);
             const float vo = __shfl_xor(v, 16);
             const int si = c0 + (hl & 15);
-            const float ms = hl < 16 ? v : vo, ls = hl < 16 ? vo : v;
-            const bool use = (si < n) & (si != split) & (ls > 0.f);
+            const bool own = si == split;
+            const float ms = own ? M : (hl < 16 ? v : vo), ls = own ? lt : (hl < 16 ? vo : v);
+            const bool use = (si < n) & (ls > 0.f);
             const float mi = use ? ms : -INFINITY;
             const float mc = fmaxf(Mg, row_max(mi));
             if (mc > Mg) {                           // Mg = -inf gives 0 * 0
@@ -1030,7 +1068,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             const float e = use ? ex2(mi - Mg) : 0.f;
             den += row_sum(use ? ls * e : 0.f);
 #pragma unroll
-            for (int i = 0; i < kMergeChunk; ++i) num += __uint_as_float((uint32_t)pp.po[i]) * lane_f(e, i);
+            for (int i = 0; i < kMergeChunk; ++i)
+                num += (c0 + i == split ? o : __uint_as_float((uint32_t)pp.po[i])) * lane_f(e, i);
         };
         Poll pa;
         int poll = 0;
@@ -1040,19 +1079,23 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                 merge(pa);
                 break;
             }
-            if (++poll >= kMaxPolls) {
+            if (++poll >= a.max_polls) {
                 failed = true;
                 break;
             }
         }
     }
     // (a timed-out merge writes quiet-NaN bits: an integer select, so that the
-    // no-NaN arithmetic this file is built with cannot fold it away)
+    // no-NaN arithmetic this file is built with cannot fold it away) and is
+    // flagged in the status word
     if (tid < D)
         reinterpret_cast<uint32_t *>(outp)[tid] =
             failed ? 0x7fc00000u : __float_as_uint(den > 0.f ? num / den : 0.f);
-    if (tid == 0 && n > 1)
-        __hip_atomic_store(ticket, (epoch + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0 && n > 1) {
+        if (failed) __hip_atomic_fetch_or(a.status, kStatusMergeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t next = epoch + 1u == kEpochWrap ? 0u : epoch + 1u;
+        __hip_atomic_store(ticket, (uint64_t)next << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int S, int CG, typename CB>

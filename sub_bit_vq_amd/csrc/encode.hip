@@ -156,7 +156,11 @@ __device__ __forceinline__ void load_tile(XTile<NCH> &t, __amdgpu_buffer_rsrc_t 
     }
 }
 
-template <int G, int CG, int P, typename CB>
+// kScreen: also store every unmarked screen value to a.screen (the
+// diagnostic entry point that measures the screen's error; the values, the
+// operands and the instructions that form them are those of the plain
+// instance)
+template <int G, int CG, int P, typename CB, bool kScreen>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     using Sh = EncShape<G, CG, P, CB>;
     constexpr int NCH = Sh::NCH;
@@ -352,6 +356,12 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int blk = 0; blk < 16; ++blk) {
                 const floatx4 acc = accs[blk % kPipe];
+                if constexpr (kScreen) {
+                    if (valid) {
+                        float *dst = a.screen + (((size_t)(n0 + row) * a.H + h) * a.S + j) * 256 + blk * 16 + kq * 4;
+                        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                    }
+                }
                 // lane holds codes blk*16 + kq*4 + i of token n0 + row; the low
                 // 6 bits of each value become its slot blk*4 + i in the lane
                 float v[4];
@@ -580,6 +590,18 @@ __global__ __launch_bounds__(kSmallThreads) void encode_small(EncodeArgs a) {
 
 template <int G, int CG>
 hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
+    if (a.screen) {
+        // the screen path at any length, storing the screen values
+        const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW,
+                        a.H * a.n_tensors);
+        if (a.cb_bf16)
+            hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t, true>), grid, dim3(kThreads), 0, st, a);
+        else if constexpr (G <= 16)
+            hipLaunchKernelGGL((encode_kernel<G, CG, 3, float, true>), grid, dim3(kThreads), 0, st, a);
+        else
+            return hipErrorInvalidValue;
+        return hipGetLastError();
+    }
     if (a.n_tokens <= kSmallTokens) {
         const dim3 grid((unsigned)(a.S / kJW * a.H * a.n_tensors));
         if (a.cb_bf16)
@@ -593,10 +615,10 @@ hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW,
                     a.H * a.n_tensors);
     if (a.cb_bf16) {
-        hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t, false>), grid, dim3(kThreads), 0, st, a);
     } else {
         if constexpr (G <= 16)
-            hipLaunchKernelGGL((encode_kernel<G, CG, 3, float>), grid, dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((encode_kernel<G, CG, 3, float, false>), grid, dim3(kThreads), 0, st, a);
         else
             return hipErrorInvalidValue;
     }

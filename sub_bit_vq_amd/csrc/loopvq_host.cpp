@@ -2,6 +2,7 @@
 // configuration.  Everything before the kernel launch is plain host
 // arithmetic, so every error path returns before any HIP call.
 #include "../../include/loopvq.h"
+#include "../../include/loopvq_diag.h"
 
 #include <algorithm>
 #include <cmath>
@@ -33,6 +34,7 @@ bool config_ok(const lvq_config *c) {
     if (c->n_kv_heads < 0 || c->n_kv_heads > c->n_heads) return false;
     if (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0) return false;
     if (c->n_loops < 0 || c->n_loops > LVQ_MAX_LOOPS || c->n_loops % c->loop_steps != 0) return false;
+    if (c->decode_poll_limit < 0) return false;
     return true;
 }
 
@@ -74,6 +76,7 @@ struct Splits {
     int32_t n_win;      // the last n_win of them split the window slots (0: none)
 };
 constexpr int64_t kTargetGroups = 256;
+constexpr int32_t kDefaultPolls = 1 << 22;   // a merger's wait: seconds, far beyond any call
 constexpr int64_t kFixedBatches = 6;
 constexpr int64_t kMaxWindowGroups = LVQ_MAX_WINDOW_GROUPS;
 
@@ -123,7 +126,7 @@ Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1) 
 // launch per group).  Every argument is checked before anything is launched.
 lvq_status encode_tensors(const lvq_config *c, int n, const void *const *x, const int64_t *x_strides,
                           int64_t n_tokens, const void *const *codebook, uint8_t *const *index_cache,
-                          int32_t seq, int64_t first_token, void *stream) {
+                          int32_t seq, int64_t first_token, void *stream, float *screen = nullptr) {
     if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
     for (int i = 0; i < n; ++i)
         if (!x[i] || !codebook[i] || !index_cache[i]) return LVQ_ERR_INVALID_ARG;
@@ -170,6 +173,7 @@ lvq_status encode_tensors(const lvq_config *c, int n, const void *const *x, cons
     a.t_max = c->max_tokens;
     a.seq = seq;
     a.first_token = first_token;
+    a.screen = screen;
     for (int64_t g = 0; g < R / Tc; ++g) {
         // group g: loop steps g*Tc .. g*Tc + Tc - 1, codebook slices of those
         // steps, and the group's index cache block
@@ -238,7 +242,7 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
     const int64_t q_shape[3] = {B, H, d};
     set_tensor(&o->query, 3, q_shape, 2);
     set_tensor(&o->output, 3, q_shape, 4);
-    o->workspace_bytes = lvq::workspace_bytes(B, H, d);
+    o->workspace_bytes = lvq::workspace_bytes(B, H);
     return LVQ_OK;
 }
 
@@ -261,6 +265,18 @@ lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strid
     return encode_tensors(c, 1, xs, x_strides, n_tokens, cbs, idx, seq, first_token, stream);
 }
 
+lvq_status lvq_encode_screen(const lvq_config *c, const void *x, const int64_t *x_strides,
+                             int64_t n_tokens, const void *codebook, uint8_t *index_cache,
+                             int32_t seq, int64_t first_token, float *screen, void *stream) {
+    if (!screen) return LVQ_ERR_INVALID_ARG;
+    if (config_ok(c) && n_loops(c) != c->loop_steps) return LVQ_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(screen) % 16) return LVQ_ERR_INVALID_ARG;
+    const void *xs[1] = {x};
+    const void *cbs[1] = {codebook};
+    uint8_t *idx[1] = {index_cache};
+    return encode_tensors(c, 1, xs, x_strides, n_tokens, cbs, idx, seq, first_token, stream, screen);
+}
+
 lvq_status lvq_encode_kv(const lvq_config *c, const void *k_x, const void *v_x,
                          const int64_t *x_strides, int64_t n_tokens, const void *k_codebook,
                          const void *v_codebook, uint8_t *k_index, uint8_t *v_index, int32_t seq,
@@ -274,8 +290,8 @@ lvq_status lvq_encode_kv(const lvq_config *c, const void *k_x, const void *v_x,
 namespace {
 
 // Every check of a decode call, then one launch per kMaxLayersPerLaunch
-// layers.  Layer l uses the single-layer workspace layout at workspace +
-// l * workspace_bytes(B, H, d).
+// layers.  Layer l uses the workspace blocks (l * B + b) * H + h after the
+// header.
 lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_step,
                          const lvq_decode_layer *layers, const int32_t *ctx_len,
                          const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
@@ -303,12 +319,17 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
             reinterpret_cast<uintptr_t>(L.v_codebook) % 16)
             return LVQ_ERR_INVALID_ARG;
     }
-    if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16))
+    if (!lvq::decode_supported(c->head_dim, S, cg, c->codebook_dtype == LVQ_BF16) ||
+        c->head_dim > lvq::kMaxDecodeDim)
         return LVQ_ERR_UNSUPPORTED;
     // the index rows of one (b, h) are addressed with 32-bit byte offsets
     if ((int64_t)c->max_tokens * S > 0x7fffffff - 65536LL * S) return LVQ_ERR_UNSUPPORTED;
-    const uint64_t per_layer = lvq::workspace_bytes(c->batch, c->n_heads, c->head_dim);
-    if (!workspace || workspace_bytes / per_layer < (uint64_t)n_layers) return LVQ_ERR_WORKSPACE;
+    // the header, then one block per (layer, b, h); n_layers single-layer
+    // workspaces hold that
+    const uint64_t per_layer = lvq::layer_block_bytes(c->batch, c->n_heads);
+    if (!workspace || workspace_bytes < lvq::kHeaderBytes ||
+        (workspace_bytes - lvq::kHeaderBytes) / per_layer < (uint64_t)n_layers)
+        return LVQ_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
 
     const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
@@ -345,9 +366,9 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         a.vq_len = vq_len;
         a.win_bstride = n_loops(c) * a.Hk * W * c->head_dim;
         a.scale_log2 = sm_scale * 1.4426950408889634f;
-        a.ws = static_cast<char *>(workspace) + (size_t)l0 * per_layer;
-        a.ws_stride = per_layer;
-        a.ws_tickets = lvq::partial_bytes(c->batch, c->n_heads, c->head_dim);
+        a.blocks = static_cast<char *>(workspace) + lvq::kHeaderBytes + (size_t)l0 * per_layer;
+        a.status = static_cast<uint32_t *>(workspace);
+        a.max_polls = c->decode_poll_limit > 0 ? c->decode_poll_limit : kDefaultPolls;
         // loop step r reads the index rows of group r / Tc, codebook slice r
         // and window buffers of step r
         const size_t grp = (size_t)(loop_step / c->loop_steps) * c->batch * Hk * c->max_tokens * S;
@@ -392,6 +413,37 @@ lvq_status lvq_decode_attn_layers(const lvq_config *c, int32_t n_layers, int32_t
                                   void *workspace, uint64_t workspace_bytes, void *stream) {
     return decode_layers(c, n_layers, loop_step, layers, ctx_len, vq_len, max_ctx_len, sm_scale,
                          workspace, workspace_bytes, stream);
+}
+
+lvq_status lvq_decode_status(void *workspace, uint32_t *flags, int32_t clear, void *stream) {
+    if (!workspace || !flags) return LVQ_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t w = 0;
+    if (hipStreamSynchronize(st) != hipSuccess) return LVQ_ERR_HIP;
+    if (hipMemcpy(&w, workspace, sizeof w, hipMemcpyDeviceToHost) != hipSuccess) return LVQ_ERR_HIP;
+    if (clear && w != 0) {
+        const uint32_t zero = 0;
+        if (hipMemcpy(workspace, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+            return LVQ_ERR_HIP;
+    }
+    *flags = w;
+    return LVQ_OK;
+}
+
+int32_t lvq_decode_role(const lvq_config *c, int32_t n_layers, int32_t max_ctx_len,
+                        int32_t workgroup, int32_t *layer, int32_t *seq, int32_t *head) {
+    if (!config_ok(c) || n_layers < 1 || n_layers > lvq::kMaxLayersPerLaunch) return -1;
+    if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return -1;
+    const Splits sp = choose_splits(c, max_vq_tokens(c, max_ctx_len, true), n_layers);
+    const int64_t total = (int64_t)sp.n * c->batch * c->n_heads * n_layers;
+    if (workgroup < 0 || workgroup >= total) return -1;
+    const lvq::WgRole r = lvq::decode_role((unsigned)workgroup, (unsigned)total, (unsigned)sp.n);
+    const int64_t bh = (int64_t)c->batch * c->n_heads;
+    if (layer) *layer = (int32_t)(r.group / bh);
+    if (seq) *seq = (int32_t)(r.group % bh / c->n_heads);
+    if (head) *head = (int32_t)(r.group % c->n_heads);
+    return r.role;
 }
 
 }  // extern "C"

@@ -23,9 +23,15 @@ LVQ_MAX_WINDOW_GROUPS = 4
 LVQ_MAX_LAYERS = 4096
 N_CODES = 256
 
+LVQ_STATUS_MERGE_TIMEOUT, LVQ_STATUS_VALUE_RANGE = 1, 2
+# the workspace opens with a 256-byte header (the status word) followed by
+# one fixed-size block per (layer, b, h)
+WORKSPACE_HEADER_BYTES = 256
+
 EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
-           "lvq_decode_attn_layers", "lvq_decode_splits", "lvq_decode_window_groups",
-           "lvq_status_string")
+           "lvq_decode_attn_layers", "lvq_decode_status", "lvq_decode_role",
+           "lvq_decode_splits", "lvq_decode_window_groups", "lvq_status_string",
+           "lvq_encode_screen")
 
 
 class LoopVQError(RuntimeError):
@@ -38,7 +44,7 @@ class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
         "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops",
-        "decode_window_groups")]
+        "decode_window_groups", "decode_poll_limit")]
 
 
 class _DecodeLayer(ctypes.Structure):
@@ -77,6 +83,7 @@ class Config:
     n_kv_heads: int = 0          # 0: as many KV heads as query heads
     n_loops: int = 0             # 0: the model has loop_steps loop steps
     decode_window_groups: int = 0  # with decode_splits: workgroups taking window slots
+    decode_poll_limit: int = 0     # 0: the library's bound of a merger's wait
 
     @property
     def kv_heads(self) -> int:
@@ -110,6 +117,8 @@ def library() -> ctypes.CDLL:
         lib.lvq_cache_layout.argtypes = [cfgp, ctypes.POINTER(_Layout)]
         lib.lvq_encode.restype = i32
         lib.lvq_encode.argtypes = [cfgp, vp, ctypes.POINTER(i64), i64, vp, vp, i32, i64, vp]
+        lib.lvq_encode_screen.restype = i32
+        lib.lvq_encode_screen.argtypes = [cfgp, vp, ctypes.POINTER(i64), i64, vp, vp, i32, i64, vp, vp]
         lib.lvq_encode_kv.restype = i32
         lib.lvq_encode_kv.argtypes = [cfgp, vp, vp, ctypes.POINTER(i64), i64, vp, vp, vp, vp,
                                       i32, i64, vp]
@@ -119,6 +128,11 @@ def library() -> ctypes.CDLL:
         lib.lvq_decode_attn_layers.restype = i32
         lib.lvq_decode_attn_layers.argtypes = [cfgp, i32, i32, ctypes.POINTER(_DecodeLayer), vp, vp,
                                                i32, ctypes.c_float, vp, u64, vp]
+        lib.lvq_decode_status.restype = i32
+        lib.lvq_decode_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), i32, vp]
+        lib.lvq_decode_role.restype = i32
+        lib.lvq_decode_role.argtypes = [cfgp, i32, i32, i32, ctypes.POINTER(i32),
+                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
         lib.lvq_decode_splits.restype = i32
         lib.lvq_decode_splits.argtypes = [cfgp, i32]
         lib.lvq_decode_window_groups.restype = i32
@@ -161,6 +175,27 @@ def lvq_decode_window_groups(cfg: Config, max_ctx_len: int) -> int:
     return int(library().lvq_decode_window_groups(ctypes.byref(cfg.c()), int(max_ctx_len)))
 
 
+def lvq_decode_role(cfg: Config, n_layers: int, max_ctx_len: int, workgroup: int):
+    """(role, layer, seq, head) of a decode workgroup (host arithmetic), or
+    None for an invalid workgroup index or config."""
+    ly, sq, hd = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    r = library().lvq_decode_role(ctypes.byref(cfg.c()), int(n_layers), int(max_ctx_len),
+                                  int(workgroup), ctypes.byref(ly), ctypes.byref(sq),
+                                  ctypes.byref(hd))
+    return None if r < 0 else (int(r), ly.value, sq.value, hd.value)
+
+
+def lvq_decode_status(workspace: torch.Tensor, clear: bool = False, stream=None) -> int:
+    """Status flags (``LVQ_STATUS_*``) the decode calls set in ``workspace``;
+    waits for the stream.  ``clear`` zeroes them."""
+    flags = ctypes.c_uint32()
+    st = library().lvq_decode_status(_dev_ptr(workspace, "workspace"), ctypes.byref(flags),
+                                     int(bool(clear)), _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_decode_status", st)
+    return int(flags.value)
+
+
 def _dev_ptr(t, name, dtype=None, shape=None, allow_none=False):
     if t is None:
         if allow_none:
@@ -197,6 +232,25 @@ def lvq_encode(cfg: Config, x: torch.Tensor, codebook: torch.Tensor, index_cache
                               int(seq), int(first_token), _stream(stream))
     if st != LVQ_OK:
         raise LoopVQError("lvq_encode", st)
+
+
+def lvq_encode_screen(cfg: Config, x: torch.Tensor, codebook: torch.Tensor,
+                      index_cache: torch.Tensor, screen: torch.Tensor, seq: int = 0,
+                      first_token: int = 0, stream=None) -> None:
+    """:func:`lvq_encode` through the MFMA screen at any length, also storing
+    every screen value ``|c_k|^2 - 2 x.c_k`` into fp32 ``screen``
+    ``[n][Hk][S][256]`` (diagnostic, ``include/loopvq_diag.h``)."""
+    lay = lvq_cache_layout(cfg)
+    xp = _encode_input(cfg, x, "x")
+    strides = (ctypes.c_int64 * 3)(x.stride(0), x.stride(1), x.stride(2))
+    cbp = _dev_ptr(codebook, "codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"])
+    ip = _dev_ptr(index_cache, "index_cache", torch.uint8, lay["k_index"]["shape"])
+    sp = _dev_ptr(screen, "screen", torch.float32,
+                  (x.shape[0], cfg.kv_heads, lay["n_sub"], N_CODES))
+    st = library().lvq_encode_screen(ctypes.byref(cfg.c()), xp, strides, int(x.shape[0]), cbp, ip,
+                                     int(seq), int(first_token), sp, _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_encode_screen", st)
 
 
 def _encode_input(cfg: Config, x: torch.Tensor, name: str):

@@ -276,3 +276,33 @@ def fp32_sequential_argmin(xs: np.ndarray, cn: np.ndarray, fused: bool = False) 
         else:
             acc = (acc + (e * e).astype(np.float32)).astype(np.float32)
     return acc.argmin(-1)          # numpy returns the first (lowest) index on ties
+
+
+# fp16 rounding of a token weight (round to nearest: relative error <= 2^-11)
+# plus the fp32 summation order of a token's score (which lane, and so which
+# order, adds a token's table entries depends on the split: ~1e-6 relative)
+WEIGHT_ROUNDING = 2.0 ** -11 + 2e-6
+
+
+def weight_rounding_bound(c: Cache, t: int, ref: np.ndarray) -> np.ndarray:
+    """Per (b, h, ch): how far two decodes of the same cache may differ when
+    they split the tokens differently (split counts, token order).  The kernel
+    rounds each token weight p_n to fp16 (relative error u) and divides by the
+    sum of the same rounded weights, so its output is the exact weighted mean
+    of the values with weights p_n (1 + d_n), |d_n| <= u:
+        o - o* = sum_n p_n d_n (v_n - o*) / sum_n p_n (1 + d_n),
+        |o - o*| <= u / (1 - u) * max_n |v_n - o*|,
+    and two such outputs differ by at most twice that.  Needs a cache whose
+    tokens are the values attended (exact windows; codeword VQ tokens), and
+    the oracle's output ``ref`` for o*."""
+    u = WEIGHT_ROUNDING
+    Hq, Hk = c.n_q_heads, c.n_heads
+    out = np.zeros(ref.shape, np.float64)
+    for b, L in enumerate(c.lengths):
+        if L == 0:
+            continue
+        V = c.v_tokens[b][:L, :, t, :].double().numpy()         # [L][Hk][d]
+        for h in range(Hq):
+            spread = np.abs(V[:, h // (Hq // Hk), :] - ref[b, h][None, :]).max(axis=0)
+            out[b, h] = 2.0 * u / (1.0 - u) * spread + 1e-6 * np.abs(ref[b, h]).max()
+    return out

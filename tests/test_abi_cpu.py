@@ -28,9 +28,10 @@ def _cfg(B, H, d, Tc, G, T, dt, **kw):
 
 
 def test_library_exports_header_symbols():
-    header = (ROOT / "include" / "loopvq.h").read_text()
-    declared = set(re.findall(r"^\s*(?:const\s+char\s*\*|lvq_status|int32_t)\s*(lvq_\w+)\s*\(",
-                              header, flags=re.M))
+    declared = set()
+    for header in sorted((ROOT / "include").glob("*.h")):
+        declared |= set(re.findall(r"^\s*(?:const\s+char\s*\*|lvq_status|int32_t)\s*(lvq_\w+)\s*\(",
+                                   header.read_text(), flags=re.M))
     assert declared == set(lv.EXPORTS)
     lib = lv.library()
     for name in declared:
@@ -250,7 +251,8 @@ def test_decode_layers_validation():
     assert _decode_layers(cfg, layer_over={(0, "v_codebook"): P.value + 8}) == INV
     assert _decode_layers(cfg, loop_step=4) == INV
     assert _decode_layers(cfg, sm_scale=float("inf")) == INV
-    assert _decode_layers(cfg, ws_bytes=3 * per - 1) == WS              # one workspace per layer
+    hdr = lv.WORKSPACE_HEADER_BYTES
+    assert _decode_layers(cfg, ws_bytes=hdr + 3 * (per - hdr) - 1) == WS   # one block set per layer
     assert _decode_layers(cfg, ws=None) == WS
     assert _decode_layers(_cfg(1, 2, 384, 4, 16, 1024, lv.LVQ_BF16)) == UNS
 
@@ -278,3 +280,72 @@ def test_encode_validation():
     assert _encode(_cfg(1, 1, 64, 4, 64, 100, lv.LVQ_BF16)) == UNS      # G = 64
     assert _encode(_cfg(1, 1, 128, 4, 32, 100, lv.LVQ_F32)) == UNS      # fp32, G = 32
     assert _encode(cfg, n=0) == lv.LVQ_OK                              # nothing to launch
+
+
+# --- workspace grid and merge roles (host arithmetic) ---------------------------
+
+def test_workspace_grid_is_fixed():
+    """The workspace is a header plus one fixed-size block per (layer, b, h):
+    its size is linear in B * H and does not depend on head_dim, group or
+    context, so blocks keep their places when the batch changes."""
+    size = lambda **kw: lv.lvq_cache_layout(_cfg(**{**dict(B=1, H=16, d=128, Tc=4, G=16,  # noqa: E731
+                                                       T=4096, dt=lv.LVQ_BF16), **kw}))["workspace_bytes"]
+    hdr = lv.WORKSPACE_HEADER_BYTES
+    blk = size(B=1, H=1) - hdr
+    assert blk % 256 == 0 and blk >= lv.LVQ_MAX_SPLITS * (128 + 2) * 8
+    for B, H in ((1, 16), (32, 16), (64, 16), (3, 5)):
+        assert size(B=B, H=H) == hdr + B * H * blk
+    assert size(d=64) == size(d=128) == size(G=32) == size(T=40000)
+
+
+def _roles(B, H, n, layers=1, L=32768):
+    """role, (layer, seq, head) of every workgroup of a forced n-split launch"""
+    cfg = _cfg(B, H, 128, 4, 16, max(L, 1), lv.LVQ_BF16, decode_splits=n)
+    total = n * B * H * layers
+    out = [lv.lvq_decode_role(cfg, layers, L, p) for p in range(total)]
+    assert lv.lvq_decode_role(cfg, layers, L, total) is None
+    assert lv.lvq_decode_role(cfg, layers, L, -1) is None
+    return out
+
+
+def test_merge_roles_follow_dispatch_order():
+    """For every launch of at most 256 workgroups (every split count 1..64
+    and number of (b, h) groups): each group gets roles 0..n-1 once, the
+    member with role n - 1 (the merger of a window-workgroup launch) is the
+    group's last in dispatch order, and a group that fits one XCD slab sits
+    on one XCD (dispatch index mod 8)."""
+    checked = 0
+    for n in range(1, lv.LVQ_MAX_SPLITS + 1):
+        for groups in range(1, 256 // n + 1):
+            roles = _roles(groups, 1, n)
+            members = {}
+            for p, r in enumerate(roles):
+                assert r is not None
+                members.setdefault((r[1], r[2], r[3]), []).append((p, r[0]))
+            assert len(members) == groups
+            total = n * groups
+            for key, ms in members.items():
+                assert sorted(r for _, r in ms) == list(range(n)), (n, groups, key)
+                last = max(ms)                   # highest dispatch index
+                assert last[1] == n - 1, (n, groups, key, ms)
+                # roles follow dispatch order within the group
+                assert [r for _, r in sorted(ms)] == list(range(n)), (n, groups, key)
+                if total % 8 == 0:
+                    slab = total // 8
+                    g = key[1]
+                    if (g * n) // slab == (g * n + n - 1) // slab:
+                        assert len({p % 8 for p, _ in ms}) == 1
+            checked += 1
+    assert checked > 1000
+
+
+def test_merge_roles_multi_layer():
+    """Layers are the outermost groups; roles still follow dispatch order."""
+    for B, H, n, layers in ((1, 16, 5, 3), (2, 3, 7, 4), (1, 2, 16, 8)):
+        roles = _roles(B, H, n, layers)
+        members = {}
+        for p, r in enumerate(roles):
+            members.setdefault(r[1:], []).append((p, r[0]))
+        assert set(members) == {(l, b, h) for l in range(layers) for b in range(B) for h in range(H)}
+        for ms in members.values():
+            assert [r for _, r in sorted(ms)] == list(range(n))

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from cases import (DeviceCache, make_cache, merge_loop_groups, oracle_decode, oracle_encoder,
-                   rel_err_rows)
+                   rel_err_rows, weight_rounding_bound)
 from sub_bit_vq_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -140,10 +140,13 @@ def test_split_count_invariance(lv):
         assert rel_err_rows(got, ref) <= TOL, splits
         outs.append(got)
     # split counts change each wave's running max and hence the fp16 rounding
-    # of the token weights (2^-11 relative); a dropped or doubled split would
-    # move the output by ~1/splits
+    # of the token weights (2^-11 relative): the outputs may differ by the
+    # bound that rounding implies (a dropped or doubled split would move the
+    # output by ~1/splits)
+    bound = weight_rounding_bound(c, 1, ref)
     for o in outs[1:]:
-        assert rel_err_rows(o, outs[0]) <= 5e-4
+        assert (np.abs(o - outs[0]) <= bound).all()
+        _note(f"  largest difference / bound: {float((np.abs(o - outs[0]) / bound).max()):.3f}")
 
 
 def test_window_group_counts(lv):
@@ -161,11 +164,12 @@ def test_window_group_counts(lv):
             ref = oracle_decode(oracle, c, t)
             base = dc.decode(t)
             assert rel_err_rows(base, ref) <= TOL, (G, t)
+            bound = weight_rounding_bound(c, t, ref)
             for splits, w in ((2, 1), (5, 2), (5, 3), (6, 4), (9, 4)):
                 cfg = dataclasses.replace(dc.cfg, decode_splits=splits, decode_window_groups=w)
                 got = dc.decode(t, cfg=cfg)
                 assert rel_err_rows(got, ref) <= TOL, (G, t, splits, w)
-                assert rel_err_rows(got, base) <= 5e-4, (G, t, splits, w)
+                assert (np.abs(got - base) <= bound).all(), (G, t, splits, w)
 
 
 def test_window_groups_small_windows(lv):
@@ -196,7 +200,7 @@ def test_longest_first_order(lv):
         ref = oracle_decode(oracle, c, t)
         got = dc.decode(t, cfg=cfg)
         assert rel_err_rows(got, ref) <= TOL, t
-        assert rel_err_rows(got, dc.decode(t)) <= 5e-4, t
+        assert (np.abs(got - dc.decode(t)) <= weight_rounding_bound(c, t, ref)).all(), t
 
 
 @pytest.mark.parametrize("batch", [256, 257])
@@ -223,11 +227,12 @@ def test_token_permutation_invariance(lv):
                    codeword_tokens=True)
     dc = DeviceCache(lv, c)
     base = dc.decode(2)
+    bound = weight_rounding_bound(c, 2, oracle_decode(oracle, c, 2))
     lo, hi = c.vq_range(0).start, c.vq_range(0).stop
     perm = torch.randperm(hi - lo, generator=torch.Generator().manual_seed(3)) + lo
     dc.k_index[0, :, lo:hi] = dc.k_index[0, :, perm.cuda()]
     dc.v_index[0, :, lo:hi] = dc.v_index[0, :, perm.cuda()]
-    assert rel_err_rows(dc.decode(2), base) <= 5e-4
+    assert (np.abs(dc.decode(2) - base) <= bound).all()
 
 
 def test_slice_isolation_nan(lv):
@@ -273,10 +278,9 @@ def test_sm_scale(lv):
 
 
 def test_empty_context_and_repeat(lv):
-    """L = 0 gives zeros; repeated calls on one workspace stay correct (the
-    merge tickets reset themselves).  Repeats agree to rounding only: where
-    the last workgroup to arrive merges the partials, which one that is (and
-    with it the order of the merge's sums) can change from run to run."""
+    """L = 0 gives zeros; repeated calls on one workspace give identical bits
+    (the blocks' epochs advance themselves, and the merge adds the split
+    partials in slot order whichever workgroup merges)."""
     _note("empty + repeat")
     c = make_cache(batch=3, n_heads=2, head_dim=64, group=16, lengths=(1, 900, 1), seed=16,
                    codeword_tokens=True)
@@ -289,7 +293,7 @@ def test_empty_context_and_repeat(lv):
     for _ in range(3):
         r = dc.decode(0)
         assert np.all(r[0] == 0.0)
-        assert rel_err_rows(r, a) <= 2e-6
+        assert np.array_equal(r, a)
     b = dc.decode(3)
     assert rel_err_rows(b, oracle_decode(oracle, c, 3)) <= TOL
 
@@ -307,7 +311,7 @@ def test_max_ctx_len_bound(lv):
     assert rel_err_rows(got, oracle_decode(oracle, c, 1)) <= TOL
 
 
-# --- full-size workloads: sampled against the oracle ---------------------------
+# --- full-size grouped-query workload -----------------------------------------
 
 def _full_size_cache(lv, H, d, G, lengths, seed, device="cuda", Hq=None):
     """Device-resident cache at full size (H KV heads, Hq query heads):
@@ -342,40 +346,13 @@ def _full_size_cache(lv, H, d, G, lengths, seed, device="cuda", Hq=None):
     return cfg, bufs, kcb, vcb, q, ctx
 
 
-def _host_slice(t, b):
-    return t[b:b + 1].cpu()
-
-
-@pytest.mark.parametrize("G", [16, 32])
-def test_full_32k_context(lv, G):
-    """One 32768-token sequence, 16 heads, d = 128, 0.5 bit (G = 16) and
-    0.25 bit (G = 32): every head at loop steps 0 and 3 against the oracle,
-    in the launch configuration the benchmark times."""
-    _note(f"32K G={G}")
-    cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 16, 128, G, [32768], seed=100 + G)
-    for t in (0, 3):
-        lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, 32768, bufs["k_index"],
-                           bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
-                           bufs["workspace"], bufs["out"])
-        torch.cuda.synchronize()
-        got = bufs["out"].double().cpu().numpy()
-        ref = oracle.decode_attn(loop_step=t, q=q[t].cpu(), ctx_len=[32768],
-                                 k_index=bufs["k_index"].cpu(), v_index=bufs["v_index"].cpu(),
-                                 k_codebook=kcb.cpu(), v_codebook=vcb.cpu(),
-                                 k_window=bufs["k_window"].cpu(), v_window=bufs["v_window"].cpu(),
-                                 n_sink=64, n_recent=256, group=G)
-        err = rel_err_rows(got, ref)
-        _note(f"  t={t} rel err {err:.2e}")
-        assert err <= TOL
-
-
 def test_full_32k_gqa(lv):
     """32 query heads over 8 KV heads, one 32768-token sequence, 0.5 bit:
-    every query head at loop steps 1 and 2 against the oracle, in the launch
+    every query head at every loop step against the oracle, in the launch
     configuration the benchmark's GQA workload times."""
     _note("32K GQA 32q/8kv")
     cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 8, 128, 16, [32768], seed=500, Hq=32)
-    for t in (1, 2):
+    for t in range(4):
         lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, 32768, bufs["k_index"],
                            bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
                            bufs["workspace"], bufs["out"])
@@ -388,33 +365,4 @@ def test_full_32k_gqa(lv):
                                  n_sink=64, n_recent=256, group=16)
         err = rel_err_rows(got, ref)
         _note(f"  t={t} rel err {err:.2e}")
-        assert err <= TOL
-
-
-def test_batched_ragged_64(lv):
-    """Batch 64, L_b = 2048 + U{4096, 8192, 16384}, 16 heads: sampled (b, h)
-    rows of one sequence per length class against the oracle."""
-    _note("batch 64 ragged")
-    lengths = synth.ragged_lengths(64, seed=1003)
-    cfg, bufs, kcb, vcb, q, ctx = _full_size_cache(lv, 16, 128, 16, lengths, seed=300)
-    t = 2
-    lv.lvq_decode_attn(cfg, t, q[t].contiguous(), ctx, max(lengths), bufs["k_index"],
-                       bufs["v_index"], kcb, vcb, bufs["k_window"], bufs["v_window"],
-                       bufs["workspace"], bufs["out"])
-    torch.cuda.synchronize()
-    out = bufs["out"].double().cpu().numpy()
-    picked = {}
-    for b, L in enumerate(lengths):
-        picked.setdefault(L, b)
-    kcb_h, vcb_h = kcb.cpu(), vcb.cpu()
-    for L, b in sorted(picked.items()):
-        ref = oracle.decode_attn(loop_step=t, q=_host_slice(q[t], b), ctx_len=[L],
-                                 k_index=_host_slice(bufs["k_index"], b),
-                                 v_index=_host_slice(bufs["v_index"], b),
-                                 k_codebook=kcb_h, v_codebook=vcb_h,
-                                 k_window=_host_slice(bufs["k_window"], b),
-                                 v_window=_host_slice(bufs["v_window"], b),
-                                 n_sink=64, n_recent=256, group=16, heads=(0, 16))
-        err = rel_err_rows(out[b:b + 1], ref)
-        _note(f"  b={b} L={L} rel err {err:.2e}")
         assert err <= TOL

@@ -276,18 +276,3 @@ def test_placement_and_untouched_rows(lv):
     got = _gpu_encode(lv, x, cb, H, d, Tc, G, T=300, B=3, seq=2, first=123, fill=0xCD)
     ref = _oracle_encode(x, cb, H, d, Tc, G, T=300, B=3, seq=2, first=123, fill=0xCD)
     _assert_same(got, ref, "placement")
-
-
-def test_full_prefill_sampled(lv):
-    """32768 tokens x 16 heads x 4 loop steps x 128 channels, G = 16 (the
-    prefill-encoder workload): the GPU encodes everything, the oracle a seeded
-    sample of 256 tokens (all heads and sub-vectors)."""
-    _note("full prefill sampled")
-    N, H, Tc, d, G = 32768, 16, 4, 128, 16
-    x = synth.loop_correlated_kv(N, H, Tc, d, seed=1004, device="cuda")
-    cb = synth.codebooks(H, d, Tc, G, seed=1005, device="cuda")
-    got = _gpu_encode(lv, x, cb, H, d, Tc, G)[0]                 # [H][N][S]
-    pick = torch.randperm(N, generator=torch.Generator().manual_seed(9))[:256].sort().values
-    xs = x[pick.cuda()].cpu()
-    ref = _oracle_encode(xs, cb.cpu(), H, d, Tc, G)[0]            # [H][256][S]
-    _assert_same(got[:, pick.numpy()], ref, "prefill sample")
