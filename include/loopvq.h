@@ -265,6 +265,39 @@ lvq_status lvq_decode_attn(const lvq_config *cfg, int32_t loop_step, const void 
                            const void *v_window, float sm_scale, void *workspace,
                            uint64_t workspace_bytes, float *out, void *stream);
 
+/*
+ * lvq_decode_attn for callers that cannot allocate device memory at all (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with no workspace argument.
+ * The split partials live in a static device array of the library
+ * (LVQ_NOALLOC_SCRATCH_BYTES per device, zero at load and kept until the
+ * process ends; its address is looked up with hipGetSymbolAddress on a
+ * device's first call, which allocates nothing).  The call itself calls no
+ * allocating routine.
+ *
+ * Limit: a call whose plan merges split partials (more than one workgroup
+ * per (b, h), e.g. long contexts at small batch) may cover at most
+ * LVQ_NOALLOC_MAX_HEADS (b, h) pairs; larger ones return LVQ_ERR_WORKSPACE
+ * before anything is launched.  Calls with one workgroup per (b, h) (e.g. a
+ * batch of 64 sequences of 16 heads) have no limit.
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (other streams, other threads) race and must not be
+ * made.  The status flags these calls set are kept in the array and cannot
+ * be read; a merge that timed out shows as a NaN row of out, after which
+ * later merging calls on that device may be wrong (the array cannot be
+ * cleared): use lvq_decode_attn with a workspace of your own then.
+ * Arguments, results and other errors as for lvq_decode_attn.
+ */
+#define LVQ_NOALLOC_MAX_HEADS 256
+#define LVQ_NOALLOC_SCRATCH_BYTES 17105152u
+lvq_status lvq_decode_attn_noalloc(const lvq_config *cfg, int32_t loop_step, const void *q,
+                                   const int32_t *ctx_len, const int32_t *vq_len,
+                                   int32_t max_ctx_len, const uint8_t *k_index,
+                                   const uint8_t *v_index, const void *k_codebook,
+                                   const void *v_codebook, const void *k_window,
+                                   const void *v_window, float sm_scale, float *out,
+                                   void *stream);
+
 /* The operands of one layer of lvq_decode_attn_layers: the device buffers
  * that lvq_decode_attn takes, with the same layouts and alignments. */
 typedef struct {

@@ -57,7 +57,15 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
+
+// Workspace of lvq_decode_attn_noalloc: a file-scope device array (zero at
+// load, one copy per device, held until the process ends).  Host code never
+// passes its name to a kernel (on the host it is only a stand-in for the
+// symbol); it passes the device address that hipGetSymbolAddress returns for
+// the device the call runs on (lvq::scratch_address).
+static __device__ __align__(256) unsigned char scratch[lvq::kScratchBytes];
 
 namespace lvq {
 namespace {
@@ -769,7 +777,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // The block's epoch cannot change before this workgroup arrives, so it is
     // read now, overlapped with the prologue; it tags the partials.
     uint64_t arrival_word = 0;
-    if (tid == 0) arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0 && a.n_split > 1)
+        arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
     {
         const int slice = vq_wg ? 256 * S * CG * (int)sizeof(CB) : 0;
@@ -978,9 +987,15 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < G; ++g) o += red[g * D + tid];
     }
+    // One workgroup per (b, h): nothing to merge, and the workspace is not
+    // touched.
+    if (n == 1) {
+        if (tid < D) outp[tid] = lt > 0.f ? o / lt : 0.f;
+        return;
+    }
     // Every workgroup publishes at once (before it knows whether it is last,
     // so the others' pairs are already on their way when the last one looks).
-    if (n > 1 && sep) {
+    if (sep) {
         if (split != n - 1) {                    // token splits publish and leave
             if (tid < D) publish(&part[2 + tid], o, tag);
             if (tid == 0) {
@@ -989,7 +1004,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             }
             return;
         }
-    } else if (n > 1) {
+    } else {
         if (tid < D) publish(&part[2 + tid], o, tag);
         if (tid == 0) {
             publish(&part[0], M, tag);
@@ -1091,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     if (tid < D)
         reinterpret_cast<uint32_t *>(outp)[tid] =
             failed ? 0x7fc00000u : __float_as_uint(den > 0.f ? num / den : 0.f);
-    if (tid == 0 && n > 1) {
+    if (tid == 0) {
         if (failed) __hip_atomic_fetch_or(a.status, kStatusMergeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t next = epoch + 1u == kEpochWrap ? 0u : epoch + 1u;
         __hip_atomic_store(ticket, (uint64_t)next << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1130,7 +1145,39 @@ hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+hipError_t scratch_address(hipStream_t stream, void **addr) {
+    static std::mutex mu;
+    static void *cached[kMaxDevices] = {};
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!cached[dev]) {
+        // the address is per device: look it up with that device current
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        cached[dev] = ptr;
+    }
+    *addr = cached[dev];
+    return hipSuccess;
+}
 
 bool decode_supported(int d, int S, int cg, int cb_bf16) {
 #define LVQ_FIT(S_, CG_) \

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/loopvq.h"
+
 namespace lvq {
 
 // Workspace of lvq_decode_attn.  A 256-byte header (a uint32 status word at
@@ -31,6 +33,14 @@ constexpr uint64_t kSlotBase = 256;          // byte offset of slot 0 in a block
 constexpr uint64_t kBlockBytes = kSlotBase + (uint64_t)kSlots * (kMaxDecodeDim + 2) * 8;
 static_assert(kBlockBytes % 256 == 0, "blocks stay 256-byte aligned");
 constexpr uint32_t kEpochWrap = 0xffffffffu; // epochs run 0 .. kEpochWrap - 1
+
+// lvq_decode_attn_noalloc's workspace: a static device array holding the
+// header and kScratchBlocks blocks (launches that merge may use at most that
+// many (layer, b, h) groups)
+constexpr uint64_t kScratchBlocks = 256;
+constexpr uint64_t kScratchBytes = kHeaderBytes + kScratchBlocks * kBlockBytes;
+static_assert(kScratchBlocks == LVQ_NOALLOC_MAX_HEADS && kScratchBytes == LVQ_NOALLOC_SCRATCH_BYTES,
+              "the header states the static workspace's size");
 
 // status flags (include/loopvq.h: LVQ_STATUS_*)
 constexpr uint32_t kStatusMergeTimeout = 1u;  // a merge gave up waiting; its row is NaN
@@ -152,6 +162,9 @@ struct EncodeArgs {
 bool decode_supported(int d, int S, int cg, int cb_bf16);
 bool encode_supported(int G, int cg, int S, int cb_bf16);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// device address of the static workspace on the device of `stream` (looked
+// up once per device)
+hipError_t scratch_address(hipStream_t stream, void **addr);
 hipError_t launch_encode(const EncodeArgs &a, hipStream_t stream);
 
 }  // namespace lvq

@@ -292,10 +292,14 @@ namespace {
 // Every check of a decode call, then one launch per kMaxLayersPerLaunch
 // layers.  Layer l uses the workspace blocks (l * B + b) * H + h after the
 // header.
+// With use_scratch the workspace is the library's static device array
+// (lvq_decode_attn_noalloc): it needs room for the blocks only where a launch
+// merges, and its address is looked up once every check has passed.
 lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_step,
                          const lvq_decode_layer *layers, const int32_t *ctx_len,
                          const int32_t *vq_len, int32_t max_ctx_len, float sm_scale,
-                         void *workspace, uint64_t workspace_bytes, void *stream) {
+                         void *workspace, uint64_t workspace_bytes, void *stream,
+                         bool use_scratch = false) {
     if (!config_ok(c)) return LVQ_ERR_INVALID_ARG;
     if (n_layers < 1 || n_layers > LVQ_MAX_LAYERS || !layers || !ctx_len) return LVQ_ERR_INVALID_ARG;
     if (loop_step < 0 || loop_step >= n_loops(c)) return LVQ_ERR_INVALID_ARG;
@@ -327,12 +331,24 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
     // the header, then one block per (layer, b, h); n_layers single-layer
     // workspaces hold that
     const uint64_t per_layer = lvq::layer_block_bytes(c->batch, c->n_heads);
-    if (!workspace || workspace_bytes < lvq::kHeaderBytes ||
-        (workspace_bytes - lvq::kHeaderBytes) / per_layer < (uint64_t)n_layers)
-        return LVQ_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
-
     const int64_t max_vq = max_vq_tokens(c, max_ctx_len, vq_len == nullptr);
+    if (use_scratch) {
+        workspace_bytes = lvq::kScratchBytes;
+        for (int32_t l0 = 0; l0 < n_layers; l0 += lvq::kMaxLayersPerLaunch) {
+            const int32_t nl = std::min<int32_t>(lvq::kMaxLayersPerLaunch, n_layers - l0);
+            if (choose_splits(c, max_vq, nl).n > 1 &&
+                (workspace_bytes - lvq::kHeaderBytes) / per_layer < (uint64_t)(l0 + nl))
+                return LVQ_ERR_WORKSPACE;
+        }
+        const hipError_t e = lvq::scratch_address(static_cast<hipStream_t>(stream), &workspace);
+        if (e != hipSuccess) return LVQ_ERR_HIP;
+    } else {
+        if (!workspace || workspace_bytes < lvq::kHeaderBytes ||
+            (workspace_bytes - lvq::kHeaderBytes) / per_layer < (uint64_t)n_layers)
+            return LVQ_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(workspace) % 256) return LVQ_ERR_INVALID_ARG;
+    }
+
     const int64_t Hk = kv_heads(c);
     const size_t W = (size_t)c->n_sink + c->n_recent;
     for (int32_t l0 = 0; l0 < n_layers; l0 += lvq::kMaxLayersPerLaunch) {
@@ -405,6 +421,18 @@ lvq_status lvq_decode_attn(const lvq_config *c, int32_t loop_step, const void *q
     const lvq_decode_layer layer{q, k_index, v_index, k_codebook, v_codebook, k_window, v_window, out};
     return decode_layers(c, 1, loop_step, &layer, ctx_len, vq_len, max_ctx_len, sm_scale, workspace,
                          workspace_bytes, stream);
+}
+
+lvq_status lvq_decode_attn_noalloc(const lvq_config *c, int32_t loop_step, const void *q,
+                                   const int32_t *ctx_len, const int32_t *vq_len,
+                                   int32_t max_ctx_len, const uint8_t *k_index,
+                                   const uint8_t *v_index, const void *k_codebook,
+                                   const void *v_codebook, const void *k_window,
+                                   const void *v_window, float sm_scale, float *out,
+                                   void *stream) {
+    const lvq_decode_layer layer{q, k_index, v_index, k_codebook, v_codebook, k_window, v_window, out};
+    return decode_layers(c, 1, loop_step, &layer, ctx_len, vq_len, max_ctx_len, sm_scale, nullptr, 0,
+                         stream, true);
 }
 
 lvq_status lvq_decode_attn_layers(const lvq_config *c, int32_t n_layers, int32_t loop_step,

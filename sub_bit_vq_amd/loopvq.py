@@ -28,8 +28,10 @@ LVQ_STATUS_MERGE_TIMEOUT, LVQ_STATUS_VALUE_RANGE = 1, 2
 # one fixed-size block per (layer, b, h)
 WORKSPACE_HEADER_BYTES = 256
 
+LVQ_NOALLOC_MAX_HEADS = 256
+
 EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
-           "lvq_decode_attn_layers", "lvq_decode_status", "lvq_decode_role",
+           "lvq_decode_attn_noalloc", "lvq_decode_attn_layers", "lvq_decode_status", "lvq_decode_role",
            "lvq_decode_splits", "lvq_decode_window_groups", "lvq_status_string",
            "lvq_encode_screen")
 
@@ -125,6 +127,9 @@ def library() -> ctypes.CDLL:
         lib.lvq_decode_attn.restype = i32
         lib.lvq_decode_attn.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
                                         ctypes.c_float, vp, u64, vp, vp]
+        lib.lvq_decode_attn_noalloc.restype = i32
+        lib.lvq_decode_attn_noalloc.argtypes = [cfgp, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                                ctypes.c_float, vp, vp]
         lib.lvq_decode_attn_layers.restype = i32
         lib.lvq_decode_attn_layers.argtypes = [cfgp, i32, i32, ctypes.POINTER(_DecodeLayer), vp, vp,
                                                i32, ctypes.c_float, vp, u64, vp]
@@ -309,6 +314,34 @@ def lvq_decode_attn(cfg: Config, loop_step: int, q: torch.Tensor, ctx_len: torch
     st = library().lvq_decode_attn(ctypes.byref(cfg.c()), int(loop_step), *args, _stream(stream))
     if st != LVQ_OK:
         raise LoopVQError("lvq_decode_attn", st)
+
+
+def lvq_decode_attn_noalloc(cfg: Config, loop_step: int, q: torch.Tensor, ctx_len: torch.Tensor,
+                            max_ctx_len: int, k_index, v_index, k_codebook, v_codebook, k_window,
+                            v_window, out: torch.Tensor, sm_scale: float = 1.0,
+                            vq_len: torch.Tensor | None = None, stream=None) -> None:
+    """:func:`lvq_decode_attn` with the library's static device workspace
+    (allocates nothing; calls on one device must not overlap)."""
+    lay = lvq_cache_layout(cfg)
+    B = cfg.batch
+    args = [
+        _dev_ptr(q, "q", torch.bfloat16, lay["query"]["shape"]),
+        _dev_ptr(ctx_len, "ctx_len", torch.int32, (B,)),
+        _dev_ptr(vq_len, "vq_len", torch.int32, (B,), allow_none=True),
+        int(max_ctx_len),
+        _dev_ptr(k_index, "k_index", torch.uint8, lay["k_index"]["shape"]),
+        _dev_ptr(v_index, "v_index", torch.uint8, lay["v_index"]["shape"]),
+        _dev_ptr(k_codebook, "k_codebook", cfg.torch_codebook_dtype, lay["k_codebook"]["shape"]),
+        _dev_ptr(v_codebook, "v_codebook", cfg.torch_codebook_dtype, lay["v_codebook"]["shape"]),
+        _dev_ptr(k_window, "k_window", torch.bfloat16, lay["k_window"]["shape"]),
+        _dev_ptr(v_window, "v_window", torch.bfloat16, lay["v_window"]["shape"]),
+        ctypes.c_float(sm_scale),
+        _dev_ptr(out, "out", torch.float32, lay["output"]["shape"]),
+    ]
+    st = library().lvq_decode_attn_noalloc(ctypes.byref(cfg.c()), int(loop_step), *args,
+                                           _stream(stream))
+    if st != LVQ_OK:
+        raise LoopVQError("lvq_decode_attn_noalloc", st)
 
 
 LAYER_KEYS = ("q", "k_index", "v_index", "k_codebook", "v_codebook", "k_window", "v_window", "out")

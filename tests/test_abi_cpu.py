@@ -217,6 +217,36 @@ def test_decode_validation():
                                         ctypes.c_uint64(1 << 30), P, None) == INV
 
 
+def _decode_noalloc(cfg, **over):
+    a = dict(loop_step=0, q=P, ctx_len=P, vq_len=None, max_ctx_len=cfg.max_tokens, k_index=P,
+             v_index=P, k_cb=P, v_cb=P, k_win=P, v_win=P, sm_scale=1.0, out=P)
+    a.update(over)
+    return lv.library().lvq_decode_attn_noalloc(
+        ctypes.byref(cfg.c()), a["loop_step"], a["q"], a["ctx_len"], a["vq_len"],
+        a["max_ctx_len"], a["k_index"], a["v_index"], a["k_cb"], a["v_cb"], a["k_win"],
+        a["v_win"], ctypes.c_float(a["sm_scale"]), a["out"], None)
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free entry point checks its arguments like
+    lvq_decode_attn, and rejects a merging plan over more (b, h) pairs than
+    its static workspace holds, before any HIP call."""
+    cfg = _cfg(1, 2, 64, 4, 16, 1024, lv.LVQ_BF16)
+    INV, UNS, WS = lv.LVQ_ERR_INVALID_ARG, lv.LVQ_ERR_UNSUPPORTED, lv.LVQ_ERR_WORKSPACE
+    assert _decode_noalloc(cfg, q=None) == INV
+    assert _decode_noalloc(cfg, out=None) == INV
+    assert _decode_noalloc(cfg, loop_step=4) == INV
+    assert _decode_noalloc(cfg, k_win=ctypes.c_void_p(P.value + 8)) == INV
+    assert _decode_noalloc(_cfg(1, 2, 256, 4, 16, 1024, lv.LVQ_BF16)) == UNS
+    limit = lv.LVQ_NOALLOC_MAX_HEADS
+    big = _cfg(20, 16, 64, 4, 16, 1200, lv.LVQ_BF16, decode_splits=2)   # 320 > 256 pairs, merging
+    assert 20 * 16 > limit and lv.lvq_decode_splits(big, 1200) == 2
+    assert _decode_noalloc(big) == WS
+    hdr = lv.WORKSPACE_HEADER_BYTES
+    blk = lv.lvq_cache_layout(_cfg(1, 1, 64, 4, 16, 16, lv.LVQ_BF16))["workspace_bytes"] - hdr
+    assert hdr + limit * blk == 17105152          # LVQ_NOALLOC_SCRATCH_BYTES
+
+
 def _decode_layers(cfg, n_layers=3, layer_over=None, **over):
     lay = lv.lvq_cache_layout(cfg)
     arr = (lv._DecodeLayer * max(1, n_layers))()
