@@ -125,29 +125,46 @@ def test_merge_timeout_is_flagged(lv):
     assert lv.lvq_decode_status(dc.ws) == 0
 
 
-def test_value_range_is_flagged(lv):
+@pytest.mark.parametrize("splits", [0, 40, 1])
+def test_value_range_is_flagged(lv, splits):
     """A bf16 value codebook entry of 2^17 in slice 1 (beyond fp16): a decode
     of loop step 1 flags it; decodes of other steps (which read other
-    slices) do not."""
-    _note("value range flag")
-    c = make_cache(batch=1, n_heads=2, head_dim=128, group=16, lengths=(3000,), seed=75,
+    slices) do not.  Each plan checks the slice its own way: the library's
+    plan (window workgroups check it), 40 splits (arrival tickets: the VQ
+    workgroups share the staged pieces) and one workgroup per (b, h) (it
+    checks everything it stages)."""
+    _note(f"value range flag, splits {splits}")
+    c = make_cache(batch=1, n_heads=8, head_dim=128, group=16, lengths=(3000,), seed=75,
                    codeword_tokens=True)
-    dc = DeviceCache(lv, c)
+    dc = DeviceCache(lv, c, decode_splits=splits)
+    wg = lv.lvq_decode_window_groups(dc.cfg, 3000)
+    assert (wg > 0) == (splits == 0)
     for t in range(4):
         dc.decode(t)
         assert lv.lvq_decode_status(dc.ws, clear=True) == 0, t
-    dc.v_cb[1, 1, 200, 17, 2] = 2.0 ** 17
-    for t in (0, 2, 3):
-        dc.decode(t)
-        assert lv.lvq_decode_status(dc.ws, clear=True) == 0, t
-    dc.decode(1)
-    assert lv.lvq_decode_status(dc.ws, clear=True) == lv.LVQ_STATUS_VALUE_RANGE
-    dc.v_cb[1, 1, 200, 17, 2] = -2.0 ** 16
-    dc.decode(1)
-    assert lv.lvq_decode_status(dc.ws, clear=True) == lv.LVQ_STATUS_VALUE_RANGE
-    dc.v_cb[1, 1, 200, 17, 2] = 65280.0                # the largest bf16 below 2^16: in range
-    dc.decode(1)
-    assert lv.lvq_decode_status(dc.ws, clear=True) == 0
+    for code, sub in ((200, 17), (0, 0), (255, 31)):
+        dc.v_cb[1, 5, code, sub, 2] = 2.0 ** 17
+        for t in (0, 2, 3):
+            dc.decode(t)
+            assert lv.lvq_decode_status(dc.ws, clear=True) == 0, (code, sub, t)
+        dc.decode(1)
+        assert lv.lvq_decode_status(dc.ws, clear=True) == lv.LVQ_STATUS_VALUE_RANGE, (code, sub)
+        dc.v_cb[1, 5, code, sub, 2] = -2.0 ** 16
+        dc.decode(1)
+        assert lv.lvq_decode_status(dc.ws, clear=True) == lv.LVQ_STATUS_VALUE_RANGE, (code, sub)
+        dc.v_cb[1, 5, code, sub, 2] = 65280.0          # the largest bf16 below 2^16: in range
+        dc.decode(1)
+        assert lv.lvq_decode_status(dc.ws, clear=True) == 0, (code, sub)
+    # in range, the flag-free decode is still right
+    assert rel_err_rows(dc.decode(1), oracle_decode(oracle, _with_codebooks(c, dc), 1)) <= TOL
+
+
+def _with_codebooks(c, dc):
+    """the cache with the device's (edited) codebooks"""
+    import copy
+    c2 = copy.copy(c)
+    c2.k_codebook, c2.v_codebook = dc.k_cb.cpu(), dc.v_cb.cpu()
+    return c2
 
 
 @pytest.mark.parametrize("splits", [0, 6, 50])
