@@ -29,8 +29,10 @@
 // Every wave keeps its own running max, weight sum and accumulators (online
 // softmax, base 2), so the token loop has no barrier; per-token score sums
 // use DPP.  Token weights p = 2^(s - m) enter the value sum as fp16
-// p * 2^14, and the weight sum adds the same rounded values, so the result is
+// p * 2^13, and the weight sum adds the same rounded values, so the result is
 // an exact weighted average with weights perturbed by at most 2^-11 relative.
+// The running max of the VQ tokens lags: it is raised only when a token
+// exceeds it by more than 2 (log2).
 // Where the R lanes of a token fill whole 4-lane blocks and a gather is 4
 // fp16 channels (S = 32, cg = 4: the 0.5-bit head_dim-128 cache), the value
 // sums run on the matrix cores: v_mfma_f32_4x4x4_16b_f16 with A = the 4
@@ -73,7 +75,9 @@ namespace {
 constexpr int kThreads = kDecodeThreads;
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = kDecodeUnroll;         // token passes per batch
-constexpr float kPScale = 16384.f;             // p' = p * 2^14 (normal in fp16 down to p ~ 4e-9)
+constexpr float kPScale = 8192.f;              // p' = p * 2^13 (normal in fp16 down to p ~ 7e-9)
+constexpr float kMaxSlack = 2.f;               // a VQ token may exceed the running max by this
+                                               // (log2) before it is raised: p' <= 2^15
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kMergeChunk = 16;                // partial slots loaded per poll
 constexpr int kVTab = 65536;                   // LDS byte offset of the value table
@@ -311,7 +315,7 @@ __device__ __forceinline__ constexpr uint32_t sel_v(int i) {
 }
 
 // Per-wave online-softmax state: running max m (base 2), weight sum l (scaled
-// by 2^14; every lane of a token adds its weight, so the wave sum counts each
+// by 2^13; every lane of a token adds its weight, so the wave sum counts each
 // token R times) and accumulators.
 template <int NACC>
 struct Online {
@@ -624,7 +628,11 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
         s[u] = ok[u] ? acc : -INFINITY;
         mx = fmaxf(mx, s[u]);
     }
-    st.raise(wave_max(mx));
+    // The running max is raised only when a token of the batch exceeds it by
+    // more than kMaxSlack (rare after the first batch): the weights of the
+    // others stay exact relative to it, and p' = 2^(s - m) * 2^13 <= 2^15 fits
+    // fp16.  A ballot replaces a wave-wide max reduction per batch.
+    if (__ballot(mx > st.m + kMaxSlack) != 0) st.raise(wave_max(mx));
     if constexpr (Sh::kMfma) {
         // value gathers of pass u + 1 go out before the MFMAs of pass u
         uint2 av[2][8];
