@@ -14,8 +14,12 @@ set exceeds the 256 MB last-level cache twice.  The step is captured once in a
 HIP graph and replayed.
 
 Extra fields: ``roofline`` for the decode-attention kernel (algorithmic cache
-bytes per launch / its mean duration from HIP events) and ``cpu_baseline`` (the
-C oracle on a bounded sample of the same workload).
+bytes per launch / its mean duration from HIP events), ``cpu_baseline`` (the
+C oracle on a bounded sample of the same workload) and ``workloads``: the
+other configurations, each timed the same way (decode launches at 0.25 bit,
+batch 64 with ragged contexts, grouped-query heads; the 32768-token K and V
+prefill encode against HBM and MFMA peaks) with the largest error of a
+sampled parity check against the oracle (run in the CPU-baseline leg).
 """
 from __future__ import annotations
 
@@ -62,6 +66,47 @@ def cache_bytes(H, d, Tc, G, lengths):
         n_win = min(L, N_SINK) + min(max(L - N_SINK, 0), N_RECENT)
         total += n_vq * H * 2 * S + n_win * H * 2 * d * 2
     return total
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak of MI355X
+PREFILL_TOKENS = 32768
+
+
+def encode_bytes(n, H, d, Tc, G, tensors=1):
+    """Algorithmic bytes of encoding n tokens: bf16 input, one index byte per
+    sub-vector, and the bf16 codebook read once, per tensor."""
+    S = d // (G // Tc)
+    return tensors * (n * H * Tc * d * 2 + n * H * S + Tc * H * 256 * S * (G // Tc) * 2)
+
+
+def encode_mfma_flops(n, H, d, Tc, G, tensors=1, issued=False):
+    """Algorithmic flops of the encoder's distance contraction: every
+    sub-vector against all 256 codes, G products each (x . c_k).  With
+    ``issued``: what the matrix cores execute, the augmented contraction axis
+    (the G products and the three bf16 parts of |c_k|^2, padded to a multiple
+    of 32)."""
+    S = d // (G // Tc)
+    k = (G + 3 + 31) // 32 * 32 if issued else G
+    return tensors * 2.0 * n * H * S * 256 * k
+
+
+def cpu_model():
+    try:
+        for line in pathlib.Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def rel_err_rows(got, ref):
+    """max over (b, h) rows of max_ch |got - ref| / max_ch |ref|"""
+    import numpy as np
+    got = np.asarray(got, np.float64).reshape(-1, got.shape[-1])
+    ref = np.asarray(ref, np.float64).reshape(-1, ref.shape[-1])
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((np.abs(got - ref).max(axis=1) / den).max())
 
 
 # everything the decode kernel's code depends on: its source, the header it
@@ -178,21 +223,28 @@ class Setup:
 
 class PrefillEncode:
     """Prefill encoder workload: 32768 tokens x 16 heads x 4 loop steps x 128
-    channels of bf16 K (and V), G = 16, into a 32768-row index cache."""
+    channels of bf16 K (and V), G = 16, into a 32768-row index cache; ``run``
+    encodes K, ``run_kv`` K and V in one lvq_encode_kv launch."""
 
-    N = 32768
+    N = PREFILL_TOKENS
 
     def __init__(self, lv, synth, torch, setup, seed=1004):
         dev = torch.device("cuda")
         self.lv = lv
+        self.H, self.d, self.Tc, self.G = setup.Hk, setup.d, setup.Tc, setup.G
         self.cfg = lv.Config(batch=1, n_heads=setup.Hk, head_dim=setup.d, loop_steps=setup.Tc,
                              group=setup.G, max_tokens=self.N)
         self.x = synth.loop_correlated_kv(self.N, setup.Hk, setup.Tc, setup.d, seed, device=dev)
-        self.cb = setup.kcb
-        self.idx = lv.allocate(self.cfg, dev)["k_index"]
+        self.xv = synth.loop_correlated_kv(self.N, setup.Hk, setup.Tc, setup.d, seed + 1, device=dev)
+        self.cb, self.vcb = setup.kcb, setup.vcb
+        bufs = lv.allocate(self.cfg, dev)
+        self.idx, self.vidx = bufs["k_index"], bufs["v_index"]
 
     def run(self):
         self.lv.lvq_encode(self.cfg, self.x, self.cb, self.idx, 0, 0)
+
+    def run_kv(self):
+        self.lv.lvq_encode_kv(self.cfg, self.x, self.xv, self.cb, self.vcb, self.idx, self.vidx, 0, 0)
 
 
 def spin_cycles_for(torch, ms):
@@ -235,27 +287,31 @@ def decode_kernel_time_ms(setup, torch, n=64, reps=8, spread=None):
     return ev[0].elapsed_time(ev[reps]) / (n * reps)
 
 
-def prefill_encode_time_ms(lv, synth, torch, setup, n=10):
-    """Mean duration of one 32768-token prefill encode (one tensor): HIP events
-    around ``n`` back-to-back launches on the current stream, after ten
-    untimed ones (the clock ramps up over the first few)."""
-    enc = PrefillEncode(lv, synth, torch, setup)
+def prefill_encode_time_ms(enc, torch, n=10, kv=False):
+    """Mean duration of one 32768-token prefill encode (one tensor, or K and
+    V in one launch): HIP events around ``n`` back-to-back launches on the
+    current stream, after ten untimed ones (the clock ramps up over the first
+    few)."""
+    run = enc.run_kv if kv else enc.run
     for _ in range(10):
-        enc.run()
+        run()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(n):
-        enc.run()
+        run()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / n
 
 
-def cpu_baseline(setup, torch, budget_s=15.0):
+def cpu_baseline(setup, torch, checks=(), budget_s=15.0):
     """The C oracle on a bounded sample of the same workload: whole decode
     calls (all heads, loop step 0) repeated for about ``budget_s`` seconds, and
-    one page encode, combined into the time of one step."""
+    one page encode, combined into the time of one step.  Also the parity
+    samples of ``checks`` (see ``parity_checks``): the oracle's output for the
+    sampled rows next to the device's, as the largest row error (decode) or
+    the number of differing indices (encode)."""
     import oracle
     c = setup.copies[0]
     kidx, vidx = c["k_index"].cpu(), c["v_index"].cpu()
@@ -287,10 +343,24 @@ def cpu_baseline(setup, torch, budget_s=15.0):
     oracle.encode(setup.page_k.cpu(), kcb, n_heads=setup.Hk, head_dim=setup.d,
                   loop_steps=setup.Tc, group=setup.G, threads=1)
     t_enc1 = time.perf_counter() - t3
+    parity = {}
+    for chk in checks:
+        if chk["kind"] == "decode":
+            ref = oracle.decode_attn(threads=threads, **chk["oracle"])
+            if chk.get("heads"):
+                h0, h1 = chk["heads"]
+                ref = ref[:, h0:h1]
+            parity[chk["name"]] = {"max_rel_err": rel_err_rows(chk["gpu"], ref), "rows": chk["rows"]}
+        else:
+            import numpy as np
+            ref = oracle.encode(threads=threads, **chk["oracle"])
+            parity[chk["name"]] = {"indices_differing": int((np.asarray(chk["gpu"]) != ref).sum()),
+                                   "indices": int(ref.size), "rows": chk["rows"]}
     return {
         "value": setup.tokens_steps_per_step / t_step,
         "unit": "ctx-token*loop-steps/s",
         "cores": threads,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{calls} whole decode calls ({setup.H} heads, {setup.L}-token context, loop step 0, "
                    f"{t_dec * 1e3:.1f} ms each) and one 8-token page encode ({t_enc * 1e3:.1f} ms, "
@@ -299,7 +369,37 @@ def cpu_baseline(setup, torch, budget_s=15.0):
         "value_1core": setup.tokens_steps_per_step / (PAGE * setup.Tc * t_dec1 + 2 * t_enc1),
         "sample_1core": (f"one whole decode call ({t_dec1 * 1e3:.0f} ms) and one page encode "
                          f"({t_enc1 * 1e3:.1f} ms) on one thread, combined the same way"),
+        "parity": parity,
     }
+
+
+def parity_checks(setup, torch, name, heads=None, seqs=None):
+    """One device decode call of loop step 0 on the workload's first cache
+    copy and the oracle's arguments for the same rows: ``heads`` (h0, h1) of
+    every sequence, or the sequences ``seqs`` (all heads)."""
+    c = setup.copies[0]
+    setup.lv.lvq_decode_attn(setup.cfg, 0, setup.q[0, 0].contiguous(), setup.ctx, setup.L,
+                             c["k_index"], c["v_index"], setup.kcb, setup.vcb, c["k_window"],
+                             c["v_window"], setup.ws, setup.out)
+    torch.cuda.synchronize()
+    out = setup.out.double().cpu().numpy()
+    common = dict(loop_step=0, k_codebook=setup.kcb.cpu(), v_codebook=setup.vcb.cpu(),
+                  n_sink=N_SINK, n_recent=N_RECENT, group=setup.G)
+    if seqs is None:
+        h0, h1 = heads
+        return {"name": name, "kind": "decode", "heads": heads, "gpu": out[:, h0:h1],
+                "rows": f"heads {h0}..{h1 - 1} of every sequence",
+                "oracle": dict(common, q=setup.q[0, 0].cpu(), ctx_len=setup.lengths,
+                               k_index=c["k_index"].cpu(), v_index=c["v_index"].cpu(),
+                               k_window=c["k_window"].cpu(), v_window=c["v_window"].cpu(),
+                               heads=heads)}
+    sel = list(seqs)
+    idx = torch.tensor(sel, device=c["k_index"].device)
+    return {"name": name, "kind": "decode", "gpu": out[sel],
+            "rows": f"sequences {sel} (lengths {[setup.lengths[b] for b in sel]}), every head",
+            "oracle": dict(common, q=setup.q[0, 0][idx].cpu(), ctx_len=[setup.lengths[b] for b in sel],
+                           k_index=c["k_index"][idx].cpu(), v_index=c["v_index"][idx].cpu(),
+                           k_window=c["k_window"][idx].cpu(), v_window=c["v_window"][idx].cpu())}
 
 
 def stream_rates(torch, reps=10):
@@ -446,6 +546,8 @@ def main():
     ap.add_argument("--workload", default="ouro1p4b_layer_32k_0p5bit", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0, help="cache copies (0 = auto, >= 2x LLC)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="time only the main workload (not the other configurations)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying")
     ap.add_argument("--decode-only", action="store_true",
                     help="time the 32 decode calls of a step without the page encode")
@@ -453,6 +555,9 @@ def main():
                     help="only run N decode launches (for rocprofv3 runs) and exit")
     ap.add_argument("--profile-encode", type=int, default=0,
                     help="only run N prefill encodes of 32768 tokens (for rocprofv3 runs) and exit")
+    ap.add_argument("--profile-encode-kv", type=int, default=0,
+                    help="only run N prefill encodes of 32768 tokens, K and V in one launch (for "
+                         "rocprofv3 runs) and exit")
     ap.add_argument("--profile-page", type=int, default=0,
                     help="only run N page encodes (8 tokens, K and V in one launch; for "
                          "rocprofv3 runs) and exit")
@@ -489,7 +594,7 @@ def main():
         f"{lv.lvq_decode_splits(setup.cfg, setup.L)} workgroups per (sequence, head), "
         f"{lv.lvq_decode_window_groups(setup.cfg, setup.L)} of them on the window slots")
 
-    if args.profile_decode or args.profile_encode or args.profile_page:
+    if args.profile_decode or args.profile_encode or args.profile_page or args.profile_encode_kv:
         if args.copy_calibrate:
             src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
             dst = torch.empty_like(src)
@@ -500,47 +605,44 @@ def main():
             del src, dst
         for i in range(args.profile_decode):
             setup.decode(i % PAGE, i % setup.Tc)
-        if args.profile_encode:
+        if args.profile_encode or args.profile_encode_kv:
             enc = PrefillEncode(lv, synth, torch, setup)
             for _ in range(args.profile_encode):
                 enc.run()
+            for _ in range(args.profile_encode_kv):
+                enc.run_kv()
         for _ in range(args.profile_page):
             setup.page_encode()
         torch.cuda.synchronize()
         log(f"ran {args.profile_decode} decode launches, {args.profile_encode} prefill encodes, "
-            f"{args.profile_page} page encodes")
+            f"{args.profile_encode_kv} K+V prefill encodes, {args.profile_page} page encodes")
         return
 
-    # warmup (eager), then capture one step in a graph
+    # warmup (eager), then capture exactly the timed steps in one graph (the
+    # cache copies keep rotating from call to call)
     for _ in range(max(1, args.warmup)):
         setup.step(args.decode_only)
     torch.cuda.synchronize()
+    steps = max(1, args.steps)
     graph = None
     if not args.no_graph:
-        # capture a whole rotation cycle so every graph replay touches each copy
-        n_steps_graph = max(1, setup.rotate // math.gcd(setup.rotate, PAGE * setup.Tc))
         stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            for _ in range(n_steps_graph):
+            for _ in range(steps):
                 setup.step(args.decode_only)
         torch.cuda.synchronize()
-        graph.replay()
+        graph.replay()                                # untimed: first replay
         torch.cuda.synchronize()
-        log(f"graph: {n_steps_graph} steps per replay")
-    else:
-        n_steps_graph = 1
-
-    reps = max(1, math.ceil(args.steps / n_steps_graph))
-    steps = reps * n_steps_graph
+        log(f"graph: {steps} steps")
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(reps):
-        if graph is not None:
-            graph.replay()
-        else:
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(steps):
             setup.step(args.decode_only)
     end.record()
     torch.cuda.synchronize()
@@ -556,18 +658,24 @@ def main():
     log(f"decode launch: mean {mean_ms * 1e3:.2f} us (replay median {spread['median_ms'] * 1e3:.2f}, "
         f"min {spread['min_ms'] * 1e3:.2f}), {achieved:.0f} GB/s on {bpl} cache bytes")
 
-    if setup.B == 1:
-        enc_ms = prefill_encode_time_ms(lv, synth, torch, setup)
-        enc_bytes = PrefillEncode.N * setup.Hk * setup.Tc * setup.d * 2 + \
-            PrefillEncode.N * setup.Hk * (setup.d // (setup.G // setup.Tc))
-        log(f"prefill encode ({PrefillEncode.N} tokens, one tensor): mean {enc_ms * 1e3:.1f} us, "
-            f"{enc_bytes / (enc_ms / 1e3) / 1e9:.0f} GB/s on {enc_bytes} bytes")
+    checks = [] if args.no_cpu_baseline else [parity_checks(setup, torch, args.workload, heads=(0, 2))]
+    workloads = {}
+    if not args.no_secondary:
+        workloads, more = secondary_workloads(lv, synth, torch, args.workload, setup,
+                                              with_checks=not args.no_cpu_baseline)
+        checks += more
 
     streams = stream_rates(torch)
     cb_bytes = 2 * setup.Hk * 256 * setup.d * 2     # the K and V slices of step t, bf16
     log(f"stream rates on this GPU: read {streams['read_GBps']:.0f} GB/s, copy {streams['copy_GBps']:.0f} GB/s")
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(setup, torch, checks)
+    if cpu is not None:
+        for name, res in cpu["parity"].items():
+            if name in workloads:
+                workloads[name]["parity"] = res
+        log("parity samples: " + ", ".join(
+            f"{k}: {v.get('max_rel_err', v.get('indices_differing'))}" for k, v in cpu["parity"].items()))
     rec = {
         "metric": METRIC,
         "value": value,
@@ -579,7 +687,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16/fp16->fp32",
         "data": "synthetic (seeded loop-correlated K/V, N(0,1) codebooks)",
         "config": {
             "workload": args.workload,
@@ -590,6 +698,8 @@ def main():
             "step": ("8 tokens x 4 loop-step decodes" if args.decode_only else
                      "8 tokens x 4 loop-step decodes + 8-token page encode (K and V, one launch)"),
             "cache_copies": setup.rotate, "graph": graph is not None,
+            "arithmetic": ("uint8 indices; score tables fp32 from bf16 products; value terms "
+                           "fp16 codewords x fp16 weights; fp32 accumulation and output"),
         },
         "roofline": {
             "bound": "hbm",
@@ -613,8 +723,79 @@ def main():
             "frac_of_measured_copy": achieved / streams["copy_GBps"],
         },
         "cpu_baseline": cpu,
+        "parity": None if cpu is None else cpu["parity"].get(args.workload),
+        "workloads": workloads,
     }
     print(json.dumps(rec), flush=True)
+
+
+SECONDARY = ("ouro1p4b_layer_32k_0p25bit", "batch64_ragged_0p5bit", "gqa32q8kv_32k_0p5bit")
+
+
+def secondary_workloads(lv, synth, torch, main_workload, setup, with_checks=True):
+    """The other configurations, each timed like the main one (mean decode
+    launch over graph replays of 64 back-to-back launches on rotated cache
+    copies) and the K + V prefill encode of 32768 tokens; with their parity
+    samples for the CPU-baseline leg."""
+    out, checks = {}, []
+    for wl in SECONDARY:
+        if wl == main_workload:
+            continue
+        log(f"workload {wl}: setup")
+        s2 = Setup(lv, synth, torch, wl, 0)
+        spread = {}
+        ms = decode_kernel_time_ms(s2, torch, spread=spread)
+        nbytes = cache_bytes(s2.Hk, s2.d, s2.Tc, s2.G, s2.lengths)
+        gbs = nbytes / (ms / 1e3) / 1e9
+        out[wl] = {
+            "metric": "context-token*loop-steps/s per decode call", "value": sum(s2.lengths) / (ms / 1e3),
+            "mean_launch_us": ms * 1e3, "median_launch_us": spread["median_ms"] * 1e3,
+            "min_launch_us": spread["min_ms"] * 1e3, "bytes_per_launch": nbytes, "GBps": gbs,
+            "frac": gbs / HBM_PEAK_GBS, "batch": s2.B, "heads": s2.H, "kv_heads": s2.Hk, "group": s2.G,
+            "context": sum(s2.lengths), "workgroups_per_head": lv.lvq_decode_splits(s2.cfg, s2.L),
+            "cache_copies": s2.rotate,
+        }
+        log(f"  decode launch {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)")
+        if with_checks:
+            if s2.B > 1:
+                picked = {}
+                for b, L in enumerate(s2.lengths):
+                    picked.setdefault(L, b)
+                checks.append(parity_checks(s2, torch, wl, seqs=sorted(picked.values())))
+            else:
+                checks.append(parity_checks(s2, torch, wl, heads=(0, 2)))
+        del s2
+        torch.cuda.empty_cache()
+    # prefill encode: 32768 tokens of K and V in one launch, and one tensor
+    enc = PrefillEncode(lv, synth, torch, setup)
+    ms_kv = prefill_encode_time_ms(enc, torch, kv=True)
+    ms_k = prefill_encode_time_ms(enc, torch)
+    nb = encode_bytes(enc.N, enc.H, enc.d, enc.Tc, enc.G, 2)
+    fl = encode_mfma_flops(enc.N, enc.H, enc.d, enc.Tc, enc.G, 2)
+    fl_issued = encode_mfma_flops(enc.N, enc.H, enc.d, enc.Tc, enc.G, 2, issued=True)
+    gbs = nb / (ms_kv / 1e3) / 1e9
+    tfl = fl / (ms_kv / 1e3) / 1e12
+    out["prefill_encode_kv_32k_0p5bit"] = {
+        "metric": "tokens/s (K and V, 16 KV heads, 4 loop steps, d 128)", "value": enc.N / (ms_kv / 1e3),
+        "mean_launch_us": ms_kv * 1e3, "bytes_per_launch": nb, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+        "mfma_flops_per_launch": fl, "TFLOPs": tfl, "frac_mfma_bf16": tfl / MFMA_BF16_PEAK_TFLOPS,
+        "mfma_flops_issued_per_launch": fl_issued,
+        "frac_mfma_bf16_issued": fl_issued / (ms_kv / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "one_tensor_us": ms_k * 1e3, "tokens": enc.N,
+    }
+    log(f"prefill encode K+V ({enc.N} tokens): {ms_kv * 1e3:.1f} us, {gbs:.0f} GB/s "
+        f"({gbs / HBM_PEAK_GBS:.3f} of HBM), {tfl:.0f} TFLOP/s ({tfl / MFMA_BF16_PEAK_TFLOPS:.3f} of bf16 MFMA); "
+        f"one tensor {ms_k * 1e3:.1f} us")
+    if with_checks:
+        # bit-exact sample: the first 64 tokens of K (every head and sub-vector)
+        n = 64
+        checks.append({"name": "prefill_encode_kv_32k_0p5bit", "kind": "encode",
+                       "gpu": enc.idx[:, :, :n].cpu().numpy(), "rows": f"tokens 0..{n - 1} of K, every head",
+                       "oracle": dict(x=enc.x[:n].cpu(), codebook=enc.cb.cpu(), n_heads=enc.H,
+                                      head_dim=enc.d, loop_steps=enc.Tc, group=enc.G)})
+    del enc
+    torch.cuda.empty_cache()
+    return out, checks
 
 
 if __name__ == "__main__":

@@ -24,6 +24,27 @@ def test_cache_bytes_match_workload_sizes():
                                                             + bench.cache_bytes(2, 128, 4, 16, [900]))
 
 
+def test_encode_workload_sizes():
+    # 32768 tokens x 16 heads x 4 steps x 128 channels of bf16, one index byte
+    # per sub-vector (32 per token and head), the bf16 codebook once
+    assert bench.encode_bytes(32768, 16, 128, 4, 16) == 32768 * 16 * 4 * 128 * 2 + 32768 * 16 * 32 + 4 * 16 * 256 * 32 * 4 * 2
+    assert bench.encode_bytes(32768, 16, 128, 4, 16, 2) == 1_115_684_864          # K and V
+    # x . c over G = 16 products for 256 codes of each sub-vector: 274.9 GFLOP for K and V;
+    # the matrix cores run an augmented axis of 32
+    assert bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2) == 2 * 2 * 32768 * 16 * 32 * 256 * 16
+    assert abs(bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2) / 1e9 - 274.9) < 0.1
+    assert bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2, issued=True) == \
+        2 * bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2)
+    assert bench.encode_mfma_flops(1, 1, 128, 4, 32, issued=True) == 2 * 16 * 256 * 64
+
+
+def test_rel_err_rows():
+    import numpy as np
+    ref = np.array([[[1.0, -2.0], [0.5, 0.25]]])
+    got = ref + np.array([[[0.0, 0.02], [0.0, 0.0]]])
+    assert abs(bench.rel_err_rows(got, ref) - 0.01) < 1e-12
+
+
 def test_counter_traffic_needs_matching_sources(monkeypatch):
     wl = "ouro1p4b_layer_32k_0p5bit"
     text = (ROOT / "profiles" / f"decode_attn_{wl}.md").read_text()
