@@ -83,7 +83,8 @@ typedef struct {
     int32_t loop_steps;     /* Tc, divides group                              */
     int32_t group;          /* G; cg = G/Tc must divide d                     */
     int32_t n_sink;         /* bf16 sink tokens, >= 0 (64 on the pages)       */
-    int32_t n_recent;       /* bf16 recent tokens, >= 1 (256 on the pages)    */
+    int32_t n_recent;       /* bf16 recent tokens, >= 1 (256 on the pages);
+                               n_sink + n_recent <= LVQ_MAX_WINDOW_SLOTS    */
     int32_t max_tokens;     /* rows of the index cache per (b, h)             */
     int32_t codebook_dtype; /* lvq_dtype                                      */
     int32_t decode_splits;  /* workgroups per (b, h) for lvq_decode_attn;
@@ -113,6 +114,7 @@ typedef struct {
 
 #define LVQ_MAX_SPLITS 64
 #define LVQ_MAX_WINDOW_GROUPS 4
+#define LVQ_MAX_WINDOW_SLOTS (1 << 24)
 #define LVQ_MAX_LOOPS 64
 #define LVQ_MAX_LAYERS 4096
 #define LVQ_CODES 256

@@ -9,8 +9,9 @@
 // may hold several layers' buffers: layers are the outermost workgroup
 // index).  When the grid fits the chip, workgroup s < n_split - w of (b, h)
 // takes VQ tokens [n_s + s*chunk, ...) and the last w split the bf16 window
-// slots into w equal ranges; otherwise workgroup s takes a VQ chunk and
-// window slots [s*W/n_split, ...).  The host picks n_split, w and chunk.
+// slots into w ranges of ceil(W / w) slots; otherwise workgroup s takes a VQ
+// chunk and window slots [s*per, (s+1)*per), per = ceil(W / n_split).  The
+// host picks n_split, w and chunk.
 // With one workgroup per (b, h) over several rounds, workgroups take the
 // sequences longest first, in dispatch order.
 // A workgroup with VQ tokens stages two tables of (h, t) in LDS, both with one
@@ -807,10 +808,14 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // converted later so that no wait is placed here) and the table slices.
     const uint32_t qraw = lp.q[bh * D + min(tid, D - 1)];
     // The block's epoch cannot change before this workgroup arrives, so it is
-    // read now, overlapped with the prologue; it tags the partials.
-    uint64_t arrival_word = 0;
+    // read now, overlapped with the prologue; it tags the partials.  Only the
+    // epoch half of the arrival word is read (a 64-bit load whose low half is
+    // dead would let the compiler reuse that register and wait for the load
+    // before the index rows go out).
+    uint32_t epoch_word = 0;
     if (tid == 0 && a.n_split > 1)
-        arrival_word = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        epoch_word = __hip_atomic_load(reinterpret_cast<uint32_t *>(ticket) + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
     {
         const int slice = vq_wg ? 256 * S * CG * (int)sizeof(CB) : 0;
@@ -823,9 +828,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // at n_sink.  Rows outside the range are masked later by the true range,
     // so these loads need not wait for the context length.
     // window rows of the first pass (wave w takes slots s0 + w + kWaves * (tk + pass * TPW))
-    const int s0 = sep ? (vq_wg ? 0 : (int)((int64_t)W * wi / n_win)) : (int)((int64_t)W * split / n_split);
-    const int s1 = sep ? (vq_wg ? 0 : (int)((int64_t)W * (wi + 1) / n_win))
-                       : (int)((int64_t)W * (split + 1) / n_split);
+    const int wr_idx = sep ? wi : split;                   // window range (sep: if >= 0)
+    const int s0 = (sep && vq_wg) ? 0 : min(W, wr_idx * a.win_per);
+    const int s1 = (sep && vq_wg) ? 0 : min(W, s0 + a.win_per);
     using Win = WindowPass<S, CG, CB>;
     // With at most 4 channels per sub-vector step a second pass's rows fit
     // the registers: pass p + 1 is in flight while pass p is folded.
@@ -862,7 +867,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         qs[tid] = qv * scale;
         qh[tid] = (uint16_t)qraw;
     }
-    if (tid == 0) *arrival = (uint32_t)(arrival_word >> 32);
+    if (tid == 0) *arrival = epoch_word;
     __syncthreads();
     if constexpr (!kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 

@@ -117,9 +117,11 @@ struct DecodeArgs {
     int64_t t_max;
     int n_split;      // workgroups per (layer, b, h)
     int window_wg;    // w > 0: the last w workgroups of (b, h) split the window
-                      // slots into w equal ranges and the others take one VQ
-                      // chunk each; 0: each takes a VQ chunk and an equal
-                      // share of the window slots
+                      // slots into w ranges and the others take one VQ chunk
+                      // each; 0: each takes a VQ chunk and a range of the
+                      // window slots
+    int win_per;      // window slots per range: range i is
+                      // [i * win_per, (i + 1) * win_per) within [0, W)
     int chunk;        // VQ tokens per chunk (multiple of 64)
     int by_length;    // 1 (one workgroup per (b, h), 2 <= B <= kMaxOrderedBatch,
                       // one layer): workgroups take sequences longest first

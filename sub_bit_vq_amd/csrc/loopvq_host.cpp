@@ -26,6 +26,7 @@ bool config_ok(const lvq_config *c) {
     const int cg = c->group / c->loop_steps;
     if (c->head_dim % cg != 0) return false;
     if (c->n_sink < 0 || c->n_recent < 1 || c->max_tokens < 0) return false;
+    if ((int64_t)c->n_sink + c->n_recent > LVQ_MAX_WINDOW_SLOTS) return false;
     if (c->codebook_dtype != LVQ_F32 && c->codebook_dtype != LVQ_BF16) return false;
     if (c->decode_splits < 0 || c->decode_splits > LVQ_MAX_SPLITS) return false;
     if (c->decode_window_groups < 0 || c->decode_window_groups > LVQ_MAX_WINDOW_GROUPS) return false;
@@ -374,6 +375,10 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         a.t_max = c->max_tokens;
         a.n_split = n_split;
         a.window_wg = sp.n_win;
+        {
+            const int64_t ranges = sp.n_win > 0 ? sp.n_win : n_split;
+            a.win_per = (int)(((int64_t)W + ranges - 1) / ranges);
+        }
         a.chunk = (int)chunk;
         a.by_length = n_split == 1 && nl == 1 && c->batch > 1 && c->batch <= lvq::kMaxOrderedBatch;
         a.cb_bf16 = c->codebook_dtype == LVQ_BF16;

@@ -20,6 +20,7 @@ LVQ_OK, LVQ_ERR_INVALID_ARG, LVQ_ERR_UNSUPPORTED, LVQ_ERR_WORKSPACE, LVQ_ERR_HIP
 LVQ_F32, LVQ_BF16 = 0, 1
 LVQ_MAX_SPLITS = 64
 LVQ_MAX_WINDOW_GROUPS = 4
+LVQ_MAX_WINDOW_SLOTS = 1 << 24
 LVQ_MAX_LAYERS = 4096
 N_CODES = 256
 

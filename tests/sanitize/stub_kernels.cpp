@@ -43,6 +43,12 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
     fail |= bad(a.n_split < 1 || a.n_split > kMaxSplits);
     fail |= bad(a.window_wg < 0 || (a.window_wg > 0 && a.window_wg >= a.n_split));
     fail |= bad(a.chunk < 64 || a.chunk % 64 != 0);
+    {
+        // the window ranges cover [0, W) and index arithmetic stays in 32 bits
+        const int64_t W = (int64_t)a.n_sink + a.n_recent;
+        const int64_t ranges = a.window_wg > 0 ? a.window_wg : a.n_split;
+        fail |= bad(a.win_per < 1 || ranges * a.win_per < W || (int64_t)a.n_split * a.win_per > 0x7fffffff);
+    }
     fail |= bad(a.n_layers < 1 || a.n_layers > kMaxLayersPerLaunch);
     fail |= bad(a.Hk < 1 || a.q_per_kv < 1 || a.Hk * a.q_per_kv != a.H);
     fail |= bad(a.S * a.cg != a.d || a.t_max < 1 || a.max_polls < 1);

@@ -124,6 +124,7 @@ def test_default_windows_match_pages():
     dict(n_loops=-4), dict(n_loops=6), dict(n_loops=68),
     dict(decode_window_groups=1), dict(decode_splits=8, decode_window_groups=-1),
     dict(decode_splits=8, decode_window_groups=5), dict(decode_splits=3, decode_window_groups=3),
+    dict(n_sink=lv.LVQ_MAX_WINDOW_SLOTS // 2, n_recent=lv.LVQ_MAX_WINDOW_SLOTS // 2 + 1),
 ])
 def test_layout_rejects_bad_config(bad):
     base = dict(batch=1, n_heads=2, head_dim=64, loop_steps=4, group=16, max_tokens=100)
