@@ -11,34 +11,40 @@
 // Layout of the work.  A workgroup owns 4 sub-vectors j (one wave each) of one
 // head and a chunk of tokens.  It first stages the 4 codebooks (all Tc
 // slices, all 256 codes; the storage is code-major, so each (slice, code) row
-// piece is one contiguous read) in LDS, with their squared norms.
+// piece is one contiguous read) in LDS, with their squared norms, and builds
+// the MFMA operands from them; that LDS then holds the chunk's codes, which
+// the workgroup writes out at the end (the 4 codes of a token row as one
+// 4-byte store).
 //
 // Screen (MFMA).  The screen value S_k = |c_k|^2 - 2 x.c_k differs from D_k by
-// |x|^2, the same for every k.  One v_mfma_f32_16x16x32_bf16 multiplies 16
-// codes (rows) by 16 tokens (columns) over an augmented K axis:
-//     code row  = [-2 c_k (split into P bf16 parts), b0, b1, b2, 0...]
-//     token col = [ x (repeated P times),           1,  1,  1, 0...]
-// where b0 + b1 + b2 = fl32(|c_k|^2) in bf16 parts (and, for fp32 codebooks,
-// c = c0 + c1 + c2 in bf16 parts, P = 3).  Products of bf16 values are exact
-// in fp32, so the only screen errors are the accumulation roundings.  Each
-// wave keeps its codebook in registers as MFMA A operands and streams 16-token
-// tiles through it.  Each lane tracks the two smallest screen values of its 64
-// codes, a pair (a, b) at a time: the smallest is min3(m1, a, b) and the
-// second smallest min(m2, med3(m1, a, b)).  The low 6 bits of each value are
+// |x|^2, the same for every k.  MFMAs multiply 16 codes (rows) by 16 tokens
+// (columns) over the K axis
+//     code row  = [-2 c_k (split into P bf16 parts), 0...]
+//     token col = [ x (repeated P times),           0...]
+// (for fp32 codebooks c = c0 + c1 + c2 in bf16 parts, P = 3; bf16 codebooks
+// P = 1), starting from the accumulator C = fl32(|c_k|^2): one
+// v_mfma_f32_16x16x16_bf16 when P G <= 16, else one v_mfma_f32_16x16x32_bf16
+// per 32 entries of K.  Products of bf16 values are exact in fp32, so the only
+// screen errors are the accumulation roundings.  Each wave keeps its codebook
+// in registers as MFMA A operands and streams 16-token tiles through it.
+// Each lane tracks the two smallest screen values of its 64 codes, a pair
+// (a, b) at a time: the smallest is min3(m1, a, b) and the second smallest
+// min(m2, med3(m1, a, b)).  The low 6 bits of each value are
 // replaced by its slot among the lane's 64 codes, so the smallest value also
 // names its code (the lane supplies the rest of the index).
 //
 // Exactness.  With R = |x| + max_k |c_k|, the 6 bits written into a value
 // move it by at most 2^-17 R^2; the fp32 error of D_k is at most
-// (G+2) 2^-24 R^2 and that of the screen at most F (P*G+3) 2^-24 R^2 for an
-// accumulation F times worse than a sequential fp32 sum.  If the two smallest
-// (marked) screen values are more than eps = 2^-14 R^2 apart, eps exceeds
-// twice the sum of these (for F up to 10 at G = 32, P = 1 and up to 7 at
-// G = 16, P = 3), so the screen
-// winner is the exact winner.  Otherwise the wave re-scores all 256 codes of
-// that sub-vector exactly as defined above from the staged codebook (64 lanes
-// x 4 codes, strict < per lane in ascending k, then a lowest-index argmin
-// across lanes), which reproduces the definition bit for bit.
+// (G+2) 2^-24 R^2 and that of the screen (C plus P*G exact products) at most
+// F (P*G+3) 2^-24 R^2 for an accumulation F times worse than a sequential
+// fp32 sum (P*G+1 terms; the bound keeps two terms of slack).  If the two
+// smallest (marked) screen values are more than eps = 2^-14 R^2 apart, eps
+// exceeds twice the sum of these (for F up to 10 at G = 32, P = 1 and up to 7
+// at G = 16, P = 3), so the screen winner is the exact winner.  Otherwise the
+// wave re-scores all 256 codes of that sub-vector exactly as defined above
+// from the codebook (64 lanes x 4 codes, strict < per lane in ascending k,
+// then a lowest-index argmin across lanes), which reproduces the definition
+// bit for bit.
 #include "kernels.h"
 
 #include <math.h>
@@ -53,8 +59,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;     // 4 waves, one sub-vector index j each
 constexpr int kJW = 4;            // sub-vectors per workgroup
-constexpr int kTokChunk = 2048;   // tokens per workgroup (queued rows fit 16 bits)
+constexpr int kTokChunk = 2048;   // tokens per workgroup
 constexpr float kEpsScale = 6.103515625e-05f;  // 2^-14
+constexpr uint16_t kRescore = 0x100;
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -112,8 +119,13 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 template <int G, int CG, int P, typename CB>
 struct EncShape {
     static constexpr int T = G / CG;                       // loop steps
-    static constexpr int KAUG = (P * G + 3 + 31) / 32 * 32;
-    static constexpr int NCH = KAUG / 32;                  // MFMAs per 16 codes x 16 tokens
+    static constexpr int KX = P * G;                       // K entries that carry x
+    static constexpr bool K16 = KX <= 16;                  // one 16x16x16 MFMA, else 16x16x32 ones
+    static constexpr int KC = K16 ? 16 : 32;               // K entries per MFMA
+    static constexpr int NCH = (KX + KC - 1) / KC;         // MFMAs per 16 codes x 16 tokens
+    static constexpr int KL = KC / 4;                      // K entries per lane per MFMA
+    static constexpr int LE = CG < KL ? CG : KL;           // x elements per load
+    static constexpr int NLD = KL / LE;                    // loads per lane per MFMA
     static constexpr int EB = (int)sizeof(CB);
     static constexpr int ROWB = kJW * CG * EB;             // bytes of one (slice, code) row piece
     static constexpr int EC = 16 / EB;                     // elements per 16-byte chunk
@@ -123,36 +135,53 @@ struct EncShape {
 };
 
 // One 16-token tile of x as MFMA B-operand words: lane (row, kq) holds, for
-// each K chunk ch, the 4 words (8 bf16) of entries kk = ch*32 + kq*8 .. +7 of
-// token n0 + row (zero where kk is not an x entry or the token is past the end).
-template <int NCH>
+// each K chunk ch, the KL/2 words (KL bf16) of entries kk = ch*KC + kq*KL ..
+// + KL - 1 of token n0 + row (zero where kk is not an x entry or the token is
+// past the end).
+template <int NCH, int KL>
 struct XTile {
-    uint32_t w[NCH][4];
+    uint32_t w[NCH][KL / 2];
 };
 
 constexpr uint32_t kOob = 0xffffff00u;            // offset past any buffer: loads return 0
 constexpr int kBufferWord3 = 0x00020000;          // raw buffer resource, gfx9 family
 
-template <int CG, int NCH>
-__device__ __forceinline__ void load_tile(XTile<NCH> &t, __amdgpu_buffer_rsrc_t rs,
-                                          const uint32_t (&off)[NCH][8 / CG > 0 ? 8 / CG : 1],
-                                          bool valid) {
-    constexpr int NLD = 8 / CG;
+// NLD loads of LE x elements per lane and MFMA (offsets from the tile base)
+template <int NCH, int KL, int LE>
+__device__ __forceinline__ void load_tile(XTile<NCH, KL> &t, __amdgpu_buffer_rsrc_t rs,
+                                          const uint32_t (&off)[NCH][KL / LE], bool valid) {
+    constexpr int NLD = KL / LE;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
         for (int s = 0; s < NLD; ++s) {
             const uint32_t o = valid ? off[ch][s] : kOob;
-            if constexpr (CG == 8) {
+            if constexpr (LE == 8) {
                 const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, 0));
                 t.w[ch][0] = v.x; t.w[ch][1] = v.y; t.w[ch][2] = v.z; t.w[ch][3] = v.w;
-            } else if constexpr (CG == 4) {
+            } else if constexpr (LE == 4) {
                 const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
                 t.w[ch][2 * s] = v.x; t.w[ch][2 * s + 1] = v.y;
             } else {
                 t.w[ch][s] = __builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0);
             }
         }
+    }
+}
+
+typedef short bf16x4s __attribute__((ext_vector_type(4)));   // 16x16x16 operand (bf16 bits)
+
+// acc = A * B + acc for one K chunk
+template <bool K16>
+__device__ __forceinline__ floatx4 mfma_chunk(const uint32_t *aw, const uint32_t *bw, floatx4 acc) {
+    if constexpr (K16) {
+        const bf16x4s A = __builtin_bit_cast(bf16x4s, make_uint2(aw[0], aw[1]));
+        const bf16x4s B = __builtin_bit_cast(bf16x4s, make_uint2(bw[0], bw[1]));
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, acc, 0, 0, 0);
+    } else {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+        const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
     }
 }
 
@@ -164,9 +193,16 @@ template <int G, int CG, int P, typename CB, bool kScreen>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     using Sh = EncShape<G, CG, P, CB>;
     constexpr int NCH = Sh::NCH;
-    __shared__ __align__(16) CB cbs[kJW * 256 * G];    // [jl][k][i]
+    // The staged codebooks [jl][k][i] are read only until the MFMA operands
+    // are built; then the same LDS holds, per wave, the code of each chunk
+    // row or kRescore (re-score it exactly).  Sharing the space lets more
+    // workgroups fit a compute unit.
+    constexpr int kCbBytes = kJW * 256 * G * (int)sizeof(CB);
+    constexpr int kCodeBytes = kJW * kTokChunk * 2;
+    __shared__ __align__(16) unsigned char stage[kCbBytes > kCodeBytes ? kCbBytes : kCodeBytes];
     __shared__ float nrm[kJW * 256];
-    __shared__ uint16_t amb_queue[kJW][kTokChunk];     // per wave: chunk rows to re-score
+    CB *cbs = reinterpret_cast<CB *>(stage);
+    uint16_t(*row_code)[kTokChunk] = reinterpret_cast<uint16_t(*)[kTokChunk]>(stage);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // grid z = tensor * H + head (a launch may encode two tensors, e.g. K and V)
     const int tz = (int)blockIdx.z / a.H;
@@ -213,7 +249,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
         nrm[m * 256 + tid] = (float)s;
     }
     __syncthreads();
-    if (j >= a.S) return;
+    // (S is a multiple of kJW, so every wave has a sub-vector j < S)
     float max_norm2 = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) max_norm2 = fmaxf(max_norm2, nrm[wave * 256 + lane + 64 * r]);
@@ -223,111 +259,107 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
 
     // this wave's codebook as MFMA A operands: lane (row, kq) holds entries
-    // kk = ch*32 + kq*8 + e of code blk*16 + row (kq unrolled so that every
-    // register index is a constant)
+    // kk = ch*KC + kq*KL + e of code blk*16 + row, two bf16 a word (kq
+    // unrolled so that every register index is a constant)
+    constexpr int KL = Sh::KL, KC = Sh::KC, LE = Sh::LE, NLD = Sh::NLD;
     const CB *mycb = cbs + wave * 256 * G;
-    bf16x8 afrag[16][NCH];
+    uint32_t afrag[16][NCH][KL / 2];
 #pragma unroll
     for (int blk = 0; blk < 16; ++blk) {
         const int code = blk * 16 + row;
         const CB *cw = mycb + code * G;
-        const float bias = nrm[wave * 256 + code];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (kq != q) continue;
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) {
-                bf16x8 f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kk = ch * 32 + q * 8 + e;
-                    float v = 0.f;
-                    if (kk < P * G)
-                        v = -2.f * (P == 1 ? to_f(cw[kk % G]) : split_part(to_f(cw[kk % G]), kk / G));
-                    else if (kk < P * G + 3)
-                        v = split_part(bias, kk - P * G);
-                    f[e] = __builtin_bit_cast(__bf16, bf16_rne(v));
+                for (int e = 0; e < KL; e += 2) {
+                    uint32_t wv = 0;
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int kk = ch * KC + q * KL + e + h2;
+                        float v = 0.f;
+                        if (kk < P * G)
+                            v = -2.f * (P == 1 ? to_f(cw[kk % G]) : split_part(to_f(cw[kk % G]), kk / G));
+                        wv |= (uint32_t)bf16_rne(v) << (16 * h2);
+                    }
+                    afrag[blk][ch][e / 2] = wv;
                 }
-                afrag[blk][ch] = f;
             }
         }
     }
+    // the accumulator of block blk starts at the squared norms of the lane's
+    // 4 codes blk*16 + kq*4 + i (the same for every token column)
+    const float *bias_row = nrm + wave * 256 + kq * 4;
+    __syncthreads();                                  // the staged codebooks are dead
 
-    uint8_t *out_rows = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token) * a.S + j;
+    // byte j0 of the index row of the chunk's first token
+    uint8_t *out_base = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j0;
 
     // per-lane x offsets (bytes from the tile base) of the loads that fill the
-    // lane's B words; lanes whose K entries are not x read nothing
-    constexpr int NLD = 8 / CG;
+    // lane's B words: load s of chunk ch holds entries kk = ch*KC + kq*KL +
+    // s*LE .. + LE - 1, i.e. x_i with i = kk mod G (step i / CG, channels
+    // i mod CG ..); lanes whose K entries are not x read nothing
     uint32_t xoff[NCH][NLD];
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-        const int kk0 = ch * 32 + kq * 8;
-        const int i0 = kk0 % G;
 #pragma unroll
         for (int s = 0; s < NLD; ++s) {
-            const int64_t e = (int64_t)row * a.sx_tok + (int64_t)(i0 / CG + s) * a.sx_step +
-                              (int64_t)j * CG;
-            xoff[ch][s] = kk0 < P * G ? (uint32_t)(2 * e) : kOob;
+            const int kk = ch * KC + kq * KL + s * LE;
+            const int i = kk % G;
+            const int64_t e = (int64_t)row * a.sx_tok + (int64_t)(i / CG) * a.sx_step + (int64_t)j * CG + i % CG;
+            xoff[ch][s] = kk < P * G ? (uint32_t)(2 * e) : kOob;
         }
     }
-    // the three ones of the bias column sit in the K chunk and lanes of kk = P*G
-    constexpr int ONES_CH = P * G / 32;
-    const bool ones_lane = kq == (P * G % 32) / 8;
-    const uint32_t ones0 = ones_lane ? 0x3f803f80u : 0u;    // bf16 1.0, 1.0
-    const uint32_t ones1 = ones_lane ? 0x00003f80u : 0u;    // bf16 1.0, 0
     // lanes whose words are x entries i < G (counted once for |x|^2)
-    const bool norm_lane = kq * 8 < G;
+    const bool norm_lane = kq * KL < G;
 
     const uint16_t *xh = xin + h * a.sx_head;
     auto rsrc = [&](int64_t n0) {
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(xh + n0 * a.sx_tok), (short)0,
                                                  0x7ffffff0, kBufferWord3);
     };
-    uint16_t *queue = amb_queue[wave];
-    int n_amb = 0;
+    uint16_t *codes = row_code[wave];
 
-    // tiles are processed in groups of kDepth; rows past the chunk's end (a
-    // ragged last group) load nothing and store nothing
-    constexpr int kDepth = 4;                          // tiles in flight per wave
+    // Tiles go in groups of kDepth through two register rings: while one
+    // group is screened from ring A, the next is in flight into ring B, and
+    // the other way round.  A group's loads are issued a whole group before
+    // its first use and after the loads of the group before it, and every
+    // load of the main loop is unconditional with loop-invariant lane
+    // offsets, so the compiler's wait for a group counts exactly the loads
+    // behind it (a conditional load, or a per-load offset select whose
+    // register gets reused for loaded data, made it wait for all of them).
+    // The main loop covers whole pairs of groups; the rows after them go tile
+    // by tile, where rows past the chunk's end load nothing and store
+    // nothing.
+    constexpr int kDepth = 4;                          // tiles per group
+    constexpr int kPair = 32 * kDepth;                 // rows of a pair of groups
     const int ntok = (int)(tok_end - tok0);
-    XTile<NCH> ring[kDepth];
+    const int nfull = ntok / kPair * kPair;
+    using Tile = XTile<NCH, KL>;
+    Tile ringA[kDepth], ringB[kDepth];
+    // every row of the group exists (rg0 + 16 * kDepth <= nfull)
+    auto load_group = [&](Tile (&rg)[kDepth], int rg0) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u)
-        load_tile<CG, NCH>(ring[u], rsrc(tok0 + 16 * u), xoff, 16 * u + row < ntok);
-
-    for (int rb = 0; rb < ntok; rb += 16 * kDepth) {
-#pragma unroll
-        for (int u = 0; u < kDepth; ++u) {
-            const int r0 = rb + 16 * u;                // tile's first row in the chunk
+        for (int u = 0; u < kDepth; ++u) load_tile<NCH, KL, LE>(rg[u], rsrc(tok0 + rg0 + 16 * u), xoff, true);
+    };
+    auto screen_tile = [&](const Tile &cur, const int r0) {
             const int64_t n0 = tok0 + r0;
-            const XTile<NCH> cur = ring[u];
-            {
-                const int rn = r0 + 16 * kDepth;
-                load_tile<CG, NCH>(ring[u], rsrc(tok0 + rn), xoff, rn + row < ntok);
-            }
             const bool valid = r0 + row < ntok;
 
-            // B operand and |x|^2 (bf16 squares are exact; the sum only feeds a bound)
-            bf16x8 bfrag[NCH];
+            // |x|^2 from the lane's words of chunk 0 (bf16 squares are exact;
+            // the sum only feeds a bound); the words are the B operand as loaded
             float xs = 0.f;
+            {
+                float d = 0.f;
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
-                uint32_t w0 = cur.w[ch][0], w1 = cur.w[ch][1];
-                if (ch == 0) {
-                    float d = 0.f;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                        const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[0][q]);
-                        d = __builtin_amdgcn_fdot2_f32_bf16(v, v, d, false);
-                    }
-                    xs = norm_lane ? d : 0.f;
+                for (int q = 0; q < KL / 2; ++q) {
+                    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                    const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[0][q]);
+                    d = __builtin_amdgcn_fdot2_f32_bf16(v, v, d, false);
                 }
-                if (ch == ONES_CH) {
-                    w0 |= ones0;
-                    w1 |= ones1;
-                }
-                bfrag[ch] = __builtin_bit_cast(bf16x8, make_uint4(w0, w1, cur.w[ch][2], cur.w[ch][3]));
+                xs = norm_lane ? d : 0.f;
             }
             float xa, xb;
             pair16(xs, xa, xb);
@@ -340,17 +372,24 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             // min3(m1, a, b)
             // MFMAs run kPipe blocks ahead of the min tracking so that their
             // latency overlaps it (the scheduling barriers keep that order)
+            // The accumulators start at the codes' squared norms, read from LDS
+            // kBiasAhead blocks before their MFMA so that the read's latency
+            // overlaps the min tracking.
             constexpr int kPipe = 4;
-            auto screen = [&](int blk) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            constexpr int kBiasAhead = 2;
+            constexpr int NB = kPipe + kBiasAhead;
+            auto bias_of = [&](int blk) { return *reinterpret_cast<const floatx4 *>(bias_row + blk * 16); };
+            auto screen = [&](int blk, floatx4 acc) {
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afrag[blk][ch], bfrag[ch], acc, 0, 0, 0);
+                for (int ch = 0; ch < NCH; ++ch) acc = mfma_chunk<Sh::K16>(afrag[blk][ch], cur.w[ch], acc);
                 return acc;
             };
+            floatx4 bias[NB];
+#pragma unroll
+            for (int p = 0; p < NB; ++p) bias[p] = bias_of(p);
             floatx4 accs[kPipe];
 #pragma unroll
-            for (int p = 0; p < kPipe; ++p) accs[p] = screen(p);
+            for (int p = 0; p < kPipe; ++p) accs[p] = screen(p, bias[p]);
             __builtin_amdgcn_sched_barrier(0);
             float m1 = INFINITY, m2 = INFINITY;
 #pragma unroll
@@ -373,7 +412,10 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
                     m2 = fminf(m2, __builtin_amdgcn_fmed3f(m1, v[i], v[i + 1]));
                     m1 = fminf(m1, fminf(v[i], v[i + 1]));
                 }
-                if (blk + kPipe < 16) accs[blk % kPipe] = screen(blk + kPipe);
+                if (blk + kPipe < 16) {
+                    accs[blk % kPipe] = screen(blk + kPipe, bias[(blk + kPipe) % NB]);
+                    if (blk + NB < 16) bias[blk % NB] = bias_of(blk + NB);   // slot of block blk + kPipe - NB
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             // combine the four lanes holding the same token; the lane whose own
@@ -398,31 +440,48 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             const float eps = kEpsScale * rad * rad;
             const bool unique = (m2 - m1) > eps;
             // when the winner is unique no other lane holds an equal value (it
-            // would be the second smallest), so exactly one lane stores
-            if (holder && valid && unique) out_rows[(size_t)(n0 + row) * a.S] = (uint8_t)k1;
-
-            // queue the ambiguous sub-vectors of this tile (rows of the chunk)
-            const bool amb = kq == 0 && valid && !unique;
-            const uint64_t amb_mask = __ballot(amb);
-            if (amb) {
-                const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(amb_mask >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)amb_mask, 0));
-                queue[n_amb + pos] = (uint16_t)(r0 + row);
-            }
-            n_amb += __builtin_popcountll(amb_mask);
-        }
+            // would be the second smallest), so exactly one lane records it;
+            // otherwise the lane of kq = 0 marks the row for the exact re-score
+            if (valid && (unique ? holder : kq == 0)) codes[r0 + row] = unique ? (uint16_t)k1 : kRescore;
+    };
+    if (nfull > 0) load_group(ringA, 0);
+    for (int rb = 0; rb < nfull; rb += kPair) {
+        load_group(ringB, rb + 16 * kDepth);
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) screen_tile(ringA[u], rb + 16 * u);
+        // the last pair reloads rows of its own second group (read again,
+        // never screened): the loads stay unconditional and in bounds
+        load_group(ringA, rb + kPair < nfull ? rb + kPair : rb + 16 * kDepth);
+#pragma unroll
+        for (int u = 0; u < kDepth; ++u) screen_tile(ringB[u], rb + 16 * (kDepth + u));
+    }
+    for (int r0 = nfull; r0 < ntok; r0 += 16) {
+        Tile t;
+        load_tile<NCH, KL, LE>(t, rsrc(tok0 + r0), xoff, r0 + row < ntok);
+        screen_tile(t, r0);
     }
 
-    // exact re-score of the queued sub-vectors: every lane scores 4 codes
-    // k = lane + 64 r, then the wave takes the lowest index of the smallest
-    // distance
+    // exact re-score of the marked sub-vectors (rare): every lane scores 4
+    // codes k = lane + 64 r, read from the codebook in memory, then the wave
+    // takes the lowest index of the smallest distance
+    bool any_marked = false;
+    for (int rb = 0; rb < ntok; rb += 64)
+        any_marked |= __ballot(rb + lane < ntok && codes[rb + lane] == kRescore) != 0;
+    const int ntok_rescore = any_marked ? ntok : 0;  // wave-uniform
     float cf[4][G];
+    if (any_marked) {
+        const CB *cbg = static_cast<const CB *>(cbin);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int i = 0; i < G; ++i) cf[r][i] = to_f(mycb[(lane + 64 * r) * G + i]);
-    for (int q = 0; q < n_amb; ++q) {
-        const int rq = __builtin_amdgcn_readfirstlane(queue[q]);
+            for (int i = 0; i < G; ++i)
+                cf[r][i] = to_f(cbg[((((size_t)(i / CG) * a.H + h) * 256 + lane + 64 * r) * a.S + j) * CG + i % CG]);
+    }
+    for (int rb = 0; rb < ntok_rescore; rb += 64) {
+      uint64_t marked = __ballot(rb + lane < ntok && codes[rb + lane] == kRescore);
+      while (marked != 0) {                            // wave-uniform
+        const int rq = rb + (int)__builtin_ctzll(marked);
+        marked &= marked - 1;
         const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
         float xe[G];
 #pragma unroll
@@ -449,7 +508,23 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
         // distances are >= 0, so their bit patterns order like them
         const uint32_t dmin = wave_min_u32(__float_as_uint(best));
         const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
-        if (lane == 0) out_rows[(size_t)(tok0 + rq) * a.S] = (uint8_t)kmin;
+        if (lane == 0) codes[rq] = (uint16_t)kmin;
+      }
+    }
+    // The workgroup's kJW codes of a row are adjacent bytes of the index row:
+    // one 4-byte store per row where the rows are 4-byte aligned.
+    __syncthreads();
+    static_assert(kJW == 4, "one 32-bit word per row");
+    if ((reinterpret_cast<uintptr_t>(out_base) & 3u) == 0) {
+        for (int r = tid; r < ntok; r += kThreads) {
+            const uint32_t w = (uint32_t)(row_code[0][r] & 0xff) | (uint32_t)(row_code[1][r] & 0xff) << 8 |
+                               (uint32_t)(row_code[2][r] & 0xff) << 16 | (uint32_t)(row_code[3][r] & 0xff) << 24;
+            *reinterpret_cast<uint32_t *>(out_base + (size_t)r * a.S) = w;
+        }
+    } else {
+        for (int r = tid; r < ntok; r += kThreads)
+#pragma unroll
+            for (int jl = 0; jl < kJW; ++jl) out_base[(size_t)r * a.S + jl] = (uint8_t)row_code[jl][r];
     }
 }
 
