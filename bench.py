@@ -82,11 +82,11 @@ def encode_bytes(n, H, d, Tc, G, tensors=1):
 def encode_mfma_flops(n, H, d, Tc, G, tensors=1, issued=False):
     """Algorithmic flops of the encoder's distance contraction: every
     sub-vector against all 256 codes, G products each (x . c_k).  With
-    ``issued``: what the matrix cores execute, the augmented contraction axis
-    (the G products and the three bf16 parts of |c_k|^2, padded to a multiple
-    of 32)."""
+    ``issued``: what the matrix cores execute for bf16 codebooks, the
+    contraction axis padded to the MFMA's K (16 when G <= 16, else a multiple
+    of 32; the squared norms enter as the accumulator, not as products)."""
     S = d // (G // Tc)
-    k = (G + 3 + 31) // 32 * 32 if issued else G
+    k = (16 if G <= 16 else (G + 31) // 32 * 32) if issued else G
     return tensors * 2.0 * n * H * S * 256 * k
 
 

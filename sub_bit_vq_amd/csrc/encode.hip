@@ -12,9 +12,8 @@
 // head and a chunk of tokens.  It first stages the 4 codebooks (all Tc
 // slices, all 256 codes; the storage is code-major, so each (slice, code) row
 // piece is one contiguous read) in LDS, with their squared norms, and builds
-// the MFMA operands from them; that LDS then holds the chunk's codes, which
-// the workgroup writes out at the end (the 4 codes of a token row as one
-// 4-byte store).
+// the MFMA operands from them; that LDS then holds the chunk's codes on their
+// way out.
 //
 // Screen (MFMA).  The screen value S_k = |c_k|^2 - 2 x.c_k differs from D_k by
 // |x|^2, the same for every k.  MFMAs multiply 16 codes (rows) by 16 tokens
@@ -203,7 +202,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     __shared__ float nrm[kJW * 256];
     CB *cbs = reinterpret_cast<CB *>(stage);
     uint16_t(*row_code)[kTokChunk] = reinterpret_cast<uint16_t(*)[kTokChunk]>(stage);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // (the wave index is uniform; saying so keeps the buffer resources built
+    // from it in scalar registers)
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // grid z = tensor * H + head (a launch may encode two tensors, e.g. K and V)
     const int tz = (int)blockIdx.z / a.H;
     const int h = (int)blockIdx.z - tz * a.H;
@@ -294,8 +295,11 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     const float *bias_row = nrm + wave * 256 + kq * 4;
     __syncthreads();                                  // the staged codebooks are dead
 
-    // byte j0 of the index row of the chunk's first token
-    uint8_t *out_base = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j0;
+    // byte j of the index row of the chunk's first token; as a buffer resource,
+    // a store at offset kOob is dropped
+    uint8_t *out_wave = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j;
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(out_wave, (short)0, 0x7ffffff0, kBufferWord3);
 
     // per-lane x offsets (bytes from the tile base) of the loads that fill the
     // lane's B words: load s of chunk ch holds entries kk = ch*KC + kq*KL +
@@ -440,9 +444,14 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             const float eps = kEpsScale * rad * rad;
             const bool unique = (m2 - m1) > eps;
             // when the winner is unique no other lane holds an equal value (it
-            // would be the second smallest), so exactly one lane records it;
-            // otherwise the lane of kq = 0 marks the row for the exact re-score
-            if (valid && (unique ? holder : kq == 0)) codes[r0 + row] = unique ? (uint16_t)k1 : kRescore;
+            // would be the second smallest), so exactly one lane stores it (the
+            // store instruction is unconditional, the other lanes' offsets are
+            // out of range, so the compiler's wait counts stay exact); otherwise
+            // the lane of kq = 0 marks the row for the exact re-score
+            const bool store = valid && unique && holder;
+            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)k1, out_rsrc,
+                                                 store ? (uint32_t)((r0 + row) * a.S) : kOob, 0, 0);
+            codes[r0 + row] = (valid && !unique) ? kRescore : (uint16_t)0;
     };
     if (nfull > 0) load_group(ringA, 0);
     for (int rb = 0; rb < nfull; rb += kPair) {
@@ -508,23 +517,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
         // distances are >= 0, so their bit patterns order like them
         const uint32_t dmin = wave_min_u32(__float_as_uint(best));
         const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
-        if (lane == 0) codes[rq] = (uint16_t)kmin;
+        if (lane == 0) out_wave[(size_t)rq * a.S] = (uint8_t)kmin;
       }
-    }
-    // The workgroup's kJW codes of a row are adjacent bytes of the index row:
-    // one 4-byte store per row where the rows are 4-byte aligned.
-    __syncthreads();
-    static_assert(kJW == 4, "one 32-bit word per row");
-    if ((reinterpret_cast<uintptr_t>(out_base) & 3u) == 0) {
-        for (int r = tid; r < ntok; r += kThreads) {
-            const uint32_t w = (uint32_t)(row_code[0][r] & 0xff) | (uint32_t)(row_code[1][r] & 0xff) << 8 |
-                               (uint32_t)(row_code[2][r] & 0xff) << 16 | (uint32_t)(row_code[3][r] & 0xff) << 24;
-            *reinterpret_cast<uint32_t *>(out_base + (size_t)r * a.S) = w;
-        }
-    } else {
-        for (int r = tid; r < ntok; r += kThreads)
-#pragma unroll
-            for (int jl = 0; jl < kJW; ++jl) out_base[(size_t)r * a.S + jl] = (uint8_t)row_code[jl][r];
     }
 }
 

@@ -33,9 +33,12 @@ def test_encode_workload_sizes():
     # the matrix cores run an augmented axis of 32
     assert bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2) == 2 * 2 * 32768 * 16 * 32 * 256 * 16
     assert abs(bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2) / 1e9 - 274.9) < 0.1
+    # issued: one 16x16x16 MFMA per 16 codes x 16 tokens at G = 16 (K = G),
+    # one 16x16x32 at G = 32, K = 16 at G = 8 (half of it padding)
     assert bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2, issued=True) == \
-        2 * bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2)
-    assert bench.encode_mfma_flops(1, 1, 128, 4, 32, issued=True) == 2 * 16 * 256 * 64
+        bench.encode_mfma_flops(32768, 16, 128, 4, 16, 2)
+    assert bench.encode_mfma_flops(1, 1, 128, 4, 32, issued=True) == 2 * 16 * 256 * 32
+    assert bench.encode_mfma_flops(1, 1, 64, 4, 8, issued=True) == 2 * 32 * 256 * 16
 
 
 def test_rel_err_rows():
