@@ -129,10 +129,11 @@ def test_merge_timeout_is_flagged(lv):
 def test_value_range_is_flagged(lv, splits):
     """A bf16 value codebook entry of 2^17 in slice 1 (beyond fp16): a decode
     of loop step 1 flags it; decodes of other steps (which read other
-    slices) do not.  Each plan checks the slice its own way: the library's
-    plan (window workgroups check it), 40 splits (arrival tickets: the VQ
-    workgroups share the staged pieces) and one workgroup per (b, h) (it
-    checks everything it stages)."""
+    slices) do not.  The VQ workgroups of a head share the check of the
+    slice they stage (role s of n checks the staged units u = s mod
+    min(n, 8)); the plans cover the library's (VQ splits beside window
+    workgroups), 40 splits (arrival tickets) and one workgroup per (b, h)
+    (it checks everything it stages)."""
     _note(f"value range flag, splits {splits}")
     c = make_cache(batch=1, n_heads=8, head_dim=128, group=16, lengths=(3000,), seed=75,
                    codeword_tokens=True)
