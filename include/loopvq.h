@@ -234,7 +234,7 @@ lvq_status lvq_encode_kv(const lvq_config *cfg, const void *k_x, const void *v_x
  * (b, h) merges the split partials.  Results depend on the split count only through
  * rounding.
  *
- * q          device bf16 [B][H][d]
+ * q          device bf16 [B][H][d], 16-byte aligned
  * ctx_len    device int32 [B]: L_b, precondition 0 <= L_b <= max_tokens
  *            (clamped on the device; L_b = 0 writes zeros)
  * vq_len     device int32 [B] or NULL (exact windows).  Precondition

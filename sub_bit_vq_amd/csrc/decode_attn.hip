@@ -42,7 +42,9 @@
 // (bf16 window values use the fp32 4x4x1 form, so they stay exact).
 // Otherwise v_dot2_f32_f16 does them on the vector ALUs.
 // Index rows stream from HBM through a three-deep register ring of buffer
-// loads; the first batch is issued before the tables are staged.  At
+// loads; the first batch is issued with the table slices, the second once a
+// wave has built its part of the tables (bf16 codebooks: each thread reads the
+// 16 bytes of q its part needs, so no wave waits for another's q).  At
 // the end the lanes write their (rotated) accumulators to the freed table
 // space at their channel positions and the workgroup sums them there.
 // Every workgroup but the merger of (b, h) publishes (m, l, o[d]) as 64-bit
@@ -133,7 +135,7 @@ struct Shape {
     static constexpr int RS = kQuadRed ? D * 4 + 16 : D * 4;   // row stride, bytes
     static constexpr int kDumpBytes = NR * RS;
     static constexpr int kBase = kDumpBytes > kTabBytes ? kDumpBytes : kTabBytes;
-    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16 + 2 * D;
+    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16;
     static constexpr int kLds = kBase + kExtra;
     static_assert(S >= 8 && S <= 64 && (S & (S - 1)) == 0, "8 sub-vectors per lane");
     static_assert(S * EB <= 256, "a value-table row holds every sub-vector");
@@ -376,9 +378,12 @@ struct Stage {
         else return __uint_as_float(w[i]);
     }
 
-    // qs: the scaled query (fp32); qw: the raw bf16 query, two channels a word.
-    // Returns whether a bf16 value entry of the units in `check` (bit u: unit
-    // u) falls outside fp16's range (value_out_of_fp16).
+    // qs: the scaled query (fp32, LDS; used with fp32 codebooks); qw: with
+    // bf16 codebooks, this thread's raw bf16 query words, two channels a word:
+    // the EPU entries of every unit it stages are sub-vectors j0 .. j0 + EPU - 1
+    // with the same j0 = (tid * EPU) mod S, so one 16-byte piece of q serves
+    // them all.  Returns whether a bf16 value entry of the units in `check`
+    // (bit u: unit u) falls outside fp16's range (value_out_of_fp16).
     __device__ __forceinline__ bool finish(const float *qs, const uint32_t *qw, float scale,
                                            unsigned char *smem, uint32_t check) const {
         const int tid = threadIdx.x;
@@ -398,7 +403,7 @@ struct Stage {
                     constexpr int WPE = CG / 2;
 #pragma unroll
                     for (int m = 0; m < WPE; ++m)
-                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[j * WPE + m]),
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[e * WPE + m]),
                                                               __builtin_bit_cast(bf16x2_t, kw[u][e * WPE + m]),
                                                               acc, false);
                     acc *= scale;
@@ -734,7 +739,6 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     float *wstat = qs + D;                      // [kWaves][m, l]
     float *red = wstat + 2 * kWaves;            // [G][D]
     uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);
-    uint16_t *qh = reinterpret_cast<uint16_t *>(smem + Sh::kBase + 4 * (D + 2 * kWaves + kThreads) + 16);
 
     // The splits of one (layer, b, h) share an XCD (and its L2, which then
     // serves their table slices once); within the group, roles follow the
@@ -807,6 +811,12 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
     const uint32_t qraw = lp.q[bh * D + min(tid, D - 1)];
+    // bf16 codebooks: the q words this thread's part of the score table needs
+    // (Stage::finish), so that each wave builds its part as soon as its own
+    // loads are in, without a barrier for every wave's q
+    uint4 qk = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (Sh::kF16V)
+        qk = *reinterpret_cast<const uint4 *>(lp.q + bh * D + ((tid * Sh::EPU) % S) * CG);
     // The block's epoch cannot change before this workgroup arrives, so it is
     // read now, overlapped with the prologue; it tags the partials.  Only the
     // epoch half of the arrival word is read (a 64-bit load whose low half is
@@ -851,9 +861,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // The second batch waits: at start-up every workgroup's first loads queue
     // for HBM together, and the table slices, which gate the token loop, get
     // through sooner with fewer rows ahead of them.  With the longer rows of
-    // S >= 32 it goes out once the tables are built, otherwise after the
-    // first barrier (measured).
-    constexpr bool kSecondAfterTables = S >= 32;
+    // S >= 32 a wave issues it once its own part of the tables is built,
+    // otherwise after the first barrier (measured).
+    constexpr bool kSecondAfterBuild = S >= 32;
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
@@ -863,13 +873,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     ir.init(kidx, vidx, max(t1, 0), lane_off, S);
 
     const float qv = bf16f((uint16_t)qraw);
-    if (tid < D) {
-        qs[tid] = qv * scale;
-        qh[tid] = (uint16_t)qraw;
-    }
+    if (tid < D) qs[tid] = qv * scale;
     if (tid == 0) *arrival = epoch_word;
-    __syncthreads();
-    if constexpr (!kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+    // q in LDS is read by the window passes and by fp32-codebook table builds;
+    // a VQ workgroup with bf16 codebooks needs neither (the barrier is
+    // workgroup-uniform)
+    if (!Sh::kF16V || s0 < s1) __syncthreads();
+    if constexpr (!kSecondAfterBuild) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
 
     // The window tokens need no table: where registers allow, fold them while
     // the table slices are still arriving, then build the tables.
@@ -888,14 +898,18 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         for (int u = split % nq; u < Sh::UPT; u += nq) check_units |= 1u << u;
     }
     auto build_tables = [&]() {
-        const bool bad = stg.finish(qs, reinterpret_cast<const uint32_t *>(qh), scale, smem, check_units);
+        const uint32_t qkw[4] = {qk.x, qk.y, qk.z, qk.w};
+        const bool bad = stg.finish(qs, qkw, scale, smem, check_units);
         if constexpr (Sh::kF16V) {
             if (__ballot(bad) != 0 && lane == 0)
                 __hip_atomic_fetch_or(a.status, kStatusValueRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     };
     if constexpr (!kWindowFirst) {
-        if (vq_wg) build_tables();
+        if (vq_wg) {
+            build_tables();
+            if constexpr (kSecondAfterBuild) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+        }
         __syncthreads();
     }
     if constexpr (kWinDB) {
@@ -916,7 +930,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
     }
     if constexpr (kWindowFirst) {
-        if (vq_wg) build_tables();
+        if (vq_wg) {
+            build_tables();
+            if constexpr (kSecondAfterBuild) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+        }
         __syncthreads();
     }
     // Waves w and w + 4 share a SIMD; the older one would win every issue slot
@@ -930,7 +947,6 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             __builtin_amdgcn_s_setprio(0);
         ++turn;
     };
-    if constexpr (kSecondAfterTables) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;

@@ -320,6 +320,8 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
             return LVQ_ERR_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(L.k_window) % 16 || reinterpret_cast<uintptr_t>(L.v_window) % 16)
             return LVQ_ERR_INVALID_ARG;
+        // the score tables read q in 16-byte pieces
+        if (reinterpret_cast<uintptr_t>(L.q) % 16) return LVQ_ERR_INVALID_ARG;
         if (reinterpret_cast<uintptr_t>(L.k_codebook) % 16 ||
             reinterpret_cast<uintptr_t>(L.v_codebook) % 16)
             return LVQ_ERR_INVALID_ARG;

@@ -128,7 +128,8 @@ def drive_host(path):
     # every rejection path
     c = cfg()
     for over in (dict(q=None), dict(ki=None), dict(out=None), dict(t=4), dict(t=-1), dict(L=5001),
-                 dict(sc=float("nan")), dict(kw=ctypes.c_void_p(P.value + 8)), dict(ws=None),
+                 dict(sc=float("nan")), dict(kw=ctypes.c_void_p(P.value + 8)), dict(q=ctypes.c_void_p(P.value + 8)),
+                 dict(ws=None),
                  dict(wsb=0), dict(ws=ctypes.c_void_p(P.value + 64))):
         assert decode(c, **over) != OK, over
     for bad in (cfg(head_dim=256), cfg(head_dim=384), cfg(group=18), cfg(loop_steps=3),
