@@ -227,12 +227,22 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             const int t = r >> 8, k = r & 255;
             const size_t off = ((((size_t)t * a.H + h) * 256 + k) * a.S + j0) * (CG * Sh::EB) + pc * 16;
             const uint4 v = *reinterpret_cast<const uint4 *>(src + off);
-            const CB *e = reinterpret_cast<const CB *>(&v);
+            // the chunk holds runs of one sub-vector's consecutive entries
+            // (a (t, k) piece of cg entries, or half of one): one aligned
+            // store per run
+            constexpr int RUN = CG * Sh::EB < 16 ? CG * Sh::EB : 16;   // bytes
+            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int q = 0; q < Sh::EC; ++q) {
-                const int fe = pc * Sh::EC + q;          // element of the (t, k) row piece
+            for (int q = 0; q < 16 / RUN; ++q) {
+                const int fe = pc * Sh::EC + q * (RUN / Sh::EB);      // first element of the run
                 const int jl = fe / CG, cc = fe % CG;
-                cbs[(jl * 256 + k) * G + t * CG + cc] = e[q];
+                CB *dst = cbs + (jl * 256 + k) * G + t * CG + cc;
+                if constexpr (RUN == 16)
+                    *reinterpret_cast<uint4 *>(dst) = v;
+                else if constexpr (RUN == 8)
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(vw[2 * q], vw[2 * q + 1]);
+                else
+                    *reinterpret_cast<uint32_t *>(dst) = vw[q];
             }
         }
     }
@@ -240,12 +250,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
     // squared norms (fp64 sum, rounded once); the max over the wave's codes
 #pragma unroll
     for (int m = 0; m < kJW; ++m) {
-        const CB *cw = cbs + (m * 256 + tid) * G;
+        // the code's G entries as 16-byte reads (rows are 16-byte aligned)
+        const uint4 *cw = reinterpret_cast<const uint4 *>(cbs + (m * 256 + tid) * G);
         double s = 0.0;
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const double v = to_f(cw[i]);
-            s += v * v;
+        for (int c = 0; c < G * Sh::EB / 16; ++c) {
+            const uint4 w = cw[c];
+            const CB *e = reinterpret_cast<const CB *>(&w);
+#pragma unroll
+            for (int i = 0; i < Sh::EC; ++i) {
+                const double v = to_f(e[i]);
+                s += v * v;
+            }
         }
         nrm[m * 256 + tid] = (float)s;
     }
@@ -451,7 +467,9 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             const bool store = valid && unique && holder;
             __builtin_amdgcn_raw_buffer_store_b8((unsigned char)k1, out_rsrc,
                                                  store ? (uint32_t)((r0 + row) * a.S) : kOob, 0, 0);
-            codes[r0 + row] = (valid && !unique) ? kRescore : (uint16_t)0;
+            // (one lane per row writes the mark: four lanes writing one
+            // address would serialise in LDS)
+            if (kq == 0) codes[r0 + row] = (valid && !unique) ? kRescore : (uint16_t)0;
     };
     if (nfull > 0) load_group(ringA, 0);
     for (int rb = 0; rb < nfull; rb += kPair) {
