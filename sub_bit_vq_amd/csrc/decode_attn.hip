@@ -720,11 +720,16 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
     }
 }
 
-// kMulti: the launch holds several layers (the layer index comes from the
-// workgroup index); a single-layer launch reads layer 0's operands at fixed
-// argument offsets, in the first round of argument loads.
-template <int S, int CG, typename CB, bool kMulti>
+// Launch modes.  kModeMulti: the launch holds several layers (the layer
+// index comes from the workgroup index).  kModeByLength: one layer, one
+// workgroup per (b, h), sequences taken longest first.  kModeOne: one layer,
+// no ranking; a single-layer launch reads layer 0's operands at fixed
+// argument offsets.
+constexpr int kModeOne = 0, kModeMulti = 1, kModeByLength = 2;
+
+template <int S, int CG, typename CB, int kMode>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
+    constexpr bool kMulti = kMode == kModeMulti;
     using Sh = Shape<S, CG, CB>;
     constexpr int D = Sh::D, R = Sh::R, TPW = Sh::TPW;
     constexpr int NRD = Sh::NRD, CPR = Sh::CPR, G = Sh::G;
@@ -751,7 +756,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int split = wr.role;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int h = (int)(gq % a.H), b = (int)(gq / a.H);
-    if (!kMulti && a.by_length) {
+    if constexpr (kMode == kModeByLength) {
         // One workgroup per (b, h) over several rounds: the longest
         // sequences go first (in dispatch order), so the last round holds the
         // shortest ones.  Rank by (length descending, index ascending), a
@@ -857,13 +862,20 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     IndexRows ir0;                              // rows up to the end of the split's chunk
     ir0.init(kidx, vidx, vq_wg ? (int)min((int64_t)vq0 + a.chunk, t_max) : 0, lane_off, S);
     Batch r0, r1, r2;
-    load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
     // The second batch waits: at start-up every workgroup's first loads queue
     // for HBM together, and the table slices, which gate the token loop, get
     // through sooner with fewer rows ahead of them.  With the longer rows of
     // S >= 32 a wave issues it once its own part of the tables is built,
     // otherwise after the first barrier (measured).
     constexpr bool kSecondAfterBuild = S >= 32;
+    // The two waves of a SIMD issue their loads one after the other (waves
+    // 0-3 first), and index rows, which miss to HBM, hold up the slice loads
+    // queued behind them.  So in a launch of split heads (all workgroups
+    // starting together) waves 0-3 issue their first batch too after their
+    // part of the tables, behind waves 4-7's slices (measured: 32K, 0.5 bit,
+    // 14.2-14.4 -> 13.9 us).  Wave-uniform.
+    const bool defer0 = kSecondAfterBuild && kMode == kModeOne && n_split > 1 && wave < kWaves / 2;
+    if (!defer0) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
     const int t0 = w.n_s + split * a.chunk;   // == vq0 whenever t0 < t1
@@ -908,7 +920,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     if constexpr (!kWindowFirst) {
         if (vq_wg) {
             build_tables();
-            if constexpr (kSecondAfterBuild) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+            if constexpr (kSecondAfterBuild) {
+                if (defer0) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
+                load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+            }
         }
         __syncthreads();
     }
@@ -932,7 +947,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     if constexpr (kWindowFirst) {
         if (vq_wg) {
             build_tables();
-            if constexpr (kSecondAfterBuild) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+            if constexpr (kSecondAfterBuild) {
+                if (defer0) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
+                load_batch<S, CG, CB>(ir0, vq0 + wave * TPW + BSTEP, r1);
+            }
         }
         __syncthreads();
     }
@@ -1249,22 +1267,26 @@ constexpr bool fits() {
 template <int S, int CG>
 hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
     const dim3 grid((unsigned)a.n_split * a.H * a.B * a.n_layers);
-    const bool multi = a.n_layers > 1;
+    const int mode = a.n_layers > 1 ? kModeMulti : a.by_length ? kModeByLength : kModeOne;
     if (a.cb_bf16) {
         if constexpr (fits<S, CG, uint16_t>()) {
-            if (multi)
-                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, true>), grid, dim3(kThreads), 0, st, a);
+            if (mode == kModeMulti)
+                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModeMulti>), grid, dim3(kThreads), 0, st, a);
+            else if (mode == kModeByLength)
+                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModeByLength>), grid, dim3(kThreads), 0, st, a);
             else
-                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, false>), grid, dim3(kThreads), 0, st, a);
+                hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModeOne>), grid, dim3(kThreads), 0, st, a);
         } else {
             return hipErrorInvalidValue;
         }
     } else {
         if constexpr (fits<S, CG, float>()) {
-            if (multi)
-                hipLaunchKernelGGL((decode_main<S, CG, float, true>), grid, dim3(kThreads), 0, st, a);
+            if (mode == kModeMulti)
+                hipLaunchKernelGGL((decode_main<S, CG, float, kModeMulti>), grid, dim3(kThreads), 0, st, a);
+            else if (mode == kModeByLength)
+                hipLaunchKernelGGL((decode_main<S, CG, float, kModeByLength>), grid, dim3(kThreads), 0, st, a);
             else
-                hipLaunchKernelGGL((decode_main<S, CG, float, false>), grid, dim3(kThreads), 0, st, a);
+                hipLaunchKernelGGL((decode_main<S, CG, float, kModeOne>), grid, dim3(kThreads), 0, st, a);
         } else {
             return hipErrorInvalidValue;
         }
