@@ -131,7 +131,9 @@ struct Shape {
     // that 16 consecutive rows read at one 16-byte offset hit distinct banks,
     // and each thread sums 4 positions of every SS-th row.
     static constexpr bool kQuadRed = D == 64 || D == 128;
-    static constexpr int NR = kWaves * TPW;            // dump rows
+    // dump rows: one per token slot, or with MFMA value sums one per pair of
+    // slots (folded in registers first)
+    static constexpr int NR = kMfma ? kWaves * TPW / 2 : kWaves * TPW;
     static constexpr int RS = kQuadRed ? D * 4 + 16 : D * 4;   // row stride, bytes
     static constexpr int kDumpBytes = NR * RS;
     static constexpr int kBase = kDumpBytes > kTabBytes ? kDumpBytes : kTabBytes;
@@ -300,11 +302,6 @@ struct Lanes {
     // channel of read h of step i (output position of its first element)
     __device__ __forceinline__ int channel(int i, int h) const {
         return (8 * r + ((i + rot) & 7)) * CG + Sh::CPR * (h ^ sw);
-    }
-    // MFMA layout: channel held by accumulator element e of step i
-    // (row e of the lane's 4-lane block, column r mod 4)
-    __device__ __forceinline__ int mfma_channel(int i, int e) const {
-        return (8 * ((r & ~3) + e) + ((i + rot) & 7)) * CG + (r & 3);
     }
 };
 
@@ -991,6 +988,24 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint32_t epoch = *arrival;                 // 0 .. kEpochWrap - 1
     const uint32_t tag = epoch + 1u;                 // never 0 (zero-filled slots)
     const int n = n_split;
+    // MFMA layout: token slots tk and tk + TPW/2 (lanes 32 apart) have the
+    // same rotation, so their accumulators hold the same channels.  One lane
+    // swap and an add per pair of accumulators fold them while other waves
+    // are still in their loops: lanes 0-31 keep the sums of blocks 0-3 (the
+    // first operand), lanes 32-63 those of blocks 4-7.
+    float fold[Sh::kMfma ? 16 : 1];
+    if constexpr (Sh::kMfma) {
+        static_assert(D == 128 && R == 4 && TPW == 16, "one MFMA shape");
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.acc[4 * i + e]),
+                                                                 __float_as_uint(st.acc[4 * (i + 4) + e]),
+                                                                 false, false);
+                fold[4 * i + e] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+            }
+    }
     __syncthreads();                             // every wave is done with the tables
     // Who merges.  With window workgroups (the grid fits the chip) it is the
     // last of them: it has the highest index of its (b, h), so its peers were
@@ -1001,7 +1016,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     if (tid == 0 && n > 1 && !sep)
         ticket_word = __hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float *dump = reinterpret_cast<float *>(smem);
-    const int drow = wave * TPW + tk;
+    constexpr int RPW = Sh::NR / kWaves;        // dump rows per wave
+    const int drow = wave * RPW + tk % RPW;
     if constexpr (Sh::kQuadRed) {
         // 16-byte (or 8-byte) pieces at padded rows.  MFMA layout: the lane's
         // accumulators 4i .. 4i + 3 (rows e of its block) hold channels
@@ -1009,11 +1025,11 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         // otherwise positions are channels.
         unsigned char *rowp = smem + (size_t)drow * Sh::RS;
         if constexpr (Sh::kMfma) {
-            static_assert(D == 128 && R == 4, "one MFMA shape");
+            const int hb = lane >> 5;            // folded blocks 4 hb .. 4 hb + 3
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<float4 *>(rowp + 16 * (4 * ((i + ln.rot) & 7) + r)) =
-                    make_float4(st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]);
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<float4 *>(rowp + 16 * (4 * ((i + 4 * hb + ln.rot) & 7) + r)) =
+                    make_float4(fold[4 * i], fold[4 * i + 1], fold[4 * i + 2], fold[4 * i + 3]);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1029,13 +1045,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             }
         }
     } else {
+        static_assert(!Sh::kMfma, "MFMA value sums come with head_dim 128");
         float *mine = dump + (size_t)drow * D;
-        if constexpr (Sh::kMfma) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) mine[ln.mfma_channel(i, e)] = st.acc[4 * i + e];
-        } else
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -1084,10 +1095,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         for (int i = 0; i < RPT; ++i) {
             const int row = sb + SS * i;
             // the row's wave, among the few a row of this i can belong to
-            float sc = ew[(SS * i) / TPW];
+            float sc = ew[(SS * i) / RPW];
 #pragma unroll
-            for (int w = (SS * i) / TPW + 1; w <= (SS * i + SS - 1) / TPW; ++w)
-                if (row >= w * TPW) sc = ew[w];
+            for (int w = (SS * i) / RPW + 1; w <= (SS * i + SS - 1) / RPW; ++w)
+                if (row >= w * RPW) sc = ew[w];
             const float4 v = *reinterpret_cast<const float4 *>(smem + (size_t)row * Sh::RS + 16 * q);
             a4.x += sc * v.x;
             a4.y += sc * v.y;
