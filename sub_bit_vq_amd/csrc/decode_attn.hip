@@ -861,10 +861,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     Batch r0, r1, r2;
     // The second batch waits: at start-up every workgroup's first loads queue
     // for HBM together, and the table slices, which gate the token loop, get
-    // through sooner with fewer rows ahead of them.  With the longer rows of
-    // S >= 32 a wave issues it once its own part of the tables is built,
-    // otherwise after the first barrier (measured).
-    constexpr bool kSecondAfterBuild = S >= 32;
+    // through sooner with fewer rows ahead of them.  With the rows of S >= 16
+    // a wave issues it once its own part of the tables is built, otherwise
+    // after the first barrier (measured: 32K at 0.25 bit 15.5 -> 15.3 us).
+    constexpr bool kSecondAfterBuild = S >= 16;
     // The two waves of a SIMD issue their loads one after the other (waves
     // 0-3 first), and index rows, which miss to HBM, hold up the slice loads
     // queued behind them.  So in a launch of split heads (all workgroups
