@@ -110,6 +110,20 @@ typedef struct {
                                before it gives up (writes NaN for that row and
                                sets LVQ_STATUS_MERGE_TIMEOUT); 0 = the default,
                                2^22 polls (seconds)                              */
+    int32_t decode_heads_per_group; /* query heads per decode workgroup.  With
+                               grouped-query attention two consecutive query
+                               heads of one KV head can share a workgroup,
+                               which reads each index row and window row once
+                               for both.  0 = the library's choice: 2 where
+                               possible (n_heads / n_kv_heads even, S = 32,
+                               cg = 4, bf16 codebooks, head_dim 128, one layer
+                               per launch, and a plan that merges through
+                               window workgroups or needs no merge), else 1;
+                               1 = one head; 2 = two (lvq_decode_attn returns
+                               LVQ_ERR_UNSUPPORTED where not possible).  With
+                               two heads, decode_splits counts workgroups per
+                               (b, head pair).  Changes only the rounding of
+                               the result.                                       */
 } lvq_config;
 
 #define LVQ_MAX_SPLITS 64
@@ -354,15 +368,24 @@ lvq_status lvq_decode_status(void *workspace, uint32_t *flags, int32_t clear, vo
  * ordered by dispatch index; where the launch merges by window workgroups,
  * role n-1 merges, so it is the member of its group dispatched last.  With
  * one workgroup per (b, h) and 2 <= B <= 256 the kernel assigns sequences
- * by length at run time, and `seq` is then a position in that order.
+ * by length at run time, and `seq` is then a position in that order.  Where
+ * a workgroup serves two query heads (lvq_decode_heads_per_workgroup), `head`
+ * is the first of them and the groups are (layer, b, head pair).
  * Returns the role, or -1 for an invalid config or workgroup index. */
 int32_t lvq_decode_role(const lvq_config *cfg, int32_t n_layers, int32_t max_ctx_len,
                         int32_t workgroup, int32_t *layer, int32_t *seq, int32_t *head);
 
 /* Number of workgroups per (b, h) that lvq_decode_attn launches for
- * max_ctx_len with exact windows (vq_len == NULL); host arithmetic only; 0 on
- * an invalid config. */
+ * max_ctx_len with exact windows (vq_len == NULL), per (b, head pair) when
+ * lvq_decode_heads_per_workgroup is 2; host arithmetic only; 0 on an invalid
+ * config. */
 int32_t lvq_decode_splits(const lvq_config *cfg, int32_t max_ctx_len);
+
+/* Query heads each decode workgroup serves (1 or 2, see
+ * lvq_config.decode_heads_per_group) for a launch of n_layers layers
+ * (1..LVQ_MAX_LAYERS) and max_ctx_len; host arithmetic only; 0 on an invalid
+ * config or when decode_heads_per_group = 2 is not possible. */
+int32_t lvq_decode_heads_per_workgroup(const lvq_config *cfg, int32_t n_layers, int32_t max_ctx_len);
 
 /* How many of those workgroups take the bf16 window slots instead of a VQ
  * chunk (0: every workgroup takes a VQ chunk and a share of the window

@@ -137,7 +137,8 @@ struct Shape {
     static constexpr int RS = kQuadRed ? D * 4 + 16 : D * 4;   // row stride, bytes
     static constexpr int kDumpBytes = NR * RS;
     static constexpr int kBase = kDumpBytes > kTabBytes ? kDumpBytes : kTabBytes;
-    static constexpr int kExtra = 4 * (D + 2 * kWaves + kThreads) + 16;
+    // q (up to two heads), wave stats, reduction partials, arrival words
+    static constexpr int kExtra = 4 * (2 * D + 4 * kWaves + kThreads) + 16;
     static constexpr int kLds = kBase + kExtra;
     static_assert(S >= 8 && S <= 64 && (S & (S - 1)) == 0, "8 sub-vectors per lane");
     static_assert(S * EB <= 256, "a value-table row holds every sub-vector");
@@ -381,8 +382,13 @@ struct Stage {
     // with the same j0 = (tid * EPU) mod S, so one 16-byte piece of q serves
     // them all.  Returns whether a bf16 value entry of the units in `check`
     // (bit u: unit u) falls outside fp16's range (value_out_of_fp16).
-    __device__ __forceinline__ bool finish(const float *qs, const uint32_t *qw, float scale,
+    // NH query heads (consecutive, one KV head): head hh's score table
+    // takes the replica slots KCOP*hh .. of every row (NH = 2: S = 32, one
+    // replica, so the second head's scores fill the upper half of the row).
+    template <int NH>
+    __device__ __forceinline__ bool finish(const float *qs, const uint32_t (*qw)[4], float scale,
                                            unsigned char *smem, uint32_t check) const {
+        static_assert(NH == 1 || Sh::kF16V, "head pairs: bf16 codebooks");
         const int tid = threadIdx.x;
         float *lutk = reinterpret_cast<float *>(smem);
         uint32_t mx = 0;
@@ -390,6 +396,8 @@ struct Stage {
         for (int u = 0; u < Sh::UPT; ++u) {
             const int e0 = (tid + u * kThreads) * Sh::EPU;   // first entry of the unit
             const int k = e0 / S, j0 = e0 % S;
+#pragma unroll
+          for (int hh = 0; hh < NH; ++hh) {
             float accs[Sh::EPU];
 #pragma unroll
             for (int e = 0; e < Sh::EPU; ++e) {
@@ -400,7 +408,7 @@ struct Stage {
                     constexpr int WPE = CG / 2;
 #pragma unroll
                     for (int m = 0; m < WPE; ++m)
-                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[e * WPE + m]),
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[hh][e * WPE + m]),
                                                               __builtin_bit_cast(bf16x2_t, kw[u][e * WPE + m]),
                                                               acc, false);
                     acc *= scale;
@@ -413,7 +421,7 @@ struct Stage {
             // a unit's entries are adjacent in the row: written together
 #pragma unroll
             for (int cp = 0; cp < Sh::KCOP; ++cp) {
-                float *row = lutk + k * 64 + S * cp + j0;
+                float *row = lutk + k * 64 + S * (Sh::KCOP * hh + cp) + j0;
                 if constexpr (Sh::EPU % 4 == 0) {
 #pragma unroll
                     for (int e = 0; e < Sh::EPU; e += 4)
@@ -426,6 +434,7 @@ struct Stage {
                     row[0] = accs[0];
                 }
             }
+          }
             // value entries of the unit, converted, into every replica of row k
             uint32_t o[UW];
 #pragma unroll
@@ -553,6 +562,51 @@ struct WindowPass {
             for (int e = 0; e < CPR / 2; ++e) {
                 st.acc[q * CPR + 2 * e] += p * bf16lo(v[q][e]);
                 st.acc[q * CPR + 2 * e + 1] += p * bf16hi(v[q][e]);
+            }
+        }
+    }
+
+    // The same slot for two query heads (q of head hh at qs + hh * D): the
+    // rows are read once, each head scores them and takes the values with its
+    // own weight.
+    template <typename OnlineT>
+    __device__ __forceinline__ void fold_pair(const float *qs, OnlineT *sts, int r, const Windows &w,
+                                              int n_sink, int n_recent) {
+        static_assert(Sh::kMfma, "head pairs: the MFMA shape");
+        constexpr int R = Sh::R, D = Sh::D;
+        const bool ok = in && slot_valid(slot, w, n_sink, n_recent);
+        const int n = r & 3;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            OnlineT &st = sts[hh];
+            const float *qh = qs + hh * D;
+            float dot = 0.f;
+            if (ok) {
+#pragma unroll
+                for (int i = 0; i < CL / 2; ++i) {
+                    dot += qh[r * CL + 2 * i] * bf16lo(k[i]);
+                    dot += qh[r * CL + 2 * i + 1] * bf16hi(k[i]);
+                }
+            }
+            dot = token_sum<R>(dot);
+            const float s = ok ? dot : -INFINITY;
+            const float mx = wave_max(s);
+            if (mx == -INFINITY) return;          // wave-uniform, the same for both heads
+            st.raise(mx);
+            const float p = ok ? ex2(s - st.m) * kPScale : 0.f;
+            st.l += p;
+            float bc[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) bc[c] = n == c ? p : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float4_t d = {st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]};
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16lo(v[i][0]), bc[0], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16hi(v[i][0]), bc[1], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16lo(v[i][1]), bc[2], d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_4x4x1f32(bf16hi(v[i][1]), bc[3], d, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.acc[4 * i + e] = d[e];
             }
         }
     }
@@ -717,17 +771,98 @@ __device__ __forceinline__ void fold_batch(const Batch &bt, int base, int t1,
     }
 }
 
+// A batch for two query heads of one KV head (kModePair): every index row is
+// read and decoded once; each lane's score gathers for the second head use
+// the same addresses 4S bytes further (the upper half of the table row), and
+// the value gathers are shared, each head summing them with its own weights.
+template <int S, int CG, typename CB, typename OnlineT>
+__device__ __forceinline__ void fold_pair(const Batch &bt, int base, int t1,
+                                          const unsigned char *smem,
+                                          const Lanes<S, CG, CB> &ln, OnlineT *sts) {
+    using Sh = Shape<S, CG, CB>;
+    static_assert(Sh::kMfma && Sh::KCOP == 1, "head pairs: the MFMA shape");
+    constexpr int R = Sh::R, STEP = kWaves * Sh::TPW;
+    constexpr uint32_t kSecond = 4 * S;               // second head's scores in a row
+    const int tk = (threadIdx.x & 63) / R;
+    float s[2][kUnroll];
+    bool ok[kUnroll];
+    float mx[2] = {-INFINITY, -INFINITY};
+    float g[kUnroll][2][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t w0 = perm(bt.k[u].y, bt.k[u].x, ln.rotA);   // index bytes in step order
+        const uint32_t w1 = perm(bt.k[u].y, bt.k[u].x, ln.rotB);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t ad = perm(ln.offK[i >> 2], i < 4 ? w0 : w1, sel_k(i));
+            g[u][0][i] = *reinterpret_cast<const float *>(smem + ad);
+            g[u][1][i] = *reinterpret_cast<const float *>(smem + ad + kSecond);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        ok[u] = base + u * STEP + tk < t1;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float *gg = g[u][hh];
+            float acc = ((gg[0] + gg[1]) + (gg[2] + gg[3])) + ((gg[4] + gg[5]) + (gg[6] + gg[7]));
+            acc = token_sum<R>(acc);
+            s[hh][u] = ok[u] ? acc : -INFINITY;
+            mx[hh] = fmaxf(mx[hh], s[hh][u]);
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        if (__ballot(mx[hh] > sts[hh].m + kMaxSlack) != 0) sts[hh].raise(wave_max(mx[hh]));
+    uint2 av[2][8];
+    auto gather = [&](int u, uint2 *dst) {
+        const uint32_t w0 = perm(bt.v[u].y, bt.v[u].x, ln.rotA);
+        const uint32_t w1 = perm(bt.v[u].y, bt.v[u].x, ln.rotB);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            dst[i] = *reinterpret_cast<const uint2 *>(smem + perm(ln.offV[i >> 1], i < 4 ? w0 : w1, sel_v(i)));
+    };
+    gather(0, av[0]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (u + 1 < kUnroll) gather(u + 1, av[(u + 1) & 1]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            OnlineT &st = sts[hh];
+            // tokens past the range take weight 0 (out-of-range rows read code 0)
+            const _Float16 ph = (_Float16)(ok[u] ? ex2(s[hh][u] - st.m) * kPScale : 0.f);
+            st.l += (float)ph;
+            const uint32_t ph2 = (uint32_t)__builtin_bit_cast(uint16_t, ph) * 0x00010001u;
+            const half4_t bop = __builtin_bit_cast(half4_t, make_uint2(ph2 & ln.bmask0, ph2 & ln.bmask1));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float4_t d = {st.acc[4 * i], st.acc[4 * i + 1], st.acc[4 * i + 2], st.acc[4 * i + 3]};
+                d = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(half4_t, av[u & 1][i]), bop, d, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st.acc[4 * i + e] = d[e];
+            }
+        }
+    }
+}
+
 // Launch modes.  kModeMulti: the launch holds several layers (the layer
 // index comes from the workgroup index).  kModeByLength: one layer, one
 // workgroup per (b, h), sequences taken longest first.  kModeOne: one layer,
 // no ranking; a single-layer launch reads layer 0's operands at fixed
-// argument offsets.
-constexpr int kModeOne = 0, kModeMulti = 1, kModeByLength = 2;
+// argument offsets.  kModePair: like kModeOne, but a workgroup serves two
+// consecutive query heads of one KV head (grouped-query attention): it reads
+// each index row once and scores it against both heads' tables (see
+// fold_pair).
+constexpr int kModeOne = 0, kModeMulti = 1, kModeByLength = 2, kModePair = 3;
 
 template <int S, int CG, typename CB, int kMode>
 __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     constexpr bool kMulti = kMode == kModeMulti;
     using Sh = Shape<S, CG, CB>;
+    // query heads per workgroup; the second head's scores sit in the upper
+    // half of every score-table row (one copy per row at S = 32)
+    constexpr int NH = kMode == kModePair ? 2 : 1;
+    static_assert(NH == 1 || (Sh::kMfma && Sh::KCOP == 1 && 2 * S == 64), "head pairs: the MFMA shape");
     constexpr int D = Sh::D, R = Sh::R, TPW = Sh::TPW;
     constexpr int NRD = Sh::NRD, CPR = Sh::CPR, G = Sh::G;
     constexpr int BSTEP = kWaves * TPW * kUnroll;   // tokens per batch of the workgroup
@@ -737,22 +872,23 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // The only LDS object: tables at byte 0 and 64K, then q, wave stats,
     // reduction partials and the arrival word.
     __shared__ __align__(16) unsigned char smem[Sh::kLds];
-    float *qs = reinterpret_cast<float *>(smem + Sh::kBase);
-    float *wstat = qs + D;                      // [kWaves][m, l]
-    float *red = wstat + 2 * kWaves;            // [G][D]
-    uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);
+    float *qs = reinterpret_cast<float *>(smem + Sh::kBase);   // [NH][D]
+    float *wstat = qs + NH * D;                 // [NH][kWaves][m, l]
+    float *red = wstat + 2 * NH * kWaves;       // [G][D], or [NH][D]
+    uint32_t *arrival = reinterpret_cast<uint32_t *>(red + kThreads);   // [NH]
 
     // The splits of one (layer, b, h) share an XCD (and its L2, which then
     // serves their table slices once); within the group, roles follow the
     // dispatch order (decode_role).  Layers are outermost.
     const unsigned p = blockIdx.x;
     const WgRole wr = decode_role(p, gridDim.x, (unsigned)a.n_split);
-    const unsigned groups_per_layer = (unsigned)a.H * a.B;
+    const unsigned hgroups = (unsigned)a.H / NH;     // head groups per sequence
+    const unsigned groups_per_layer = hgroups * a.B;
     const int layer = kMulti ? (int)(wr.group / groups_per_layer) : 0;
     const unsigned gq = kMulti ? wr.group % groups_per_layer : wr.group;
     const int split = wr.role;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int h = (int)(gq % a.H), b = (int)(gq / a.H);
+    int h = (int)(gq % hgroups) * NH, b = (int)(gq / hgroups);   // h: the first head
     if constexpr (kMode == kModeByLength) {
         // One workgroup per (b, h) over several rounds: the longest
         // sequences go first (in dispatch order), so the last round holds the
@@ -787,7 +923,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const int64_t t_max = a.t_max;
     const int Lraw = a.ctx_len[b];
     const int vqraw = a.vq_len ? a.vq_len[b] : -1;
-    const size_t bh = (size_t)b * a.H + h;             // query head: q, partials, out
+    const size_t bh = (size_t)b * a.H + h;             // (first) query head: q, partials, out
     const int hk = h / a.q_per_kv;                      // KV head: caches, codebooks, windows
     const size_t bhk = (size_t)b * a.Hk + hk;
     const CB *kcb = static_cast<const CB *>(lp.kcb_t) + (size_t)hk * 256 * S * CG;
@@ -798,11 +934,14 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     const uint8_t *kidx = lp.k_index + bhk * (size_t)t_max * S;
     const uint8_t *vidx = lp.v_index + bhk * (size_t)t_max * S;
     const uint32_t lane_off = (uint32_t)(tk * S + 8 * r);
+    // the heads of a workgroup are consecutive, so are their workspace blocks
+    // and output rows: head hh's block is blk + hh * kBlockBytes
     char *blk = a.blocks + ((size_t)layer * a.B * a.H + bh) * kBlockBytes;
     uint64_t *ticket = reinterpret_cast<uint64_t *>(blk);          // arrival word
     const uint64_t *parts = reinterpret_cast<const uint64_t *>(blk + kSlotBase);
     uint64_t *part = reinterpret_cast<uint64_t *>(blk + kSlotBase) + (size_t)split * (D + 2);
     float *outp = lp.out + bh * D;
+    constexpr size_t kBlockWords = kBlockBytes / sizeof(uint64_t);
     const float scale = a.scale_log2;
     const int n_split = a.n_split;
     const int n_win = a.window_wg;
@@ -812,22 +951,27 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // Loads that depend only on (b, h, t) go out first: q (raw bf16 bits,
     // converted later so that no wait is placed here) and the table slices.
-    const uint32_t qraw = lp.q[bh * D + min(tid, D - 1)];
+    const uint32_t qraw = lp.q[bh * D + min(tid, NH * D - 1)];
     // bf16 codebooks: the q words this thread's part of the score table needs
     // (Stage::finish), so that each wave builds its part as soon as its own
     // loads are in, without a barrier for every wave's q
-    uint4 qk = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (Sh::kF16V)
-        qk = *reinterpret_cast<const uint4 *>(lp.q + bh * D + ((tid * Sh::EPU) % S) * CG);
+    uint32_t qk[NH][4];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+        uint4 w4 = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (Sh::kF16V)
+            w4 = *reinterpret_cast<const uint4 *>(lp.q + (bh + hh) * D + ((tid * Sh::EPU) % S) * CG);
+        qk[hh][0] = w4.x; qk[hh][1] = w4.y; qk[hh][2] = w4.z; qk[hh][3] = w4.w;
+    }
     // The block's epoch cannot change before this workgroup arrives, so it is
     // read now, overlapped with the prologue; it tags the partials.  Only the
     // epoch half of the arrival word is read (a 64-bit load whose low half is
     // dead would let the compiler reuse that register and wait for the load
     // before the index rows go out).
-    uint32_t epoch_word = 0;
-    if (tid == 0 && a.n_split > 1)
-        epoch_word = __hip_atomic_load(reinterpret_cast<uint32_t *>(ticket) + 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t epoch_word = 0;                    // thread hh < NH: head hh's
+    if (tid < NH && a.n_split > 1)
+        epoch_word = __hip_atomic_load(reinterpret_cast<uint32_t *>(ticket + tid * kBlockWords) + 1,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Stage<S, CG, CB> stg;
     {
         const int slice = vq_wg ? 256 * S * CG * (int)sizeof(CB) : 0;
@@ -846,7 +990,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     using Win = WindowPass<S, CG, CB>;
     // With at most 4 channels per sub-vector step a second pass's rows fit
     // the registers: pass p + 1 is in flight while pass p is folded.
-    constexpr bool kWinDB = CG <= 4;
+    constexpr bool kWinDB = NH == 1 && CG <= 4;
     constexpr int WP = kWaves * TPW;             // window slots per pass
     int wslot = s0 + wave;
     Win win, win2;
@@ -882,8 +1026,8 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     ir.init(kidx, vidx, max(t1, 0), lane_off, S);
 
     const float qv = bf16f((uint16_t)qraw);
-    if (tid < D) qs[tid] = qv * scale;
-    if (tid == 0) *arrival = epoch_word;
+    if (tid < NH * D) qs[tid] = qv * scale;
+    if (tid < NH) arrival[tid] = epoch_word;
     // q in LDS is read by the window passes and by fp32-codebook table builds;
     // a VQ workgroup with bf16 codebooks needs neither (the barrier is
     // workgroup-uniform)
@@ -892,9 +1036,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // The window tokens need no table: where registers allow, fold them while
     // the table slices are still arriving, then build the tables.
-    constexpr bool kWindowFirst = Sh::NACC <= 32;
-    Online<Sh::NACC> st;
-    st.init();
+    // (with two heads the window rows wait for the build: their registers
+    // and the staged slices would not fit together)
+    constexpr bool kWindowFirst = NH == 1 && Sh::NACC <= 32;
+    Online<Sh::NACC> sts[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) sts[hh].init();
+    Online<Sh::NACC> &st = sts[0];
     // Build the tables.  A value codebook entry outside fp16's range is
     // flagged in the status word.  The VQ workgroups of a head stage the same
     // slice, so they share that check: the one of VQ role `split` among
@@ -907,8 +1055,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         for (int u = split % nq; u < Sh::UPT; u += nq) check_units |= 1u << u;
     }
     auto build_tables = [&]() {
-        const uint32_t qkw[4] = {qk.x, qk.y, qk.z, qk.w};
-        const bool bad = stg.finish(qs, qkw, scale, smem, check_units);
+        const bool bad = stg.template finish<NH>(qs, qk, scale, smem, check_units);
         if constexpr (Sh::kF16V) {
             if (__ballot(bad) != 0 && lane == 0)
                 __hip_atomic_fetch_or(a.status, kStatusValueRange, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -924,7 +1071,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
         __syncthreads();
     }
-    if constexpr (kWinDB) {
+    if constexpr (NH == 2) {
+        while (wslot < s1) {                     // wave-uniform
+            win.fold_pair(qs, sts, r, w, n_sink, n_recent);
+            wslot += WP;
+            if (wslot < s1) win.load(kw, vw, wslot + kWaves * tk, s1, ln);
+        }
+    } else if constexpr (kWinDB) {
         while (wslot < s1) {                     // wave-uniform
             win.fold(qs, st, r, w, n_sink, n_recent);
             wslot += WP;
@@ -962,49 +1115,65 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
             __builtin_amdgcn_s_setprio(0);
         ++turn;
     };
+    auto fold_next = [&](const Batch &bt) {
+        if constexpr (NH == 2)
+            fold_pair<S, CG, CB>(bt, base, t1, smem, ln, sts);
+        else
+            fold_batch<S, CG, CB>(bt, base, t1, smem, ln, st);
+    };
     // three-deep ring, unrolled so that every batch lives in named registers
     while (true) {                               // wave-uniform
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r2);
         take_turn();
-        fold_batch<S, CG, CB>(r0, base, t1, smem, ln, st);
+        fold_next(r0);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r0);
         take_turn();
-        fold_batch<S, CG, CB>(r1, base, t1, smem, ln, st);
+        fold_next(r1);
         base += BSTEP;
         if (base >= t1) break;
         load_batch<S, CG, CB>(ir, base + 2 * BSTEP, r1);
         take_turn();
-        fold_batch<S, CG, CB>(r2, base, t1, smem, ln, st);
+        fold_next(r2);
         base += BSTEP;
     }
     __builtin_amdgcn_s_setprio(0);
 
     // Lane accumulators to the freed table space: row (wave, tk), natural
     // channel order.  Then wave (m, l).
-    const float lw = wave_sum(st.l) * (1.f / R);     // every token was counted R times
-    const uint32_t epoch = *arrival;                 // 0 .. kEpochWrap - 1
-    const uint32_t tag = epoch + 1u;                 // never 0 (zero-filled slots)
+    // per head: the wave's l (every token was counted R times), the block's
+    // epoch (0 .. kEpochWrap - 1) and the call's tag (never 0: zero-filled
+    // slots)
+    float lwh[NH];
+    uint32_t epochh[NH], tagh[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+        lwh[hh] = wave_sum(sts[hh].l) * (1.f / R);
+        epochh[hh] = arrival[hh];
+        tagh[hh] = epochh[hh] + 1u;
+    }
     const int n = n_split;
     // MFMA layout: token slots tk and tk + TPW/2 (lanes 32 apart) have the
     // same rotation, so their accumulators hold the same channels.  One lane
     // swap and an add per pair of accumulators fold them while other waves
     // are still in their loops: lanes 0-31 keep the sums of blocks 0-3 (the
     // first operand), lanes 32-63 those of blocks 4-7.
-    float fold[Sh::kMfma ? 16 : 1];
+    float fold[NH][Sh::kMfma ? 16 : 1];
     if constexpr (Sh::kMfma) {
         static_assert(D == 128 && R == 4 && TPW == 16, "one MFMA shape");
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int hh = 0; hh < NH; ++hh)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.acc[4 * i + e]),
-                                                                 __float_as_uint(st.acc[4 * (i + 4) + e]),
-                                                                 false, false);
-                fold[4 * i + e] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-            }
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(sts[hh].acc[4 * i + e]),
+                                                                     __float_as_uint(sts[hh].acc[4 * (i + 4) + e]),
+                                                                     false, false);
+                    fold[hh][4 * i + e] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+                }
     }
     __syncthreads();                             // every wave is done with the tables
     // Who merges.  With window workgroups (the grid fits the chip) it is the
@@ -1013,7 +1182,7 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // their partials.  Otherwise the last workgroup to take an arrival ticket
     // merges; the ticket travels while the partial is reduced.
     uint64_t ticket_word = 0;
-    if (tid == 0 && n > 1 && !sep)
+    if (NH == 1 && tid == 0 && n > 1 && !sep)
         ticket_word = __hip_atomic_fetch_add(ticket, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     float *dump = reinterpret_cast<float *>(smem);
     constexpr int RPW = Sh::NR / kWaves;        // dump rows per wave
@@ -1025,11 +1194,15 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         // otherwise positions are channels.
         unsigned char *rowp = smem + (size_t)drow * Sh::RS;
         if constexpr (Sh::kMfma) {
+            // head hh's rows follow the first head's NR rows
             const int hb = lane >> 5;            // folded blocks 4 hb .. 4 hb + 3
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<float4 *>(rowp + 16 * (4 * ((i + 4 * hb + ln.rot) & 7) + r)) =
-                    make_float4(fold[4 * i], fold[4 * i + 1], fold[4 * i + 2], fold[4 * i + 3]);
+            for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<float4 *>(rowp + (size_t)hh * Sh::NR * Sh::RS +
+                                                16 * (4 * ((i + 4 * hb + ln.rot) & 7) + r)) =
+                        make_float4(fold[hh][4 * i], fold[hh][4 * i + 1], fold[hh][4 * i + 2], fold[hh][4 * i + 3]);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -1061,28 +1234,38 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         }
     }
     if (lane == 0) {
-        wstat[2 * wave] = st.m;
-        wstat[2 * wave + 1] = lw;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+            wstat[2 * (hh * kWaves + wave)] = sts[hh].m;
+            wstat[2 * (hh * kWaves + wave) + 1] = lwh[hh];
+        }
     }
     __syncthreads();
 
     // Workgroup partial: scale every wave to the common max (empty waves have
     // l == 0 and zero accumulators) and sum the dumped rows.
-    float mw[kWaves], lv[kWaves], ew[kWaves];
+    float ewh[NH][kWaves], Mh[NH], lth[NH];
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        mw[v] = wstat[2 * v];
-        lv[v] = wstat[2 * v + 1];
+    for (int hh = 0; hh < NH; ++hh) {
+        float mw[kWaves], lv[kWaves];
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            mw[v] = wstat[2 * (hh * kWaves + v)];
+            lv[v] = wstat[2 * (hh * kWaves + v) + 1];
+        }
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) Mx = lv[v] > 0.f ? fmaxf(Mx, mw[v]) : Mx;
+        float lx = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) {
+            ewh[hh][v] = lv[v] > 0.f ? ex2(mw[v] - Mx) : 0.f;
+            lx += lv[v] * ewh[hh][v];
+        }
+        Mh[hh] = Mx;
+        lth[hh] = lx;
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = lv[v] > 0.f ? fmaxf(M, mw[v]) : M;
-    float lt = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-        ew[v] = lv[v] > 0.f ? ex2(mw[v] - M) : 0.f;
-        lt += lv[v] * ew[v];
-    }
+    const float *ew = ewh[0];
     if constexpr (Sh::kQuadRed) {
         // thread (q, s): positions 4q .. 4q + 3 of rows s, s + SS, ...; the
         // SS subsets of a quad are consecutive lanes, summed with DPP (and one
@@ -1090,16 +1273,18 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         constexpr int QD = D / 4, SS = kThreads / QD, RPT = Sh::NR / SS;
         static_assert(SS == 16 || SS == 32, "subsets fill DPP rows");
         const int sb = tid % SS, q = tid / SS;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
         float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const int row = sb + SS * i;
             // the row's wave, among the few a row of this i can belong to
-            float sc = ew[(SS * i) / RPW];
+            float sc = ewh[hh][(SS * i) / RPW];
 #pragma unroll
             for (int w = (SS * i) / RPW + 1; w <= (SS * i + SS - 1) / RPW; ++w)
-                if (row >= w * RPW) sc = ew[w];
-            const float4 v = *reinterpret_cast<const float4 *>(smem + (size_t)row * Sh::RS + 16 * q);
+                if (row >= w * RPW) sc = ewh[hh][w];
+            const float4 v = *reinterpret_cast<const float4 *>(smem + (size_t)(hh * Sh::NR + row) * Sh::RS + 16 * q);
             a4.x += sc * v.x;
             a4.y += sc * v.y;
             a4.z += sc * v.z;
@@ -1119,8 +1304,9 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         if (sb == 0) {
             const float av[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[Sh::kMfma ? 32 * e + q : 4 * q + e] = av[e];
+            for (int e = 0; e < 4; ++e) red[hh * D + (Sh::kMfma ? 32 * e + q : 4 * q + e)] = av[e];
         }
+      }
     } else {
         const int ch = tid % D, g = tid / D;
         float acc = 0.f;
@@ -1134,8 +1320,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
         red[g * D + ch] = acc;
     }
     __syncthreads();
+    // Thread tid < NH * D owns channel tid % D of head hme = tid / D (the
+    // heads' output rows and workspace blocks are consecutive).
+    const int hme = tid / D < NH ? tid / D : NH - 1;
+    const float M = Mh[hme], lt = lth[hme];
+    const uint32_t tag = tagh[hme];
     float o = 0.f;
-    if (tid < D) {
+    if (tid < NH * D) {
         if constexpr (Sh::kQuadRed) {
             o = red[tid];
         } else {
@@ -1146,20 +1337,23 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // One workgroup per (b, h): nothing to merge, and the workspace is not
     // touched.
     if (n == 1) {
-        if (tid < D) outp[tid] = lt > 0.f ? o / lt : 0.f;
+        if (tid < NH * D) outp[tid] = lt > 0.f ? o / lt : 0.f;
         return;
     }
+    uint64_t *const part_me = part + hme * kBlockWords;
     // Every workgroup publishes at once (before it knows whether it is last,
     // so the others' pairs are already on their way when the last one looks).
     if (sep) {
         if (split != n - 1) {                    // token splits publish and leave
-            if (tid < D) publish(&part[2 + tid], o, tag);
-            if (tid == 0) {
-                publish(&part[0], M, tag);
-                publish(&part[1], lt, tag);
+            if (tid < NH * D) publish(&part_me[2 + tid % D], o, tag);
+            if (tid < NH * D && tid % D == 0) {
+                publish(&part_me[0], M, tag);
+                publish(&part_me[1], lt, tag);
             }
             return;
         }
+    } else if constexpr (NH == 2) {
+        return;                                  // (never launched: head pairs use window workgroups)
     } else {
         if (tid < D) publish(&part[2 + tid], o, tag);
         if (tid == 0) {
@@ -1173,10 +1367,13 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 
     // The merger: every other workgroup of (b, h) has started (and will
     // publish); poll their pairs (slot `split` is this workgroup's own).
-    // Threads below D own a channel; at least 32 take part (the per-slot
-    // m and l pairs are read by lanes 0..31).
-    if (tid >= (D > 32 ? D : 32)) return;
-    const int ch = tid < D ? tid : 0;
+    // Threads below NH * D own a channel (of head hme: with two heads, waves
+    // 0-1 merge the first, waves 2-3 the second); at least 32 take part (the
+    // per-slot m and l pairs are read by lanes 0..31).
+    constexpr int kMergeThreads = NH * D > 32 ? NH * D : 32;
+    if (tid >= kMergeThreads) return;
+    const int ch = tid < NH * D ? tid % D : 0;
+    const uint64_t *const parts_me = parts + hme * kBlockWords;
     // slots in ascending order, this workgroup's own (slot `split`) from its
     // registers: the same sum whichever workgroup merges
     float Mg = -INFINITY;
@@ -1198,10 +1395,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
 #pragma unroll
             for (int i = 0; i < kMergeChunk; ++i) {
                 const size_t sl = (size_t)min(c0 + i, n - 1) * (D + 2);
-                pp.po[i] = __hip_atomic_load(&parts[sl + 2 + ch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                pp.po[i] = __hip_atomic_load(&parts_me[sl + 2 + ch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             const size_t sl = (size_t)min(c0 + (hl & 15), n - 1) * (D + 2);
-            pp.ml = __hip_atomic_load(&parts[sl + (hl >> 4)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            pp.ml = __hip_atomic_load(&parts_me[sl + (hl >> 4)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
         // branch-free: a slot counts if it exists and is not this workgroup's
         auto current = [&](const Poll &pp) {
@@ -1259,13 +1456,15 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // (a timed-out merge writes quiet-NaN bits: an integer select, so that the
     // no-NaN arithmetic this file is built with cannot fold it away) and is
     // flagged in the status word
-    if (tid < D)
+    if (tid < NH * D)
         reinterpret_cast<uint32_t *>(outp)[tid] =
             failed ? 0x7fc00000u : __float_as_uint(den > 0.f ? num / den : 0.f);
-    if (tid == 0) {
+    if (tid < NH * D && ch == 0) {
         if (failed) __hip_atomic_fetch_or(a.status, kStatusMergeTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t epoch = epochh[hme];
         const uint32_t next = epoch + 1u == kEpochWrap ? 0u : epoch + 1u;
-        __hip_atomic_store(ticket, (uint64_t)next << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ticket + hme * kBlockWords, (uint64_t)next << 32, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -1277,11 +1476,19 @@ constexpr bool fits() {
 
 template <int S, int CG>
 hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
-    const dim3 grid((unsigned)a.n_split * a.H * a.B * a.n_layers);
-    const int mode = a.n_layers > 1 ? kModeMulti : a.by_length ? kModeByLength : kModeOne;
+    const dim3 grid((unsigned)a.n_split * (a.H / a.heads_per_wg) * a.B * a.n_layers);
+    const int mode = a.heads_per_wg == 2 ? kModePair
+                     : a.n_layers > 1    ? kModeMulti
+                     : a.by_length       ? kModeByLength
+                                         : kModeOne;
     if (a.cb_bf16) {
         if constexpr (fits<S, CG, uint16_t>()) {
-            if (mode == kModeMulti)
+            if (mode == kModePair) {
+                if constexpr (Shape<S, CG, uint16_t>::kMfma && Shape<S, CG, uint16_t>::KCOP == 1)
+                    hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModePair>), grid, dim3(kThreads), 0, st, a);
+                else
+                    return hipErrorInvalidValue;
+            } else if (mode == kModeMulti)
                 hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModeMulti>), grid, dim3(kThreads), 0, st, a);
             else if (mode == kModeByLength)
                 hipLaunchKernelGGL((decode_main<S, CG, uint16_t, kModeByLength>), grid, dim3(kThreads), 0, st, a);
@@ -1292,7 +1499,9 @@ hipError_t launch_sc(const DecodeArgs &a, hipStream_t st) {
         }
     } else {
         if constexpr (fits<S, CG, float>()) {
-            if (mode == kModeMulti)
+            if (mode == kModePair)
+                return hipErrorInvalidValue;
+            else if (mode == kModeMulti)
                 hipLaunchKernelGGL((decode_main<S, CG, float, kModeMulti>), grid, dim3(kThreads), 0, st, a);
             else if (mode == kModeByLength)
                 hipLaunchKernelGGL((decode_main<S, CG, float, kModeByLength>), grid, dim3(kThreads), 0, st, a);

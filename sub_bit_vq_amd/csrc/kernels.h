@@ -128,6 +128,9 @@ struct DecodeArgs {
                       // in dispatch order
     int cb_bf16;
     int n_layers;     // layers of this launch, 1..kMaxLayersPerLaunch
+    int heads_per_wg; // 1, or 2: a workgroup serves query heads 2i, 2i + 1
+                      // (one KV head, one layer, window workgroups or
+                      // n_split == 1; S = 32, cg = 4, bf16 codebooks)
     const int32_t *ctx_len;     // [B], shared by the layers
     const int32_t *vq_len;      // [B] or null
     int64_t win_bstride;        // elements between sequences of a window buffer

@@ -36,6 +36,7 @@ bool config_ok(const lvq_config *c) {
     if (c->n_kv_heads > 0 && c->n_heads % c->n_kv_heads != 0) return false;
     if (c->n_loops < 0 || c->n_loops > LVQ_MAX_LOOPS || c->n_loops % c->loop_steps != 0) return false;
     if (c->decode_poll_limit < 0) return false;
+    if (c->decode_heads_per_group < 0 || c->decode_heads_per_group > 2) return false;
     return true;
 }
 
@@ -81,9 +82,9 @@ constexpr int32_t kDefaultPolls = 1 << 22;   // a merger's wait: seconds, far be
 constexpr int64_t kFixedBatches = 6;
 constexpr int64_t kMaxWindowGroups = LVQ_MAX_WINDOW_GROUPS;
 
-Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1) {
+Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1, int nh = 1) {
     if (max_vq <= 0) return {1, 0};
-    const int64_t bh = n_layers * c->batch * c->n_heads;
+    const int64_t bh = n_layers * c->batch * (c->n_heads / nh);   // workgroup groups
     if (c->decode_splits != 0) {
         int64_t want = c->decode_splits;
         if (want < 1) want = 1;
@@ -121,6 +122,32 @@ Splits choose_splits(const lvq_config *c, int64_t max_vq, int64_t n_layers = 1) 
         }
     }
     return {(int32_t)best_n, best_n > 1 ? (int32_t)best_win : 0};
+}
+
+// Query heads per decode workgroup: 2 (two consecutive query heads of one KV
+// head read its index rows once) when the kernel has that variant (S = 32,
+// cg = 4, bf16 codebooks, head_dim 128, one layer per launch, an even number
+// of query heads per KV head) and the plan for head pairs merges through
+// window workgroups or needs no merge; otherwise 1.  decode_heads_per_group
+// forces 1, or 2 (0 where 2 is not possible).
+struct Plan {
+    Splits sp;
+    int nh;
+};
+Plan decode_plan(const lvq_config *c, int64_t max_vq, int64_t n_layers) {
+    const int want = c->decode_heads_per_group;
+    if (want != 1) {
+        const int cg = c->group / c->loop_steps;
+        const int64_t S = c->head_dim / cg;
+        const bool shape = n_layers == 1 && (c->n_heads / kv_heads(c)) % 2 == 0 && S == 32 && cg == 4 &&
+                           c->head_dim == 128 && c->codebook_dtype == LVQ_BF16;
+        if (shape) {
+            const Splits sp = choose_splits(c, max_vq, n_layers, 2);
+            if (sp.n == 1 || sp.n_win > 0) return {sp, 2};
+        }
+        if (want == 2) return {{0, 0}, 0};
+    }
+    return {choose_splits(c, max_vq, n_layers, 1), 1};
 }
 
 // Encode n tensors of one shape (1: lvq_encode; 2: the K and V of a page in one
@@ -249,12 +276,20 @@ lvq_status lvq_cache_layout(const lvq_config *c, lvq_layout *o) {
 
 int32_t lvq_decode_splits(const lvq_config *c, int32_t max_ctx_len) {
     if (!config_ok(c) || max_ctx_len < 0 || max_ctx_len > c->max_tokens) return 0;
-    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true)).n;
+    return decode_plan(c, max_vq_tokens(c, max_ctx_len, true), 1).sp.n;
 }
 
 int32_t lvq_decode_window_groups(const lvq_config *c, int32_t max_ctx_len) {
     if (!config_ok(c) || max_ctx_len < 0 || max_ctx_len > c->max_tokens) return -1;
-    return choose_splits(c, max_vq_tokens(c, max_ctx_len, true)).n_win;
+    const Plan plan = decode_plan(c, max_vq_tokens(c, max_ctx_len, true), 1);
+    return plan.nh == 0 ? -1 : plan.sp.n_win;
+}
+
+int32_t lvq_decode_heads_per_workgroup(const lvq_config *c, int32_t n_layers, int32_t max_ctx_len) {
+    if (!config_ok(c) || n_layers < 1 || n_layers > LVQ_MAX_LAYERS) return 0;
+    if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return 0;
+    const int64_t nl = n_layers < lvq::kMaxLayersPerLaunch ? n_layers : lvq::kMaxLayersPerLaunch;
+    return decode_plan(c, max_vq_tokens(c, max_ctx_len, true), nl).nh;
 }
 
 lvq_status lvq_encode(const lvq_config *c, const void *x, const int64_t *x_strides,
@@ -339,7 +374,7 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
         workspace_bytes = lvq::kScratchBytes;
         for (int32_t l0 = 0; l0 < n_layers; l0 += lvq::kMaxLayersPerLaunch) {
             const int32_t nl = std::min<int32_t>(lvq::kMaxLayersPerLaunch, n_layers - l0);
-            if (choose_splits(c, max_vq, nl).n > 1 &&
+            if (decode_plan(c, max_vq, nl).sp.n > 1 &&
                 (workspace_bytes - lvq::kHeaderBytes) / per_layer < (uint64_t)(l0 + nl))
                 return LVQ_ERR_WORKSPACE;
         }
@@ -356,7 +391,9 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
     const size_t W = (size_t)c->n_sink + c->n_recent;
     for (int32_t l0 = 0; l0 < n_layers; l0 += lvq::kMaxLayersPerLaunch) {
         const int32_t nl = std::min<int32_t>(lvq::kMaxLayersPerLaunch, n_layers - l0);
-        const Splits sp = choose_splits(c, max_vq, nl);
+        const Plan plan = decode_plan(c, max_vq, nl);
+        if (plan.nh == 0) return LVQ_ERR_UNSUPPORTED;     // two heads per workgroup asked, not possible
+        const Splits sp = plan.sp;
         const int32_t n_split = sp.n;
         if ((int64_t)n_split * c->batch * c->n_heads * nl > 0x7fffffff) return LVQ_ERR_UNSUPPORTED;
         const int64_t n_vq = n_split - sp.n_win;
@@ -382,9 +419,12 @@ lvq_status decode_layers(const lvq_config *c, int32_t n_layers, int32_t loop_ste
             a.win_per = (int)(((int64_t)W + ranges - 1) / ranges);
         }
         a.chunk = (int)chunk;
-        a.by_length = n_split == 1 && nl == 1 && c->batch > 1 && c->batch <= lvq::kMaxOrderedBatch;
+        // (the head-pair variant takes sequences in index order)
+        a.by_length = plan.nh == 1 && n_split == 1 && nl == 1 && c->batch > 1 &&
+                      c->batch <= lvq::kMaxOrderedBatch;
         a.cb_bf16 = c->codebook_dtype == LVQ_BF16;
         a.n_layers = nl;
+        a.heads_per_wg = plan.nh;
         a.ctx_len = ctx_len;
         a.vq_len = vq_len;
         a.win_bstride = n_loops(c) * a.Hk * W * c->head_dim;
@@ -470,14 +510,17 @@ int32_t lvq_decode_role(const lvq_config *c, int32_t n_layers, int32_t max_ctx_l
                         int32_t workgroup, int32_t *layer, int32_t *seq, int32_t *head) {
     if (!config_ok(c) || n_layers < 1 || n_layers > lvq::kMaxLayersPerLaunch) return -1;
     if (max_ctx_len < 0 || max_ctx_len > c->max_tokens) return -1;
-    const Splits sp = choose_splits(c, max_vq_tokens(c, max_ctx_len, true), n_layers);
-    const int64_t total = (int64_t)sp.n * c->batch * c->n_heads * n_layers;
+    const Plan plan = decode_plan(c, max_vq_tokens(c, max_ctx_len, true), n_layers);
+    if (plan.nh == 0) return -1;
+    const Splits sp = plan.sp;
+    const int64_t hg = c->n_heads / plan.nh;            // head groups per sequence
+    const int64_t total = (int64_t)sp.n * c->batch * hg * n_layers;
     if (workgroup < 0 || workgroup >= total) return -1;
     const lvq::WgRole r = lvq::decode_role((unsigned)workgroup, (unsigned)total, (unsigned)sp.n);
-    const int64_t bh = (int64_t)c->batch * c->n_heads;
+    const int64_t bh = (int64_t)c->batch * hg;
     if (layer) *layer = (int32_t)(r.group / bh);
-    if (seq) *seq = (int32_t)(r.group % bh / c->n_heads);
-    if (head) *head = (int32_t)(r.group % c->n_heads);
+    if (seq) *seq = (int32_t)(r.group % bh / hg);
+    if (head) *head = (int32_t)(r.group % hg * plan.nh);
     return r.role;
 }
 

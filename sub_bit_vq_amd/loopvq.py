@@ -33,7 +33,8 @@ LVQ_NOALLOC_MAX_HEADS = 256
 
 EXPORTS = ("lvq_cache_layout", "lvq_encode", "lvq_encode_kv", "lvq_decode_attn",
            "lvq_decode_attn_noalloc", "lvq_decode_attn_layers", "lvq_decode_status", "lvq_decode_role",
-           "lvq_decode_splits", "lvq_decode_window_groups", "lvq_status_string",
+           "lvq_decode_splits", "lvq_decode_window_groups", "lvq_decode_heads_per_workgroup",
+           "lvq_status_string",
            "lvq_encode_screen")
 
 
@@ -47,7 +48,7 @@ class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "n_heads", "head_dim", "loop_steps", "group", "n_sink", "n_recent",
         "max_tokens", "codebook_dtype", "decode_splits", "n_kv_heads", "n_loops",
-        "decode_window_groups", "decode_poll_limit")]
+        "decode_window_groups", "decode_poll_limit", "decode_heads_per_group")]
 
 
 class _DecodeLayer(ctypes.Structure):
@@ -87,6 +88,7 @@ class Config:
     n_loops: int = 0             # 0: the model has loop_steps loop steps
     decode_window_groups: int = 0  # with decode_splits: workgroups taking window slots
     decode_poll_limit: int = 0     # 0: the library's bound of a merger's wait
+    decode_heads_per_group: int = 0  # query heads per decode workgroup: 0 library's choice, 1, 2
 
     @property
     def kv_heads(self) -> int:
@@ -143,6 +145,8 @@ def library() -> ctypes.CDLL:
         lib.lvq_decode_splits.argtypes = [cfgp, i32]
         lib.lvq_decode_window_groups.restype = i32
         lib.lvq_decode_window_groups.argtypes = [cfgp, i32]
+        lib.lvq_decode_heads_per_workgroup.restype = i32
+        lib.lvq_decode_heads_per_workgroup.argtypes = [cfgp, i32, i32]
         lib.lvq_status_string.restype = ctypes.c_char_p
         lib.lvq_status_string.argtypes = [i32]
         _lib = lib
@@ -179,6 +183,11 @@ def lvq_decode_splits(cfg: Config, max_ctx_len: int) -> int:
 
 def lvq_decode_window_groups(cfg: Config, max_ctx_len: int) -> int:
     return int(library().lvq_decode_window_groups(ctypes.byref(cfg.c()), int(max_ctx_len)))
+
+
+def lvq_decode_heads_per_workgroup(cfg: Config, n_layers: int, max_ctx_len: int) -> int:
+    return int(library().lvq_decode_heads_per_workgroup(ctypes.byref(cfg.c()), int(n_layers),
+                                                        int(max_ctx_len)))
 
 
 def lvq_decode_role(cfg: Config, n_layers: int, max_ctx_len: int, workgroup: int):

@@ -94,7 +94,9 @@ def drive_host(path):
         for L in (0, 1, 320, 321, 2000, c.max_tokens):
             n = lv.lvq_decode_splits(c, L)
             assert n >= 1 and lv.lvq_decode_window_groups(c, L) >= 0
-            total = n * c.batch * c.n_heads
+            nh = lv.lvq_decode_heads_per_workgroup(c, 1, L)
+            assert nh in (1, 2)
+            total = n * c.batch * (c.n_heads // nh)
             for p in (0, total // 2, total - 1):
                 assert lv.lvq_decode_role(c, 1, L, p) is not None
     for n in range(1, 65):
@@ -119,9 +121,11 @@ def drive_host(path):
     launches = lib.lvq_stub_counts(0)
     for c in (cfg(), cfg(group=32), cfg(n_kv_heads=1), cfg(n_loops=8), cfg(decode_splits=17),
               cfg(decode_splits=5, decode_window_groups=3), cfg(batch=64, n_heads=16, max_tokens=18432),
-              cfg(head_dim=64, codebook_dtype=lv.LVQ_F32), cfg(decode_poll_limit=1)):
+              cfg(head_dim=64, codebook_dtype=lv.LVQ_F32), cfg(decode_poll_limit=1),
+              cfg(n_kv_heads=2), cfg(n_kv_heads=2, decode_splits=1), cfg(n_kv_heads=2, decode_heads_per_group=1),
+              cfg(n_kv_heads=2, decode_heads_per_group=2), cfg(n_kv_heads=2, decode_splits=64, batch=8)):
         for L in (1, 321, c.max_tokens):
-            assert decode(c, L=L) == OK
+            assert decode(c, L=L) == OK, (c, L, decode(c, L=L))
             assert decode(c, L=L, vq=P) == OK
             assert decode(c, t=c.loops - 1, L=L, sc=0.125) == OK
     assert lib.lvq_stub_counts(0) > launches
@@ -133,7 +137,8 @@ def drive_host(path):
                  dict(wsb=0), dict(ws=ctypes.c_void_p(P.value + 64))):
         assert decode(c, **over) != OK, over
     for bad in (cfg(head_dim=256), cfg(head_dim=384), cfg(group=18), cfg(loop_steps=3),
-                cfg(n_kv_heads=3), cfg(n_loops=6), cfg(decode_window_groups=2)):
+                cfg(n_kv_heads=3), cfg(n_loops=6), cfg(decode_window_groups=2), cfg(decode_heads_per_group=3),
+                cfg(decode_heads_per_group=2), cfg(n_kv_heads=2, group=32, decode_heads_per_group=2)):
         assert decode(bad) != OK, bad
     # layers: 20 layers are two launches
     arr = (lv._DecodeLayer * 20)()

@@ -54,6 +54,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
     fail |= bad(a.S * a.cg != a.d || a.t_max < 1 || a.max_polls < 1);
     fail |= bad(!a.ctx_len || !a.blocks || !a.status);
     fail |= bad(a.by_length && (a.n_split != 1 || a.n_layers != 1 || a.B < 2 || a.B > kMaxOrderedBatch));
+    // head pairs: the kernel's variant for S = 32, cg = 4, bf16, d = 128, one
+    // layer, two query heads of one KV head, merging through window
+    // workgroups (or no merge)
+    fail |= bad(a.heads_per_wg != 1 && a.heads_per_wg != 2);
+    fail |= bad(a.heads_per_wg == 2 &&
+                (a.S != 32 || a.cg != 4 || !a.cb_bf16 || a.d != 128 || a.n_layers != 1 || a.by_length ||
+                 a.q_per_kv % 2 != 0 || (a.n_split > 1 && a.window_wg == 0)));
     for (int l = 0; l < a.n_layers; ++l) {
         const DecodeLayer &L = a.layer[l];
         fail |= bad(!L.q || !L.k_index || !L.v_index || !L.kcb_t || !L.vcb_t || !L.kwin_t || !L.vwin_t || !L.out);
