@@ -752,7 +752,10 @@ def secondary_workloads(lv, synth, torch, main_workload, setup, with_checks=True
             "mean_launch_us": ms * 1e3, "median_launch_us": spread["median_ms"] * 1e3,
             "min_launch_us": spread["min_ms"] * 1e3, "bytes_per_launch": nbytes, "GBps": gbs,
             "frac": gbs / HBM_PEAK_GBS, "batch": s2.B, "heads": s2.H, "kv_heads": s2.Hk, "group": s2.G,
-            "context": sum(s2.lengths), "workgroups_per_head": lv.lvq_decode_splits(s2.cfg, s2.L),
+            "context": sum(s2.lengths),
+            # workgroups per (sequence, head group) and query heads per workgroup
+            "workgroups_per_head_group": lv.lvq_decode_splits(s2.cfg, s2.L),
+            "heads_per_workgroup": lv.lvq_decode_heads_per_workgroup(s2.cfg, 1, s2.L),
             "cache_copies": s2.rotate,
         }
         log(f"  decode launch {ms * 1e3:.2f} us, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of peak)")
