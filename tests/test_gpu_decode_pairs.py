@@ -130,3 +130,47 @@ def test_pair_repeats_and_epoch_wrap(lv):
         _check(dc, t)
         host = dc.ws.cpu().numpy()
         assert all(int(host[o:o + 8].view(np.uint64)[0]) == want << 32 for o in offs), t
+
+
+def test_pair_page_lag_vq_len(lv):
+    """vq_len above the exact-window count (the recent ring holds fewer than
+    256 tokens, some of its slots stale), with head pairs."""
+    _note("pairs: page lag")
+    lengths = (700, 1000, 3333)
+    vq = [L - 320 + e for L, e in zip(lengths, (8, 5, 255))]
+    c = make_cache(batch=3, n_heads=2, q_heads=4, head_dim=128, group=16, lengths=lengths, seed=981,
+                   codeword_tokens=True, vq_len=vq)
+    dc = DeviceCache(lv, c)
+    assert lv.lvq_decode_heads_per_workgroup(dc.cfg, 1, max(lengths)) == 2
+    for t in (0, 2):
+        _check(dc, t)
+
+
+def test_pair_small_windows(lv):
+    """Window ranges that are empty or a single slot, with head pairs (the
+    merger's own range may be empty)."""
+    for n_sink, n_recent, splits, w in ((2, 3, 6, 4), (0, 1, 5, 3), (1, 2, 3, 2)):
+        _note(f"pairs: small windows {n_sink}+{n_recent}, {splits} splits, {w} window groups")
+        c = make_cache(batch=2, n_heads=1, q_heads=2, head_dim=128, group=16, lengths=(1800, 900),
+                       seed=991 + w, codeword_tokens=True, n_sink=n_sink, n_recent=n_recent)
+        dc = DeviceCache(lv, c, decode_splits=splits, decode_window_groups=w)
+        assert lv.lvq_decode_heads_per_workgroup(dc.cfg, 1, 1800) == 2
+        for t in (1, 3):
+            _check(dc, t)
+
+
+def test_pair_merge_timeout_is_flagged(lv):
+    """A merger bounded to one poll gives up on both heads: both rows NaN,
+    the status word flagged; after clearing, the default bound is right."""
+    _note("pairs: merge timeout")
+    c = make_cache(batch=1, n_heads=1, q_heads=2, head_dim=128, group=16, lengths=(32768,), seed=995,
+                   codeword_tokens=True)
+    dc = DeviceCache(lv, c, decode_splits=3)
+    assert lv.lvq_decode_heads_per_workgroup(dc.cfg, 1, 32768) == 2
+    got = dc.decode(2, cfg=dataclasses.replace(dc.cfg, decode_poll_limit=1))
+    flags = lv.lvq_decode_status(dc.ws, clear=True)
+    assert np.isnan(got).all()
+    assert flags == lv.LVQ_STATUS_MERGE_TIMEOUT
+    dc.ws.zero_()
+    _check(dc, 2)
+    assert lv.lvq_decode_status(dc.ws) == 0

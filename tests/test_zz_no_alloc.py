@@ -62,6 +62,9 @@ CASES = {
                      50),
     "0.25 bit": (dict(batch=2, n_heads=8, head_dim=128, group=32, lengths=(9000, 5000), seed=85),
                  dict(batch=1, n_heads=2, head_dim=128, group=32, lengths=(1500,), seed=86), 0),
+    "head pairs": (dict(batch=1, n_heads=4, q_heads=16, head_dim=128, group=16, lengths=(12000,), seed=89),
+                   dict(batch=2, n_heads=2, q_heads=4, head_dim=128, group=16, lengths=(3000, 900), seed=90),
+                   0),
     "one workgroup per head, 512 heads": (
         dict(batch=64, n_heads=8, head_dim=64, group=16,
              lengths=tuple(300 + 37 * i for i in range(64)), seed=87),
