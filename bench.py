@@ -499,7 +499,7 @@ def layers_experiment(lv, synth, torch, workload, n_layers, reps=8, n_calls=16):
         "unit": "ctx-token*loop-steps/s",
         "n_gpus": 1,
         "higher_is_better": True,
-        "dtype": "fp32",
+        "dtype": "bf16/fp16->fp32",
         "data": "synthetic (seeded loop-correlated K/V encoded by the HIP encoder, N(0,1) codebooks per layer)",
         "config": {"workload": workload, "layers_per_call": n_layers, "cache_sets": sets,
                    "heads": setup.H, "head_dim": setup.d, "group": setup.G,
