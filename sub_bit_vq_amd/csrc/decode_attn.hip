@@ -131,9 +131,14 @@ struct Shape {
     // that 16 consecutive rows read at one 16-byte offset hit distinct banks,
     // and each thread sums 4 positions of every SS-th row.
     static constexpr bool kQuadRed = D == 64 || D == 128;
-    // dump rows: one per token slot, or with MFMA value sums one per pair of
-    // slots (folded in registers first)
-    static constexpr int NR = kMfma ? kWaves * TPW / 2 : kWaves * TPW;
+    // Token slots tk and tk + TPW/2 (lanes 32 apart) fold in registers before
+    // the dump when their accumulators hold the same channels: with MFMA value
+    // sums, and with the plain ones at R <= 2 (the same rotation, and the
+    // same order of a sub-vector's value reads: sw below)
+    static constexpr bool kFold =
+        kMfma || (kQuadRed && R <= 2 && (TPW / 2) % (8 * VCOP) == 0 && ((TPW / 2) / (8 * VCOP)) % NRD == 0);
+    // dump rows: one per token slot, or per pair of slots when they fold
+    static constexpr int NR = kFold ? kWaves * TPW / 2 : kWaves * TPW;
     static constexpr int RS = kQuadRed ? D * 4 + 16 : D * 4;   // row stride, bytes
     static constexpr int kDumpBytes = NR * RS;
     static constexpr int kBase = kDumpBytes > kTabBytes ? kDumpBytes : kTabBytes;
@@ -1175,6 +1180,20 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                     fold[hh][4 * i + e] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
                 }
     }
+    // Plain value sums, folded slots: one lane swap and an add per pair of
+    // accumulators a, a + NACC/2 leave lanes 0-31 with sub-vector steps 0-3
+    // (the first half of the array) and lanes 32-63 with steps 4-7.
+    constexpr bool kFoldPlain = Sh::kFold && !Sh::kMfma;
+    float foldp[kFoldPlain ? Sh::NACC / 2 : 1];
+    if constexpr (kFoldPlain) {
+        static_assert(NH == 1 && Sh::NACC == 8 * NRD * CPR, "one head, 8 steps of NRD reads");
+#pragma unroll
+        for (int k = 0; k < Sh::NACC / 2; ++k) {
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(st.acc[k]),
+                                                             __float_as_uint(st.acc[k + Sh::NACC / 2]), false, false);
+            foldp[k] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
+    }
     __syncthreads();                             // every wave is done with the tables
     // Who merges.  With window workgroups (the grid fits the chip) it is the
     // last of them: it has the highest index of its (b, h), so its peers were
@@ -1204,12 +1223,16 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
                                                 16 * (4 * ((i + 4 * hb + ln.rot) & 7) + r)) =
                         make_float4(fold[hh][4 * i], fold[hh][4 * i + 1], fold[hh][4 * i + 2], fold[hh][4 * i + 3]);
         } else {
+            // folded: this lane's steps i0 .. i0 + 3
+            constexpr int NI = kFoldPlain ? 4 : 8;
+            const int i0 = kFoldPlain ? (lane >> 5) * 4 : 0;
+            const float *accs = kFoldPlain ? foldp : st.acc;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < NI; ++i) {
 #pragma unroll
                 for (int hh = 0; hh < NRD; ++hh) {
-                    const float *acc = st.acc + (i * NRD + hh) * CPR;
-                    float *dst = reinterpret_cast<float *>(rowp) + ln.channel(i, hh);
+                    const float *acc = accs + (i * NRD + hh) * CPR;
+                    float *dst = reinterpret_cast<float *>(rowp) + ln.channel(i0 + i, hh);
                     if constexpr (CPR == 4)
                         *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
                     else
