@@ -1019,8 +1019,10 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeArgs a) {
     // queued behind them.  So in a launch of split heads (all workgroups
     // starting together) waves 0-3 issue their first batch too after their
     // part of the tables, behind waves 4-7's slices (measured: 32K, 0.5 bit,
-    // 14.2-14.4 -> 13.9 us).  Wave-uniform.
-    const bool defer0 = kSecondAfterBuild && kMode == kModeOne && n_split > 1 && wave < kWaves / 2;
+    // 14.2-14.4 -> 13.9 us; 2-8 layers per launch -0.2 to -0.4 us; no gain
+    // with head pairs).  Wave-uniform.
+    const bool defer0 = kSecondAfterBuild && (kMode == kModeOne || kMode == kModeMulti) && n_split > 1 &&
+                        wave < kWaves / 2;
     if (!defer0) load_batch<S, CG, CB>(ir0, vq0 + wave * TPW, r0);
 
     const Windows w = seq_windows(Lraw, vqraw, t_max, n_sink, n_recent);
