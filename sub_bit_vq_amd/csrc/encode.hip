@@ -26,20 +26,25 @@
 // per 32 entries of K.  Products of bf16 values are exact in fp32, so the only
 // screen errors are the accumulation roundings.  Each wave keeps its codebook
 // in registers as MFMA A operands and streams 16-token tiles through it.
-// Each lane tracks the two smallest screen values of its 64 codes, a pair
-// (a, b) at a time: the smallest is min3(m1, a, b) and the second smallest
-// min(m2, med3(m1, a, b)).  The low 6 bits of each value are
-// replaced by its slot among the lane's 64 codes, so the smallest value also
-// names its code (the lane supplies the rest of the index).
+// Each lane finds the two smallest screen values of its 64 codes from two
+// partitions of them (8 groups and 8 chains of 8 codes; a group and a chain
+// share one code): the minimum of every group and every chain (min3, two new
+// values an instruction), then the two smallest group minima and the two
+// smallest chain minima.  The smallest value is the smallest of either list,
+// the second smallest the smaller of the two lists' second entries.  The low
+// 3 bits of the minima are replaced by their group or chain, so the smallest
+// value also names its code (the lane supplies the rest of the index).
 //
-// Exactness.  With R = |x| + max_k |c_k|, the 6 bits written into a value
-// move it by at most 2^-17 R^2; the fp32 error of D_k is at most
+// Exactness.  With R = |x| + max_k |c_k|, the (at most 6) bits written into a
+// value move it by at most 2^-17 R^2; the fp32 error of D_k is at most
 // (G+2) 2^-24 R^2 and that of the screen (C plus P*G exact products) at most
 // F (P*G+3) 2^-24 R^2 for an accumulation F times worse than a sequential
 // fp32 sum (P*G+1 terms; the bound keeps two terms of slack).  If the two
 // smallest (marked) screen values are more than eps = 2^-14 R^2 apart, eps
 // exceeds twice the sum of these (for F up to 10 at G = 32, P = 1 and up to 7
-// at G = 16, P = 3), so the screen winner is the exact winner.  Otherwise the
+// at G = 16, P = 3), so the screen winner is the exact winner.  (Where the
+// group and the chain of a lane's smallest value would name different codes,
+// two of its values are within a few marks of each other, so the test fails.)  Otherwise the
 // wave re-scores all 256 codes of that sub-vector exactly as defined above
 // from the codebook (64 lanes x 4 codes, strict < per lane in ascending k,
 // then a lowest-index argmin across lanes), which reproduces the definition
@@ -189,7 +194,8 @@ __device__ __forceinline__ floatx4 mfma_chunk(const uint32_t *aw, const uint32_t
 // operands and the instructions that form them are those of the plain
 // instance)
 template <int G, int CG, int P, typename CB, bool kScreen>
-__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G * P <= 16 ? 4 : 1))) void
+encode_kernel(EncodeArgs a) {
     using Sh = EncShape<G, CG, P, CB>;
     constexpr int NCH = Sh::NCH;
     // The staged codebooks [jl][k][i] are read only until the MFMA operands
@@ -386,58 +392,104 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeArgs a) {
             pair32(xa + xb, xa, xb);
             const float xn2 = xa + xb;
 
-            // two smallest marked screen values of the lane's 64 codes, taken a
-            // pair (a, b) at a time: with m1 <= m2, the second smallest of
-            // {m1, m2, a, b} is min(m2, med3(m1, a, b)) and the smallest is
-            // min3(m1, a, b)
-            // MFMAs run kPipe blocks ahead of the min tracking so that their
-            // latency overlaps it (the scheduling barriers keep that order)
-            // The accumulators start at the codes' squared norms, read from LDS
-            // kBiasAhead blocks before their MFMA so that the read's latency
-            // overlaps the min tracking.
-            constexpr int kPipe = 4;
-            constexpr int kBiasAhead = 2;
-            constexpr int NB = kPipe + kBiasAhead;
+            // Smallest and second smallest screen value of the lane's 64 codes.
+            // The lane's value of code blk*16 + kq*4 + i sits at slot
+            // s = 4 blk + i.  Two partitions of the slots, groups s / 8 (blocks
+            // 2g and 2g + 1) and chains s % 8, have no two slots in common in
+            // both a group and a chain, so of the two smallest values one is
+            // the minimum of its group and the other the minimum of its chain
+            // or of its group: the lane's second smallest is the smaller of
+            // the second smallest group minimum and the second smallest chain
+            // minimum.  Minima are taken with min3 over 3 operands, two new
+            // values an instruction; only the 8 group and 8 chain minima get
+            // marks (their low 3 bits become g or c), and the lane's smallest
+            // value carries both (low 6 bits = s), which names its code.
+            // Blocks go a quad (4 blocks, two groups) at a time: the MFMAs of
+            // the next quad run while this one is reduced (the scheduling
+            // barriers keep that order), and the accumulators start at the
+            // codes' squared norms, read from LDS a quad ahead of their MFMAs.
             auto bias_of = [&](int blk) { return *reinterpret_cast<const floatx4 *>(bias_row + blk * 16); };
             auto screen = [&](int blk, floatx4 acc) {
 #pragma unroll
                 for (int ch = 0; ch < NCH; ++ch) acc = mfma_chunk<Sh::K16>(afrag[blk][ch], cur.w[ch], acc);
                 return acc;
             };
-            floatx4 bias[NB];
+            auto mark3 = [](float v, uint32_t m) { return __uint_as_float((__float_as_uint(v) & ~7u) | m); };
+            auto min3 = [](float p, float q, float r) { return fminf(fminf(p, q), r); };
+            floatx4 acc[2][4], bq[4];
 #pragma unroll
-            for (int p = 0; p < NB; ++p) bias[p] = bias_of(p);
-            floatx4 accs[kPipe];
+            for (int b = 0; b < 4; ++b) bq[b] = bias_of(b);
 #pragma unroll
-            for (int p = 0; p < kPipe; ++p) accs[p] = screen(p, bias[p]);
+            for (int b = 0; b < 4; ++b) acc[0][b] = screen(b, bq[b]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bq[b] = bias_of(4 + b);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[1][b] = screen(4 + b, bq[b]);
             __builtin_amdgcn_sched_barrier(0);
-            float m1 = INFINITY, m2 = INFINITY;
+            float cm[8], g1 = 0.f, g2 = 0.f;
 #pragma unroll
-            for (int blk = 0; blk < 16; ++blk) {
-                const floatx4 acc = accs[blk % kPipe];
+            for (int qd = 0; qd < 4; ++qd) {
+                if (qd + 2 < 4) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) bq[b] = bias_of(4 * (qd + 2) + b);
+                }
+                const floatx4 *v = acc[qd & 1];
                 if constexpr (kScreen) {
                     if (valid) {
-                        float *dst = a.screen + (((size_t)(n0 + row) * a.H + h) * a.S + j) * 256 + blk * 16 + kq * 4;
-                        *reinterpret_cast<float4 *>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+                        for (int b = 0; b < 4; ++b) {
+                            float *dst = a.screen + (((size_t)(n0 + row) * a.H + h) * a.S + j) * 256 +
+                                         (4 * qd + b) * 16 + kq * 4;
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v[b][0], v[b][1], v[b][2], v[b][3]);
+                        }
                     }
                 }
-                // lane holds codes blk*16 + kq*4 + i of token n0 + row; the low
-                // 6 bits of each value become its slot blk*4 + i in the lane
-                float v[4];
+                // groups 2 qd (blocks 0, 1 of the quad) and 2 qd + 1 (blocks 2, 3)
+                float ga = min3(v[0][0], v[0][1], v[0][2]);
+                ga = min3(ga, v[0][3], v[1][0]);
+                ga = min3(ga, v[1][1], v[1][2]);
+                ga = mark3(fminf(ga, v[1][3]), 2 * qd);
+                float gb = min3(v[2][0], v[2][1], v[2][2]);
+                gb = min3(gb, v[2][3], v[3][0]);
+                gb = min3(gb, v[3][1], v[3][2]);
+                gb = mark3(fminf(gb, v[3][3]), 2 * qd + 1);
+                // chains i (even blocks) and 4 + i (odd blocks)
+                if (qd == 0) {
+                    g1 = fminf(ga, gb);
+                    g2 = fmaxf(ga, gb);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v[i] = __uint_as_float((__float_as_uint(acc[i]) & 0xffffffc0u) | (uint32_t)(blk * 4 + i));
+                    for (int i = 0; i < 4; ++i) {
+                        cm[i] = fminf(v[0][i], v[2][i]);
+                        cm[4 + i] = fminf(v[1][i], v[3][i]);
+                    }
+                } else {
+                    g2 = fminf(g2, __builtin_amdgcn_fmed3f(g1, ga, gb));
+                    g1 = min3(g1, ga, gb);
 #pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    m2 = fminf(m2, __builtin_amdgcn_fmed3f(m1, v[i], v[i + 1]));
-                    m1 = fminf(m1, fminf(v[i], v[i + 1]));
+                    for (int i = 0; i < 4; ++i) {
+                        cm[i] = min3(cm[i], v[0][i], v[2][i]);
+                        cm[4 + i] = min3(cm[4 + i], v[1][i], v[3][i]);
+                    }
                 }
-                if (blk + kPipe < 16) {
-                    accs[blk % kPipe] = screen(blk + kPipe, bias[(blk + kPipe) % NB]);
-                    if (blk + NB < 16) bias[blk % NB] = bias_of(blk + NB);   // slot of block blk + kPipe - NB
+                if (qd + 2 < 4) {
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) acc[qd & 1][b] = screen(4 * (qd + 2) + b, bq[b]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            // the two smallest marked chain minima
+            float c1 = fminf(mark3(cm[0], 0), mark3(cm[1], 1));
+            float c2 = fmaxf(mark3(cm[0], 0), mark3(cm[1], 1));
+#pragma unroll
+            for (int c = 2; c < 8; c += 2) {
+                const float p = mark3(cm[c], c), q = mark3(cm[c + 1], c + 1);
+                c2 = fminf(c2, __builtin_amdgcn_fmed3f(c1, p, q));
+                c1 = min3(c1, p, q);
+            }
+            // the lane's smallest value with its slot (group from g1, chain from
+            // c1) in the low 6 bits, and its second smallest
+            float m1 = __uint_as_float((__float_as_uint(c1) & ~0x38u) | ((__float_as_uint(g1) & 7u) << 3));
+            float m2 = fminf(c2, g2);
             // combine the four lanes holding the same token; the lane whose own
             // smallest value is the token's smallest holds the winner
             const float own = m1;
