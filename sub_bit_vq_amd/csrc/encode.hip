@@ -282,8 +282,9 @@ encode_kernel(EncodeArgs a) {
     const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
 
     // this wave's codebook as MFMA A operands: lane (row, kq) holds entries
-    // kk = ch*KC + kq*KL + e of code blk*16 + row, two bf16 a word (kq
-    // unrolled so that every register index is a constant)
+    // kk = ch*KC + kq*KL + e of code blk*16 + row, two bf16 a word (kq enters
+    // only the LDS address and the selects, so the wave builds them without
+    // divergent branches)
     constexpr int KL = Sh::KL, KC = Sh::KC, LE = Sh::LE, NLD = Sh::NLD;
     const CB *mycb = cbs + wave * 256 * G;
     uint32_t afrag[16][NCH][KL / 2];
@@ -292,23 +293,19 @@ encode_kernel(EncodeArgs a) {
         const int code = blk * 16 + row;
         const CB *cw = mycb + code * G;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (kq != q) continue;
+        for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
-            for (int ch = 0; ch < NCH; ++ch) {
+            for (int e = 0; e < KL; e += 2) {
+                uint32_t wv = 0;
 #pragma unroll
-                for (int e = 0; e < KL; e += 2) {
-                    uint32_t wv = 0;
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int kk = ch * KC + q * KL + e + h2;
-                        float v = 0.f;
-                        if (kk < P * G)
-                            v = -2.f * (P == 1 ? to_f(cw[kk % G]) : split_part(to_f(cw[kk % G]), kk / G));
-                        wv |= (uint32_t)bf16_rne(v) << (16 * h2);
-                    }
-                    afrag[blk][ch][e / 2] = wv;
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int kk = ch * KC + kq * KL + e + h2;
+                    const float c = to_f(cw[kk % G]);
+                    const float part = P == 1 ? c : split_part(c, kk / G);
+                    const float v = kk < P * G ? -2.f * part : 0.f;
+                    wv |= (uint32_t)bf16_rne(v) << (16 * h2);
                 }
+                afrag[blk][ch][e / 2] = wv;
             }
         }
     }
