@@ -202,10 +202,10 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  * codebook   device, cfg->codebook_dtype, layout above, 16-byte aligned (one
  *            call encodes one tensor: call once with the K codebook and once
  *            with the V one)
- * index_cache device uint8 [B][Hk][max_tokens][S]; rows
+ * index_cache device uint8 [B][Hk][max_tokens][S], 4-byte aligned; rows
  *            [first_token, first_token + n_tokens) of sequence seq are written
  * n_tokens   may be 0 (nothing launched)
- * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned x or codebook, seq
+ * Errors: LVQ_ERR_INVALID_ARG (null pointers, misaligned x, codebook or index_cache, seq
  * or rows out of range, bad strides), LVQ_ERR_UNSUPPORTED (G not in
  * {8, 16, 32}, cg not in {2, 4, 8}, S = d/cg not a multiple of 4, or fp32
  * codebooks with G = 32), LVQ_ERR_HIP.

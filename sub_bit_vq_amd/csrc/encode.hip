@@ -16,36 +16,38 @@
 // way out.
 //
 // Screen (MFMA).  The screen value S_k = |c_k|^2 - 2 x.c_k differs from D_k by
-// |x|^2, the same for every k.  MFMAs multiply 16 codes (rows) by 16 tokens
+// |x|^2, the same for every k.  MFMAs multiply 32 codes (rows) by 32 tokens
 // (columns) over the K axis
 //     code row  = [-2 c_k (split into P bf16 parts), 0...]
 //     token col = [ x (repeated P times),           0...]
 // (for fp32 codebooks c = c0 + c1 + c2 in bf16 parts, P = 3; bf16 codebooks
 // P = 1), starting from the accumulator C = fl32(|c_k|^2): one
-// v_mfma_f32_16x16x16_bf16 when P G <= 16, else one v_mfma_f32_16x16x32_bf16
-// per 32 entries of K.  Products of bf16 values are exact in fp32, so the only
-// screen errors are the accumulation roundings.  Each wave keeps its codebook
-// in registers as MFMA A operands and streams 16-token tiles through it.
-// Each lane finds the two smallest screen values of its 64 codes from two
-// partitions of them (8 groups and 8 chains of 8 codes; a group and a chain
-// share one code): the minimum of every group and every chain (min3, two new
-// values an instruction), then the two smallest group minima and the two
-// smallest chain minima.  The smallest value is the smallest of either list,
-// the second smallest the smaller of the two lists' second entries.  The low
-// 3 bits of the minima are replaced by their group or chain, so the smallest
-// value also names its code (the lane supplies the rest of the index).
+// v_mfma_f32_32x32x16_bf16 per 16 entries of K (one at the 0.5-bit shape,
+// P G = 16).  Products of bf16 values are exact in fp32, so the only screen
+// errors are the accumulation roundings.  Each wave keeps its codebook in
+// registers as MFMA A operands and streams 32-token tiles through it; a token
+// sits on two lanes (col, col + 32), each with 128 of its 256 codes.
+// Each lane finds the two smallest screen values of its 128 codes from two
+// partitions of them (16 groups of 8 codes, half an MFMA block each, and 8
+// chains of 16; a group and a chain share one code): the minimum of every
+// group and every chain (min3, two new values an instruction), then the two
+// smallest group minima and the two smallest chain minima.  The smallest
+// value is the smallest of either list, the second smallest the smaller of
+// the two lists' second entries.  The low 4 bits of the group minima and the
+// low 3 bits of the chain minima are replaced by their group or chain, so the
+// smallest value names its code (the lane supplies the rest of the index).
 //
-// Exactness.  With R = |x| + max_k |c_k|, the (at most 6) bits written into a
-// value move it by at most 2^-17 R^2; the fp32 error of D_k is at most
+// Exactness.  With R = |x| + max_k |c_k|, the (at most 4) bits written into a
+// value move it by at most 2^-19 R^2; the fp32 error of D_k is at most
 // (G+2) 2^-24 R^2 and that of the screen (C plus P*G exact products) at most
 // F (P*G+3) 2^-24 R^2 for an accumulation F times worse than a sequential
 // fp32 sum (P*G+1 terms; the bound keeps two terms of slack).  If the two
 // smallest (marked) screen values are more than eps = 2^-14 R^2 apart, eps
-// exceeds twice the sum of these (for F up to 10 at G = 32, P = 1 and up to 7
-// at G = 16, P = 3), so the screen winner is the exact winner.  (Where the
+// exceeds twice the sum of these (for F up to 12.7 at G = 32, P = 1 and up to
+// 9 at G = 16, P = 3), so the screen winner is the exact winner.  (Where the
 // group and the chain of a lane's smallest value would name different codes,
-// two of its values are within a few marks of each other, so the test fails.)  Otherwise the
-// wave re-scores all 256 codes of that sub-vector exactly as defined above
+// two of its values are within a few marks of each other, so the test
+// fails.)  Otherwise the wave re-scores all 256 codes of that sub-vector exactly as defined above
 // from the codebook (64 lanes x 4 codes, strict < per lane in ascending k,
 // then a lowest-index argmin across lanes), which reproduces the definition
 // bit for bit.
@@ -124,10 +126,9 @@ template <int G, int CG, int P, typename CB>
 struct EncShape {
     static constexpr int T = G / CG;                       // loop steps
     static constexpr int KX = P * G;                       // K entries that carry x
-    static constexpr bool K16 = KX <= 16;                  // one 16x16x16 MFMA, else 16x16x32 ones
-    static constexpr int KC = K16 ? 16 : 32;               // K entries per MFMA
-    static constexpr int NCH = (KX + KC - 1) / KC;         // MFMAs per 16 codes x 16 tokens
-    static constexpr int KL = KC / 4;                      // K entries per lane per MFMA
+    static constexpr int KC = 16;                          // K entries per 32x32x16 MFMA
+    static constexpr int NCH = (KX + KC - 1) / KC;         // MFMAs per 32 codes x 32 tokens
+    static constexpr int KL = KC / 2;                      // K entries per lane per MFMA
     static constexpr int LE = CG < KL ? CG : KL;           // x elements per load
     static constexpr int NLD = KL / LE;                    // loads per lane per MFMA
     static constexpr int EB = (int)sizeof(CB);
@@ -138,9 +139,9 @@ struct EncShape {
     static_assert(G % 8 == 0 && (P * G) % 8 == 0, "operand blocks of 8");
 };
 
-// One 16-token tile of x as MFMA B-operand words: lane (row, kq) holds, for
-// each K chunk ch, the KL/2 words (KL bf16) of entries kk = ch*KC + kq*KL ..
-// + KL - 1 of token n0 + row (zero where kk is not an x entry or the token is
+// One 32-token tile of x as MFMA B-operand words: lane (col, hf) holds, for
+// each K chunk ch, the KL/2 words (KL bf16) of entries kk = ch*KC + hf*KL ..
+// + KL - 1 of token n0 + col (zero where kk is not an x entry or the token is
 // past the end).
 template <int NCH, int KL>
 struct XTile {
@@ -173,20 +174,15 @@ __device__ __forceinline__ void load_tile(XTile<NCH, KL> &t, __amdgpu_buffer_rsr
     }
 }
 
-typedef short bf16x4s __attribute__((ext_vector_type(4)));   // 16x16x16 operand (bf16 bits)
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// acc = A * B + acc for one K chunk
-template <bool K16>
-__device__ __forceinline__ floatx4 mfma_chunk(const uint32_t *aw, const uint32_t *bw, floatx4 acc) {
-    if constexpr (K16) {
-        const bf16x4s A = __builtin_bit_cast(bf16x4s, make_uint2(aw[0], aw[1]));
-        const bf16x4s B = __builtin_bit_cast(bf16x4s, make_uint2(bw[0], bw[1]));
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, B, acc, 0, 0, 0);
-    } else {
-        const bf16x8 A = __builtin_bit_cast(bf16x8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
-        const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
-    }
+// acc = A * B + acc for one K chunk of 16: lane (col, hf) supplies A[col][8 hf
+// .. 8 hf + 7] and B[8 hf .. 8 hf + 7][col]; it receives D[8 (v / 4) + 4 hf +
+// v % 4][col] in acc[v]
+__device__ __forceinline__ floatx16 mfma_chunk(const uint32_t *aw, const uint32_t *bw, floatx16 acc) {
+    const bf16x8 A = __builtin_bit_cast(bf16x8, make_uint4(aw[0], aw[1], aw[2], aw[3]));
+    const bf16x8 B = __builtin_bit_cast(bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
 }
 
 // kScreen: also store every unmarked screen value to a.screen (the
@@ -194,7 +190,7 @@ __device__ __forceinline__ floatx4 mfma_chunk(const uint32_t *aw, const uint32_t
 // operands and the instructions that form them are those of the plain
 // instance)
 template <int G, int CG, int P, typename CB, bool kScreen>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G * P <= 16 ? 4 : 1))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G * P <= 16 && !kScreen ? 4 : 1))) void
 encode_kernel(EncodeArgs a) {
     using Sh = EncShape<G, CG, P, CB>;
     constexpr int NCH = Sh::NCH;
@@ -212,15 +208,27 @@ encode_kernel(EncodeArgs a) {
     // from it in scalar registers)
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // grid z = tensor * H + head (a launch may encode two tensors, e.g. K and V)
-    const int tz = (int)blockIdx.z / a.H;
-    const int h = (int)blockIdx.z - tz * a.H;
+    // One linear grid over (tensor * H + head, token chunk, group of kJW
+    // sub-vectors), the group fastest.  Workgroups are dealt to the 8 XCDs in
+    // turn (dispatch d to XCD d % 8), so XCD k takes a contiguous run of the
+    // linear index: the workgroups of a chunk that cover the groups of one
+    // input row (32 bytes of it each) and fill its index rows (4 bytes each)
+    // start together on one XCD and share its L2.
+    const int ny = (a.S + kJW - 1) / kJW;
+    const int nchunk = (int)((a.n_tokens + kTokChunk - 1) / kTokChunk);
+    const int n_wg = nchunk * ny * a.H * a.n_tensors;
+    const int dsp = (int)blockIdx.x, xcd = dsp % 8, per = n_wg / 8, rem = n_wg % 8;
+    const int lin = xcd * per + min(xcd, rem) + dsp / 8;
+    const int yg = lin % ny, chunk = (lin / ny) % nchunk, zz = lin / (ny * nchunk);
+    const int tz = zz / a.H;
+    const int h = zz - tz * a.H;
     const uint16_t *xin = tz ? a.x_b : a.x;
     const void *cbin = tz ? a.cb_b : a.cb;
     uint8_t *idxout = tz ? a.index_b : a.index;
-    const int j0 = blockIdx.y * kJW, j = j0 + wave;
-    const int64_t tok0 = (int64_t)blockIdx.x * kTokChunk;
+    const int j0 = yg * kJW, j = j0 + wave;
+    const int64_t tok0 = (int64_t)chunk * kTokChunk;
     const int64_t tok_end = min(tok0 + kTokChunk, a.n_tokens);
-    const int row = lane & 15, kq = lane >> 4;
+    const int col = lane & 31, hf = lane >> 5;
 
     // stage the 4 codebooks: chunk c of row (t, k) piece p -> entries (jl, c) of slice t
     {
@@ -281,16 +289,16 @@ encode_kernel(EncodeArgs a) {
     // upper bound of max_k |c_k| (slack covers the rounding of the norm)
     const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
 
-    // this wave's codebook as MFMA A operands: lane (row, kq) holds entries
-    // kk = ch*KC + kq*KL + e of code blk*16 + row, two bf16 a word (kq enters
+    // this wave's codebook as MFMA A operands: lane (col, hf) holds entries
+    // kk = ch*KC + hf*KL + e of code blk*32 + col, two bf16 a word (hf enters
     // only the LDS address and the selects, so the wave builds them without
     // divergent branches)
     constexpr int KL = Sh::KL, KC = Sh::KC, LE = Sh::LE, NLD = Sh::NLD;
     const CB *mycb = cbs + wave * 256 * G;
-    uint32_t afrag[16][NCH][KL / 2];
+    uint32_t afrag[8][NCH][KL / 2];
 #pragma unroll
-    for (int blk = 0; blk < 16; ++blk) {
-        const int code = blk * 16 + row;
+    for (int blk = 0; blk < 8; ++blk) {
+        const int code = blk * 32 + col;
         const CB *cw = mycb + code * G;
 #pragma unroll
         for (int ch = 0; ch < NCH; ++ch) {
@@ -299,7 +307,7 @@ encode_kernel(EncodeArgs a) {
                 uint32_t wv = 0;
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    const int kk = ch * KC + kq * KL + e + h2;
+                    const int kk = ch * KC + hf * KL + e + h2;
                     const float c = to_f(cw[kk % G]);
                     const float part = P == 1 ? c : split_part(c, kk / G);
                     const float v = kk < P * G ? -2.f * part : 0.f;
@@ -310,18 +318,12 @@ encode_kernel(EncodeArgs a) {
         }
     }
     // the accumulator of block blk starts at the squared norms of the lane's
-    // 4 codes blk*16 + kq*4 + i (the same for every token column)
-    const float *bias_row = nrm + wave * 256 + kq * 4;
+    // 16 codes blk*32 + 8 q + 4 hf + i, q, i < 4 (the same for every token)
+    const float *bias_row = nrm + wave * 256 + hf * 4;
     __syncthreads();                                  // the staged codebooks are dead
 
-    // byte j of the index row of the chunk's first token; as a buffer resource,
-    // a store at offset kOob is dropped
-    uint8_t *out_wave = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j;
-    const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(out_wave, (short)0, 0x7ffffff0, kBufferWord3);
-
     // per-lane x offsets (bytes from the tile base) of the loads that fill the
-    // lane's B words: load s of chunk ch holds entries kk = ch*KC + kq*KL +
+    // lane's B words: load s of chunk ch holds entries kk = ch*KC + hf*KL +
     // s*LE .. + LE - 1, i.e. x_i with i = kk mod G (step i / CG, channels
     // i mod CG ..); lanes whose K entries are not x read nothing
     uint32_t xoff[NCH][NLD];
@@ -329,14 +331,12 @@ encode_kernel(EncodeArgs a) {
     for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
         for (int s = 0; s < NLD; ++s) {
-            const int kk = ch * KC + kq * KL + s * LE;
+            const int kk = ch * KC + hf * KL + s * LE;
             const int i = kk % G;
-            const int64_t e = (int64_t)row * a.sx_tok + (int64_t)(i / CG) * a.sx_step + (int64_t)j * CG + i % CG;
+            const int64_t e = (int64_t)col * a.sx_tok + (int64_t)(i / CG) * a.sx_step + (int64_t)j * CG + i % CG;
             xoff[ch][s] = kk < P * G ? (uint32_t)(2 * e) : kOob;
         }
     }
-    // lanes whose words are x entries i < G (counted once for |x|^2)
-    const bool norm_lane = kq * KL < G;
 
     const uint16_t *xh = xin + h * a.sx_head;
     auto rsrc = [&](int64_t n0) {
@@ -345,195 +345,178 @@ encode_kernel(EncodeArgs a) {
     };
     uint16_t *codes = row_code[wave];
 
-    // Tiles go in groups of kDepth through two register rings: while one
-    // group is screened from ring A, the next is in flight into ring B, and
-    // the other way round.  A group's loads are issued a whole group before
-    // its first use and after the loads of the group before it, and every
-    // load of the main loop is unconditional with loop-invariant lane
-    // offsets, so the compiler's wait for a group counts exactly the loads
-    // behind it (a conditional load, or a per-load offset select whose
+    // Tiles of 32 tokens go in groups of kDepth through two register rings:
+    // while one group is screened from ring A, the next is in flight into
+    // ring B, and the other way round.  A group's loads are issued a whole
+    // group before its first use and after the loads of the group before it,
+    // and every load of the main loop is unconditional with loop-invariant
+    // lane offsets, so the compiler's wait for a group counts exactly the
+    // loads behind it (a conditional load, or a per-load offset select whose
     // register gets reused for loaded data, made it wait for all of them).
     // The main loop covers whole pairs of groups; the rows after them go tile
     // by tile, where rows past the chunk's end load nothing and store
     // nothing.
-    constexpr int kDepth = 4;                          // tiles per group
-    constexpr int kPair = 32 * kDepth;                 // rows of a pair of groups
+    constexpr int kTile = 32;                          // tokens per tile
+    constexpr int kDepth = 1;                          // tiles per group
+    constexpr int kPair = 2 * kTile * kDepth;          // rows of a pair of groups
     const int ntok = (int)(tok_end - tok0);
     const int nfull = ntok / kPair * kPair;
     using Tile = XTile<NCH, KL>;
     Tile ringA[kDepth], ringB[kDepth];
-    // every row of the group exists (rg0 + 16 * kDepth <= nfull)
+    // every row of the group exists (rg0 + kTile * kDepth <= nfull)
     auto load_group = [&](Tile (&rg)[kDepth], int rg0) {
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) load_tile<NCH, KL, LE>(rg[u], rsrc(tok0 + rg0 + 16 * u), xoff, true);
+        for (int u = 0; u < kDepth; ++u) load_tile<NCH, KL, LE>(rg[u], rsrc(tok0 + rg0 + kTile * u), xoff, true);
     };
     auto screen_tile = [&](const Tile &cur, const int r0) {
             const int64_t n0 = tok0 + r0;
-            const bool valid = r0 + row < ntok;
+            const bool valid = r0 + col < ntok;
 
-            // |x|^2 from the lane's words of chunk 0 (bf16 squares are exact;
-            // the sum only feeds a bound); the words are the B operand as loaded
+            // |x|^2 from the lane's words that hold entries i < G (bf16
+            // squares are exact; the sum only feeds a bound); the words are the
+            // B operand as loaded
             float xs = 0.f;
-            {
-                float d = 0.f;
+#pragma unroll
+            for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
                 for (int q = 0; q < KL / 2; ++q) {
                     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                    const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[0][q]);
-                    d = __builtin_amdgcn_fdot2_f32_bf16(v, v, d, false);
+                    const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[ch][q]);
+                    const float d = __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.f, false);
+                    xs += (ch * KC + hf * KL + 2 * q < G) ? d : 0.f;
                 }
-                xs = norm_lane ? d : 0.f;
             }
             float xa, xb;
-            pair16(xs, xa, xb);
-            pair32(xa + xb, xa, xb);
+            pair32(xs, xa, xb);
             const float xn2 = xa + xb;
 
-            // Smallest and second smallest screen value of the lane's 64 codes.
-            // The lane's value of code blk*16 + kq*4 + i sits at slot
-            // s = 4 blk + i.  Two partitions of the slots, groups s / 8 (blocks
-            // 2g and 2g + 1) and chains s % 8, have no two slots in common in
-            // both a group and a chain, so of the two smallest values one is
-            // the minimum of its group and the other the minimum of its chain
-            // or of its group: the lane's second smallest is the smaller of
-            // the second smallest group minimum and the second smallest chain
+            // Smallest and second smallest screen value of the lane's 128
+            // codes.  The lane's value of code blk*32 + 8 (v / 4) + 4 hf + v % 4
+            // (acc[v] of block blk) sits at slot s = 16 blk + v.  Two
+            // partitions of the slots, groups s / 8 (half a block: acc[0..7],
+            // acc[8..15]) and chains s % 8, have no two slots in common in both
+            // a group and a chain, so of the two smallest values one is the
+            // minimum of its group and the other the minimum of its chain or
+            // of its group: the lane's second smallest is the smaller of the
+            // second smallest group minimum and the second smallest chain
             // minimum.  Minima are taken with min3 over 3 operands, two new
-            // values an instruction; only the 8 group and 8 chain minima get
-            // marks (their low 3 bits become g or c), and the lane's smallest
-            // value carries both (low 6 bits = s), which names its code.
-            // Blocks go a quad (4 blocks, two groups) at a time: the MFMAs of
-            // the next quad run while this one is reduced (the scheduling
-            // barriers keep that order), and the accumulators start at the
-            // codes' squared norms, read from LDS a quad ahead of their MFMAs.
-            auto bias_of = [&](int blk) { return *reinterpret_cast<const floatx4 *>(bias_row + blk * 16); };
-            auto screen = [&](int blk, floatx4 acc) {
+            // values an instruction; only the 16 group and 8 chain minima get
+            // marks (their low 4 bits become the group, their low 3 bits the
+            // chain), and the smallest chain minimum names the chain, the
+            // smallest group minimum the group of the lane's smallest value.
+            // Block b + 1's MFMAs run while block b is reduced (the
+            // scheduling barriers keep that order); the accumulators start at
+            // the codes' squared norms, read from LDS.
+            auto bias_of = [&](int blk) {
+                floatx16 bv;
 #pragma unroll
-                for (int ch = 0; ch < NCH; ++ch) acc = mfma_chunk<Sh::K16>(afrag[blk][ch], cur.w[ch], acc);
+                for (int q = 0; q < 4; ++q) {
+                    const floatx4 b4 = *reinterpret_cast<const floatx4 *>(bias_row + blk * 32 + 8 * q);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) bv[4 * q + i] = b4[i];
+                }
+                return bv;
+            };
+            auto screen = [&](int blk, floatx16 acc) {
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) acc = mfma_chunk(afrag[blk][ch], cur.w[ch], acc);
                 return acc;
             };
-            auto mark3 = [](float v, uint32_t m) { return __uint_as_float((__float_as_uint(v) & ~7u) | m); };
+            auto mark = [](float v, uint32_t bits, uint32_t m) {
+                return __uint_as_float((__float_as_uint(v) & ~bits) | m);
+            };
             auto min3 = [](float p, float q, float r) { return fminf(fminf(p, q), r); };
-            floatx4 acc[2][4], bq[4];
-#pragma unroll
-            for (int b = 0; b < 4; ++b) bq[b] = bias_of(b);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[0][b] = screen(b, bq[b]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) bq[b] = bias_of(4 + b);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[1][b] = screen(4 + b, bq[b]);
+            floatx16 acc[2];
+            acc[0] = screen(0, bias_of(0));
+            acc[1] = screen(1, bias_of(1));
             __builtin_amdgcn_sched_barrier(0);
             float cm[8], g1 = 0.f, g2 = 0.f;
 #pragma unroll
-            for (int qd = 0; qd < 4; ++qd) {
-                if (qd + 2 < 4) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) bq[b] = bias_of(4 * (qd + 2) + b);
-                }
-                const floatx4 *v = acc[qd & 1];
+            for (int blk = 0; blk < 8; ++blk) {
+                const floatx16 &v = acc[blk & 1];
                 if constexpr (kScreen) {
                     if (valid) {
+                        float *dst = a.screen + (((size_t)(n0 + col) * a.H + h) * a.S + j) * 256 + blk * 32 + 4 * hf;
 #pragma unroll
-                        for (int b = 0; b < 4; ++b) {
-                            float *dst = a.screen + (((size_t)(n0 + row) * a.H + h) * a.S + j) * 256 +
-                                         (4 * qd + b) * 16 + kq * 4;
-                            *reinterpret_cast<float4 *>(dst) = make_float4(v[b][0], v[b][1], v[b][2], v[b][3]);
-                        }
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<float4 *>(dst + 8 * q) =
+                                make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
                     }
                 }
-                // groups 2 qd (blocks 0, 1 of the quad) and 2 qd + 1 (blocks 2, 3)
-                float ga = min3(v[0][0], v[0][1], v[0][2]);
-                ga = min3(ga, v[0][3], v[1][0]);
-                ga = min3(ga, v[1][1], v[1][2]);
-                ga = mark3(fminf(ga, v[1][3]), 2 * qd);
-                float gb = min3(v[2][0], v[2][1], v[2][2]);
-                gb = min3(gb, v[2][3], v[3][0]);
-                gb = min3(gb, v[3][1], v[3][2]);
-                gb = mark3(fminf(gb, v[3][3]), 2 * qd + 1);
-                // chains i (even blocks) and 4 + i (odd blocks)
-                if (qd == 0) {
+                // groups 2 blk (acc[0..7]) and 2 blk + 1 (acc[8..15])
+                float ga = min3(v[0], v[1], v[2]);
+                ga = min3(ga, v[3], v[4]);
+                ga = min3(ga, v[5], v[6]);
+                ga = mark(fminf(ga, v[7]), 15u, 2 * blk);
+                float gb = min3(v[8], v[9], v[10]);
+                gb = min3(gb, v[11], v[12]);
+                gb = min3(gb, v[13], v[14]);
+                gb = mark(fminf(gb, v[15]), 15u, 2 * blk + 1);
+                // chains c (acc[c] and acc[8 + c])
+                if (blk == 0) {
                     g1 = fminf(ga, gb);
                     g2 = fmaxf(ga, gb);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        cm[i] = fminf(v[0][i], v[2][i]);
-                        cm[4 + i] = fminf(v[1][i], v[3][i]);
-                    }
+                    for (int c = 0; c < 8; ++c) cm[c] = fminf(v[c], v[8 + c]);
                 } else {
                     g2 = fminf(g2, __builtin_amdgcn_fmed3f(g1, ga, gb));
                     g1 = min3(g1, ga, gb);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        cm[i] = min3(cm[i], v[0][i], v[2][i]);
-                        cm[4 + i] = min3(cm[4 + i], v[1][i], v[3][i]);
-                    }
+                    for (int c = 0; c < 8; ++c) cm[c] = min3(cm[c], v[c], v[8 + c]);
                 }
-                if (qd + 2 < 4) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) acc[qd & 1][b] = screen(4 * (qd + 2) + b, bq[b]);
-                }
+                if (blk + 2 < 8) acc[blk & 1] = screen(blk + 2, bias_of(blk + 2));
                 __builtin_amdgcn_sched_barrier(0);
             }
             // the two smallest marked chain minima
-            float c1 = fminf(mark3(cm[0], 0), mark3(cm[1], 1));
-            float c2 = fmaxf(mark3(cm[0], 0), mark3(cm[1], 1));
+            float c1 = fminf(mark(cm[0], 7u, 0), mark(cm[1], 7u, 1));
+            float c2 = fmaxf(mark(cm[0], 7u, 0), mark(cm[1], 7u, 1));
 #pragma unroll
             for (int c = 2; c < 8; c += 2) {
-                const float p = mark3(cm[c], c), q = mark3(cm[c + 1], c + 1);
+                const float p = mark(cm[c], 7u, c), q = mark(cm[c + 1], 7u, c + 1);
                 c2 = fminf(c2, __builtin_amdgcn_fmed3f(c1, p, q));
                 c1 = min3(c1, p, q);
             }
-            // the lane's smallest value with its slot (group from g1, chain from
-            // c1) in the low 6 bits, and its second smallest
-            float m1 = __uint_as_float((__float_as_uint(c1) & ~0x38u) | ((__float_as_uint(g1) & 7u) << 3));
-            float m2 = fminf(c2, g2);
-            // combine the four lanes holding the same token; the lane whose own
-            // smallest value is the token's smallest holds the winner
-            const float own = m1;
+            // the two lanes holding the same token combine: the lane whose
+            // own smallest value is the token's smallest holds the winner
+            const float own = c1;
+            float m1, m2;
             {
                 float a1, b1, a2, b2;
-                pair16(m1, a1, b1);
-                pair16(m2, a2, b2);
-                m2 = fminf(fmaxf(a1, b1), fminf(a2, b2));
-                m1 = fminf(a1, b1);
-                pair32(m1, a1, b1);
-                pair32(m2, a2, b2);
+                pair32(c1, a1, b1);
+                pair32(fminf(c2, g2), a2, b2);
                 m2 = fminf(fmaxf(a1, b1), fminf(a2, b2));
                 m1 = fminf(a1, b1);
             }
-            const uint32_t slot = __float_as_uint(m1) & 63u;
-            const int k1 = (int)((slot >> 2) * 16 + kq * 4 + (slot & 3));
+            // slot s = 8 g + c: group from the smallest group minimum, chain
+            // from the smallest chain minimum
+            const uint32_t slot = ((__float_as_uint(g1) & 15u) << 3) | (__float_as_uint(own) & 7u);
+            const int v1 = (int)(slot & 15u);
+            const int k1 = (int)(slot >> 4) * 32 + 8 * (v1 >> 2) + 4 * hf + (v1 & 3);
             const bool holder = __float_as_uint(own) == __float_as_uint(m1);
             // hardware square root (within 1 ulp): the slack covers it
             const float rad = __builtin_amdgcn_sqrtf(xn2) * (1.f + 1e-5f) + max_norm;
             const float eps = kEpsScale * rad * rad;
             const bool unique = (m2 - m1) > eps;
-            // when the winner is unique no other lane holds an equal value (it
-            // would be the second smallest), so exactly one lane stores it (the
-            // store instruction is unconditional, the other lanes' offsets are
-            // out of range, so the compiler's wait counts stay exact); otherwise
-            // the lane of kq = 0 marks the row for the exact re-score
-            const bool store = valid && unique && holder;
-            __builtin_amdgcn_raw_buffer_store_b8((unsigned char)k1, out_rsrc,
-                                                 store ? (uint32_t)((r0 + row) * a.S) : kOob, 0, 0);
-            // (one lane per row writes the mark: four lanes writing one
-            // address would serialise in LDS)
-            if (kq == 0) codes[r0 + row] = (valid && !unique) ? kRescore : (uint16_t)0;
+            // the token's code, or the re-score mark, goes to this wave's row
+            // of the LDS code array, written by one lane: the holder when the
+            // winner is unique (the other lane then holds no equal value: it
+            // would be the second smallest), else the lane of hf = 0
+            if (valid && (unique ? holder : hf == 0)) codes[r0 + col] = unique ? (uint16_t)k1 : kRescore;
     };
     if (nfull > 0) load_group(ringA, 0);
     for (int rb = 0; rb < nfull; rb += kPair) {
-        load_group(ringB, rb + 16 * kDepth);
+        load_group(ringB, rb + kTile * kDepth);
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) screen_tile(ringA[u], rb + 16 * u);
+        for (int u = 0; u < kDepth; ++u) screen_tile(ringA[u], rb + kTile * u);
         // the last pair reloads rows of its own second group (read again,
         // never screened): the loads stay unconditional and in bounds
-        load_group(ringA, rb + kPair < nfull ? rb + kPair : rb + 16 * kDepth);
+        load_group(ringA, rb + kPair < nfull ? rb + kPair : rb + kTile * kDepth);
 #pragma unroll
-        for (int u = 0; u < kDepth; ++u) screen_tile(ringB[u], rb + 16 * (kDepth + u));
+        for (int u = 0; u < kDepth; ++u) screen_tile(ringB[u], rb + kTile * (kDepth + u));
     }
-    for (int r0 = nfull; r0 < ntok; r0 += 16) {
+    for (int r0 = nfull; r0 < ntok; r0 += kTile) {
         Tile t;
-        load_tile<NCH, KL, LE>(t, rsrc(tok0 + r0), xoff, r0 + row < ntok);
+        load_tile<NCH, KL, LE>(t, rsrc(tok0 + r0), xoff, r0 + col < ntok);
         screen_tile(t, r0);
     }
 
@@ -584,8 +567,21 @@ encode_kernel(EncodeArgs a) {
         // distances are >= 0, so their bit patterns order like them
         const uint32_t dmin = wave_min_u32(__float_as_uint(best));
         const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
-        if (lane == 0) out_wave[(size_t)rq * a.S] = (uint8_t)kmin;
+        if (lane == 0) codes[rq] = (uint16_t)kmin;
       }
+    }
+
+    // The chunk's index rows: each token's kJW codes (sub-vectors j0 ..
+    // j0 + kJW - 1, one 32-bit word of its row) in one 4-byte store.  The
+    // workgroups that fill the other words of these rows run alongside on the
+    // same XCD, so the rows reach memory whole.
+    __syncthreads();
+    uint8_t *out_rows = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j0;
+    for (int t = tid; t < ntok; t += kThreads) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int q = 0; q < kJW; ++q) w |= (uint32_t)(row_code[q][t] & 0xffu) << (8 * q);
+        *reinterpret_cast<uint32_t *>(out_rows + (size_t)t * a.S) = w;
     }
 }
 
@@ -724,12 +720,17 @@ __global__ __launch_bounds__(kSmallThreads) void encode_small(EncodeArgs a) {
     }
 }
 
+// workgroups of encode_kernel: token chunks x groups of kJW sub-vectors x
+// heads x tensors (one linear grid)
+inline unsigned screen_workgroups(const EncodeArgs &a) {
+    return (unsigned)(((a.n_tokens + kTokChunk - 1) / kTokChunk) * ((a.S + kJW - 1) / kJW) * a.H * a.n_tensors);
+}
+
 template <int G, int CG>
 hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
     if (a.screen) {
         // the screen path at any length, storing the screen values
-        const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW,
-                        a.H * a.n_tensors);
+        const dim3 grid(screen_workgroups(a));
         if (a.cb_bf16)
             hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t, true>), grid, dim3(kThreads), 0, st, a);
         else if constexpr (G <= 16)
@@ -748,8 +749,7 @@ hipError_t launch_gc(const EncodeArgs &a, hipStream_t st) {
             return hipErrorInvalidValue;
         return hipGetLastError();
     }
-    const dim3 grid((unsigned)((a.n_tokens + kTokChunk - 1) / kTokChunk), (a.S + kJW - 1) / kJW,
-                    a.H * a.n_tensors);
+    const dim3 grid(screen_workgroups(a));
     if (a.cb_bf16) {
         hipLaunchKernelGGL((encode_kernel<G, CG, 1, uint16_t, false>), grid, dim3(kThreads), 0, st, a);
     } else {

@@ -176,9 +176,11 @@ lvq_status encode_tensors(const lvq_config *c, int n, const void *const *x, cons
         if (reinterpret_cast<uintptr_t>(x[i]) % (2 * (uintptr_t)cg) != 0) return LVQ_ERR_INVALID_ARG;
         // the codebooks are staged in 16-byte pieces
         if (reinterpret_cast<uintptr_t>(codebook[i]) % 16 != 0) return LVQ_ERR_INVALID_ARG;
+        // index rows are written a 4-byte word (4 sub-vectors) at a time
+        if (reinterpret_cast<uintptr_t>(index_cache[i]) % 4 != 0) return LVQ_ERR_INVALID_ARG;
     }
-    // a 16-token tile of one head is addressed with 32-bit byte offsets
-    if (2 * (15 * st[0] + Tc * st[2] + d) >= 0x7ffffff0LL) return LVQ_ERR_UNSUPPORTED;
+    // a 32-token tile of one head is addressed with 32-bit byte offsets
+    if (2 * (31 * st[0] + Tc * st[2] + d) >= 0x7ffffff0LL) return LVQ_ERR_UNSUPPORTED;
     if (!lvq::encode_supported(c->group, cg, (int)(c->head_dim / cg),
                                c->codebook_dtype == LVQ_BF16))
         return LVQ_ERR_UNSUPPORTED;

@@ -308,6 +308,7 @@ def test_encode_validation():
     assert _encode(cfg, n=-1) == INV
     assert _encode(cfg, strides=(512, 256, 63)) == INV                  # not a multiple of cg
     assert _encode(cfg, x=ctypes.c_void_p(P.value + 2)) == INV         # misaligned
+    assert _encode(cfg, index=ctypes.c_void_p(P.value + 2)) == INV     # index rows written as 4-byte words
     assert _encode(_cfg(1, 1, 64, 4, 64, 100, lv.LVQ_BF16)) == UNS      # G = 64
     assert _encode(_cfg(1, 1, 128, 4, 32, 100, lv.LVQ_F32)) == UNS      # fp32, G = 32
     assert _encode(cfg, n=0) == lv.LVQ_OK                              # nothing to launch
