@@ -41,16 +41,17 @@
 // value move it by at most 2^-19 R^2; the fp32 error of D_k is at most
 // (G+2) 2^-24 R^2 and that of the screen (C plus P*G exact products) at most
 // F (P*G+3) 2^-24 R^2 for an accumulation F times worse than a sequential
-// fp32 sum (P*G+1 terms; the bound keeps two terms of slack).  If the two
-// smallest (marked) screen values are more than eps = 2^-14 R^2 apart, eps
-// exceeds twice the sum of these (for F up to 12.7 at G = 32, P = 1 and up to
-// 9 at G = 16, P = 3), so the screen winner is the exact winner.  (Where the
-// group and the chain of a lane's smallest value would name different codes,
-// two of its values are within a few marks of each other, so the test
-// fails.)  Otherwise the wave re-scores all 256 codes of that sub-vector exactly as defined above
-// from the codebook (64 lanes x 4 codes, strict < per lane in ascending k,
-// then a lowest-index argmin across lanes), which reproduces the definition
-// bit for bit.
+// fp32 sum (P*G+1 terms; the bound keeps two terms of slack; any fp32
+// summation order, rounded to nearest or truncated, has F <= 2).  If the two
+// smallest (marked) screen values are more than eps = 2^-15 R^2 apart, eps
+// exceeds twice the sum of these (for F up to 10.8 at G = 16 and 5.4 at
+// G = 32 with P = 1, 4.0 at G = 16 with P = 3), so the screen winner is the
+// exact winner.  (Where the group and the chain of a lane's smallest value
+// would name different codes, two of its values are within a few marks of
+// each other, so the test fails.)  Otherwise the wave re-scores all 256 codes
+// of that sub-vector exactly as defined above from the codebook (64 lanes x 4
+// codes, strict < per lane in ascending k, then a lowest-index argmin across
+// lanes), which reproduces the definition bit for bit.
 #include "kernels.h"
 
 #include <math.h>
@@ -66,7 +67,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;     // 4 waves, one sub-vector index j each
 constexpr int kJW = 4;            // sub-vectors per workgroup
 constexpr int kTokChunk = 2048;   // tokens per workgroup
-constexpr float kEpsScale = 6.103515625e-05f;  // 2^-14
+constexpr float kEpsScale = 3.0517578125e-05f;  // 2^-15
 constexpr uint16_t kRescore = 0x100;
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
