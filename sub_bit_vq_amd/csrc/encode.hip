@@ -355,8 +355,9 @@ encode_kernel(EncodeArgs a) {
     // loads behind it (a conditional load, or a per-load offset select whose
     // register gets reused for loaded data, made it wait for all of them).
     // The main loop covers whole pairs of groups; the rows after them go tile
-    // by tile, where rows past the chunk's end load nothing and store
-    // nothing.
+    // by tile, where rows past the chunk's end load nothing and write no
+    // code.  (A group is one tile: two fit the 128-register budget only with
+    // spills, and a third ring slot, one more tile ahead, gained nothing.)
     constexpr int kTile = 32;                          // tokens per tile
     constexpr int kDepth = 1;                          // tiles per group
     constexpr int kPair = 2 * kTile * kDepth;          // rows of a pair of groups
