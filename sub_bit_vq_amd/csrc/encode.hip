@@ -201,7 +201,10 @@ encode_kernel(EncodeArgs a) {
     // workgroups fit a compute unit.
     constexpr int kCbBytes = kJW * 256 * G * (int)sizeof(CB);
     constexpr int kCodeBytes = kJW * kTokChunk * 2;
-    __shared__ __align__(16) unsigned char stage[kCbBytes > kCodeBytes ? kCbBytes : kCodeBytes];
+    constexpr int kMarkWords = kTokChunk / 32;                    // one word per 32-token tile
+    constexpr int kMarkBytes = kJW * kMarkWords * 4;
+    __shared__ __align__(16) unsigned char
+        stage[kCbBytes > kCodeBytes + kMarkBytes ? kCbBytes : kCodeBytes + kMarkBytes];
     __shared__ float nrm[kJW * 256];
     CB *cbs = reinterpret_cast<CB *>(stage);
     uint16_t(*row_code)[kTokChunk] = reinterpret_cast<uint16_t(*)[kTokChunk]>(stage);
@@ -345,6 +348,8 @@ encode_kernel(EncodeArgs a) {
                                                  0x7ffffff0, kBufferWord3);
     };
     uint16_t *codes = row_code[wave];
+    // bit i of word t: row 32 t + i of the chunk is marked for the re-score
+    uint32_t *marks = reinterpret_cast<uint32_t *>(stage + kCodeBytes) + wave * kMarkWords;
 
     // Tiles of 32 tokens go in groups of kDepth through two register rings:
     // while one group is screened from ring A, the next is in flight into
@@ -359,6 +364,7 @@ encode_kernel(EncodeArgs a) {
     // code.  (A group is one tile: two fit the 128-register budget only with
     // spills, and a third ring slot, one more tile ahead, gained nothing.)
     constexpr int kTile = 32;                          // tokens per tile
+    static_assert(kTokChunk / kTile == kMarkWords, "one mark word per tile");
     constexpr int kDepth = 1;                          // tiles per group
     constexpr int kPair = 2 * kTile * kDepth;          // rows of a pair of groups
     const int ntok = (int)(tok_end - tok0);
@@ -504,6 +510,8 @@ encode_kernel(EncodeArgs a) {
             // winner is unique (the other lane then holds no equal value: it
             // would be the second smallest), else the lane of hf = 0
             if (valid && (unique ? holder : hf == 0)) codes[r0 + col] = unique ? (uint16_t)k1 : kRescore;
+            const uint64_t mk = __ballot(valid && !unique && hf == 0);   // rows of the tile: lanes 0-31
+            if (lane == 0) marks[r0 / kTile] = (uint32_t)mk;
     };
     if (nfull > 0) load_group(ringA, 0);
     for (int rb = 0; rb < nfull; rb += kPair) {
@@ -524,13 +532,14 @@ encode_kernel(EncodeArgs a) {
 
     // exact re-score of the marked sub-vectors (rare): every lane scores 4
     // codes k = lane + 64 r, read from the codebook in memory, then the wave
-    // takes the lowest index of the smallest distance
-    bool any_marked = false;
-    for (int rb = 0; rb < ntok; rb += 64)
-        any_marked |= __ballot(rb + lane < ntok && codes[rb + lane] == kRescore) != 0;
-    const int ntok_rescore = any_marked ? ntok : 0;  // wave-uniform
+    // takes the lowest index of the smallest distance.  The tiles' mark words
+    // (one per lane, kMarkWords <= 64) say which rows, and whether any.
+    static_assert(kMarkWords <= 64, "one mark word per lane");
+    const int ntiles = (ntok + kTile - 1) / kTile;
+    const uint32_t mword = lane < ntiles ? marks[lane] : 0u;
+    uint64_t mtiles = __ballot(mword != 0u);
     float cf[4][G];
-    if (any_marked) {
+    if (mtiles != 0) {
         const CB *cbg = static_cast<const CB *>(cbin);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -538,10 +547,12 @@ encode_kernel(EncodeArgs a) {
             for (int i = 0; i < G; ++i)
                 cf[r][i] = to_f(cbg[((((size_t)(i / CG) * a.H + h) * 256 + lane + 64 * r) * a.S + j) * CG + i % CG]);
     }
-    for (int rb = 0; rb < ntok_rescore; rb += 64) {
-      uint64_t marked = __ballot(rb + lane < ntok && codes[rb + lane] == kRescore);
+    while (mtiles != 0) {                              // wave-uniform
+      const int tt = (int)__builtin_ctzll(mtiles);
+      mtiles &= mtiles - 1;
+      uint32_t marked = (uint32_t)__builtin_amdgcn_readlane((int)mword, tt);
       while (marked != 0) {                            // wave-uniform
-        const int rq = rb + (int)__builtin_ctzll(marked);
+        const int rq = tt * kTile + (int)__builtin_ctz(marked);
         marked &= marked - 1;
         const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
         float xe[G];
