@@ -235,7 +235,7 @@ encode_kernel(EncodeArgs a) {
     const int col = lane & 31, hf = lane >> 5;
 
     // stage the 4 codebooks: chunk c of row (t, k) piece p -> entries (jl, c) of slice t
-    {
+    auto stage_codebooks = [&]() {
         const char *src = static_cast<const char *>(cbin);
         constexpr int PER_ROW = Sh::ROWB / 16;
 #pragma unroll
@@ -263,7 +263,8 @@ encode_kernel(EncodeArgs a) {
                     *reinterpret_cast<uint32_t *>(dst) = vw[q];
             }
         }
-    }
+    };
+    stage_codebooks();
     __syncthreads();
     // squared norms (fp64 sum, rounded once); the max over the wave's codes
 #pragma unroll
@@ -530,64 +531,15 @@ encode_kernel(EncodeArgs a) {
         screen_tile(t, r0);
     }
 
-    // exact re-score of the marked sub-vectors (rare): every lane scores 4
-    // codes k = lane + 64 r, read from the codebook in memory, then the wave
-    // takes the lowest index of the smallest distance.  The tiles' mark words
-    // (one per lane, kMarkWords <= 64) say which rows, and whether any.
+    // The chunk's index rows: each token's kJW codes (sub-vectors j0 ..
+    // j0 + kJW - 1, one 32-bit word of its row) in one 4-byte store.  The
+    // workgroups that fill the other words of these rows run alongside on the
+    // same XCD, so the rows reach memory whole.  Rows marked for the exact
+    // re-score get their byte again below.
     static_assert(kMarkWords <= 64, "one mark word per lane");
     const int ntiles = (ntok + kTile - 1) / kTile;
     const uint32_t mword = lane < ntiles ? marks[lane] : 0u;
     uint64_t mtiles = __ballot(mword != 0u);
-    float cf[4][G];
-    if (mtiles != 0) {
-        const CB *cbg = static_cast<const CB *>(cbin);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int i = 0; i < G; ++i)
-                cf[r][i] = to_f(cbg[((((size_t)(i / CG) * a.H + h) * 256 + lane + 64 * r) * a.S + j) * CG + i % CG]);
-    }
-    while (mtiles != 0) {                              // wave-uniform
-      const int tt = (int)__builtin_ctzll(mtiles);
-      mtiles &= mtiles - 1;
-      uint32_t marked = (uint32_t)__builtin_amdgcn_readlane((int)mword, tt);
-      while (marked != 0) {                            // wave-uniform
-        const int rq = tt * kTile + (int)__builtin_ctz(marked);
-        marked &= marked - 1;
-        const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
-        float xe[G];
-#pragma unroll
-        for (int t = 0; t < G / CG; ++t)
-#pragma unroll
-            for (int c = 0; c < CG; ++c) xe[t * CG + c] = bf16f(xr[t * a.sx_step + c]);
-        float best = INFINITY;
-        int bk = 256;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float dist = 0.f;
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                // separate roundings: this file is built without contraction
-                const float e = xe[i] - cf[r][i];
-                const float sq = e * e;
-                dist = dist + sq;
-            }
-            if (dist < best) {
-                best = dist;
-                bk = lane + 64 * r;
-            }
-        }
-        // distances are >= 0, so their bit patterns order like them
-        const uint32_t dmin = wave_min_u32(__float_as_uint(best));
-        const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
-        if (lane == 0) codes[rq] = (uint16_t)kmin;
-      }
-    }
-
-    // The chunk's index rows: each token's kJW codes (sub-vectors j0 ..
-    // j0 + kJW - 1, one 32-bit word of its row) in one 4-byte store.  The
-    // workgroups that fill the other words of these rows run alongside on the
-    // same XCD, so the rows reach memory whole.
     __syncthreads();
     uint8_t *out_rows = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j0;
     for (int t = tid; t < ntok; t += kThreads) {
@@ -595,6 +547,63 @@ encode_kernel(EncodeArgs a) {
 #pragma unroll
         for (int q = 0; q < kJW; ++q) w |= (uint32_t)(row_code[q][t] & 0xffu) << (8 * q);
         *reinterpret_cast<uint32_t *>(out_rows + (size_t)t * a.S) = w;
+    }
+    // (the words are written before any re-scored byte of them: the barrier
+    // also waits for the stores)
+    __syncthreads();
+
+    // Exact re-score of the marked rows (rare): the code array is dead, so
+    // the workgroup stages its codebooks in LDS again (one coalesced pass
+    // for the 4 sub-vectors) and each lane takes its codewords from there.
+    // Every lane scores 4 codes k = lane + 64 r, then the wave takes the
+    // lowest index of the smallest distance; the mark words (in registers)
+    // say which rows.
+    if (__syncthreads_or(mtiles != 0)) {               // workgroup-uniform
+        stage_codebooks();
+        __syncthreads();
+        if (mtiles != 0) {                             // wave-uniform
+            float cf[4][G];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < G; ++i) cf[r][i] = to_f(cbs[(wave * 256 + lane + 64 * r) * G + i]);
+            while (mtiles != 0) {                      // wave-uniform
+              const int tt = (int)__builtin_ctzll(mtiles);
+              mtiles &= mtiles - 1;
+              uint32_t marked = (uint32_t)__builtin_amdgcn_readlane((int)mword, tt);
+              while (marked != 0) {                    // wave-uniform
+                const int rq = tt * kTile + (int)__builtin_ctz(marked);
+                marked &= marked - 1;
+                const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
+                float xe[G];
+#pragma unroll
+                for (int t = 0; t < G / CG; ++t)
+#pragma unroll
+                    for (int c = 0; c < CG; ++c) xe[t * CG + c] = bf16f(xr[t * a.sx_step + c]);
+                float best = INFINITY;
+                int bk = 256;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float dist = 0.f;
+#pragma unroll
+                    for (int i = 0; i < G; ++i) {
+                        // separate roundings: this file is built without contraction
+                        const float e = xe[i] - cf[r][i];
+                        const float sq = e * e;
+                        dist = dist + sq;
+                    }
+                    if (dist < best) {
+                        best = dist;
+                        bk = lane + 64 * r;
+                    }
+                }
+                // distances are >= 0, so their bit patterns order like them
+                const uint32_t dmin = wave_min_u32(__float_as_uint(best));
+                const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
+                if (lane == 0) out_rows[(size_t)rq * a.S + wave] = (uint8_t)kmin;
+              }
+            }
+        }
     }
 }
 
