@@ -43,10 +43,11 @@
 // F (P*G+3) 2^-24 R^2 for an accumulation F times worse than a sequential
 // fp32 sum (P*G+1 terms; the bound keeps two terms of slack; any fp32
 // summation order, rounded to nearest or truncated, has F <= 2).  If the two
-// smallest (marked) screen values are more than eps = 2^-15 R^2 apart, eps
-// exceeds twice the sum of these (for F up to 10.8 at G = 16 and 5.4 at
-// G = 32 with P = 1, 4.0 at G = 16 with P = 3), so the screen winner is the
-// exact winner.  (Where the group and the chain of a lane's smallest value
+// smallest (marked) screen values are more than eps apart, eps exceeds twice
+// the sum of these, so the screen winner is the exact winner.  eps is
+// 2^-16 R^2 where that still holds for F up to 3 or more (4.1 at G = 16 and
+// 7.8 at G = 8 with P = 1, 3.2 at G = 8 with P = 3), else 2^-15 R^2 (5.4 at
+// G = 32 with P = 1, 4.0 at G = 16 with P = 3).  (Where the group and the chain of a lane's smallest value
 // would name different codes, two of its values are within a few marks of
 // each other, so the test fails.)  Otherwise the wave re-scores all 256 codes
 // of that sub-vector exactly as defined above from the codebook (64 lanes x 4
@@ -67,7 +68,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;     // 4 waves, one sub-vector index j each
 constexpr int kJW = 4;            // sub-vectors per workgroup
 constexpr int kTokChunk = 2048;   // tokens per workgroup
-constexpr float kEpsScale = 3.0517578125e-05f;  // 2^-15
+// eps / R^2 for G-entry sub-vectors and P-part codewords: eps = 256 units of
+// 2^-24 R^2 when the marks (2 x 32), the exact distances (2 (G + 2)) and a
+// screen with F = 3 (2 x 3 (P G + 3)) fit in it, else 512 units
+template <int G, int P>
+constexpr float eps_scale() {
+    return 2 * 32 + 2 * (G + 2) + 2 * 3 * (P * G + 3) <= 256 ? 1.52587890625e-05f   // 2^-16
+                                                              : 3.0517578125e-05f;  // 2^-15
+}
 constexpr uint16_t kRescore = 0x100;
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -504,7 +512,7 @@ encode_kernel(EncodeArgs a) {
             const bool holder = __float_as_uint(own) == __float_as_uint(m1);
             // hardware square root (within 1 ulp): the slack covers it
             const float rad = __builtin_amdgcn_sqrtf(xn2) * (1.f + 1e-5f) + max_norm;
-            const float eps = kEpsScale * rad * rad;
+            const float eps = eps_scale<G, P>() * rad * rad;
             const bool unique = (m2 - m1) > eps;
             // the token's code, or the re-score mark, goes to this wave's row
             // of the LDS code array, written by one lane: the holder when the
