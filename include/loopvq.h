@@ -201,7 +201,8 @@ lvq_status lvq_cache_layout(const lvq_config *cfg, lvq_layout *out);
  *            stride a multiple of cg.
  * codebook   device, cfg->codebook_dtype, layout above, 16-byte aligned (one
  *            call encodes one tensor: call once with the K codebook and once
- *            with the V one)
+ *            with the V one); entries finite and below 2^127 in magnitude
+ *            (the screen holds -2c)
  * index_cache device uint8 [B][Hk][max_tokens][S], 4-byte aligned; rows
  *            [first_token, first_token + n_tokens) of sequence seq are written
  * n_tokens   may be 0 (nothing launched)

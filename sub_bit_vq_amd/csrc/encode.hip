@@ -560,26 +560,16 @@ encode_kernel(EncodeArgs a) {
     // also waits for the stores)
     __syncthreads();
 
-    // Exact re-score of the marked rows (rare): the code array is dead, so
-    // the workgroup stages its codebooks in LDS again (one coalesced pass
-    // for the 4 sub-vectors) and each lane takes its codewords from there.
-    // Every lane scores 4 codes k = lane + 64 r, then the wave takes the
-    // lowest index of the smallest distance; the mark words (in registers)
-    // say which rows.
-    if (__syncthreads_or(mtiles != 0)) {               // workgroup-uniform
-        stage_codebooks();
-        __syncthreads();
-        if (mtiles != 0) {                             // wave-uniform
-            float cf[4][G];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int i = 0; i < G; ++i) cf[r][i] = to_f(cbs[(wave * 256 + lane + 64 * r) * G + i]);
-            while (mtiles != 0) {                      // wave-uniform
-              const int tt = (int)__builtin_ctzll(mtiles);
-              mtiles &= mtiles - 1;
-              uint32_t marked = (uint32_t)__builtin_amdgcn_readlane((int)mword, tt);
-              while (marked != 0) {                    // wave-uniform
+    // Exact re-score of the marked rows (rare).  Every lane scores 4 codes
+    // (cf[r] = code kr(r), ascending in r), then the wave takes the lowest
+    // index of the smallest distance; the mark words (in registers) say which
+    // rows.
+    auto rescore = [&](const float (&cf)[4][G], auto kr) {
+        while (mtiles != 0) {                          // wave-uniform
+            const int tt = (int)__builtin_ctzll(mtiles);
+            mtiles &= mtiles - 1;
+            uint32_t marked = (uint32_t)__builtin_amdgcn_readlane((int)mword, tt);
+            while (marked != 0) {                      // wave-uniform
                 const int rq = tt * kTile + (int)__builtin_ctz(marked);
                 marked &= marked - 1;
                 const uint16_t *xr = xh + (tok0 + rq) * a.sx_tok + (int64_t)j * CG;
@@ -602,14 +592,61 @@ encode_kernel(EncodeArgs a) {
                     }
                     if (dist < best) {
                         best = dist;
-                        bk = lane + 64 * r;
+                        bk = kr(r);
                     }
                 }
                 // distances are >= 0, so their bit patterns order like them
                 const uint32_t dmin = wave_min_u32(__float_as_uint(best));
                 const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
                 if (lane == 0) out_rows[(size_t)rq * a.S + wave] = (uint8_t)kmin;
-              }
+            }
+        }
+    };
+    if constexpr (P == 1) {
+        // bf16 codebooks: the wave's MFMA operands still hold -2c (exact) for
+        // all 256 codes, lane (col, hf) entries kk = ch*KC + hf*KL + e of
+        // codes 32 blk + col.  One lane swap per operand word pairs blocks b
+        // and b + 4: afterwards lane (col, hf) holds every entry of code
+        // 32 (b + 4 hf) + col (its first KL of each K chunk in the first
+        // result, the next KL in the second), so no codebook is read again
+        // and no barrier is needed.  c = -0.5 (-2c) is exact.
+        if (mtiles != 0) {                             // wave-uniform
+            float cf[4][G];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+                    for (int w = 0; w < KL / 2; ++w) {
+                        const auto r = __builtin_amdgcn_permlane32_swap(afrag[b][ch][w], afrag[b + 4][ch][w],
+                                                                        false, false);
+#pragma unroll
+                        for (int q = 0; q < 2; ++q)
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const int i = ch * KC + q * KL + 2 * w + h2;
+                                const uint32_t word = q ? r[1] : r[0];
+                                if (i < G)
+                                    cf[b][i] = -0.5f * __uint_as_float(h2 ? (word & 0xffff0000u) : (word << 16));
+                            }
+                    }
+            rescore(cf, [&](int r) { return 32 * (r + 4 * hf) + col; });
+        }
+    } else {
+        // fp32 codebooks (three bf16 parts in the operands): the code array
+        // is dead, so the workgroup stages its codebooks in LDS again (one
+        // coalesced pass for the 4 sub-vectors) and lane l takes codes
+        // l + 64 r from there.
+        if (__syncthreads_or(mtiles != 0)) {           // workgroup-uniform
+            stage_codebooks();
+            __syncthreads();
+            if (mtiles != 0) {                         // wave-uniform
+                float cf[4][G];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int i = 0; i < G; ++i) cf[r][i] = to_f(cbs[(wave * 256 + lane + 64 * r) * G + i]);
+                rescore(cf, [&](int r) { return lane + 64 * r; });
             }
         }
     }
