@@ -542,29 +542,26 @@ encode_kernel(EncodeArgs a) {
     // The chunk's index rows: each token's kJW codes (sub-vectors j0 ..
     // j0 + kJW - 1, one 32-bit word of its row) in one 4-byte store.  The
     // workgroups that fill the other words of these rows run alongside on the
-    // same XCD, so the rows reach memory whole.  Rows marked for the exact
-    // re-score get their byte again below.
+    // same XCD, so the rows reach memory whole.
     static_assert(kMarkWords <= 64, "one mark word per lane");
     const int ntiles = (ntok + kTile - 1) / kTile;
-    const uint32_t mword = lane < ntiles ? marks[lane] : 0u;
+    const uint32_t mword = lane < ntiles ? marks[lane] : 0u;   // this wave's marks
     uint64_t mtiles = __ballot(mword != 0u);
-    __syncthreads();
     uint8_t *out_rows = idxout + (((size_t)a.seq * a.H + h) * a.t_max + a.first_token + tok0) * a.S + j0;
-    for (int t = tid; t < ntok; t += kThreads) {
-        uint32_t w = 0;
+    auto write_rows = [&]() {
+        for (int t = tid; t < ntok; t += kThreads) {
+            uint32_t w = 0;
 #pragma unroll
-        for (int q = 0; q < kJW; ++q) w |= (uint32_t)(row_code[q][t] & 0xffu) << (8 * q);
-        *reinterpret_cast<uint32_t *>(out_rows + (size_t)t * a.S) = w;
-    }
-    // (the words are written before any re-scored byte of them: the barrier
-    // also waits for the stores)
-    __syncthreads();
+            for (int q = 0; q < kJW; ++q) w |= (uint32_t)(row_code[q][t] & 0xffu) << (8 * q);
+            *reinterpret_cast<uint32_t *>(out_rows + (size_t)t * a.S) = w;
+        }
+    };
 
     // Exact re-score of the marked rows (rare).  Every lane scores 4 codes
     // (cf[r] = code kr(r), ascending in r), then the wave takes the lowest
-    // index of the smallest distance; the mark words (in registers) say which
-    // rows.
-    auto rescore = [&](const float (&cf)[4][G], auto kr) {
+    // index of the smallest distance and put(row, code) records it; the mark
+    // words (in registers) say which rows.
+    auto rescore = [&](const float (&cf)[4][G], auto kr, auto put) {
         while (mtiles != 0) {                          // wave-uniform
             const int tt = (int)__builtin_ctzll(mtiles);
             mtiles &= mtiles - 1;
@@ -598,7 +595,7 @@ encode_kernel(EncodeArgs a) {
                 // distances are >= 0, so their bit patterns order like them
                 const uint32_t dmin = wave_min_u32(__float_as_uint(best));
                 const uint32_t kmin = wave_min_u32(__float_as_uint(best) == dmin ? (uint32_t)bk : 256u);
-                if (lane == 0) out_rows[(size_t)rq * a.S + wave] = (uint8_t)kmin;
+                put(rq, kmin);
             }
         }
     };
@@ -608,8 +605,9 @@ encode_kernel(EncodeArgs a) {
         // codes 32 blk + col.  One lane swap per operand word pairs blocks b
         // and b + 4: afterwards lane (col, hf) holds every entry of code
         // 32 (b + 4 hf) + col (its first KL of each K chunk in the first
-        // result, the next KL in the second), so no codebook is read again
-        // and no barrier is needed.  c = -0.5 (-2c) is exact.
+        // result, the next KL in the second), so no codebook is read again.
+        // c = -0.5 (-2c) is exact.  The exact code replaces the mark in the
+        // wave's row of the LDS code array, so each row is written once.
         if (mtiles != 0) {                             // wave-uniform
             float cf[4][G];
 #pragma unroll
@@ -630,13 +628,23 @@ encode_kernel(EncodeArgs a) {
                                     cf[b][i] = -0.5f * __uint_as_float(h2 ? (word & 0xffff0000u) : (word << 16));
                             }
                     }
-            rescore(cf, [&](int r) { return 32 * (r + 4 * hf) + col; });
+            rescore(cf, [&](int r) { return 32 * (r + 4 * hf) + col; },
+                    [&](int rq, uint32_t k) {
+                        if (lane == 0) codes[rq] = (uint16_t)k;
+                    });
         }
+        __syncthreads();
+        write_rows();
     } else {
+        __syncthreads();
+        write_rows();                                  // marked rows hold a placeholder byte
+        // (the words are written before any re-scored byte of them: the
+        // barrier also waits for the stores)
+        __syncthreads();
         // fp32 codebooks (three bf16 parts in the operands): the code array
         // is dead, so the workgroup stages its codebooks in LDS again (one
         // coalesced pass for the 4 sub-vectors) and lane l takes codes
-        // l + 64 r from there.
+        // l + 64 r from there; the re-scored byte replaces the placeholder.
         if (__syncthreads_or(mtiles != 0)) {           // workgroup-uniform
             stage_codebooks();
             __syncthreads();
@@ -646,7 +654,10 @@ encode_kernel(EncodeArgs a) {
                 for (int r = 0; r < 4; ++r)
 #pragma unroll
                     for (int i = 0; i < G; ++i) cf[r][i] = to_f(cbs[(wave * 256 + lane + 64 * r) * G + i]);
-                rescore(cf, [&](int r) { return lane + 64 * r; });
+                rescore(cf, [&](int r) { return lane + 64 * r; },
+                        [&](int rq, uint32_t k) {
+                            if (lane == 0) out_rows[(size_t)rq * a.S + wave] = (uint8_t)k;
+                        });
             }
         }
     }
