@@ -47,12 +47,14 @@
 // the sum of these, so the screen winner is the exact winner.  eps is
 // 2^-16 R^2 where that still holds for F up to 3 or more (4.1 at G = 16 and
 // 7.8 at G = 8 with P = 1, 3.2 at G = 8 with P = 3), else 2^-15 R^2 (5.4 at
-// G = 32 with P = 1, 4.0 at G = 16 with P = 3).  (Where the group and the chain of a lane's smallest value
-// would name different codes, two of its values are within a few marks of
-// each other, so the test fails.)  Otherwise the wave re-scores all 256 codes
-// of that sub-vector exactly as defined above from the codebook (64 lanes x 4
-// codes, strict < per lane in ascending k, then a lowest-index argmin across
-// lanes), which reproduces the definition bit for bit.
+// G = 32 with P = 1, 4.0 at G = 16 with P = 3).  (Where the group and the
+// chain of a lane's smallest value would name different codes, two of its
+// values are within a few marks of each other, so the test fails.)
+// Otherwise the wave re-scores all 256 codes of that sub-vector exactly as
+// defined above (64 lanes x 4 codes, strict < per lane in ascending k, then a
+// lowest-index argmin across lanes), which reproduces the definition bit for
+// bit; with bf16 codebooks the codewords come from the wave's MFMA operands
+// (-2c, exact), with fp32 codebooks from the codebooks staged in LDS again.
 #include "kernels.h"
 
 #include <math.h>
