@@ -320,13 +320,23 @@ encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int e = 0; e < KL; e += 2) {
                 uint32_t wv = 0;
+                if constexpr (P == 1) {
+                    // bf16 codebooks: -2c is a bf16 value, the upper half of
+                    // the fp32 product (entries kk, kk + 1 in one word)
+                    static_assert(sizeof(CB) == 2, "one part: bf16 codebooks");
+                    const int kk = ch * KC + hf * KL + e;
+                    const uint32_t pr = *reinterpret_cast<const uint32_t *>(cw + kk % G);
+                    const uint32_t u0 = __float_as_uint(-2.f * __uint_as_float(pr << 16));
+                    const uint32_t u1 = __float_as_uint(-2.f * __uint_as_float(pr & 0xffff0000u));
+                    wv = kk < G ? (u0 >> 16) | (u1 & 0xffff0000u) : 0u;
+                } else {
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int kk = ch * KC + hf * KL + e + h2;
-                    const float c = to_f(cw[kk % G]);
-                    const float part = P == 1 ? c : split_part(c, kk / G);
-                    const float v = kk < P * G ? -2.f * part : 0.f;
-                    wv |= (uint32_t)bf16_rne(v) << (16 * h2);
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int kk = ch * KC + hf * KL + e + h2;
+                        const float c = to_f(cw[kk % G]);
+                        const float v = kk < P * G ? -2.f * split_part(c, kk / G) : 0.f;
+                        wv |= (uint32_t)bf16_rne(v) << (16 * h2);
+                    }
                 }
                 afrag[blk][ch][e / 2] = wv;
             }
