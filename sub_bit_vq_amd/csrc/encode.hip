@@ -404,6 +404,9 @@ encode_kernel(EncodeArgs a) {
             // |x|^2 from the lane's words that hold entries i < G (bf16
             // squares are exact; the sum only feeds a bound); the words are the
             // B operand as loaded
+            // (with one part and G a multiple of KC every word holds entries
+            // i < G, so the dot products chain through their accumulator)
+            constexpr bool kAllX = P == 1 && G % KC == 0;
             float xs = 0.f;
 #pragma unroll
             for (int ch = 0; ch < NCH; ++ch) {
@@ -411,8 +414,12 @@ encode_kernel(EncodeArgs a) {
                 for (int q = 0; q < KL / 2; ++q) {
                     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
                     const bf16x2 v = __builtin_bit_cast(bf16x2, cur.w[ch][q]);
-                    const float d = __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.f, false);
-                    xs += (ch * KC + hf * KL + 2 * q < G) ? d : 0.f;
+                    if constexpr (kAllX) {
+                        xs = __builtin_amdgcn_fdot2_f32_bf16(v, v, xs, false);
+                    } else {
+                        const float d = __builtin_amdgcn_fdot2_f32_bf16(v, v, 0.f, false);
+                        xs += (ch * KC + hf * KL + 2 * q < G) ? d : 0.f;
+                    }
                 }
             }
             float xa, xb;
