@@ -200,8 +200,17 @@ __device__ __forceinline__ floatx16 mfma_chunk(const uint32_t *aw, const uint32_
 // diagnostic entry point that measures the screen's error; the values, the
 // operands and the instructions that form them are those of the plain
 // instance)
+// Parts the codebooks are staged in: with bf16 codebooks of 32 entries (64
+// KiB for the 4 sub-vectors) two parts of 2, where a part's row pieces are
+// whole 16-byte reads, so that 3 workgroups fit a compute unit's LDS.
+template <int G, int CG, int P, typename CB>
+constexpr int staging_parts() {
+    return P == 1 && G > 16 && (kJW / 2 * CG * (int)sizeof(CB)) % 16 == 0 ? 2 : 1;
+}
+
 template <int G, int CG, int P, typename CB, bool kScreen>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(G * P <= 16 && !kScreen ? 4 : 1))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    kScreen ? 1 : G * P <= 16 ? 4 : staging_parts<G, CG, P, CB>() == 2 ? 3 : 1))) void
 encode_kernel(EncodeArgs a) {
     using Sh = EncShape<G, CG, P, CB>;
     constexpr int NCH = Sh::NCH;
@@ -209,7 +218,10 @@ encode_kernel(EncodeArgs a) {
     // are built; then the same LDS holds, per wave, the code of each chunk
     // row or kRescore (re-score it exactly).  Sharing the space lets more
     // workgroups fit a compute unit.
-    constexpr int kCbBytes = kJW * 256 * G * (int)sizeof(CB);
+    // (each part is read by its waves before the next replaces it)
+    constexpr int kParts = staging_parts<G, CG, P, CB>();
+    constexpr int kJP = kJW / kParts;                             // sub-vectors per part
+    constexpr int kCbBytes = kJP * 256 * G * (int)sizeof(CB);
     constexpr int kCodeBytes = kJW * kTokChunk * 2;
     constexpr int kMarkWords = kTokChunk / 32;                    // one word per 32-token tile
     constexpr int kMarkBytes = kJW * kMarkWords * 4;
@@ -244,14 +256,18 @@ encode_kernel(EncodeArgs a) {
     const int64_t tok_end = min(tok0 + kTokChunk, a.n_tokens);
     const int col = lane & 31, hf = lane >> 5;
 
-    // stage the 4 codebooks: chunk c of row (t, k) piece p -> entries (jl, c) of slice t
-    auto stage_codebooks = [&]() {
+    // stage the codebooks of part `part` (sub-vectors part*kJP .. + kJP - 1):
+    // chunk c of row (t, k) piece p -> entries (jl, c) of slice t, jl counted
+    // from the part's first sub-vector
+    auto stage_codebooks = [&](int part) {
         const char *src = static_cast<const char *>(cbin);
-        constexpr int PER_ROW = Sh::ROWB / 16;
+        constexpr int PER_ROW = Sh::ROWB / 16 / kParts;            // pieces of a part's row
+        static_assert(PER_ROW * 16 * kParts == Sh::ROWB && (Sh::CHUNKS / kParts) % kThreads == 0,
+                      "parts of whole 16-byte pieces");
 #pragma unroll
-        for (int u = 0; u < Sh::CHUNKS / kThreads; ++u) {
+        for (int u = 0; u < Sh::CHUNKS / kParts / kThreads; ++u) {
             const int c = tid + u * kThreads;
-            const int r = c / PER_ROW, pc = c % PER_ROW;
+            const int r = c / PER_ROW, pc = part * PER_ROW + c % PER_ROW;
             const int t = r >> 8, k = r & 255;
             const size_t off = ((((size_t)t * a.H + h) * 256 + k) * a.S + j0) * (CG * Sh::EB) + pc * 16;
             const uint4 v = *reinterpret_cast<const uint4 *>(src + off);
@@ -263,7 +279,7 @@ encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int q = 0; q < 16 / RUN; ++q) {
                 const int fe = pc * Sh::EC + q * (RUN / Sh::EB);      // first element of the run
-                const int jl = fe / CG, cc = fe % CG;
+                const int jl = fe / CG - part * kJP, cc = fe % CG;
                 CB *dst = cbs + (jl * 256 + k) * G + t * CG + cc;
                 if constexpr (RUN == 16)
                     *reinterpret_cast<uint4 *>(dst) = v;
@@ -274,27 +290,70 @@ encode_kernel(EncodeArgs a) {
             }
         }
     };
-    stage_codebooks();
-    __syncthreads();
-    // squared norms (fp64 sum, rounded once); the max over the wave's codes
+    constexpr int KL = Sh::KL, KC = Sh::KC, LE = Sh::LE, NLD = Sh::NLD;
+    uint32_t afrag[8][NCH][KL / 2];
 #pragma unroll
-    for (int m = 0; m < kJW; ++m) {
-        // the code's G entries as 16-byte reads (rows are 16-byte aligned)
-        const uint4 *cw = reinterpret_cast<const uint4 *>(cbs + (m * 256 + tid) * G);
-        double s = 0.0;
+    for (int part = 0; part < kParts; ++part) {
+        stage_codebooks(part);
+        __syncthreads();
+        // squared norms of the part's codes (fp64 sum, rounded once)
 #pragma unroll
-        for (int c = 0; c < G * Sh::EB / 16; ++c) {
-            const uint4 w = cw[c];
-            const CB *e = reinterpret_cast<const CB *>(&w);
+        for (int m = 0; m < kJP; ++m) {
+            // the code's G entries as 16-byte reads (rows are 16-byte aligned)
+            const uint4 *cw = reinterpret_cast<const uint4 *>(cbs + (m * 256 + tid) * G);
+            double s = 0.0;
 #pragma unroll
-            for (int i = 0; i < Sh::EC; ++i) {
-                const double v = to_f(e[i]);
-                s += v * v;
+            for (int c = 0; c < G * Sh::EB / 16; ++c) {
+                const uint4 w = cw[c];
+                const CB *e = reinterpret_cast<const CB *>(&w);
+#pragma unroll
+                for (int i = 0; i < Sh::EC; ++i) {
+                    const double v = to_f(e[i]);
+                    s += v * v;
+                }
+            }
+            nrm[(part * kJP + m) * 256 + tid] = (float)s;
+        }
+        if (wave / kJP == part) {                       // wave-uniform
+            const CB *mycb = cbs + (wave - part * kJP) * 256 * G;
+            // this wave's codebook as MFMA A operands: lane (col, hf) holds entries
+            // kk = ch*KC + hf*KL + e of code blk*32 + col, two bf16 a word (hf enters
+            // only the LDS address and the selects, so the wave builds them without
+            // divergent branches)
+#pragma unroll
+            for (int blk = 0; blk < 8; ++blk) {
+                const int code = blk * 32 + col;
+                const CB *cw = mycb + code * G;
+#pragma unroll
+                for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+                    for (int e = 0; e < KL; e += 2) {
+                        uint32_t wv = 0;
+                        if constexpr (P == 1) {
+                            // bf16 codebooks: -2c is a bf16 value, the upper half of
+                            // the fp32 product (entries kk, kk + 1 in one word)
+                            static_assert(sizeof(CB) == 2, "one part: bf16 codebooks");
+                            const int kk = ch * KC + hf * KL + e;
+                            const uint32_t pr = *reinterpret_cast<const uint32_t *>(cw + kk % G);
+                            const uint32_t u0 = __float_as_uint(-2.f * __uint_as_float(pr << 16));
+                            const uint32_t u1 = __float_as_uint(-2.f * __uint_as_float(pr & 0xffff0000u));
+                            wv = kk < G ? (u0 >> 16) | (u1 & 0xffff0000u) : 0u;
+                        } else {
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const int kk = ch * KC + hf * KL + e + h2;
+                                const float c = to_f(cw[kk % G]);
+                                const float v = kk < P * G ? -2.f * split_part(c, kk / G) : 0.f;
+                                wv |= (uint32_t)bf16_rne(v) << (16 * h2);
+                            }
+                        }
+                        afrag[blk][ch][e / 2] = wv;
+                    }
+                }
             }
         }
-        nrm[m * 256 + tid] = (float)s;
+        __syncthreads();                                // the part's codebooks are dead
     }
-    __syncthreads();
     // (S is a multiple of kJW, so every wave has a sub-vector j < S)
     float max_norm2 = 0.f;
 #pragma unroll
@@ -303,49 +362,9 @@ encode_kernel(EncodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) max_norm2 = fmaxf(max_norm2, __shfl_xor(max_norm2, off));
     // upper bound of max_k |c_k| (slack covers the rounding of the norm)
     const float max_norm = sqrtf(max_norm2) * (1.f + 1e-5f);
-
-    // this wave's codebook as MFMA A operands: lane (col, hf) holds entries
-    // kk = ch*KC + hf*KL + e of code blk*32 + col, two bf16 a word (hf enters
-    // only the LDS address and the selects, so the wave builds them without
-    // divergent branches)
-    constexpr int KL = Sh::KL, KC = Sh::KC, LE = Sh::LE, NLD = Sh::NLD;
-    const CB *mycb = cbs + wave * 256 * G;
-    uint32_t afrag[8][NCH][KL / 2];
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-        const int code = blk * 32 + col;
-        const CB *cw = mycb + code * G;
-#pragma unroll
-        for (int ch = 0; ch < NCH; ++ch) {
-#pragma unroll
-            for (int e = 0; e < KL; e += 2) {
-                uint32_t wv = 0;
-                if constexpr (P == 1) {
-                    // bf16 codebooks: -2c is a bf16 value, the upper half of
-                    // the fp32 product (entries kk, kk + 1 in one word)
-                    static_assert(sizeof(CB) == 2, "one part: bf16 codebooks");
-                    const int kk = ch * KC + hf * KL + e;
-                    const uint32_t pr = *reinterpret_cast<const uint32_t *>(cw + kk % G);
-                    const uint32_t u0 = __float_as_uint(-2.f * __uint_as_float(pr << 16));
-                    const uint32_t u1 = __float_as_uint(-2.f * __uint_as_float(pr & 0xffff0000u));
-                    wv = kk < G ? (u0 >> 16) | (u1 & 0xffff0000u) : 0u;
-                } else {
-#pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const int kk = ch * KC + hf * KL + e + h2;
-                        const float c = to_f(cw[kk % G]);
-                        const float v = kk < P * G ? -2.f * split_part(c, kk / G) : 0.f;
-                        wv |= (uint32_t)bf16_rne(v) << (16 * h2);
-                    }
-                }
-                afrag[blk][ch][e / 2] = wv;
-            }
-        }
-    }
     // the accumulator of block blk starts at the squared norms of the lane's
     // 16 codes blk*32 + 8 q + 4 hf + i, q, i < 4 (the same for every token)
     const float *bias_row = nrm + wave * 256 + hf * 4;
-    __syncthreads();                                  // the staged codebooks are dead
 
     // per-lane x offsets (bytes from the tile base) of the loads that fill the
     // lane's B words: load s of chunk ch holds entries kk = ch*KC + hf*KL +
@@ -665,7 +684,7 @@ encode_kernel(EncodeArgs a) {
         // coalesced pass for the 4 sub-vectors) and lane l takes codes
         // l + 64 r from there; the re-scored byte replaces the placeholder.
         if (__syncthreads_or(mtiles != 0)) {           // workgroup-uniform
-            stage_codebooks();
+            stage_codebooks(0);
             __syncthreads();
             if (mtiles != 0) {                         // wave-uniform
                 float cf[4][G];
