@@ -196,10 +196,6 @@ __device__ __forceinline__ floatx16 mfma_chunk(const uint32_t *aw, const uint32_
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc, 0, 0, 0);
 }
 
-// kScreen: also store every unmarked screen value to a.screen (the
-// diagnostic entry point that measures the screen's error; the values, the
-// operands and the instructions that form them are those of the plain
-// instance)
 // Parts the codebooks are staged in: with bf16 codebooks of 32 entries (64
 // KiB for the 4 sub-vectors) two parts of 2, where a part's row pieces are
 // whole 16-byte reads, so that 3 workgroups fit a compute unit's LDS.
@@ -208,6 +204,10 @@ constexpr int staging_parts() {
     return P == 1 && G > 16 && (kJW / 2 * CG * (int)sizeof(CB)) % 16 == 0 ? 2 : 1;
 }
 
+// kScreen: also store every unmarked screen value to a.screen (the
+// diagnostic entry point that measures the screen's error; the values, the
+// operands and the instructions that form them are those of the plain
+// instance)
 template <int G, int CG, int P, typename CB, bool kScreen>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     kScreen ? 1 : G * P <= 16 ? 4 : staging_parts<G, CG, P, CB>() == 2 ? 3 : 1))) void
@@ -217,8 +217,8 @@ encode_kernel(EncodeArgs a) {
     // The staged codebooks [jl][k][i] are read only until the MFMA operands
     // are built; then the same LDS holds, per wave, the code of each chunk
     // row or kRescore (re-score it exactly).  Sharing the space lets more
-    // workgroups fit a compute unit.
-    // (each part is read by its waves before the next replaces it)
+    // workgroups fit a compute unit.  Each staged part is read by its waves
+    // before the next replaces it.
     constexpr int kParts = staging_parts<G, CG, P, CB>();
     constexpr int kJP = kJW / kParts;                             // sub-vectors per part
     constexpr int kCbBytes = kJP * 256 * G * (int)sizeof(CB);
